@@ -1,0 +1,262 @@
+/*
+ * CPU oracle for one SwitchGLU MoE layer over 4-bit affine, group-64 expert
+ * weights.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
+ * benchmark's CPU-baseline leg use it; the product path never does.  It shares
+ * no code with the GPU library.
+ *
+ * What it computes (sources are the web pages this build follows):
+ *
+ *  - SwitchGLU per (token, expert) pair, in the order up, gate,
+ *    silu(gate) * up, down -- mlx issue "gather_qmm at M=1 streams 4-bit expert
+ *    weights at ~half the bandwidth of M=4", its moe_bench script (function
+ *    moe).  silu(v) = v * sigmoid(v) = v / (1 + exp(-v)).
+ *  - Each (token, expert) pair is evaluated on its own, the per-pair gather
+ *    semantics described on the page "MoE GatherQMM small-M verify cost"
+ *    (Facts, the gather_qmv bullets).
+ *  - Dequantization is affine: w = scale * q + bias with one bf16 (scale, bias)
+ *    pair per 64 consecutive inputs (the issue above, "Numbers": mx.quantize
+ *    with group 64, affine, bits 4).
+ *  - Storage reading (not fixed by the pages): element c of an output row is
+ *    nibble c % 8 of word c / 8, lowest nibble first.
+ *  - Router-weighted combine out[t] = sum_j w[t, j] * y[t, j] (the pages'
+ *    SwitchGLU returns per-pair outputs; the weighted sum is the plain MoE
+ *    combine this layer adds, applied after the down projection).
+ *  - Union evaluation: the union of routed experts over the L tokens, each
+ *    unique expert's weights applied once to the tokens routed to it -- mlx
+ *    discussion "Small-L fused expert gather for fine-grained MoE decode",
+ *    implication 1 of "The data" section.
+ *
+ * Precision: every step in IEEE double.  bf16 inputs widen exactly; q, scale
+ * and bias products are exact in double; dot products accumulate in ascending
+ * index order.  No -ffast-math.
+ *
+ * Threading: OpenMP splits independent output elements (pairs x rows) across
+ * threads; no reduction is split, so results do not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_OK 0
+#define ORC_EINVAL 1
+#define ORC_ENOMEM 2
+
+static double bf16_to_double(uint16_t h) {
+    uint32_t bits = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* 4-bit code of input element c in a packed row. */
+static unsigned code_at(const uint32_t *row_words, long c) {
+    return (row_words[c / 8] >> (4 * (c % 8))) & 0xFu;
+}
+
+/* Dequantized weight at (row, c) of a matrix with K inputs per row. */
+static double weight_at(const uint32_t *W, const uint16_t *S, const uint16_t *B, long row, long K, long c) {
+    long g = row * (K / 64) + c / 64;
+    return bf16_to_double(S[g]) * (double)code_at(W + row * (K / 8), c) + bf16_to_double(B[g]);
+}
+
+static double silu(double v) { return v / (1.0 + exp(-v)); }
+
+int oracle_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* Dense dequantized copy of `rows` rows with K inputs each: out[r * K + c]. */
+int oracle_dequant(const uint32_t *W, const uint16_t *S, const uint16_t *B, long rows, long K, double *out) {
+    if (!W || !S || !B || !out || rows < 0 || K <= 0 || K % 64) return ORC_EINVAL;
+    for (long r = 0; r < rows; ++r)
+        for (long c = 0; c < K; ++c) out[r * K + c] = weight_at(W, S, B, r, K, c);
+    return ORC_OK;
+}
+
+typedef struct {
+    const uint32_t *wg; const uint16_t *sg; const uint16_t *bg;
+    const uint32_t *wu; const uint16_t *su; const uint16_t *bu;
+    const uint32_t *wd; const uint16_t *sd; const uint16_t *bd;
+} bank_t;
+
+/* Hidden activation of one (token, expert) pair: h[n] = silu(gate[n]) * up[n]. */
+static double pair_hidden_row(const bank_t *bk, const uint16_t *xrow, long e, long H, long I, long n) {
+    long row = e * I + n;
+    double g = 0.0, u = 0.0;
+    for (long c = 0; c < H; ++c) {
+        double xc = bf16_to_double(xrow[c]);
+        u += xc * weight_at(bk->wu, bk->su, bk->bu, row, H, c);
+        g += xc * weight_at(bk->wg, bk->sg, bk->bg, row, H, c);
+    }
+    return silu(g) * u;
+}
+
+/* Down projection of one pair's hidden vector: y[m] = sum_n h[n] * Wd[e, m, n]. */
+static double pair_down_row(const bank_t *bk, const double *h, long e, long H, long I, long m) {
+    long row = e * H + m;
+    double y = 0.0;
+    for (long n = 0; n < I; ++n) y += h[n] * weight_at(bk->wd, bk->sd, bk->bd, row, I, n);
+    return y;
+}
+
+static int check_shapes(const int32_t *ids, long L, long k, long E, long H, long I) {
+    if (L < 0 || k <= 0 || E <= 0 || H <= 0 || I <= 0 || H % 64 || I % 64) return ORC_EINVAL;
+    for (long p = 0; p < L * k; ++p)
+        if (ids[p] < 0 || ids[p] >= E) return ORC_EINVAL;
+    return ORC_OK;
+}
+
+/*
+ * Per-pair evaluation.  x bf16 [L, H]; ids int32 [L, k]; tw fp32 [L, k];
+ * banks as packed uint32 codes plus bf16 scale/bias (gate/up [E, I, .], down
+ * [E, H, .]).  Writes out[L, H] (double).  If h_out is not NULL it also gets
+ * every pair's hidden vector, h_out[(t * k + j) * I + n]; if y_out is not NULL,
+ * every pair's down output y_out[(t * k + j) * H + m].
+ */
+int oracle_forward_pairs(const uint16_t *x, const int32_t *ids, const float *tw,
+                         long L, long k, long E, long H, long I,
+                         const uint32_t *wg, const uint16_t *sg, const uint16_t *bg,
+                         const uint32_t *wu, const uint16_t *su, const uint16_t *bu,
+                         const uint32_t *wd, const uint16_t *sd, const uint16_t *bd,
+                         double *out, double *h_out, double *y_out) {
+    if (!out || (L > 0 && (!x || !ids || !tw))) return ORC_EINVAL;
+    int st = check_shapes(ids, L, k, E, H, I);
+    if (st) return st;
+    bank_t bk = {wg, sg, bg, wu, su, bu, wd, sd, bd};
+    long P = L * k;
+    double *h = (double *)malloc(sizeof(double) * (size_t)(P > 0 ? P : 1) * (size_t)I);
+    double *y = (double *)malloc(sizeof(double) * (size_t)(P > 0 ? P : 1) * (size_t)H);
+    if (!h || !y) { free(h); free(y); return ORC_ENOMEM; }
+
+    /* gate, up, silu(gate) * up for every pair and hidden row */
+#pragma omp parallel for schedule(dynamic, 16)
+    for (long pn = 0; pn < P * I; ++pn) {
+        long p = pn / I, n = pn % I;
+        h[pn] = pair_hidden_row(&bk, x + (p / k) * H, ids[p], H, I, n);
+    }
+    /* down projection for every pair and output row */
+#pragma omp parallel for schedule(dynamic, 16)
+    for (long pm = 0; pm < P * H; ++pm) {
+        long p = pm / H, m = pm % H;
+        y[pm] = pair_down_row(&bk, h + p * I, ids[p], H, I, m);
+    }
+    /* router-weighted combine, ascending slot order */
+    for (long t = 0; t < L; ++t)
+        for (long m = 0; m < H; ++m) {
+            double acc = 0.0;
+            for (long j = 0; j < k; ++j) acc += (double)tw[t * k + j] * y[(t * k + j) * H + m];
+            out[t * H + m] = acc;
+        }
+    if (h_out) memcpy(h_out, h, sizeof(double) * (size_t)P * (size_t)I);
+    if (y_out) memcpy(y_out, y, sizeof(double) * (size_t)P * (size_t)H);
+    free(h);
+    free(y);
+    return ORC_OK;
+}
+
+/*
+ * Union evaluation: the distinct experts of all L * k routes, ascending; each
+ * one's hidden and down vectors computed once per token routed to it, then
+ * added with that token's summed router weight for the expert.  Same
+ * arguments and output as oracle_forward_pairs.
+ */
+int oracle_forward_union(const uint16_t *x, const int32_t *ids, const float *tw,
+                         long L, long k, long E, long H, long I,
+                         const uint32_t *wg, const uint16_t *sg, const uint16_t *bg,
+                         const uint32_t *wu, const uint16_t *su, const uint16_t *bu,
+                         const uint32_t *wd, const uint16_t *sd, const uint16_t *bd,
+                         double *out) {
+    if (!out || (L > 0 && (!x || !ids || !tw))) return ORC_EINVAL;
+    int st = check_shapes(ids, L, k, E, H, I);
+    if (st) return st;
+    bank_t bk = {wg, sg, bg, wu, su, bu, wd, sd, bd};
+    long P = L * k;
+
+    /* distinct expert ids, ascending (insertion into a sorted list) */
+    long *uniq = (long *)malloc(sizeof(long) * (size_t)(P > 0 ? P : 1));
+    long u = 0;
+    for (long p = 0; p < P; ++p) {
+        long e = ids[p], pos = 0;
+        while (pos < u && uniq[pos] < e) ++pos;
+        if (pos < u && uniq[pos] == e) continue;
+        for (long q = u; q > pos; --q) uniq[q] = uniq[q - 1];
+        uniq[pos] = e;
+        ++u;
+    }
+    /* (unique expert, token) pairs that carry weight, with that weight */
+    long *pe = (long *)malloc(sizeof(long) * (size_t)(P > 0 ? P : 1));
+    long *pt = (long *)malloc(sizeof(long) * (size_t)(P > 0 ? P : 1));
+    double *pw = (double *)malloc(sizeof(double) * (size_t)(P > 0 ? P : 1));
+    long np = 0;
+    for (long i = 0; i < u; ++i)
+        for (long t = 0; t < L; ++t) {
+            double wsum = 0.0;
+            int hit = 0;
+            for (long j = 0; j < k; ++j)
+                if (ids[t * k + j] == uniq[i]) { wsum += (double)tw[t * k + j]; hit = 1; }
+            if (hit) { pe[np] = uniq[i]; pt[np] = t; pw[np] = wsum; ++np; }
+        }
+    double *h = (double *)malloc(sizeof(double) * (size_t)(np > 0 ? np : 1) * (size_t)I);
+    double *y = (double *)malloc(sizeof(double) * (size_t)(np > 0 ? np : 1) * (size_t)H);
+    if (!uniq || !pe || !pt || !pw || !h || !y) {
+        free(uniq); free(pe); free(pt); free(pw); free(h); free(y);
+        return ORC_ENOMEM;
+    }
+#pragma omp parallel for schedule(dynamic, 16)
+    for (long qn = 0; qn < np * I; ++qn) {
+        long q = qn / I, n = qn % I;
+        h[qn] = pair_hidden_row(&bk, x + pt[q] * H, pe[q], H, I, n);
+    }
+#pragma omp parallel for schedule(dynamic, 16)
+    for (long qm = 0; qm < np * H; ++qm) {
+        long q = qm / H, m = qm % H;
+        y[qm] = pair_down_row(&bk, h + q * I, pe[q], H, I, m);
+    }
+    for (long i = 0; i < L * H; ++i) out[i] = 0.0;
+    for (long q = 0; q < np; ++q)
+        for (long m = 0; m < H; ++m) out[pt[q] * H + m] += pw[q] * y[q * H + m];
+    free(uniq); free(pe); free(pt); free(pw); free(h); free(y);
+    return ORC_OK;
+}
+
+/*
+ * One output element computed on its own: out[t, m] for token t and output
+ * row m, per-pair evaluation.  Lets tests sample single outputs of full-size
+ * layers.  Returns NAN on invalid arguments.
+ */
+double oracle_output_element(const uint16_t *x, const int32_t *ids, const float *tw,
+                             long L, long k, long E, long H, long I,
+                             const uint32_t *wg, const uint16_t *sg, const uint16_t *bg,
+                             const uint32_t *wu, const uint16_t *su, const uint16_t *bu,
+                             const uint32_t *wd, const uint16_t *sd, const uint16_t *bd,
+                             long t, long m) {
+    if (t < 0 || t >= L || m < 0 || m >= H || check_shapes(ids, L, k, E, H, I)) return NAN;
+    bank_t bk = {wg, sg, bg, wu, su, bu, wd, sd, bd};
+    double *h = (double *)malloc(sizeof(double) * (size_t)I);
+    if (!h) return NAN;
+    double acc = 0.0;
+    for (long j = 0; j < k; ++j) {
+        long e = ids[t * k + j];
+#pragma omp parallel for schedule(static)
+        for (long n = 0; n < I; ++n) h[n] = pair_hidden_row(&bk, x + t * H, e, H, I, n);
+        acc += (double)tw[t * k + j] * pair_down_row(&bk, h, e, H, I, m);
+    }
+    free(h);
+    return acc;
+}

@@ -1,0 +1,61 @@
+"""Planted mistakes in a copy of the oracle's C source must fail the pins.
+
+Each mutant is a text substitution in a temporary copy of moe_oracle.c, built
+with gcc into a temporary directory; the committed oracle is never modified.
+"""
+
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "moe_oracle.c")
+
+MUTANTS = {
+    "high_nibble_first": ("(4 * (c % 8))", "(4 * (7 - c % 8))"),
+    "bias_dropped": ("* (double)code_at(W + row * (K / 8), c) + bf16_to_double(B[g])",
+                     "* (double)code_at(W + row * (K / 8), c)"),
+    "scale_group_shifted": ("long g = row * (K / 64) + c / 64;", "long g = row * (K / 64) + ((c / 64) + 1) % (K / 64);"),
+    "gate_up_swapped": ("return silu(g) * u;", "return silu(u) * g;"),
+    "router_weight_dropped": ("acc += (double)tw[t * k + j] * y[(t * k + j) * H + m];",
+                              "acc += y[(t * k + j) * H + m];"),
+    "token_index_wrong": ("pair_hidden_row(&bk, x + (p / k) * H, ids[p], H, I, n)",
+                          "pair_hidden_row(&bk, x + (p % L) * H, ids[p], H, I, n)"),
+    "down_uses_wrong_expert": ("y[pm] = pair_down_row(&bk, h + p * I, ids[p], H, I, m);",
+                               "y[pm] = pair_down_row(&bk, h + p * I, ids[(p + 1) % P], H, I, m);"),
+    "silu_wrong": ("return v / (1.0 + exp(-v));", "return v / (1.0 + exp(v));"),
+}
+
+PIN_TESTS = [
+    pins.test_nibble_order_known_pattern,
+    pins.test_scale_bias_roles_and_group_axis,
+    pins.test_dense_swiglu_special_case_matches_library,
+    lambda: pins.test_multi_expert_brute_force_matches_library(0),
+    pins.test_closed_form_saturated_silu_integers,
+    pins.test_gate_goes_through_silu_not_up,
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, name
+    mut = tmp_path / "mutant.c"
+    mut.write_text(src.replace(old, new))
+    so = str(tmp_path / "libmutant.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", so, str(mut), "-lm"], check=True)
+    prev = oracle.use_library(so)
+    failed = []
+    try:
+        for t in PIN_TESTS:
+            try:
+                t()
+            except AssertionError:
+                failed.append(getattr(t, "__name__", "brute_force"))
+    finally:
+        oracle.restore_library(prev)
+    assert failed, f"mutant {name} passed every pin"
