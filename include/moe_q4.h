@@ -1,0 +1,174 @@
+/*
+ * moe_q4.h -- C ABI of the MI355X (gfx950) union-of-experts SwitchGLU library
+ * over 4-bit affine, group-64 expert weights.
+ *
+ * One MoE layer: L tokens, each routed to k of E experts.  For every (token,
+ * expert) route the layer computes the SwitchGLU of that expert -- up and gate
+ * projections of x, h = silu(gate) * up, down projection of h -- and the
+ * tokens' outputs are the router-weighted sums over their k routes.  Sources
+ * (web pages): the SwitchGLU order and the 4-bit affine, group-64 storage come
+ * from the mlx issue "gather_qmm at M=1 streams 4-bit expert weights at ~half
+ * the bandwidth of M=4" (section "Numbers" and its moe_bench script); streaming
+ * each distinct routed expert once for all tokens routed to it comes from the
+ * mlx discussion "Small-L fused expert gather for fine-grained MoE decode"
+ * (implication 1 of the section on adjacent-token overlap); the sorted
+ * grouped path for large token counts and its expert-offset tile schedule come
+ * from the page "MoE GatherQMM small-M verify cost" (Facts: the dispatch
+ * bullets and PR 4567).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor arguments are DEVICE pointers to contiguous row-major arrays
+ *   on the current HIP device.  The caller owns every buffer, including the
+ *   workspace; the library never allocates, frees or synchronises in the
+ *   forward calls, and enqueues all work on `stream` (NULL = default stream).
+ * - Weight storage: element c of an output row is nibble c % 8 of 32-bit word
+ *   c / 8, lowest nibble first; the value is scale * q + bias with q in 0..15
+ *   and one bf16 (scale, bias) pair per 64 consecutive inputs of the row.
+ * - Status codes are plain ints (MOE_Q4_*); nothing throws or aborts across
+ *   the ABI.  Argument errors are detected on the host before any GPU work.
+ * - Expert ids outside [0, E) are a precondition violation: such routes add
+ *   nothing, and the kernels set MOE_Q4_DEV_BAD_ID in the workspace's device
+ *   status word, which every forward call (its gate/up stage) rewrites with
+ *   that call's status (see moe_q4_read_device_status).
+ */
+#ifndef MOE_Q4_H
+#define MOE_Q4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define MOE_Q4_OK 0
+#define MOE_Q4_ERR_NULL 1        /* a required pointer is NULL                              */
+#define MOE_Q4_ERR_SHAPE 2       /* L < 0, k < 1, E < 1, k > E, H or I < 1                    */
+#define MOE_Q4_ERR_UNSUPPORTED 3 /* H or I not a multiple of 64, bits != 4, group != 64,      */
+                                 /* out_dtype unknown, or L / E / L*k beyond the limits below */
+#define MOE_Q4_ERR_ALIGN 4       /* a pointer misses its alignment (see moe_swiglu_q4_forward) */
+#define MOE_Q4_ERR_WORKSPACE 5   /* workspace NULL or smaller than moe_swiglu_q4_workspace_bytes */
+#define MOE_Q4_ERR_LAUNCH 6      /* a HIP launch or runtime call failed                       */
+#define MOE_Q4_ERR_ALIAS 7       /* `out` overlaps an input or the workspace                  */
+
+/* ---- device status bits (status word in the workspace header) ---- */
+#define MOE_Q4_DEV_BAD_ID 1u     /* an expert id outside [0, E) was seen; its routes were dropped */
+
+/* ---- output dtypes ---- */
+#define MOE_Q4_OUT_BF16 0        /* out is bf16 [L, H], fp32 results rounded to nearest even  */
+#define MOE_Q4_OUT_F32 1         /* out is fp32 [L, H] (the values before the bf16 rounding)   */
+
+/* ---- paths (moe_swiglu_q4_select_path) ---- */
+#define MOE_Q4_PATH_NONE 0       /* L == 0: nothing to do                                      */
+#define MOE_Q4_PATH_UNION 1      /* small L: distinct experts streamed once, dequant GEMV       */
+#define MOE_Q4_PATH_SORTED 2     /* large L: expert-sorted pairs, grouped bf16 MFMA GEMM        */
+
+/* ---- limits ---- */
+#define MOE_Q4_UNION_MAX_L 32    /* token masks are 32-bit                                     */
+#define MOE_Q4_MAX_PAIRS 1024    /* L * k on the union path                                    */
+#define MOE_Q4_MAX_E 16384
+
+/* ---- forward stages (moe_swiglu_q4_forward_stages) ---- */
+#define MOE_Q4_STAGE_GATEUP 1u   /* route union + fused gate/up GEMV + silu(gate)*up -> workspace */
+#define MOE_Q4_STAGE_DOWN 2u     /* down GEMV + router-weighted combine -> out                    */
+#define MOE_Q4_STAGE_ALL 3u
+
+/*
+ * Bytes of caller-provided device workspace that moe_swiglu_q4_forward needs
+ * for this shape (0 for L == 0).  Returns 0 and nothing else for invalid
+ * shapes as well; validate with moe_swiglu_q4_select_path.
+ */
+size_t moe_swiglu_q4_workspace_bytes(int L, int k, int E, int H, int I);
+
+/*
+ * Path the forward call takes for this shape (MOE_Q4_PATH_*), or a negative
+ * status (-MOE_Q4_ERR_*) if the shape is invalid or unsupported.  Host only.
+ */
+int moe_swiglu_q4_select_path(int L, int k, int E, int H, int I);
+
+/*
+ * One SwitchGLU MoE layer.
+ *
+ *   x            bf16  [L, H]            activations                  (16-byte aligned)
+ *   topk_ids     int32 [L, k]            expert of each route          (4-byte aligned)
+ *   topk_weights fp32  [L, k]            router weight of each route   (4-byte aligned)
+ *   wg, wu       uint32 [E, I, H/8]      gate / up codes               (16-byte aligned)
+ *   sg, bg, su, bu bf16 [E, I, H/64]     gate / up scale and bias      (4-byte aligned)
+ *   wd           uint32 [E, H, I/8]      down codes                    (16-byte aligned)
+ *   sd, bd       bf16  [E, H, I/64]      down scale and bias           (4-byte aligned)
+ *   L, k, E, H, I  tokens, routes per token, experts, hidden size, expert
+ *                intermediate size; H and I multiples of 64
+ *   group_size   must be 64;  bits  must be 4
+ *   out          [L, H], bf16 or fp32 per out_dtype (16-byte aligned); fully
+ *                overwritten, never accumulated into; must not overlap any
+ *                input or the workspace
+ *   workspace    device scratch of at least moe_swiglu_q4_workspace_bytes
+ *                bytes (256-byte aligned); contents need no initialisation;
+ *                one workspace must not serve two calls that may run at the
+ *                same time
+ *
+ * out[t, :] = sum_j topk_weights[t, j] * Wd[e] (silu(Wg[e] x_t) * (Wu[e] x_t)),
+ * e = topk_ids[t, j].  Accumulation is fp32; the hidden vector h stays fp32.
+ * Results are deterministic (no floating-point atomics).  L == 0 returns
+ * MOE_Q4_OK without touching the GPU.
+ */
+int moe_swiglu_q4_forward(const void *x, const int32_t *topk_ids, const float *topk_weights,
+                          const uint32_t *wg, const void *sg, const void *bg,
+                          const uint32_t *wu, const void *su, const void *bu,
+                          const uint32_t *wd, const void *sd, const void *bd,
+                          int L, int k, int E, int H, int I, int group_size, int bits,
+                          void *out, int out_dtype, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
+ * Same as moe_swiglu_q4_forward, restricted to the stages in `stages`
+ * (MOE_Q4_STAGE_* bits).  MOE_Q4_STAGE_DOWN alone reads the hidden vectors a
+ * previous MOE_Q4_STAGE_GATEUP call with identical arguments left in the same
+ * workspace on the same stream.  Lets a caller time or overlap the two stages.
+ */
+int moe_swiglu_q4_forward_stages(const void *x, const int32_t *topk_ids, const float *topk_weights,
+                                 const uint32_t *wg, const void *sg, const void *bg,
+                                 const uint32_t *wu, const void *su, const void *bu,
+                                 const uint32_t *wd, const void *sd, const void *bd,
+                                 int L, int k, int E, int H, int I, int group_size, int bits,
+                                 void *out, int out_dtype, void *workspace, size_t workspace_bytes,
+                                 unsigned stages, hipStream_t stream);
+
+/*
+ * Union of the L * k routes (the dedup step of the union path), as its own
+ * call so it can be checked bit for bit.  Outputs (device, u_max = min(E, L*k)):
+ *   u            int32 [1]           number of distinct valid expert ids
+ *   uniq_ids     int32 [u_max]       distinct ids ascending; -1 past u
+ *   tok_mask     uint32 [u_max]      bit t set iff token t routes to uniq_ids[i]; 0 past u
+ *   uniq_w       fp32 [u_max, L]     sum of token t's router weights over its routes to
+ *                                    uniq_ids[i], added in ascending slot order; 0 if none
+ *   slot_to_uniq int32 [L, k]        index in uniq_ids of each route; -1 for an invalid id
+ * Requires 1 <= L <= MOE_Q4_UNION_MAX_L, L * k <= MOE_Q4_MAX_PAIRS, E <= MOE_Q4_MAX_E.
+ */
+int moe_route_union(const int32_t *topk_ids, const float *topk_weights, int L, int k, int E,
+                    int32_t *u, int32_t *uniq_ids, uint32_t *tok_mask, float *uniq_w,
+                    int32_t *slot_to_uniq, hipStream_t stream);
+
+/*
+ * Reads the device status word (MOE_Q4_DEV_* bits) that the last forward
+ * call using this workspace left in it into *status and, if last_path is not
+ * NULL, the MOE_Q4_PATH_* value that call's kernels recorded.
+ * Synchronises `stream` (debug / test use, not for hot loops).
+ */
+int moe_q4_read_device_status(const void *workspace, uint32_t *status, uint32_t *last_path,
+                              hipStream_t stream);
+
+/* Clears the device status word (enqueued on `stream`, no sync). */
+int moe_q4_clear_device_status(void *workspace, hipStream_t stream);
+
+/* Static description of a status code; never NULL. */
+const char *moe_q4_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_Q4_H */

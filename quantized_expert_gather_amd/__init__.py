@@ -1,0 +1,224 @@
+"""Python binding of libmoe_q4.so, the MI355X SwitchGLU-q4 MoE library.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI declared in ``include/moe_q4.h``.  PyTorch supplies device
+memory and the current stream.  If the built library is missing this module
+raises on first use; there is no fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_q4.so")
+
+MOE_Q4_OK = 0
+MOE_Q4_ERR_NULL = 1
+MOE_Q4_ERR_SHAPE = 2
+MOE_Q4_ERR_UNSUPPORTED = 3
+MOE_Q4_ERR_ALIGN = 4
+MOE_Q4_ERR_WORKSPACE = 5
+MOE_Q4_ERR_LAUNCH = 6
+MOE_Q4_ERR_ALIAS = 7
+MOE_Q4_DEV_BAD_ID = 1
+MOE_Q4_OUT_BF16 = 0
+MOE_Q4_OUT_F32 = 1
+MOE_Q4_PATH_NONE = 0
+MOE_Q4_PATH_UNION = 1
+MOE_Q4_PATH_SORTED = 2
+MOE_Q4_STAGE_GATEUP = 1
+MOE_Q4_STAGE_DOWN = 2
+MOE_Q4_STAGE_ALL = 3
+MOE_Q4_UNION_MAX_L = 32
+MOE_Q4_MAX_PAIRS = 1024
+
+EXPORTS = (
+    "moe_swiglu_q4_workspace_bytes",
+    "moe_swiglu_q4_select_path",
+    "moe_swiglu_q4_forward",
+    "moe_swiglu_q4_forward_stages",
+    "moe_route_union",
+    "moe_q4_read_device_status",
+    "moe_q4_clear_device_status",
+    "moe_q4_status_string",
+)
+
+_lib = None
+
+
+class MoeQ4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({moe_q4_status_string(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m quantized_expert_gather_amd.build` "
+                           "(or __graft_entry__.build()); there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ, U = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_uint
+    L.moe_swiglu_q4_workspace_bytes.argtypes = [I32] * 5
+    L.moe_swiglu_q4_workspace_bytes.restype = SZ
+    L.moe_swiglu_q4_select_path.argtypes = [I32] * 5
+    L.moe_swiglu_q4_select_path.restype = I32
+    fwd = [P] * 12 + [I32] * 7 + [P, I32, P, SZ]
+    L.moe_swiglu_q4_forward.argtypes = fwd + [P]
+    L.moe_swiglu_q4_forward.restype = I32
+    L.moe_swiglu_q4_forward_stages.argtypes = fwd + [U, P]
+    L.moe_swiglu_q4_forward_stages.restype = I32
+    L.moe_route_union.argtypes = [P, P, I32, I32, I32, P, P, P, P, P, P]
+    L.moe_route_union.restype = I32
+    L.moe_q4_read_device_status.argtypes = [P, P, P, P]
+    L.moe_q4_read_device_status.restype = I32
+    L.moe_q4_clear_device_status.argtypes = [P, P]
+    L.moe_q4_clear_device_status.restype = I32
+    L.moe_q4_status_string.argtypes = [I32]
+    L.moe_q4_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def moe_q4_status_string(status: int) -> str:
+    try:
+        return lib().moe_q4_status_string(int(status)).decode()
+    except RuntimeError:
+        return "library not loaded"
+
+
+def _stream_ptr(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev_ptr(t: Optional[torch.Tensor], dtypes, name: str) -> int:
+    if t is None:
+        return 0
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _check(status: int, where: str) -> None:
+    if status != MOE_Q4_OK:
+        raise MoeQ4Error(status, where)
+
+
+def moe_swiglu_q4_workspace_bytes(L: int, k: int, E: int, H: int, I: int) -> int:
+    return int(lib().moe_swiglu_q4_workspace_bytes(L, k, E, H, I))
+
+
+def moe_swiglu_q4_select_path(L: int, k: int, E: int, H: int, I: int) -> int:
+    return int(lib().moe_swiglu_q4_select_path(L, k, E, H, I))
+
+
+def new_workspace(L: int, k: int, E: int, H: int, I: int, device=None) -> torch.Tensor:
+    n = moe_swiglu_q4_workspace_bytes(L, k, E, H, I)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device or "cuda")
+
+
+_I32 = (torch.int32,)
+_U32 = (torch.int32, getattr(torch, "uint32", torch.int32))
+_BF16 = (torch.bfloat16,)
+_F32 = (torch.float32,)
+
+
+def moe_swiglu_q4_forward(x, topk_ids, topk_weights, wg, sg, bg, wu, su, bu, wd, sd, bd, out=None,
+                          out_dtype=torch.bfloat16, workspace=None, stream=None,
+                          stages: int = MOE_Q4_STAGE_ALL) -> torch.Tensor:
+    """One SwitchGLU-q4 MoE layer (see include/moe_q4.h for the contract).
+
+    x bf16 [L, H]; topk_ids int32 [L, k]; topk_weights fp32 [L, k];
+    wg/wu int32 (uint32 bits) [E, I, H/8]; sg/bg/su/bu bf16 [E, I, H/64];
+    wd int32 [E, H, I/8]; sd/bd bf16 [E, H, I/64].  Returns out [L, H].
+    """
+    if x.dim() != 2 or topk_ids.dim() != 2 or wg.dim() != 3 or wd.dim() != 3:
+        raise ValueError("x [L, H], topk_ids [L, k], wg [E, I, H/8] and wd [E, H, I/8] expected")
+    L, H = x.shape
+    k = topk_ids.shape[1]
+    E, I = wg.shape[0], wg.shape[1]
+    shapes = {
+        "topk_ids": (topk_ids, (L, k)), "topk_weights": (topk_weights, (L, k)),
+        "wg": (wg, (E, I, H // 8)), "wu": (wu, (E, I, H // 8)), "wd": (wd, (E, H, I // 8)),
+        "sg": (sg, (E, I, H // 64)), "bg": (bg, (E, I, H // 64)), "su": (su, (E, I, H // 64)),
+        "bu": (bu, (E, I, H // 64)), "sd": (sd, (E, H, I // 64)), "bd": (bd, (E, H, I // 64)),
+    }
+    for name, (t, shp) in shapes.items():
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    od = MOE_Q4_OUT_F32 if out_dtype == torch.float32 else MOE_Q4_OUT_BF16
+    if out is None:
+        out = torch.empty((L, H), dtype=torch.float32 if od == MOE_Q4_OUT_F32 else torch.bfloat16, device=x.device)
+    if tuple(out.shape) != (L, H):
+        raise ValueError("out must be [L, H]")
+    if workspace is None:
+        workspace = new_workspace(L, k, E, H, I, x.device)
+    st = lib().moe_swiglu_q4_forward_stages(
+        _dev_ptr(x, _BF16, "x"), _dev_ptr(topk_ids, _I32, "topk_ids"), _dev_ptr(topk_weights, _F32, "topk_weights"),
+        _dev_ptr(wg, _U32, "wg"), _dev_ptr(sg, _BF16, "sg"), _dev_ptr(bg, _BF16, "bg"),
+        _dev_ptr(wu, _U32, "wu"), _dev_ptr(su, _BF16, "su"), _dev_ptr(bu, _BF16, "bu"),
+        _dev_ptr(wd, _U32, "wd"), _dev_ptr(sd, _BF16, "sd"), _dev_ptr(bd, _BF16, "bd"),
+        L, k, E, H, I, 64, 4,
+        _dev_ptr(out, (torch.float32,) if od == MOE_Q4_OUT_F32 else _BF16, "out"), od,
+        _dev_ptr(workspace, (torch.uint8,), "workspace"), workspace.numel(),
+        int(stages), _stream_ptr(stream))
+    _check(st, "moe_swiglu_q4_forward")
+    return out
+
+
+def forward_bank(x, topk_ids, topk_weights, bank, **kw) -> torch.Tensor:
+    """moe_swiglu_q4_forward with the nine bank tensors taken from an object
+    exposing ``tensors()`` (wg, sg, bg, wu, su, bu, wd, sd, bd)."""
+    return moe_swiglu_q4_forward(x, topk_ids, topk_weights, *bank.tensors(), **kw)
+
+
+def moe_route_union(topk_ids: torch.Tensor, topk_weights: torch.Tensor, E: int, stream=None) -> Dict[str, torch.Tensor]:
+    """Distinct experts of the routes (see include/moe_q4.h).  Returns device tensors."""
+    L, k = topk_ids.shape
+    u_max = min(E, L * k)
+    dev = topk_ids.device
+    res = {
+        "u": torch.empty(1, dtype=torch.int32, device=dev),
+        "uniq_ids": torch.empty(max(u_max, 1), dtype=torch.int32, device=dev),
+        "tok_mask": torch.empty(max(u_max, 1), dtype=torch.int32, device=dev),
+        "uniq_w": torch.empty((max(u_max, 1), L), dtype=torch.float32, device=dev),
+        "slot_to_uniq": torch.empty((L, k), dtype=torch.int32, device=dev),
+    }
+    st = lib().moe_route_union(_dev_ptr(topk_ids, _I32, "topk_ids"), _dev_ptr(topk_weights, _F32, "topk_weights"),
+                               L, k, E, res["u"].data_ptr(), res["uniq_ids"].data_ptr(), res["tok_mask"].data_ptr(),
+                               res["uniq_w"].data_ptr(), res["slot_to_uniq"].data_ptr(), _stream_ptr(stream))
+    _check(st, "moe_route_union")
+    return res
+
+
+def moe_q4_read_device_status(workspace: torch.Tensor, stream=None) -> Tuple[int, int]:
+    """(status bits, path) of the last forward that used this workspace; synchronises the stream."""
+    st_v = ctypes.c_uint32(0)
+    path_v = ctypes.c_uint32(0)
+    st = lib().moe_q4_read_device_status(_dev_ptr(workspace, (torch.uint8,), "workspace"), ctypes.byref(st_v),
+                                         ctypes.byref(path_v), _stream_ptr(stream))
+    _check(st, "moe_q4_read_device_status")
+    return int(st_v.value), int(path_v.value)
+
+
+def moe_q4_clear_device_status(workspace: torch.Tensor, stream=None) -> None:
+    _check(lib().moe_q4_clear_device_status(_dev_ptr(workspace, (torch.uint8,), "workspace"), _stream_ptr(stream)),
+           "moe_q4_clear_device_status")

@@ -1,0 +1,199 @@
+// C ABI of the SwitchGLU-q4 MoE library: argument validation, workspace
+// layout, path selection and launches.  Every check here runs on the host
+// before any GPU work, so invalid calls return a status without touching the
+// device.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "moe_q4.h"
+#include "moe_q4_internal.h"
+
+namespace moeq4 {
+
+static size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
+
+UnionWorkspace union_workspace_layout(int L, int k, int E, int H, int I) {
+  (void)E;
+  UnionWorkspace w{};
+  const size_t pairs = (size_t)L * (size_t)k;
+  size_t off = 0;
+  w.hdr = off;  off = round256(off + 256);
+  w.cnt = off;  off = round256(off + (size_t)(H / 32) * 4);
+  w.hbuf = off; off = round256(off + pairs * (size_t)(I / 32) * 32 * 4);
+  w.hsum = off; off = round256(off + pairs * (size_t)(I / 32) * 4);
+  w.ys = off;   off = round256(off + pairs * (size_t)H * 4);
+  w.total = off;
+  return w;
+}
+
+__global__ void k_clear_status(uint32_t* hdr) {
+  if (threadIdx.x == 0) hdr[0] = 0u;
+}
+
+int clear_status_launch(uint32_t* hdr, hipStream_t stream) {
+  hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(64), 0, stream, hdr);
+  return hipGetLastError() == hipSuccess ? MOE_Q4_OK : MOE_Q4_ERR_LAUNCH;
+}
+
+static int shape_status(int L, int k, int E, int H, int I) {
+  if (L < 0 || k < 1 || E < 1 || H < 1 || I < 1 || k > E) return MOE_Q4_ERR_SHAPE;
+  if (H % 64 || I % 64) return MOE_Q4_ERR_UNSUPPORTED;
+  if (E > MOE_Q4_MAX_E) return MOE_Q4_ERR_UNSUPPORTED;
+  return MOE_Q4_OK;
+}
+
+static int select_path(int L, int k, int E, int H, int I) {
+  const int st = shape_status(L, k, E, H, I);
+  if (st) return -st;
+  if (L == 0) return MOE_Q4_PATH_NONE;
+  if (L <= MOE_Q4_UNION_MAX_L && (long)L * k <= MOE_Q4_MAX_PAIRS && union_shape_supported(L, k, E, H, I))
+    return MOE_Q4_PATH_UNION;
+  return -MOE_Q4_ERR_UNSUPPORTED;
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na && nb && x < y + nb && y < x + na;
+}
+
+static int num_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return -1;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
+
+}  // namespace moeq4
+
+using namespace moeq4;
+
+extern "C" {
+
+size_t moe_swiglu_q4_workspace_bytes(int L, int k, int E, int H, int I) {
+  const int path = select_path(L, k, E, H, I);
+  if (path <= 0) return 0;
+  return union_workspace_layout(L, k, E, H, I).total;
+}
+
+int moe_swiglu_q4_select_path(int L, int k, int E, int H, int I) { return select_path(L, k, E, H, I); }
+
+int moe_swiglu_q4_forward_stages(const void* x, const int32_t* topk_ids, const float* topk_weights,
+                                 const uint32_t* wg, const void* sg, const void* bg, const uint32_t* wu,
+                                 const void* su, const void* bu, const uint32_t* wd, const void* sd,
+                                 const void* bd, int L, int k, int E, int H, int I, int group_size, int bits,
+                                 void* out, int out_dtype, void* workspace, size_t workspace_bytes,
+                                 unsigned stages, hipStream_t stream) {
+  const int st = shape_status(L, k, E, H, I);
+  if (st) return st;
+  if (group_size != 64 || bits != 4) return MOE_Q4_ERR_UNSUPPORTED;
+  if (out_dtype != MOE_Q4_OUT_BF16 && out_dtype != MOE_Q4_OUT_F32) return MOE_Q4_ERR_UNSUPPORTED;
+  if (stages == 0 || (stages & ~MOE_Q4_STAGE_ALL)) return MOE_Q4_ERR_UNSUPPORTED;
+  if (L == 0) return MOE_Q4_OK;
+  const int path = select_path(L, k, E, H, I);
+  if (path < 0) return -path;
+  if (!x || !topk_ids || !topk_weights || !wg || !sg || !bg || !wu || !su || !bu || !wd || !sd || !bd || !out)
+    return MOE_Q4_ERR_NULL;
+  if (!workspace) return MOE_Q4_ERR_WORKSPACE;
+  if (!aligned(x, 16) || !aligned(wg, 16) || !aligned(wu, 16) || !aligned(wd, 16) || !aligned(out, 16) ||
+      !aligned(topk_ids, 4) || !aligned(topk_weights, 4) || !aligned(sg, 4) || !aligned(bg, 4) ||
+      !aligned(su, 4) || !aligned(bu, 4) || !aligned(sd, 4) || !aligned(bd, 4) || !aligned(workspace, 256))
+    return MOE_Q4_ERR_ALIGN;
+  const UnionWorkspace lay = union_workspace_layout(L, k, E, H, I);
+  if (workspace_bytes < lay.total) return MOE_Q4_ERR_WORKSPACE;
+
+  const size_t out_bytes = (size_t)L * H * (out_dtype == MOE_Q4_OUT_F32 ? 4 : 2);
+  const size_t gu_codes = (size_t)E * I * (H / 8) * 4, gu_sb = (size_t)E * I * (H / 64) * 2;
+  const size_t d_codes = (size_t)E * H * (I / 8) * 4, d_sb = (size_t)E * H * (I / 64) * 2;
+  const struct { const void* p; size_t n; } ins[] = {
+      {x, (size_t)L * H * 2}, {topk_ids, (size_t)L * k * 4}, {topk_weights, (size_t)L * k * 4},
+      {wg, gu_codes}, {sg, gu_sb}, {bg, gu_sb}, {wu, gu_codes}, {su, gu_sb}, {bu, gu_sb},
+      {wd, d_codes}, {sd, d_sb}, {bd, d_sb}, {workspace, lay.total}};
+  for (const auto& in : ins)
+    if (overlaps(out, out_bytes, in.p, in.n)) return MOE_Q4_ERR_ALIAS;
+
+  const int ncu = num_cus();
+  if (ncu <= 0) return MOE_Q4_ERR_LAUNCH;
+
+  UnionArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.ids = topk_ids;
+  a.tw = topk_weights;
+  a.wg = wg; a.sg = static_cast<const uint16_t*>(sg); a.bg = static_cast<const uint16_t*>(bg);
+  a.wu = wu; a.su = static_cast<const uint16_t*>(su); a.bu = static_cast<const uint16_t*>(bu);
+  a.wd = wd; a.sd = static_cast<const uint16_t*>(sd); a.bd = static_cast<const uint16_t*>(bd);
+  a.out = out;
+  a.out_f32 = out_dtype == MOE_Q4_OUT_F32;
+  a.L = L; a.k = k; a.E = E; a.H = H; a.I = I;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  a.hdr = reinterpret_cast<uint32_t*>(ws + lay.hdr);
+  a.cnt = reinterpret_cast<uint32_t*>(ws + lay.cnt);
+  a.hbuf = reinterpret_cast<uint32_t*>(ws + lay.hbuf);
+  a.hsum = reinterpret_cast<float*>(ws + lay.hsum);
+  a.ys = reinterpret_cast<float*>(ws + lay.ys);
+  return union_forward_launch(a, stages, ncu, stream);
+}
+
+int moe_swiglu_q4_forward(const void* x, const int32_t* topk_ids, const float* topk_weights, const uint32_t* wg,
+                          const void* sg, const void* bg, const uint32_t* wu, const void* su, const void* bu,
+                          const uint32_t* wd, const void* sd, const void* bd, int L, int k, int E, int H, int I,
+                          int group_size, int bits, void* out, int out_dtype, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  return moe_swiglu_q4_forward_stages(x, topk_ids, topk_weights, wg, sg, bg, wu, su, bu, wd, sd, bd, L, k, E, H, I,
+                                      group_size, bits, out, out_dtype, workspace, workspace_bytes,
+                                      MOE_Q4_STAGE_ALL, stream);
+}
+
+int moe_route_union(const int32_t* topk_ids, const float* topk_weights, int L, int k, int E, int32_t* u,
+                    int32_t* uniq_ids, uint32_t* tok_mask, float* uniq_w, int32_t* slot_to_uniq,
+                    hipStream_t stream) {
+  if (L < 1 || k < 1 || E < 1 || k > E) return MOE_Q4_ERR_SHAPE;
+  if (L > MOE_Q4_UNION_MAX_L || (long)L * k > MOE_Q4_MAX_PAIRS || E > MOE_Q4_MAX_E) return MOE_Q4_ERR_UNSUPPORTED;
+  if (!topk_ids || !topk_weights || !u || !uniq_ids || !tok_mask || !uniq_w || !slot_to_uniq)
+    return MOE_Q4_ERR_NULL;
+  if (!aligned(topk_ids, 4) || !aligned(topk_weights, 4) || !aligned(u, 4) || !aligned(uniq_ids, 4) ||
+      !aligned(tok_mask, 4) || !aligned(uniq_w, 4) || !aligned(slot_to_uniq, 4))
+    return MOE_Q4_ERR_ALIGN;
+  return route_union_launch(topk_ids, topk_weights, L, k, E, u, uniq_ids, tok_mask, uniq_w, slot_to_uniq, stream);
+}
+
+int moe_q4_read_device_status(const void* workspace, uint32_t* status, uint32_t* last_path, hipStream_t stream) {
+  if (!workspace || !status) return MOE_Q4_ERR_NULL;
+  if (!aligned(workspace, 256)) return MOE_Q4_ERR_ALIGN;
+  uint32_t hdr[4] = {0, 0, 0, 0};
+  if (hipStreamSynchronize(stream) != hipSuccess) return MOE_Q4_ERR_LAUNCH;
+  if (hipMemcpy(hdr, workspace, sizeof hdr, hipMemcpyDeviceToHost) != hipSuccess) return MOE_Q4_ERR_LAUNCH;
+  *status = hdr[0];
+  if (last_path) *last_path = hdr[1];
+  return MOE_Q4_OK;
+}
+
+int moe_q4_clear_device_status(void* workspace, hipStream_t stream) {
+  if (!workspace) return MOE_Q4_ERR_NULL;
+  if (!aligned(workspace, 256)) return MOE_Q4_ERR_ALIGN;
+  return clear_status_launch(static_cast<uint32_t*>(workspace), stream);
+}
+
+const char* moe_q4_status_string(int status) {
+  switch (status) {
+    case MOE_Q4_OK: return "ok";
+    case MOE_Q4_ERR_NULL: return "a required pointer is NULL";
+    case MOE_Q4_ERR_SHAPE: return "invalid shape (L < 0, k < 1, E < 1, k > E, H or I < 1)";
+    case MOE_Q4_ERR_UNSUPPORTED:
+      return "unsupported configuration (H or I not a multiple of 64, bits != 4, group != 64, unknown dtype, "
+             "or beyond the library limits)";
+    case MOE_Q4_ERR_ALIGN: return "pointer misaligned";
+    case MOE_Q4_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_Q4_ERR_LAUNCH: return "HIP launch or runtime call failed";
+    case MOE_Q4_ERR_ALIAS: return "output overlaps an input or the workspace";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,162 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/moe_q4.h declares, and
+reject invalid arguments on the host before any GPU work.  Pointers passed
+here are fake, aligned addresses: every call below returns from the host-side
+validation, which runs before any HIP call.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_expert_gather_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_q4.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def header_constants():
+    vals = {}
+    for name, val in re.findall(r"#define\s+(MOE_Q4_[A-Z_0-9]+)\s+([0-9]+)u?", open(HEADER).read()):
+        vals[name] = int(val)
+    return vals
+
+
+def test_library_exports_every_declared_function():
+    lib = q.lib()
+    names = header_functions()
+    assert len(names) >= 7
+    assert sorted(names) == sorted(q.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_binding_constants_match_header():
+    for name, val in header_constants().items():
+        if hasattr(q, name):
+            assert getattr(q, name) == val, name
+
+
+# fake device pointers: distinct, 256-byte aligned, far apart
+BASE = 1 << 40
+STRIDE = 1 << 34
+
+
+def fake(i):
+    return BASE + i * STRIDE
+
+
+def call(L=2, k=2, E=8, H=256, I=128, group=64, bits=4, out_dtype=0, ws_bytes=1 << 30, stages=3, ptrs=None,
+         ws=None, out=None):
+    p = [fake(i) for i in range(12)] if ptrs is None else ptrs
+    return q.lib().moe_swiglu_q4_forward_stages(*p, L, k, E, H, I, group, bits,
+                                               fake(13) if out is None else out, out_dtype,
+                                               fake(14) if ws is None else ws, ws_bytes, stages, None)
+
+
+def test_zero_tokens_is_ok_without_gpu():
+    assert call(L=0) == q.MOE_Q4_OK
+    assert q.moe_swiglu_q4_workspace_bytes(0, 2, 8, 256, 128) == 0
+    assert q.moe_swiglu_q4_select_path(0, 2, 8, 256, 128) == q.MOE_Q4_PATH_NONE
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=-1), q.MOE_Q4_ERR_SHAPE),
+    (dict(k=0), q.MOE_Q4_ERR_SHAPE),
+    (dict(E=0), q.MOE_Q4_ERR_SHAPE),
+    (dict(k=9, E=8), q.MOE_Q4_ERR_SHAPE),
+    (dict(H=0), q.MOE_Q4_ERR_SHAPE),
+    (dict(H=250), q.MOE_Q4_ERR_UNSUPPORTED),
+    (dict(I=96), q.MOE_Q4_ERR_UNSUPPORTED),
+    (dict(group=32), q.MOE_Q4_ERR_UNSUPPORTED),
+    (dict(bits=8), q.MOE_Q4_ERR_UNSUPPORTED),
+    (dict(out_dtype=5), q.MOE_Q4_ERR_UNSUPPORTED),
+    (dict(stages=0), q.MOE_Q4_ERR_UNSUPPORTED),
+    (dict(stages=4), q.MOE_Q4_ERR_UNSUPPORTED),
+    (dict(E=20000, k=2), q.MOE_Q4_ERR_UNSUPPORTED),
+    (dict(ws_bytes=64), q.MOE_Q4_ERR_WORKSPACE),
+])
+def test_invalid_arguments_rejected_on_host(kw, status):
+    assert call(**kw) == status
+
+
+def test_null_pointers_rejected():
+    for i in range(12):
+        p = [fake(j) for j in range(12)]
+        p[i] = 0
+        assert call(ptrs=p) == q.MOE_Q4_ERR_NULL, i
+    assert call(out=0) == q.MOE_Q4_ERR_NULL
+    assert call(ws=0) == q.MOE_Q4_ERR_WORKSPACE
+
+
+def test_misalignment_rejected():
+    for i, a in [(0, 8), (3, 8), (6, 4), (9, 2), (1, 2), (4, 2)]:
+        p = [fake(j) for j in range(12)]
+        p[i] += a
+        assert call(ptrs=p) == q.MOE_Q4_ERR_ALIGN, i
+    assert call(ws=fake(14) + 128) == q.MOE_Q4_ERR_ALIGN
+    assert call(out=fake(13) + 8) == q.MOE_Q4_ERR_ALIGN
+
+
+def test_output_alias_rejected():
+    assert call(out=fake(0)) == q.MOE_Q4_ERR_ALIAS          # out == x
+    assert call(out=fake(14) + 256) == q.MOE_Q4_ERR_ALIAS   # inside the workspace
+    assert call(out=fake(3) + 1024) == q.MOE_Q4_ERR_ALIAS   # inside wg
+
+
+def test_path_selection_and_limits():
+    assert q.moe_swiglu_q4_select_path(1, 8, 256, 6144, 2048) == q.MOE_Q4_PATH_UNION
+    assert q.moe_swiglu_q4_select_path(8, 8, 256, 6144, 2048) == q.MOE_Q4_PATH_UNION
+    assert q.moe_swiglu_q4_select_path(32, 8, 256, 2048, 512) == q.MOE_Q4_PATH_UNION
+    assert q.moe_swiglu_q4_select_path(2, 2, 8, 256, 128) == q.MOE_Q4_PATH_UNION
+    assert q.moe_swiglu_q4_select_path(3, 2, 8, 200, 128) == -q.MOE_Q4_ERR_UNSUPPORTED
+    assert q.moe_swiglu_q4_select_path(2, 9, 8, 256, 128) == -q.MOE_Q4_ERR_SHAPE
+
+
+def test_workspace_size_grows_with_pairs():
+    a = q.moe_swiglu_q4_workspace_bytes(1, 8, 256, 6144, 2048)
+    b = q.moe_swiglu_q4_workspace_bytes(8, 8, 256, 6144, 2048)
+    assert 0 < a < b
+    assert a % 256 == 0 and b % 256 == 0
+    # must hold the per-pair hidden (4 B per element) and output partials (4 B per element)
+    assert b >= 64 * (2048 * 4 + 6144 * 4)
+
+
+def test_route_union_host_validation():
+    f = q.lib().moe_route_union
+    ptr = [fake(i) for i in range(7)]
+    assert f(ptr[0], ptr[1], 0, 8, 256, *ptr[2:], None) == q.MOE_Q4_ERR_SHAPE
+    assert f(ptr[0], ptr[1], 33, 8, 256, *ptr[2:], None) == q.MOE_Q4_ERR_UNSUPPORTED
+    assert f(ptr[0], ptr[1], 4, 9, 8, *ptr[2:], None) == q.MOE_Q4_ERR_SHAPE
+    assert f(0, ptr[1], 4, 8, 256, *ptr[2:], None) == q.MOE_Q4_ERR_NULL
+    assert f(ptr[0] + 2, ptr[1], 4, 8, 256, *ptr[2:], None) == q.MOE_Q4_ERR_ALIGN
+
+
+def test_status_strings():
+    for s in range(8):
+        assert q.moe_q4_status_string(s)
+    assert q.moe_q4_status_string(99) == "unknown status"
+
+
+def test_binding_rejects_host_tensors_before_calling():
+    import torch
+    x = torch.zeros((2, 256), dtype=torch.bfloat16)
+    ids = torch.zeros((2, 2), dtype=torch.int32)
+    w = torch.zeros((2, 2), dtype=torch.float32)
+    bank = [torch.zeros((8, 128, 32), dtype=torch.int32), torch.zeros((8, 128, 4), dtype=torch.bfloat16),
+            torch.zeros((8, 128, 4), dtype=torch.bfloat16)] * 2 + \
+           [torch.zeros((8, 256, 16), dtype=torch.int32), torch.zeros((8, 256, 2), dtype=torch.bfloat16),
+            torch.zeros((8, 256, 2), dtype=torch.bfloat16)]
+    with pytest.raises(ValueError):
+        q.moe_swiglu_q4_forward(x, ids, w, *bank, workspace=torch.zeros(256, dtype=torch.uint8),
+                                out=torch.zeros((2, 256), dtype=torch.bfloat16))

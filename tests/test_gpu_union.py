@@ -1,0 +1,256 @@
+"""GPU parity of the union path against the CPU oracle (needs an MI355X).
+
+Bars: union / index outputs bit-exact; fp32 layer outputs within a per-row
+normwise relative error of 1e-3 (the contract), and within 1e-4, the bound
+the fp32 arithmetic of the kernels gives (fp32 accumulation of exact bf16
+products; the affine offset trick costs about 20x cancellation on 2^-24, and
+the hidden vector is carried as an exact-to-2^-17 bf16 hi + lo pair); bf16
+outputs equal the round-to-nearest-even of the fp32 outputs bit for bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+CONTRACT = 1e-3
+ARITH = 1e-4
+
+
+def _q():
+    import quantized_expert_gather_amd as q
+    return q
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def rel_err_rows(gpu: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    num = np.linalg.norm(gpu.astype(np.float64) - ref, axis=1)
+    den = np.linalg.norm(ref, axis=1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1), num)
+
+
+def run_layer(x, ids, tw, bank, out_dtype=torch.float32, stages_split=False):
+    q = _q()
+    dev = torch.device("cuda")
+    xd = x.to(dev)
+    idd = torch.as_tensor(np.asarray(ids, np.int32)).to(dev)
+    twd = torch.as_tensor(np.asarray(tw, np.float32)).to(dev)
+    bk = bank.to(dev)
+    L, k = idd.shape
+    ws = q.new_workspace(L, k, bk.E, x.shape[1], bk.wg.shape[1], dev)
+    if stages_split:
+        out = torch.empty((L, x.shape[1]), dtype=out_dtype, device=dev)
+        q.forward_bank(xd, idd, twd, bk, out=out, out_dtype=out_dtype, workspace=ws, stages=q.MOE_Q4_STAGE_GATEUP)
+        q.forward_bank(xd, idd, twd, bk, out=out, out_dtype=out_dtype, workspace=ws, stages=q.MOE_Q4_STAGE_DOWN)
+    else:
+        out = q.forward_bank(xd, idd, twd, bk, out_dtype=out_dtype, workspace=ws)
+    torch.cuda.synchronize()
+    return out, ws
+
+
+def check_layer(x, ids, tw, bank, label):
+    say(label, "L=%d k=%d E=%d H=%d I=%d" % (ids.shape[0], ids.shape[1], bank.E, x.shape[1], bank.wg.shape[1]))
+    ref = oracle.forward_pairs(x.cpu(), ids, tw, bank.to("cpu"))
+    out, ws = run_layer(x, ids, tw, bank)
+    got = out.float().cpu().numpy()
+    err = rel_err_rows(got, ref)
+    print(f"  max row rel err {err.max():.3e}", flush=True)
+    assert np.isfinite(got).all()
+    assert err.max() <= CONTRACT
+    assert err.max() <= ARITH
+    status, path = _q().moe_q4_read_device_status(ws)
+    assert status == 0 and path == _q().MOE_Q4_PATH_UNION
+    return got, ref
+
+
+# ---------------------------------------------------------------------------
+# route union, bit-exact
+# ---------------------------------------------------------------------------
+
+UNION_CASES = {
+    "random_L8": lambda rng: rng.integers(0, 256, size=(8, 8)),
+    "all_same": lambda rng: np.full((4, 8), 17),
+    "all_distinct": lambda rng: np.arange(64).reshape(8, 8)[:, ::-1],
+    "dup_in_token": lambda rng: np.array([[3, 3, 5, 255], [255, 0, 0, 3]]),
+    "last_id": lambda rng: np.full((3, 2), 255),
+    "L32": lambda rng: rng.integers(0, 256, size=(32, 8)),
+    "L1": lambda rng: rng.permutation(256)[:8].reshape(1, 8),
+    "k1": lambda rng: rng.integers(0, 256, size=(7, 1)),
+    "E288_L4": lambda rng: rng.integers(0, 288, size=(4, 8)),
+    "E16384": lambda rng: rng.integers(0, 16384, size=(16, 8)),
+    "pairs1024": lambda rng: rng.integers(0, 4096, size=(32, 32)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(UNION_CASES))
+def test_route_union_bit_exact(case):
+    q = _q()
+    rng = np.random.default_rng(abs(hash(case)) % 2**32)
+    ids = np.asarray(UNION_CASES[case](rng), np.int32)
+    E = {"E288_L4": 288, "E16384": 16384, "pairs1024": 4096}.get(case, 256)
+    L, k = ids.shape
+    tw = rng.uniform(0, 1, size=(L, k)).astype(np.float32)
+    say("route_union", case, ids.shape, E)
+    ref = oracle.route_union(ids, tw, E)
+    r = q.moe_route_union(torch.from_numpy(ids).cuda(), torch.from_numpy(tw).cuda(), E)
+    torch.cuda.synchronize()
+    u = int(r["u"].item())
+    assert u == ref["u"]
+    assert r["uniq_ids"][:u].cpu().numpy().tolist() == ref["uniq_ids"].tolist()
+    assert (r["uniq_ids"][u:].cpu().numpy() == -1).all()
+    assert np.array_equal(r["tok_mask"][:u].cpu().numpy().view(np.uint32), ref["tok_mask"])
+    assert np.array_equal(r["uniq_w"][:u].cpu().numpy().view(np.uint32), ref["uniq_w"].view(np.uint32))
+    assert (r["uniq_w"][u:].cpu().numpy() == 0).all()
+    assert np.array_equal(r["slot_to_uniq"].cpu().numpy(), ref["slot_to_uniq"])
+
+
+def test_route_union_invalid_ids_map_to_minus_one():
+    q = _q()
+    ids = np.array([[1, 300], [-5, 1]], np.int32)
+    tw = np.ones((2, 2), np.float32)
+    r = q.moe_route_union(torch.from_numpy(ids).cuda(), torch.from_numpy(tw).cuda(), 256)
+    torch.cuda.synchronize()
+    assert int(r["u"].item()) == 1
+    assert r["slot_to_uniq"].cpu().numpy().tolist() == [[0, -1], [-1, 0]]
+
+
+# ---------------------------------------------------------------------------
+# layer parity
+# ---------------------------------------------------------------------------
+
+def test_tiny_configuration():
+    lay = synth.tiny_layer()
+    check_layer(lay.x, lay.ids, lay.weights, lay.bank, "tiny E8 k2 H256 I128 L2 seed0")
+
+
+SMALL_SHAPES = [
+    # (L, k, E, H, I, dup) -- ragged lane groups (H/32, I/32 not powers of two),
+    # several row blocks, several positions per lane, duplicates
+    (1, 2, 4, 64, 64, False),
+    (3, 2, 6, 384, 192, False),
+    (5, 3, 7, 320, 128, True),
+    (8, 4, 16, 2048, 256, False),
+    (4, 8, 12, 4096, 128, True),
+    (2, 8, 64, 6144, 128, False),
+    (7, 8, 40, 6144, 64, False),
+    (16, 4, 40, 512, 512, False),
+    (32, 2, 48, 256, 512, True),
+    (6, 1, 3, 1024, 2048, False),
+    (4, 4, 4, 8192, 192, False),
+    (2, 2, 3, 16384, 64, False),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "L%d_k%d_E%d_H%d_I%d_dup%d" % s)
+def test_small_shapes(shape):
+    L, k, E, H, I, dup = shape
+    x, ids, tw, bank = synth.random_problem(L, k, E, H, I, seed=sum(shape), dup=dup)
+    check_layer(x, ids, tw, bank, "small")
+
+
+def test_all_tokens_same_expert_and_heavy_expert():
+    # one expert serves every token (more tokens than one register chunk)
+    E, H, I = 4, 1024, 256
+    for L in (5, 13, 32):
+        x, _, tw, bank = synth.random_problem(L, 2, E, H, I, seed=L)
+        ids = np.tile(np.array([[1, 3]], np.int32), (L, 1))
+        check_layer(x, ids, tw, bank, "same-expert L=%d" % L)
+
+
+def test_bf16_output_is_rne_of_fp32_output():
+    x, ids, tw, bank = synth.random_problem(4, 4, 9, 2048, 512, seed=3)
+    say("bf16 vs fp32 output")
+    o32, _ = run_layer(x, ids, tw, bank, torch.float32)
+    o16, _ = run_layer(x, ids, tw, bank, torch.bfloat16)
+    assert torch.equal(o32.to(torch.bfloat16).view(torch.int16), o16.view(torch.int16))
+
+
+def test_stages_split_equals_forward_and_determinism():
+    x, ids, tw, bank = synth.random_problem(6, 4, 20, 2048, 512, seed=4)
+    say("stages split / determinism")
+    a, _ = run_layer(x, ids, tw, bank)
+    b, _ = run_layer(x, ids, tw, bank, stages_split=True)
+    c, _ = run_layer(x, ids, tw, bank)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(a.view(torch.int32), c.view(torch.int32))
+
+
+def test_workspace_reuse_across_shapes():
+    # one workspace (sized for the largest call) reused by calls of other shapes
+    q = _q()
+    big = synth.random_problem(8, 8, 32, 2048, 512, seed=5)
+    small = synth.random_problem(2, 8, 32, 2048, 512, seed=6)
+    ws = q.new_workspace(8, 8, 32, 2048, 512)
+    say("workspace reuse")
+    for (x, ids, tw, bank) in (big, small, big):
+        ref = oracle.forward_pairs(x, ids, tw, bank)
+        out = q.forward_bank(x.cuda(), torch.from_numpy(ids).cuda(), torch.from_numpy(tw).cuda(), bank.to("cuda"),
+                             out_dtype=torch.float32, workspace=ws)
+        torch.cuda.synchronize()
+        assert rel_err_rows(out.cpu().numpy(), ref).max() <= ARITH
+
+
+def test_invalid_ids_set_status_and_drop_routes():
+    q = _q()
+    x, ids, tw, bank = synth.random_problem(3, 2, 6, 256, 128, seed=7)
+    bad = ids.copy()
+    bad[1, 1] = 6
+    bad[2, 0] = -3
+    say("invalid ids")
+    out, ws = run_layer(x, bad, tw, bank)
+    status, _ = q.moe_q4_read_device_status(ws)
+    assert status & q.MOE_Q4_DEV_BAD_ID
+    # expected: the same layer with the invalid routes' weights set to zero
+    keep = ids.copy()
+    keep[1, 1] = 0
+    keep[2, 0] = 0
+    tw0 = tw.copy()
+    tw0[1, 1] = 0
+    tw0[2, 0] = 0
+    ref = oracle.forward_pairs(x, keep, tw0, bank)
+    assert rel_err_rows(out.cpu().numpy(), ref).max() <= ARITH
+    q.moe_q4_clear_device_status(ws)
+    torch.cuda.synchronize()
+    assert q.moe_q4_read_device_status(ws)[0] == 0
+
+
+def test_all_ids_invalid_gives_zero_output():
+    x, ids, tw, bank = synth.random_problem(2, 2, 4, 256, 128, seed=8)
+    say("all ids invalid")
+    out, _ = run_layer(x, np.full_like(ids, 99), tw, bank, torch.bfloat16)
+    assert (out.float() == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# the workload shapes at full size (every output checked)
+# ---------------------------------------------------------------------------
+
+FULL = [
+    ("verify", 1, 0), ("verify", 2, 40), ("verify", 3, 60), ("verify", 4, 74), ("verify", 8, 7),
+    ("flash", 1, 0), ("flash", 4, 41),
+    ("small", 8, 0), ("small", 16, 3), ("small", 32, 15),
+    ("small_pooled", 8, 0), ("small_pooled", 16, 5), ("small_pooled", 32, 9),
+]
+
+
+@pytest.mark.parametrize("wl,L,layer", FULL, ids=lambda v: str(v))
+def test_full_size_layers(wl, L, layer):
+    w = synth.WORKLOADS[wl]
+    say("full", w.name, "L", L, "layer", layer)
+    lay = synth.make_layer(w, L, layer, seed=0, device="cuda")
+    check_layer(lay.x, lay.ids, lay.weights, lay.bank, w.name)
+
+
+def test_full_bank_layer_id_range():
+    # one layer with the whole E=256 bank resident (ids span the full range)
+    w = synth.WORKLOADS["verify"]
+    say("full bank E=256 H=6144 I=2048 L=2")
+    lay = synth.make_layer(w, 2, 11, seed=0, device="cuda", compact=False)
+    check_layer(lay.x, lay.ids, lay.weights, lay.bank, "full-bank")
