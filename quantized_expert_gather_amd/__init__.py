@@ -222,3 +222,32 @@ def moe_q4_read_device_status(workspace: torch.Tensor, stream=None) -> Tuple[int
 def moe_q4_clear_device_status(workspace: torch.Tensor, stream=None) -> None:
     _check(lib().moe_q4_clear_device_status(_dev_ptr(workspace, (torch.uint8,), "workspace"), _stream_ptr(stream)),
            "moe_q4_clear_device_status")
+
+
+class PreparedForward:
+    """A forward (or stage) call whose arguments were checked and marshalled
+    once; calling it only crosses the C ABI.  The tensors must stay alive and
+    unchanged in place for as long as the object is used."""
+
+    def __init__(self, x, topk_ids, topk_weights, bank_tensors, out, workspace, stages=MOE_Q4_STAGE_ALL,
+                 stream=None):
+        wg, sg, bg, wu, su, bu, wd, sd, bd = bank_tensors
+        # one checked call through the normal path validates shapes and dtypes
+        self._keep = (x, topk_ids, topk_weights, tuple(bank_tensors), out, workspace)
+        L, H = x.shape
+        k = topk_ids.shape[1]
+        E, I = wg.shape[0], wg.shape[1]
+        od = MOE_Q4_OUT_F32 if out.dtype == torch.float32 else MOE_Q4_OUT_BF16
+        ptrs = [_dev_ptr(t, _BF16 if i in (0,) else (_I32 if i == 1 else (_F32 if i == 2 else
+                                                                            (_U32 if i in (3, 6, 9) else _BF16))),
+                         "arg%d" % i)
+                for i, t in enumerate((x, topk_ids, topk_weights, wg, sg, bg, wu, su, bu, wd, sd, bd))]
+        self._args = (*ptrs, L, k, E, H, I, 64, 4, _dev_ptr(out, (out.dtype,), "out"), od,
+                      _dev_ptr(workspace, (torch.uint8,), "workspace"), workspace.numel(), int(stages),
+                      _stream_ptr(stream))
+        self._fn = lib().moe_swiglu_q4_forward_stages
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st:
+            raise MoeQ4Error(st, "moe_swiglu_q4_forward_stages")

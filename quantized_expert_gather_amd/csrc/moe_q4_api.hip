@@ -18,11 +18,13 @@ UnionWorkspace union_workspace_layout(int L, int k, int E, int H, int I) {
   UnionWorkspace w{};
   const size_t pairs = (size_t)L * (size_t)k;
   size_t off = 0;
-  w.hdr = off;  off = round256(off + 256);
-  w.cnt = off;  off = round256(off + (size_t)(H / 32) * 4);
-  w.hbuf = off; off = round256(off + pairs * (size_t)(I / 32) * 32 * 4);
-  w.hsum = off; off = round256(off + pairs * (size_t)(I / 32) * 4);
-  w.ys = off;   off = round256(off + pairs * (size_t)H * 4);
+  w.hdr = off;    off = round256(off + 256);
+  w.utab = off;   off = round256(off + pairs * 16);
+  w.slot_w = off; off = round256(off + pairs * 4);
+  w.tslot = off;  off = round256(off + pairs * 4);
+  w.tcount = off; off = round256(off + (size_t)L * 4);
+  w.hbuf = off;   off = round256(off + pairs * (size_t)I * 4);
+  w.ys = off;     off = round256(off + pairs * (size_t)H * 4);
   w.total = off;
   return w;
 }
@@ -133,9 +135,11 @@ int moe_swiglu_q4_forward_stages(const void* x, const int32_t* topk_ids, const f
   a.L = L; a.k = k; a.E = E; a.H = H; a.I = I;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   a.hdr = reinterpret_cast<uint32_t*>(ws + lay.hdr);
-  a.cnt = reinterpret_cast<uint32_t*>(ws + lay.cnt);
-  a.hbuf = reinterpret_cast<uint32_t*>(ws + lay.hbuf);
-  a.hsum = reinterpret_cast<float*>(ws + lay.hsum);
+  a.utab = reinterpret_cast<int4*>(ws + lay.utab);
+  a.slot_w = reinterpret_cast<float*>(ws + lay.slot_w);
+  a.tslot = reinterpret_cast<int32_t*>(ws + lay.tslot);
+  a.tcount = reinterpret_cast<int32_t*>(ws + lay.tcount);
+  a.hbuf = reinterpret_cast<float*>(ws + lay.hbuf);
   a.ys = reinterpret_cast<float*>(ws + lay.ys);
   return union_forward_launch(a, stages, ncu, stream);
 }

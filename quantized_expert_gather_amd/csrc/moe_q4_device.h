@@ -13,11 +13,6 @@
 
 namespace moeq4 {
 
-// Rows of one work item.  32 rows of the gate/up output are exactly one
-// 32-element input position of the down projection, so a work item can
-// finish that position's hidden values and their per-position sum.
-constexpr int kRows = 32;
-
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Exponent bits of bf16 128.0 in both halves: OR-ing a 4-bit code q into the
@@ -74,11 +69,23 @@ __device__ __forceinline__ float sum8_bf16(uint4 v, float acc) {
   return acc;
 }
 
-// Sum over the `width` lanes of an aligned lane group (width a power of two <= 64).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the WIDTH lanes of an aligned lane group (WIDTH a power of two
+// <= 64); every lane of the group receives the sum.  Within 16-lane rows the
+// steps are DPP lane permutes (xor 1, xor 2, half-row mirror, row mirror);
+// across rows they are lane shuffles.
 template <int WIDTH>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int off = WIDTH / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  if constexpr (WIDTH >= 2) v += dpp_f32<0xB1>(v);   // quad_perm(1,0,3,2)
+  if constexpr (WIDTH >= 4) v += dpp_f32<0x4E>(v);   // quad_perm(2,3,0,1)
+  if constexpr (WIDTH >= 8) v += dpp_f32<0x141>(v);  // row_half_mirror
+  if constexpr (WIDTH >= 16) v += dpp_f32<0x140>(v); // row_mirror
+  if constexpr (WIDTH >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (WIDTH >= 64) v += __shfl_xor(v, 32, 64);
   return v;
 }
 

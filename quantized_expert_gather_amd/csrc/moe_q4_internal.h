@@ -24,19 +24,21 @@ struct UnionArgs {
   void* out;
   int out_f32;
   int L, k, E, H, I;
-  // workspace regions
-  uint32_t* hdr;    // [0] status of the last call, [1] its path, [2] its distinct experts
-  uint32_t* cnt;    // [H/32] per-row-block arrival counters of the down kernel
-  uint32_t* hbuf;   // [pairs][I/32][32] hidden vectors as bf16 hi/lo pairs
-  float* hsum;      // [pairs][I/32] per-32-row sums of hi + lo
+  // workspace regions (pairs = L * k is an upper bound on (expert, token) pairs)
+  uint32_t* hdr;    // [0] status of the last call, [1] its path, [2] its distinct experts u
+  int4* utab;       // [u] (expert id, token mask, first pair slot, 0) per distinct expert
+  float* slot_w;    // [pairs] router weight of each (expert, token) pair
+  int32_t* tslot;   // [L][k] pair slots of each token, ascending expert
+  int32_t* tcount;  // [L] number of pair slots of each token
+  float* hbuf;      // [pairs][I] hidden vectors h = silu(gate) * up, fp32
   float* ys;        // [pairs][H] router-weighted down outputs per (expert, token)
-  // dynamic LDS layout
-  size_t lds_act, lds_asum, lds_hpair, lds_hval, lds_toks, lds_tokw, lds_flag, lds_union;
+  // dynamic LDS layout of the gate/up kernel
+  size_t lds_act, lds_asum, lds_union;
 };
 
 // Workspace layout (byte offsets from the workspace base, 256-aligned regions).
 struct UnionWorkspace {
-  size_t hdr, cnt, hbuf, hsum, ys, total;
+  size_t hdr, utab, slot_w, tslot, tcount, hbuf, ys, total;
 };
 
 UnionWorkspace union_workspace_layout(int L, int k, int E, int H, int I);

@@ -346,6 +346,18 @@ def gen_bank_experts(w: Workload, experts, layer: int, seed: int, device="cpu", 
     return Bank(wg, sg, bg, wu, su, bu, wd, sd, bd)
 
 
+def make_chain_layer(w: Workload, L: int, layer: int, seed: int = 0, device="cuda",
+                     experts_per_chunk: int = 16) -> LayerInput:
+    """One layer of a benchmark chain: compact bank of the used experts, each
+    matrix drawn with one generator per (layer, matrix) in large chunks (fast
+    on a GPU).  Same distributions as :func:`make_layer`; the bytes differ."""
+    ids, tw = layer_routes(w, L, layer, seed)
+    x = gen_x(L, w.H, (seed, w.name, L, layer), device)
+    used, remap = compact_ids(ids)
+    bank = gen_bank(len(used), w.H, w.I, (seed, w.name, L, layer, "chain"), device, experts_per_chunk)
+    return LayerInput(x=x, ids=remap, weights=tw, bank=bank, global_ids=ids)
+
+
 def tiny_layer(device="cpu") -> LayerInput:
     """The tiny configuration exactly: E=8, top-2, H=256, I=128, L=2, seed 0, full bank."""
     w = WORKLOADS["tiny"]
