@@ -13,10 +13,12 @@ adjacent-token overlap follows the measured depth-graded profile.
   the bandwidth of M=4", section "Numbers", counts bytes per expert this way;
   here only distinct experts count, not token x top-k slots).
 * A step is one pass over the four chains (L = 1, 2, 4, 8; 75 layers each).
-  Inputs are resident in HBM before timing.  Every layer is enqueued back to
-  back on one stream; a short GPU delay kernel ahead of each chain lets the
-  host enqueue the whole chain first, so the HIP events between kernels time
-  the GPU, not Python.  Per-kernel durations come from those events.
+  Inputs are resident in HBM before timing.  Every layer of a chain is
+  enqueued back to back on one stream with HIP events only at the chain ends;
+  a GPU delay kernel ahead of each chain lets the host enqueue the whole
+  chain first, so the events time the GPU, not Python.  Per-kernel durations
+  come from chains of one stage alone (gate+up, or down+combine) over the
+  same layers, timed the same way.
 * cpu_baseline: the CPU oracle (test infrastructure) timed on a bounded
   sample of the same layers on the host cores, with the same metric.
 
@@ -97,8 +99,6 @@ def main():
     ap.add_argument("--Ls", default="1,2,4,8")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the baseline sample")
-    ap.add_argument("--stages", default="split", choices=["split", "fused"],
-                    help="split: events between the gate+up and down kernels (per-kernel timing)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -132,18 +132,18 @@ def main():
                 "ids_np": lay.ids, "tw_np": lay.weights,
                 "out": torch.empty((L, H), dtype=torch.bfloat16, device=dev),
             })
-        ws = q.new_workspace(L, k, E, H, I, dev)
         for lay in layers:
             bt = lay["bank"].tensors()
-            if args.stages == "split":
-                lay["calls"] = [q.PreparedForward(lay["x"], lay["ids"], lay["tw"], bt, lay["out"], ws,
-                                                  q.MOE_Q4_STAGE_GATEUP, stream),
-                                q.PreparedForward(lay["x"], lay["ids"], lay["tw"], bt, lay["out"], ws,
-                                                  q.MOE_Q4_STAGE_DOWN, stream)]
-            else:
-                lay["calls"] = [q.PreparedForward(lay["x"], lay["ids"], lay["tw"], bt, lay["out"], ws,
-                                                  q.MOE_Q4_STAGE_ALL, stream)]
-        chains[L] = {"layers": layers, "ws": ws}
+            ws = q.new_workspace(L, k, E, H, I, dev)  # one per layer: stage-only chains read their own tables
+            lay["calls"] = {
+                "all": q.PreparedForward(lay["x"], lay["ids"], lay["tw"], bt, lay["out"], ws, q.MOE_Q4_STAGE_ALL,
+                                         stream),
+                "gateup": q.PreparedForward(lay["x"], lay["ids"], lay["tw"], bt, lay["out"], ws,
+                                            q.MOE_Q4_STAGE_GATEUP, stream),
+                "down": q.PreparedForward(lay["x"], lay["ids"], lay["tw"], bt, lay["out"], ws,
+                                          q.MOE_Q4_STAGE_DOWN, stream),
+            }
+        chains[L] = {"layers": layers}
         torch.cuda.synchronize()
         log(f"L={L}: {args.layers} layers generated, mean unique experts "
             f"{np.mean([l['u'] for l in layers]):.2f}, {time.time() - t0:.1f}s, "
@@ -159,84 +159,69 @@ def main():
         per_ms = 1_000_000 / max(a.elapsed_time(b), 1e-3)
         return int(per_ms * ms)
 
-    # host enqueue cost of one chain (no delay): measured on the warmup
-    def run_step(record):
-        """Enqueue one step; returns per-L (start event, [(mid, end) per layer], end event)."""
-        res = {}
-        for L in Ls:
-            layers = chains[L]["layers"]
-            torch.cuda._sleep(sleep_cycles)
-            ev0 = torch.cuda.Event(enable_timing=True)
-            ev0.record()
-            marks = []
-            th = time.perf_counter()
-            for lay in layers:
-                if args.stages == "split":
-                    lay["calls"][0]()
-                    m = torch.cuda.Event(enable_timing=True)
-                    m.record()
-                    lay["calls"][1]()
-                    e = torch.cuda.Event(enable_timing=True)
-                    e.record()
-                    marks.append((m, e))
-                else:
-                    lay["calls"][0]()
-            ev1 = torch.cuda.Event(enable_timing=True)
-            ev1.record()
-            host_ms = (time.perf_counter() - th) * 1e3
-            res[L] = (ev0, marks, ev1, host_ms)
-        return res
+    def run_chain(L, which):
+        """Enqueue one chain of `which` calls behind a delay kernel; returns (start, end, host ms)."""
+        layers = chains[L]["layers"]
+        torch.cuda._sleep(sleep_cycles)
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        th = time.perf_counter()
+        for lay in layers:
+            lay["calls"][which]()
+        ev1.record()
+        return ev0, ev1, (time.perf_counter() - th) * 1e3
+
+    def run_step(which="all"):
+        return {L: run_chain(L, which) for L in Ls}
 
     sleep_cycles = 0
     torch.cuda.synchronize()
-    warm = run_step(False)  # first pass: measures host enqueue time per chain
+    warm = run_step()  # first pass also measures the host enqueue time per chain
     torch.cuda.synchronize()
-    host_chain_ms = max(v[3] for v in warm.values())
+    host_chain_ms = max(v[2] for v in warm.values())
     sleep_cycles = sleep_cycles_for(1.5 * host_chain_ms + 1.0)
     for _ in range(max(0, args.warmup - 1)):
-        run_step(False)
+        run_step()
     torch.cuda.synchronize()
     log(f"warmup done; host enqueue {host_chain_ms:.2f} ms per chain, delay kernel {sleep_cycles} cycles")
 
-    # ---- timed steps ----
+    # ---- timed steps: full forward chains, no events inside a chain ----
     torch.cuda.synchronize()
-    recs = []
-    for _ in range(args.steps):
-        recs.append(run_step(True))
+    recs = [run_step("all") for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    # ---- per-kernel durations: chains of one stage only, same layers ----
+    krecs = {w_: [run_step(w_) for _ in range(max(2, args.steps // 2))] for w_ in ("gateup", "down")}
     torch.cuda.synchronize()
 
     per_L = {}
     tot_bytes = 0.0
     tot_ms = 0.0
     gu_ms, gu_bytes, gu_n = 0.0, 0.0, 0
-    dn_ms, dn_bytes = 0.0, 0.0
+    dn_ms, dn_bytes, dn_n = 0.0, 0.0, 0
     for L in Ls:
         layers = chains[L]["layers"]
+        nl = len(layers)
         u_sum = sum(l["u"] for l in layers)
-        chain_ms = []
-        for rec in recs:
-            ev0, marks, ev1, _ = rec[L]
-            chain_ms.append(ev0.elapsed_time(ev1))
-            if args.stages == "split":
-                prev = ev0
-                for lay, (m, e) in zip(layers, marks):
-                    g = prev.elapsed_time(m)
-                    d = m.elapsed_time(e)
-                    gu_ms += g
-                    dn_ms += d
-                    gu_bytes += lay["u"] * gateup_bytes(H, I) + 2 * L * H + 8 * L * k
-                    dn_bytes += lay["u"] * down_bytes(H, I) + 2 * L * H + 8 * L * k
-                    gu_n += 1
-                    prev = e
+        chain_ms = [rec[L][0].elapsed_time(rec[L][1]) for rec in recs]
+        g_ms = [rec[L][0].elapsed_time(rec[L][1]) for rec in krecs["gateup"]]
+        d_ms = [rec[L][0].elapsed_time(rec[L][1]) for rec in krecs["down"]]
+        lay_bytes_gu = sum(l["u"] * gateup_bytes(H, I) + 2 * L * H + 8 * L * k for l in layers)
+        lay_bytes_dn = sum(l["u"] * down_bytes(H, I) + 2 * L * H + 8 * L * k for l in layers)
+        gu_ms += sum(g_ms); gu_bytes += lay_bytes_gu * len(g_ms); gu_n += nl * len(g_ms)
+        dn_ms += sum(d_ms); dn_bytes += lay_bytes_dn * len(d_ms); dn_n += nl * len(d_ms)
         med = float(np.median(chain_ms))
-        us_layer = med * 1e3 / len(layers)
+        us_layer = med * 1e3 / nl
         gbps = u_sum * eb / (med * 1e-3) / 1e9
         per_L[str(L)] = {"us_per_layer": round(us_layer, 2), "eff_GBps": round(gbps, 1),
-                         "frac_peak": round(gbps / PEAK_HBM_GBPS, 4), "u_mean": round(u_sum / len(layers), 2),
-                         "chain_ms_median": round(med, 4), "host_enqueue_ms": round(warm[L][3], 3)}
+                         "frac_peak": round(gbps / PEAK_HBM_GBPS, 4), "u_mean": round(u_sum / nl, 2),
+                         "gateup_us": round(float(np.median(g_ms)) * 1e3 / nl, 2),
+                         "down_combine_us": round(float(np.median(d_ms)) * 1e3 / nl, 2),
+                         "chain_ms_median": round(med, 4), "host_enqueue_ms": round(warm[L][2], 3)}
         tot_bytes += u_sum * eb * len(recs)
         tot_ms += sum(chain_ms)
-        log(f"L={L}: {us_layer:.2f} us/layer, {gbps:.0f} GB/s effective ({gbps / PEAK_HBM_GBPS * 100:.1f}% of 8 TB/s)")
+        log(f"L={L}: {us_layer:.2f} us/layer, {gbps:.0f} GB/s effective ({gbps / PEAK_HBM_GBPS * 100:.1f}% of 8 TB/s);"
+            f" gate+up {per_L[str(L)]['gateup_us']:.1f} us, down+combine {per_L[str(L)]['down_combine_us']:.1f} us")
 
     value = tot_bytes / (tot_ms * 1e-3) / 1e9
     ms_per_step = tot_ms / len(recs)
@@ -252,7 +237,7 @@ def main():
     if "1" in per_L and "2" in per_L:
         result["L2_over_L1_time"] = round(per_L["2"]["us_per_layer"] / per_L["1"]["us_per_layer"], 3)
 
-    if args.stages == "split" and gu_n:
+    if gu_n:
         achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
         ratio = read_traffic_profile()
         result["roofline"] = {
@@ -262,9 +247,11 @@ def main():
             "traffic": None if ratio is None else round(ratio * gu_bytes / gu_n, 0),
             "avg_launch_us": round(gu_ms * 1e3 / gu_n, 3),
             "algorithmic_bytes_per_launch": round(gu_bytes / gu_n, 0),
+            "timing": "back-to-back chains of this kernel alone, HIP events at the chain ends",
         }
-        result["down_kernel"] = {"achieved_GBps": round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1),
-                                 "avg_launch_us": round(dn_ms * 1e3 / gu_n, 3)}
+        result["down_kernel"] = {"kernel": "k_down + k_combine",
+                                 "achieved_GBps": round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1),
+                                 "avg_launch_us": round(dn_ms * 1e3 / dn_n, 3)}
 
     # ---- CPU oracle baseline on a bounded sample ----
     if not args.no_cpu:

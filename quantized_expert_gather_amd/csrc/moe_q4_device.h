@@ -15,18 +15,27 @@ namespace moeq4 {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-// Exponent bits of bf16 128.0 in both halves: OR-ing a 4-bit code q into the
-// low mantissa bits of each half gives the bf16 pair (128 + q_lo, 128 + q_hi)
-// exactly (bf16 has 7 mantissa bits; at exponent 2^7 one mantissa step is 1).
-constexpr uint32_t kMagic128 = 0x43004300u;
+// Four copies of the high byte of bf16 128.0 (0x4300).  A byte permute that
+// places a 4-bit code q under each copy yields the bf16 value 128 + q exactly
+// (bf16 has 7 mantissa bits; at exponent 2^7 one mantissa step is 1).
+constexpr uint32_t kMagicBytes = 0x43434343u;
+// Same for fp16 1024.0 (0x6400): 10 mantissa bits, one step is 1 at 2^10.
+constexpr uint32_t kMagicBytesF16 = 0x64646464u;
 
 // Splits one 32-bit word of eight codes (nibble c holds element c) into four
-// bf16 pairs: out[kk] = (128 + q[kk], 128 + q[kk + 4]) in (low, high) halves.
-__device__ __forceinline__ void unpack_word(uint32_t w, uint32_t out[4]) {
-  out[0] = (w & 0x000F000Fu) | kMagic128;
-  out[1] = ((w >> 4) & 0x000F000Fu) | kMagic128;
-  out[2] = ((w >> 8) & 0x000F000Fu) | kMagic128;
-  out[3] = ((w >> 12) & 0x000F000Fu) | kMagic128;
+// bf16 pairs (low half, high half):
+//   out[0] = (128+q0, 128+q2)  out[1] = (128+q4, 128+q6)
+//   out[2] = (128+q1, 128+q3)  out[3] = (128+q5, 128+q7)
+// Three mask/shift ops isolate the even and odd nibbles as bytes; each pair
+// is then one v_perm_b32 that interleaves two of those bytes with 0x43 bytes.
+__device__ __forceinline__ void unpack_word(uint32_t w, uint32_t magic, uint32_t out[4]) {
+  const uint32_t ev = w & 0x0F0F0F0Fu;          // bytes: q0 q2 q4 q6
+  const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;   // bytes: q1 q3 q5 q7
+  // selector bytes 0-3 pick bytes of the second operand, 4-7 of the first
+  out[0] = __builtin_amdgcn_perm(magic, ev, 0x04010400u);
+  out[1] = __builtin_amdgcn_perm(magic, ev, 0x04030402u);
+  out[2] = __builtin_amdgcn_perm(magic, od, 0x04010400u);
+  out[3] = __builtin_amdgcn_perm(magic, od, 0x04030402u);
 }
 
 // acc + a.lo * b.lo + a.hi * b.hi with bf16 inputs and fp32 accumulation
@@ -34,6 +43,20 @@ __device__ __forceinline__ void unpack_word(uint32_t w, uint32_t out[4]) {
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b),
                                          acc, false);
+}
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// acc + a.lo * b.lo + a.hi * b.hi with fp16 inputs and fp32 accumulation
+// (v_dot2c_f32_f16; fp16 x fp16 products are exact in fp32).
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), acc, false);
+}
+
+// Value of lane 4*(lane/4) + A of the caller's quad (DPP quad_perm broadcast).
+template <int A>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, A * 0x55, 0xF, 0xF, false);
 }
 
 __device__ __forceinline__ float bf16_lo_to_f32(uint32_t v) { return __uint_as_float(v << 16); }
@@ -50,15 +73,20 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 // Reorders eight consecutive bf16 values e0..e7 (packed two per word, low
 // half first) into the pairs that unpack_word produces for codes:
-// (e0,e4), (e1,e5), (e2,e6), (e3,e7).
+// (e0,e2), (e4,e6), (e1,e3), (e5,e7).
 __device__ __forceinline__ uint4 pair_activations(uint4 v) {
   uint4 r;
-  r.x = (v.x & 0xFFFFu) | (v.z << 16);
-  r.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
-  r.z = (v.y & 0xFFFFu) | (v.w << 16);
-  r.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+  r.x = (v.x & 0xFFFFu) | (v.y << 16);
+  r.y = (v.z & 0xFFFFu) | (v.w << 16);
+  r.z = (v.x >> 16) | (v.y & 0xFFFF0000u);
+  r.w = (v.z >> 16) | (v.w & 0xFFFF0000u);
   return r;
 }
+
+// Element index (0..7) of the low and high halves of pair kk produced by
+// unpack_word / pair_activations.
+__device__ __forceinline__ constexpr int pair_lo(int kk) { return (kk & 2) ? ((kk & 1) ? 5 : 1) : ((kk & 1) ? 4 : 0); }
+__device__ __forceinline__ constexpr int pair_hi(int kk) { return pair_lo(kk) + 2; }
 
 // Sum of eight bf16 values packed in a uint4, ascending element order.
 __device__ __forceinline__ float sum8_bf16(uint4 v, float acc) {
@@ -86,6 +114,17 @@ __device__ __forceinline__ float group_sum(float v) {
   if constexpr (WIDTH >= 16) v += dpp_f32<0x140>(v); // row_mirror
   if constexpr (WIDTH >= 32) v += __shfl_xor(v, 16, 64);
   if constexpr (WIDTH >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// Maximum over the 64 lanes of a wave; every lane receives it.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  v = fmaxf(v, dpp_f32<0x140>(v));
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  v = fmaxf(v, __shfl_xor(v, 32, 64));
   return v;
 }
 

@@ -45,8 +45,9 @@
 
 namespace moeq4 {
 
-constexpr int kThreads = 512;        // 8 waves per block
+constexpr int kThreads = 512;        // gate/up blocks: 8 waves sharing the staged activations
 constexpr int kWaves = kThreads / 64;
+constexpr int kDownThreads = 256;    // down blocks: 4 independent waves
 constexpr int kDownUnitRows = 64;    // output rows of one down work unit
 constexpr int kDownTokChunk = 2;     // tokens per register pass in down
 
@@ -102,43 +103,118 @@ __global__ __launch_bounds__(256) void k_route_union(const int32_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------
+// shared pieces
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint4 ld16(const unsigned char* base, uint32_t off) {
+  return *reinterpret_cast<const uint4*>(base + off);
+}
+__device__ __forceinline__ uint32_t ld4(const unsigned char* base, uint32_t off) {
+  return *reinterpret_cast<const uint32_t*>(base + off);
+}
+__device__ __forceinline__ uint32_t ld2(const unsigned char* base, uint32_t off) {
+  return *reinterpret_cast<const uint16_t*>(base + off);
+}
+
+__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// D = sum over the 32 inputs of one 16-byte load of a_c * (M + q_c), with the
+// activations a as 16 packed pairs in code order; M = 128 (bf16 pairs) or
+// 1024 (fp16 pairs).
+template <bool F16>
+__device__ __forceinline__ float dot32(const uint4 w, const uint32_t (&av)[16], uint32_t magic, float d) {
+  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int wi = 0; wi < 4; ++wi) {
+    uint32_t q[4];
+    unpack_word(ww[wi], magic, q);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) d = F16 ? dot2_f16(q[kk], av[4 * wi + kk], d) : dot2_bf16(q[kk], av[4 * wi + kk], d);
+  }
+  return d;
+}
+
+// Scale and bias of the 64-input group that holds this lane's 32 inputs,
+// packed as bf16 scale (low half) | bf16 bias (high half).
+//
+// Quad-shared form: the four lanes of a quad cover two consecutive groups;
+// lane A of the quad loaded one dword (both groups) of array A, so two
+// broadcasts and one byte permute give every lane its own pair.  `sel`
+// picks the low (even group) or high (odd group) halves.
+template <int AS, int AB>
+__device__ __forceinline__ uint32_t quad_scale_bias(uint32_t q, uint32_t sel) {
+  return __builtin_amdgcn_perm(quad_bcast<AB>(q), quad_bcast<AS>(q), sel);
+}
+
+// ---------------------------------------------------------------------------
 // fused gate + up
 // ---------------------------------------------------------------------------
 
 // Packed weights of one gate/up work unit held by one lane: PPL positions x
-// RG rows x {gate, up}, each a 16-byte load plus its (scale, bias) pair.
+// RG rows x {gate, up}, each a 16-byte load, plus scales and biases: with
+// quad-shared loads one dword per (position, row) (array = lane % 4: gate
+// scale, gate bias, up scale, up bias), otherwise one packed pair per
+// (position, row, matrix).
 template <int PPL, int RG>
 struct GuFrag {
   uint4 w[PPL][RG][2];
-  uint32_t sb[PPL][RG][2];  // bf16 scale (low half) | bf16 bias (high half)
+  uint32_t sb[PPL][RG][2];
 };
 
-template <int LPR, int PPL, int RG>
-__device__ __forceinline__ void gu_load(const UnionArgs& a, int e, int row, int li, int KU, int KG,
+template <int PPL, int RG>
+struct GuOffsets {
+  uint32_t w[PPL][RG];   // byte offsets into the unit's packed codes
+  uint32_t s[PPL][RG];   // byte offsets into the unit's scale / bias rows
+};
+
+template <int PPL, int RG, bool FULL, bool QS>
+__device__ __forceinline__ void gu_load(const UnionArgs& a, size_t row0, int KU, int KG, int li, int lpr,
+                                        const unsigned char* lane_sbase, const GuOffsets<PPL, RG>& o,
                                         GuFrag<PPL, RG>& f) {
+  const unsigned char* wg = reinterpret_cast<const unsigned char*>(a.wg) + row0 * KU * 16;
+  const unsigned char* wu = reinterpret_cast<const unsigned char*>(a.wu) + row0 * KU * 16;
+  const size_t soff = row0 * KG * 2;
 #pragma unroll
   for (int p = 0; p < PPL; ++p) {
-    const int j = li + LPR * p;
-    if (j < KU) {
+    if (FULL || li + lpr * p < KU) {
 #pragma unroll
       for (int r = 0; r < RG; ++r) {
-        const size_t rr = (size_t)e * a.I + row + r;
-        f.w[p][r][0] = reinterpret_cast<const uint4*>(a.wg)[rr * KU + j];
-        f.w[p][r][1] = reinterpret_cast<const uint4*>(a.wu)[rr * KU + j];
-        const size_t g = rr * KG + (j >> 1);
-        f.sb[p][r][0] = (uint32_t)a.sg[g] | ((uint32_t)a.bg[g] << 16);
-        f.sb[p][r][1] = (uint32_t)a.su[g] | ((uint32_t)a.bu[g] << 16);
+        f.w[p][r][0] = ld16(wg, o.w[p][r]);
+        f.w[p][r][1] = ld16(wu, o.w[p][r]);
+        if (QS) {
+          f.sb[p][r][0] = ld4(lane_sbase + soff, o.s[p][r]);
+        } else {
+          const unsigned char* base = reinterpret_cast<const unsigned char*>(a.sg) + soff;
+          f.sb[p][r][0] = ld2(base, o.s[p][r]) |
+                          (ld2(reinterpret_cast<const unsigned char*>(a.bg) + soff, o.s[p][r]) << 16);
+          f.sb[p][r][1] = ld2(reinterpret_cast<const unsigned char*>(a.su) + soff, o.s[p][r]) |
+                          (ld2(reinterpret_cast<const unsigned char*>(a.bu) + soff, o.s[p][r]) << 16);
+        }
       }
     }
   }
 }
 
-// One unit: gate and up rows [row, row + RG) of distinct expert i for every
+// One unit: gate and up of RG hidden rows of one distinct expert for every
 // token routed to it, one token at a time (the unit's weights stay in
-// registers); h written to hbuf[(slot0 + token rank) * I + row].
-template <int LPR, int PPL, int RG>
+// registers); h = silu(gate) * up goes to hbuf[(slot0 + token rank) * I + row].
+template <int LPR, int PPL, int RG, bool FULL, bool QS>
 __device__ __forceinline__ void gu_compute(const UnionArgs& a, const GuFrag<PPL, RG>& f, uint32_t mask, int slot0,
-                                           int row, int li, int KU, const uint4* act, const float* asum) {
+                                           int row, int li, int KU, const uint4* act, const float* asum,
+                                           uint32_t sel) {
+  uint32_t sbv[PPL][RG][2];
+#pragma unroll
+  for (int p = 0; p < PPL; ++p)
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      if (QS) {
+        sbv[p][r][0] = quad_scale_bias<0, 1>(f.sb[p][r][0], sel);
+        sbv[p][r][1] = quad_scale_bias<2, 3>(f.sb[p][r][0], sel);
+      } else {
+        sbv[p][r][0] = f.sb[p][r][0];
+        sbv[p][r][1] = f.sb[p][r][1];
+      }
+    }
   uint32_t m = mask;
   for (int c = 0; m; ++c) {
     const int t = __builtin_ctz(m);
@@ -149,7 +225,7 @@ __device__ __forceinline__ void gu_compute(const UnionArgs& a, const GuFrag<PPL,
 #pragma unroll
     for (int p = 0; p < PPL; ++p) {
       const int j = li + LPR * p;
-      if (j < KU) {
+      if (FULL || j < KU) {
         const uint4* xa = act + (size_t)t * 4 * KU + j;
         const uint4 x0 = xa[0], x1 = xa[KU], x2 = xa[2 * KU], x3 = xa[3 * KU];
         const uint32_t xv[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
@@ -159,17 +235,9 @@ __device__ __forceinline__ void gu_compute(const UnionArgs& a, const GuFrag<PPL,
         for (int r = 0; r < RG; ++r)
 #pragma unroll
           for (int mm = 0; mm < 2; ++mm) {
-            const uint4 w = f.w[p][r][mm];
-            uint32_t q[16];
-            unpack_word(w.x, q + 0);
-            unpack_word(w.y, q + 4);
-            unpack_word(w.z, q + 8);
-            unpack_word(w.w, q + 12);
-            float d = 0.0f;
-#pragma unroll
-            for (int kk = 0; kk < 16; ++kk) d = dot2_bf16(q[kk], xv[kk], d);
-            const float sc = bf16_lo_to_f32(f.sb[p][r][mm]);
-            const float bi = bf16_hi_to_f32(f.sb[p][r][mm]) - 128.0f * sc;
+            const float d = dot32<false>(f.w[p][r][mm], xv, kMagicBytes, 0.0f);
+            const float sc = bf16_lo_to_f32(sbv[p][r][mm]);
+            const float bi = bf16_hi_to_f32(sbv[p][r][mm]) - 128.0f * sc;
             acc[r][mm] += sc * d + bi * xs;
           }
       }
@@ -183,7 +251,7 @@ __device__ __forceinline__ void gu_compute(const UnionArgs& a, const GuFrag<PPL,
   }
 }
 
-template <int LPR, int PPL>
+template <int LPR, int PPL, bool FULL, bool QS>
 __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
   constexpr int G = 64 / LPR;           // lane groups per wave
   constexpr int RG = gateup_rows(PPL);
@@ -222,8 +290,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
       a.hdr[2] = (uint32_t)u;
     }
     for (int i = tid; i < u; i += blockDim.x) {
-      const int4 ent = make_int4(s.uniq[i], (int)s.mask[i], s.off[i], 0);
-      a.utab[i] = ent;
+      a.utab[i] = make_int4(s.uniq[i], (int)s.mask[i], s.off[i], 0);
       uint32_t m = s.mask[i];
       for (int c = 0; m; ++c) {
         const int t = __builtin_ctz(m);
@@ -241,45 +308,56 @@ __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
     }
   }
 
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = wave_uniform(tid >> 6);
   const int g = lane / LPR, li = lane % LPR;
+  const int qa = li & 3;                  // this lane's array in the quad-shared scale loads
+  const unsigned char* lane_sbase = reinterpret_cast<const unsigned char*>(
+      qa == 0 ? (const void*)a.sg : qa == 1 ? (const void*)a.bg : qa == 2 ? (const void*)a.su : (const void*)a.bu);
+  const uint32_t sel = ((li >> 1) & 1) ? 0x07060302u : 0x05040100u;
+  GuOffsets<PPL, RG> o;
+#pragma unroll
+  for (int p = 0; p < PPL; ++p)
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      const int j = li + LPR * p;
+      o.w[p][r] = (uint32_t)(((g * RG + r) * KU + j) * 16);
+      const int grp = QS ? 2 * (li >> 2) + (LPR / 2) * p : (j >> 1);
+      o.s[p][r] = (uint32_t)(((g * RG + r) * KG + grp) * 2);
+    }
   const int upe = I / WROWS;                // wave units per expert
   const int nunits = u * upe;
   const int stride = gridDim.x * kWaves;
   int unit = blockIdx.x * kWaves + wave;
 
-  GuFrag<PPL, RG> fa, fb;
-  auto unit_row = [&](int un, int& i) {
-    i = un / upe;
-    return (un - i * upe) * WROWS + g * RG;
+  // unit -> (distinct expert i, first row of the wave unit); units U, U + stride,
+  // U + 2 stride, ... of this wave stream through a ring of three register
+  // fragments: two in flight while the third is computed
+  auto load = [&](int un, GuFrag<PPL, RG>& f) {
+    const int i = un / upe;
+    gu_load<PPL, RG, FULL, QS>(a, (size_t)wave_uniform(s.uniq[i]) * I + (un - i * upe) * WROWS, KU, KG, li, LPR,
+                               lane_sbase, o, f);
   };
-  int ia, ib;
-  if (unit < nunits) {
-    const int row = unit_row(unit, ia);
-    gu_load<LPR, PPL, RG>(a, s.uniq[ia], row, li, KU, KG, fa);
-  }
+  auto compute = [&](int un, const GuFrag<PPL, RG>& f) {
+    const int i = un / upe;
+    gu_compute<LPR, PPL, RG, FULL, QS>(a, f, wave_uniform((int)s.mask[i]), wave_uniform(s.off[i]),
+                                       (un - i * upe) * WROWS + g * RG, li, KU, act, asum, sel);
+  };
+  GuFrag<PPL, RG> f0, f1, f2;
+  if (unit < nunits) load(unit, f0);
+  if (unit + stride < nunits) load(unit + stride, f1);
   while (unit < nunits) {
-    int nxt = unit + stride;
-    if (nxt < nunits) {
-      const int row = unit_row(nxt, ib);
-      gu_load<LPR, PPL, RG>(a, s.uniq[ib], row, li, KU, KG, fb);
-    }
-    {
-      const int row = unit_row(unit, ia);
-      gu_compute<LPR, PPL, RG>(a, fa, s.mask[ia], s.off[ia], row, li, KU, act, asum);
-    }
-    unit = nxt;
+    if (unit + 2 * stride < nunits) load(unit + 2 * stride, f2);
+    compute(unit, f0);
+    unit += stride;
     if (unit >= nunits) break;
-    nxt = unit + stride;
-    if (nxt < nunits) {
-      const int row = unit_row(nxt, ia);
-      gu_load<LPR, PPL, RG>(a, s.uniq[ia], row, li, KU, KG, fa);
-    }
-    {
-      const int row = unit_row(unit, ib);
-      gu_compute<LPR, PPL, RG>(a, fb, s.mask[ib], s.off[ib], row, li, KU, act, asum);
-    }
-    unit = nxt;
+    if (unit + 2 * stride < nunits) load(unit + 2 * stride, f0);
+    compute(unit, f1);
+    unit += stride;
+    if (unit >= nunits) break;
+    if (unit + 2 * stride < nunits) load(unit + 2 * stride, f1);
+    compute(unit, f2);
+    unit += stride;
   }
 }
 
@@ -287,37 +365,49 @@ __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
 // down projection (per expert and token, router-weighted)
 // ---------------------------------------------------------------------------
 
+// RS rows x PPL positions of packed codes plus scales and biases: quad-shared
+// (lane % 4 = 0, 1: scale, bias of row 2k; 2, 3: of row 2k + 1) or one packed
+// pair per (row, position).
 template <int PPL, int RS>
 struct DnFrag {
   uint4 w[RS][PPL];
   uint32_t sb[RS][PPL];
 };
 
-template <int LPR, int PPL, int RS>
-__device__ __forceinline__ void dn_load(const UnionArgs& a, int e, int row, int li, int KU, int KG,
+template <int PPL, int RS>
+struct DnOffsets {
+  uint32_t w[RS][PPL];
+  uint32_t s[RS][PPL];
+};
+
+template <int PPL, int RS, bool FULL, bool QS>
+__device__ __forceinline__ void dn_load(const UnionArgs& a, size_t row0, int KU, int KG, int li, int lpr,
+                                        const unsigned char* lane_sbase, const DnOffsets<PPL, RS>& o,
                                         DnFrag<PPL, RS>& f) {
+  const unsigned char* wd = reinterpret_cast<const unsigned char*>(a.wd) + row0 * KU * 16;
+  const size_t soff = row0 * KG * 2;
 #pragma unroll
-  for (int r = 0; r < RS; ++r) {
-    const size_t rr = (size_t)e * a.H + row + r;
+  for (int r = 0; r < RS; ++r)
 #pragma unroll
-    for (int p = 0; p < PPL; ++p) {
-      const int j = li + LPR * p;
-      if (j < KU) {
-        f.w[r][p] = reinterpret_cast<const uint4*>(a.wd)[rr * KU + j];
-        const size_t gg = rr * KG + (j >> 1);
-        f.sb[r][p] = (uint32_t)a.sd[gg] | ((uint32_t)a.bd[gg] << 16);
+    for (int p = 0; p < PPL; ++p)
+      if (FULL || li + lpr * p < KU) {
+        f.w[r][p] = ld16(wd, o.w[r][p]);
+        if (QS) {
+          if ((r & 1) == 0) f.sb[r][p] = ld4(lane_sbase + soff, o.s[r][p]);
+        } else {
+          f.sb[r][p] = ld2(reinterpret_cast<const unsigned char*>(a.sd) + soff, o.s[r][p]) |
+                       (ld2(reinterpret_cast<const unsigned char*>(a.bd) + soff, o.s[r][p]) << 16);
+        }
       }
-    }
-  }
 }
 
-// One step of a down unit: RS rows of this lane group against the NT staged
-// hidden vectors; each (row, token) result times the token's router weight
-// goes to ys.
-template <int LPR, int PPL, int RS, int NT>
-__device__ __forceinline__ void dn_step(const UnionArgs& a, const DnFrag<PPL, RS>& f, const uint32_t (&hh)[NT][PPL][16],
-                                       const uint32_t (&hl)[NT][PPL][16], const float (&hs)[NT][PPL],
-                                       const float (&tw)[NT], int nt, int slot, int row0, int li, int KU) {
+// One step: RS rows of this lane group against the NT staged hidden vectors
+// (fp16 pairs scaled by 2^k per token); each (row, token) result, times the
+// token's router weight, goes to ys.
+template <int LPR, int PPL, int RS, int NT, bool FULL, bool QS>
+__device__ __forceinline__ void dn_step(const UnionArgs& a, const DnFrag<PPL, RS>& f, const uint32_t (&hv)[NT][PPL][16],
+                                       const float (&hs)[NT][PPL], const float (&tw)[NT], int nt, int slot, int row0,
+                                       int li, int KU, uint32_t sel) {
 #pragma unroll
   for (int r = 0; r < RS; ++r) {
     float acc[NT];
@@ -325,24 +415,18 @@ __device__ __forceinline__ void dn_step(const UnionArgs& a, const DnFrag<PPL, RS
     for (int c = 0; c < NT; ++c) acc[c] = 0.0f;
 #pragma unroll
     for (int p = 0; p < PPL; ++p) {
-      const int j = li + LPR * p;
-      if (j < KU) {
-        const uint4 w = f.w[r][p];
-        uint32_t q[16];
-        unpack_word(w.x, q + 0);
-        unpack_word(w.y, q + 4);
-        unpack_word(w.z, q + 8);
-        unpack_word(w.w, q + 12);
-        const float sc = bf16_lo_to_f32(f.sb[r][p]);
-        const float bi = bf16_hi_to_f32(f.sb[r][p]) - 128.0f * sc;
+      if (FULL || li + LPR * p < KU) {
+        uint32_t sb;
+        if (QS)
+          sb = (r & 1) ? quad_scale_bias<2, 3>(f.sb[r & ~1][p], sel) : quad_scale_bias<0, 1>(f.sb[r][p], sel);
+        else
+          sb = f.sb[r][p];
+        const float sc = bf16_lo_to_f32(sb);
+        const float bi = bf16_hi_to_f32(sb) - 1024.0f * sc;
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
           if (c < nt) {
-            float d = 0.0f;
-#pragma unroll
-            for (int kk = 0; kk < 16; ++kk) d = dot2_bf16(q[kk], hh[c][p][kk], d);
-#pragma unroll
-            for (int kk = 0; kk < 16; ++kk) d = dot2_bf16(q[kk], hl[c][p][kk], d);
+            const float d = dot32<true>(f.w[r][p], hv[c][p], kMagicBytesF16, 0.0f);
             acc[c] += sc * d + bi * hs[c][p];
           }
         }
@@ -358,14 +442,14 @@ __device__ __forceinline__ void dn_step(const UnionArgs& a, const DnFrag<PPL, RS
   }
 }
 
-template <int LPR, int PPL>
-__global__ __launch_bounds__(kThreads) void k_down(UnionArgs a) {
+template <int LPR, int PPL, bool FULL, bool QS>
+__global__ __launch_bounds__(kDownThreads) void k_down(UnionArgs a) {
   constexpr int G = 64 / LPR;
-  constexpr int RS = down_rows(G);       // a wave step covers G * RS rows (<= 64)
+  constexpr int RS = down_rows(G);       // a wave step covers G * RS rows
   constexpr int WSTEP = G * RS;
-  constexpr int NSTEP = kDownUnitRows / WSTEP;
   constexpr int NT = kDownTokChunk;
-  static_assert(NSTEP >= 1 && NSTEP * WSTEP == kDownUnitRows, "down step shape");
+  constexpr int NW = kDownThreads / 64;
+  static_assert(!QS || RS % 2 == 0, "quad-shared scales pair rows");
   extern __shared__ __align__(16) unsigned char smem[];
   int4* utab = reinterpret_cast<int4*>(smem);
   const int H = a.H, I = a.I;
@@ -375,68 +459,120 @@ __global__ __launch_bounds__(kThreads) void k_down(UnionArgs a) {
   for (int i = tid; i < u; i += blockDim.x) utab[i] = a.utab[i];
   __syncthreads();
 
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = wave_uniform(tid >> 6);
   const int g = lane / LPR, li = lane % LPR;
-  const int upe = H / kDownUnitRows;
-  const int nunits = u * upe;
-  const int stride = gridDim.x * kWaves;
+  const int qa = li & 3;
+  const unsigned char* lane_sbase =
+      reinterpret_cast<const unsigned char*>((qa & 1) ? (const void*)a.bd : (const void*)a.sd);
+  const uint32_t sel = ((li >> 1) & 1) ? 0x07060302u : 0x05040100u;
+  DnOffsets<PPL, RS> o;
+#pragma unroll
+  for (int r = 0; r < RS; ++r)
+#pragma unroll
+    for (int p = 0; p < PPL; ++p) {
+      const int j = li + LPR * p;
+      o.w[r][p] = (uint32_t)(((g * RS + r) * KU + j) * 16);
+      const int srow = QS ? (r & ~1) + (qa >> 1) : r;
+      const int grp = QS ? 2 * (li >> 2) + (LPR / 2) * p : (j >> 1);
+      o.s[r][p] = (uint32_t)(((g * RS + srow) * KG + grp) * 2);
+    }
 
-  for (int unit = blockIdx.x * kWaves + wave; unit < nunits; unit += stride) {
-    const int i = unit / upe;
-    const int rbase = (unit - i * upe) * kDownUnitRows + g * RS;
+  // this wave's contiguous share of the (distinct expert, row step) sequence
+  const int spe = H / WSTEP;
+  const int total = u * spe;
+  const int nwaves = gridDim.x * NW;
+  const int per = (total + nwaves - 1) / nwaves;
+  const int f_begin = min(total, (blockIdx.x * NW + wave) * per);
+  const int f_end = min(total, f_begin + per);
+
+  for (int f = f_begin; f < f_end;) {
+    const int i = f / spe;
+    const int seg_end = min(f_end, (i + 1) * spe);
     const int4 ent = utab[i];
-    const int e = ent.x, slot0 = ent.z;
-    const int ntok = __popc((uint32_t)ent.y);
+    const int e = wave_uniform(ent.x), slot0 = wave_uniform(ent.z);
+    const int ntok = __popc((uint32_t)wave_uniform(ent.y));
+    const size_t ebase = (size_t)e * H;
     for (int t0 = 0; t0 < ntok; t0 += NT) {
       const int nt = min(NT, ntok - t0);
-      // hidden vectors of up to NT tokens -> exact bf16 hi/lo pairs in code
-      // order, plus the sum of hi + lo over each 32-input position
-      uint32_t hh[NT][PPL][16], hl[NT][PPL][16];
+      // hidden vectors of up to NT tokens, each scaled by a power of two so
+      // that its largest magnitude lies in [2^13, 2^14), rounded to fp16 pairs
+      // in code order; hs = sum of the fp16 values per 32-input position
+      uint32_t hv[NT][PPL][16];
       float hs[NT][PPL], tw[NT];
 #pragma unroll
       for (int c = 0; c < NT; ++c) {
         const int slot = slot0 + t0 + (c < nt ? c : 0);
-        tw[c] = a.slot_w[slot];
+        float v[PPL][32];
+        float mx = 0.0f;
 #pragma unroll
         for (int p = 0; p < PPL; ++p) {
           const int j = li + LPR * p;
-          float sum = 0.0f;
-          if (j < KU) {
+          if (FULL || j < KU) {
             const float4* src = reinterpret_cast<const float4*>(a.hbuf + (size_t)slot * I + 32 * j);
 #pragma unroll
-            for (int wi = 0; wi < 4; ++wi) {
-              const float4 v0 = src[2 * wi], v1 = src[2 * wi + 1];
-              const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-              uint32_t hb[8], lb[8];
-#pragma unroll
-              for (int n = 0; n < 8; ++n) {
-                hb[n] = f32_to_bf16_rne(v[n]);
-                const float hf = __uint_as_float(hb[n] << 16);
-                lb[n] = f32_to_bf16_rne(v[n] - hf);
-                sum += hf + __uint_as_float(lb[n] << 16);
-              }
-#pragma unroll
-              for (int kk = 0; kk < 4; ++kk) {
-                hh[c][p][4 * wi + kk] = hb[kk] | (hb[kk + 4] << 16);
-                hl[c][p][4 * wi + kk] = lb[kk] | (lb[kk + 4] << 16);
-              }
+            for (int q4 = 0; q4 < 8; ++q4) {
+              const float4 f4 = src[q4];
+              v[p][4 * q4 + 0] = f4.x; v[p][4 * q4 + 1] = f4.y; v[p][4 * q4 + 2] = f4.z; v[p][4 * q4 + 3] = f4.w;
             }
+          } else {
+#pragma unroll
+            for (int n = 0; n < 32; ++n) v[p][n] = 0.0f;
+          }
+#pragma unroll
+          for (int n = 0; n < 32; ++n) mx = fmaxf(mx, fabsf(v[p][n]));
+        }
+        mx = wave_max(mx);
+        const int ex = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) : 0;
+        const float up = __builtin_ldexpf(1.0f, 14 - ex);
+        tw[c] = a.slot_w[slot] * __builtin_ldexpf(1.0f, ex - 14);
+#pragma unroll
+        for (int p = 0; p < PPL; ++p) {
+          float sum = 0.0f;
+#pragma unroll
+          for (int wi = 0; wi < 4; ++wi) {
+            _Float16 hb[8];
+#pragma unroll
+            for (int n = 0; n < 8; ++n) {
+              hb[n] = (_Float16)(v[p][8 * wi + n] * up);
+              sum += (float)hb[n];
+            }
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+              hv[c][p][4 * wi + kk] = (uint32_t)__builtin_bit_cast(uint16_t, hb[pair_lo(kk)]) |
+                                      ((uint32_t)__builtin_bit_cast(uint16_t, hb[pair_hi(kk)]) << 16);
           }
           hs[c][p] = sum;
         }
       }
 
-      DnFrag<PPL, RS> fa, fb;
-      dn_load<LPR, PPL, RS>(a, e, rbase, li, KU, KG, fa);
+      // steps st, st+1, ... of this segment stream through a ring of three
+      // register fragments: two in flight while the third is computed
+      auto load = [&](int sx, DnFrag<PPL, RS>& fr) {
+        dn_load<PPL, RS, FULL, QS>(a, ebase + (size_t)(sx - i * spe) * WSTEP, KU, KG, li, LPR, lane_sbase, o, fr);
+      };
+      auto step = [&](int sx, const DnFrag<PPL, RS>& fr) {
+        dn_step<LPR, PPL, RS, NT, FULL, QS>(a, fr, hv, hs, tw, nt, slot0 + t0, (sx - i * spe) * WSTEP + g * RS, li,
+                                            KU, sel);
+      };
+      DnFrag<PPL, RS> f0, f1, f2;
+      int st = f;
+      load(st, f0);
+      if (st + 1 < seg_end) load(st + 1, f1);
 #pragma unroll 1
-      for (int st = 0; st < NSTEP; st += 2) {
-        if (st + 1 < NSTEP) dn_load<LPR, PPL, RS>(a, e, rbase + (st + 1) * WSTEP, li, KU, KG, fb);
-        dn_step<LPR, PPL, RS, NT>(a, fa, hh, hl, hs, tw, nt, slot0 + t0, rbase + st * WSTEP, li, KU);
-        if (st + 1 >= NSTEP) break;
-        if (st + 2 < NSTEP) dn_load<LPR, PPL, RS>(a, e, rbase + (st + 2) * WSTEP, li, KU, KG, fa);
-        dn_step<LPR, PPL, RS, NT>(a, fb, hh, hl, hs, tw, nt, slot0 + t0, rbase + (st + 1) * WSTEP, li, KU);
+      while (st < seg_end) {
+        if (st + 2 < seg_end) load(st + 2, f2);
+        step(st, f0);
+        if (++st >= seg_end) break;
+        if (st + 2 < seg_end) load(st + 2, f0);
+        step(st, f1);
+        if (++st >= seg_end) break;
+        if (st + 2 < seg_end) load(st + 2, f1);
+        step(st, f2);
+        ++st;
       }
     }
+    f = seg_end;
   }
 }
 
@@ -492,19 +628,24 @@ int positions_per_lane(int KU, int lpr, bool down) {
   return 0;
 }
 
-template <int LPR, int PPL>
+template <int LPR, int PPL, bool FULL, bool QS>
 struct GateUpK {
-  static const void* fn() { return reinterpret_cast<const void*>(&k_gateup<LPR, PPL>); }
+  static const void* fn() { return reinterpret_cast<const void*>(&k_gateup<LPR, PPL, FULL, QS>); }
 };
-template <int LPR, int PPL>
+template <int LPR, int PPL, bool FULL, bool QS>
 struct DownK {
-  static const void* fn() { return reinterpret_cast<const void*>(&k_down<LPR, PPL>); }
+  static const void* fn() { return reinterpret_cast<const void*>(&k_down<LPR, PPL, FULL, QS>); }
 };
 
-template <template <int, int> class K>
-const void* pick_kernel(int lpr, int ppl, bool down) {
-#define MOEQ4_CASE(L_, P_) \
-  if (lpr == L_ && ppl == P_) return K<L_, P_>::fn();
+// QS (quad-shared scale loads) needs lane groups of at least 4 and an even
+// number of 64-input groups per row, so that a quad's dword never passes the
+// row's end.
+template <template <int, int, bool, bool> class K>
+const void* pick_kernel(int lpr, int ppl, bool full, bool qs, bool down) {
+#define MOEQ4_CASE(L_, P_)                                                                               \
+  if (lpr == L_ && ppl == P_)                                                                            \
+    return full ? (qs && L_ >= 4 ? K<L_, P_, true, (L_ >= 4)>::fn() : K<L_, P_, true, false>::fn())      \
+                : (qs && L_ >= 4 ? K<L_, P_, false, (L_ >= 4)>::fn() : K<L_, P_, false, false>::fn());
   if (!down) {
     MOEQ4_CASE(64, 1) MOEQ4_CASE(64, 2) MOEQ4_CASE(64, 3) MOEQ4_CASE(64, 4) MOEQ4_CASE(64, 6) MOEQ4_CASE(64, 8)
   } else {
@@ -537,13 +678,13 @@ struct OccCache {
   int blocks;
 };
 
-int blocks_per_cu(const void* fn, size_t lds) {
+int blocks_per_cu(const void* fn, int threads, size_t lds) {
   static OccCache cache[64];
   static int n = 0;
   for (int c = 0; c < n; ++c)
     if (cache[c].fn == fn && cache[c].lds == lds) return cache[c].blocks;
   int b = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, fn, kThreads, lds) != hipSuccess || b < 1) b = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, fn, threads, lds) != hipSuccess || b < 1) b = 1;
   if (n < 64) cache[n++] = OccCache{fn, lds, b};
   return b;
 }
@@ -580,10 +721,10 @@ int union_forward_launch(const UnionArgs& base, unsigned stages, int num_cu, hip
     const int KU = a.H / 32;
     const int lpr = lanes_per_row(KU), ppl = positions_per_lane(KU, lpr, false);
     const size_t lds = gateup_lds_layout(a);
-    const void* fn = pick_kernel<GateUpK>(lpr, ppl, false);
+    const void* fn = pick_kernel<GateUpK>(lpr, ppl, lpr * ppl == KU, (a.H / 64) % 2 == 0, false);
     if (!fn || lds > kMaxLds) return MOE_Q4_ERR_UNSUPPORTED;
     const int wunits = u_max * (a.I / (gateup_rows(ppl) * (64 / lpr)));
-    int grid = num_cu * blocks_per_cu(fn, lds);
+    int grid = num_cu * blocks_per_cu(fn, kThreads, lds);
     const int need = (wunits + kWaves - 1) / kWaves;
     if (grid > need) grid = need;
     if (grid < 1) grid = 1;
@@ -596,15 +737,18 @@ int union_forward_launch(const UnionArgs& base, unsigned stages, int num_cu, hip
     const int KU = a.I / 32;
     const int lpr = lanes_per_row(KU), ppl = positions_per_lane(KU, lpr, true);
     const size_t lds = align16((size_t)16 * P);
-    const void* fn = pick_kernel<DownK>(lpr, ppl, true);
+    const void* fn = pick_kernel<DownK>(lpr, ppl, lpr * ppl == KU, (a.I / 64) % 2 == 0, true);
     if (!fn || lds > kMaxLds) return MOE_Q4_ERR_UNSUPPORTED;
-    const int wunits = u_max * (a.H / kDownUnitRows);
-    int grid = num_cu * blocks_per_cu(fn, lds);
-    const int need = (wunits + kWaves - 1) / kWaves;
+    const int groups = 64 / lpr;
+    const int wstep = groups * down_rows(groups);
+    const int steps = u_max * (a.H / wstep);
+    constexpr int nw = kDownThreads / 64;
+    int grid = num_cu * blocks_per_cu(fn, kDownThreads, lds);
+    const int need = (steps + nw - 1) / nw;
     if (grid > need) grid = need;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(reinterpret_cast<void (*)(UnionArgs)>(const_cast<void*>(fn)), dim3(grid), dim3(kThreads),
-                       lds, stream, a);
+    hipLaunchKernelGGL(reinterpret_cast<void (*)(UnionArgs)>(const_cast<void*>(fn)), dim3(grid),
+                       dim3(kDownThreads), lds, stream, a);
     if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;
     dim3 cgrid((a.H / 4 + 255) / 256, a.L);
     hipLaunchKernelGGL(k_combine, cgrid, dim3(256), 0, stream, a);

@@ -1,10 +1,12 @@
 """GPU parity of the union path against the CPU oracle (needs an MI355X).
 
 Bars: union / index outputs bit-exact; fp32 layer outputs within a per-row
-normwise relative error of 1e-3 (the contract), and within 1e-4, the bound
-the fp32 arithmetic of the kernels gives (fp32 accumulation of exact bf16
-products; the affine offset trick costs about 20x cancellation on 2^-24, and
-the hidden vector is carried as an exact-to-2^-17 bf16 hi + lo pair); bf16
+normwise relative error of 1e-3 (the contract), and within 6e-4, the bound
+the kernels' arithmetic gives: gate and up accumulate exact bf16 products in
+fp32 (about 1e-6 after the affine offset's cancellation), while the down
+projection reads the hidden vector h rounded to fp16 after an exact
+power-of-two scaling -- unit roundoff 2^-11 = 4.9e-4 per element, about
+2^-11 / sqrt(3) = 2.8e-4 normwise with random-sign rounding errors; bf16
 outputs equal the round-to-nearest-even of the fp32 outputs bit for bit.
 """
 
@@ -18,7 +20,7 @@ import synth
 pytestmark = pytest.mark.gpu
 
 CONTRACT = 1e-3
-ARITH = 1e-4
+ARITH = 6e-4
 
 
 def _q():
