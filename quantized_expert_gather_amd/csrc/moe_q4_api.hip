@@ -25,6 +25,7 @@ UnionWorkspace union_workspace_layout(int L, int k, int E, int H, int I) {
   w.tcount = off; off = round256(off + (size_t)L * 4);
   w.hbuf = off;   off = round256(off + pairs * (size_t)I * 4);
   w.ys = off;     off = round256(off + pairs * (size_t)H * 4);
+  w.ys_dummy = off; off = round256(off + (size_t)H * 4);
   w.total = off;
   return w;
 }
@@ -141,6 +142,7 @@ int moe_swiglu_q4_forward_stages(const void* x, const int32_t* topk_ids, const f
   a.tcount = reinterpret_cast<int32_t*>(ws + lay.tcount);
   a.hbuf = reinterpret_cast<float*>(ws + lay.hbuf);
   a.ys = reinterpret_cast<float*>(ws + lay.ys);
+  a.ys_dummy = reinterpret_cast<float*>(ws + lay.ys_dummy);
   return union_forward_launch(a, stages, ncu, stream);
 }
 

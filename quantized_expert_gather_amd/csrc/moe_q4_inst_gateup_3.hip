@@ -1,0 +1,22 @@
+// Instantiations of the gate/up kernel, part 3.
+#include "moe_q4_inst.h"
+#include "moe_q4_union_kernels.h"
+
+namespace moeq4 {
+
+#define MOEQ4_GU(L_, P_)                                                                              \
+  if (lpr == L_ && ppl == P_) {                                                                       \
+    if (full) return qs ? (const void*)&k_gateup<L_, P_, true, (L_ >= 4)> : (const void*)&k_gateup<L_, P_, true, false>; \
+    return qs ? (const void*)&k_gateup<L_, P_, false, (L_ >= 4)> : (const void*)&k_gateup<L_, P_, false, false>;       \
+  }
+
+const void* gateup_kernel_3(int lpr, int ppl, bool full, bool qs) {
+  MOEQ4_GU(32, 1)
+  MOEQ4_GU(16, 1)
+  MOEQ4_GU(8, 1)
+  MOEQ4_GU(4, 1)
+  MOEQ4_GU(2, 1)
+  return nullptr;
+}
+
+}  // namespace moeq4

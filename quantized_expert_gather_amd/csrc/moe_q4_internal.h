@@ -32,13 +32,14 @@ struct UnionArgs {
   int32_t* tcount;  // [L] number of pair slots of each token
   float* hbuf;      // [pairs][I] hidden vectors h = silu(gate) * up, fp32
   float* ys;        // [pairs][H] router-weighted down outputs per (expert, token)
+  float* ys_dummy;  // [H] write sink for token slots past an expert's count
   // dynamic LDS layout of the gate/up kernel
   size_t lds_act, lds_asum, lds_union;
 };
 
 // Workspace layout (byte offsets from the workspace base, 256-aligned regions).
 struct UnionWorkspace {
-  size_t hdr, utab, slot_w, tslot, tcount, hbuf, ys, total;
+  size_t hdr, utab, slot_w, tslot, tcount, hbuf, ys, ys_dummy, total;
 };
 
 UnionWorkspace union_workspace_layout(int L, int k, int E, int H, int I);

@@ -1,0 +1,611 @@
+// Kernel templates of the union path of the SwitchGLU-q4 MoE layer for gfx950
+// (MI355X).  Internal header: the instantiation units include it.
+//
+// Kernels (one forward = gateup -> down -> combine on one stream):
+//   k_route_union  the distinct experts of the L*k routes, their token masks,
+//                  summed router weights and the slot -> distinct-id map
+//                  (exported on its own for bit-exact checks).
+//   k_gateup       every block builds the route union and stages the bf16
+//                  activations of all L tokens in LDS once; then each wave,
+//                  with no further barriers, streams work units (one distinct
+//                  expert, a few hidden rows) with the next unit's packed
+//                  gate and up weights already in flight, computes gate and up
+//                  for every token routed to that expert in one pass, and
+//                  writes h = silu(gate) * up in fp32.  Block 0 also writes
+//                  the per-expert and per-token tables the later kernels read.
+//   k_down         each wave streams units (one distinct expert, 64 output
+//                  rows): the expert's hidden vectors are loaded once per unit
+//                  into registers as exact bf16 hi + lo pairs, the down rows
+//                  stream through with the next rows in flight, and each
+//                  (expert, token) output, times the token's router weight, is
+//                  written per pair.
+//   k_combine      out[t] = sum of token t's per-pair outputs in ascending
+//                  expert order (deterministic; no floating-point atomics).
+//
+// Sources (web pages): streaming every distinct routed expert once and
+// applying it to each position routed to it is the union gather of the mlx
+// discussion "Small-L fused expert gather for fine-grained MoE decode"
+// (implication 1 of the overlap section); running gate and up in one pass with
+// SiLU on the gate before the product follows the splash PR "perf: Apple7/8
+// MoE gate and up in one decode pass" (section "What changed") and the
+// SwitchGLU order of the mlx issue "gather_qmm at M=1 streams 4-bit expert
+// weights at ~half the bandwidth of M=4" (moe_bench script).
+//
+// Inner product with affine codes.  For the 32 consecutive inputs c of one
+// 16-byte load (one half of a 64-input (scale s, bias b) group):
+//     sum_c a_c (s q_c + b) = s * D + (b - 128 s) * A,
+//     D = sum_c a_c (128 + q_c),  A = sum_c a_c,
+// where 128 + q_c is built exactly as bf16 by OR-ing the nibble into the
+// mantissa of 128.0, and D accumulates with bf16 dot2 in fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_q4.h"
+#include "moe_q4_device.h"
+#include "moe_q4_internal.h"
+
+namespace moeq4 {
+
+constexpr int kThreads = 512;        // gate/up blocks: 8 waves sharing the staged activations
+constexpr int kWaves = kThreads / 64;
+constexpr int kDownThreads = 256;    // down blocks: 4 independent waves
+constexpr int kDownUnitRows = 64;    // output rows of one down work unit
+constexpr int kDownTokChunk = 2;     // tokens per register pass in down
+
+// hidden rows per lane group in one gate/up unit (fewer when a row needs
+// several 16-byte positions per lane, to keep two units in registers)
+constexpr int gateup_rows(int ppl) { return ppl == 1 ? 2 : 1; }
+// output rows per lane group in one down step
+constexpr int down_rows(int groups) { return groups * 4 <= kDownUnitRows ? 4 : kDownUnitRows / groups; }
+
+// Carves the route-union LDS arrays out of `base` (layout of build_union).
+__device__ __forceinline__ void carve_union(unsigned char* base, int E, int P, UnionLds& s) {
+  const int EW = (E + 31) >> 5;
+  s.bitmap = reinterpret_cast<uint32_t*>(base);
+  s.scan = reinterpret_cast<int32_t*>(s.bitmap + EW);
+  s.uniq = s.scan + EW;
+  s.mask = reinterpret_cast<uint32_t*>(s.uniq + P);
+  s.off = reinterpret_cast<int32_t*>(s.mask + P);
+  s.scal = s.off + P + 1;
+}
+
+// ---------------------------------------------------------------------------
+// shared pieces
+// ---------------------------------------------------------------------------
+
+// Buffer resource: a wave-uniform 128-bit descriptor (base address, byte
+// range) in scalar registers plus a 32-bit per-lane offset keeps address
+// arithmetic off the vector ALU.  A load past the range returns zero without
+// touching memory, which lets the streaming loops issue every prefetch
+// unconditionally (a zero range turns it into a no-op).
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // raw (unformatted) buffer, stride 0: 0x00020000 is the data-format word of
+  // such a resource on gfx9-family parts
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bld16(rsrc_t r, uint32_t off) {
+  const v4i_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+__device__ __forceinline__ uint32_t bld2(rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t ld4(const unsigned char* base, uint32_t off) {
+  return *reinterpret_cast<const uint32_t*>(base + off);
+}
+
+__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Marks the registers of a prefetched fragment as used here, so the wait for
+// its loads lands at this point and not inside the compute loop that follows.
+__device__ __forceinline__ void touch(const uint4& v) { asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w)); }
+__device__ __forceinline__ void touch(uint32_t v) { asm volatile("" ::"v"(v)); }
+
+// D = sum over the 32 inputs of one 16-byte load of a_c * (M + q_c), with the
+// activations a as 16 packed pairs in code order; M = 128 (bf16 pairs) or
+// 1024 (fp16 pairs).
+template <bool F16>
+__device__ __forceinline__ float dot32(const uint4 w, const uint32_t (&av)[16], uint32_t magic, float d) {
+  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int wi = 0; wi < 4; ++wi) {
+    uint32_t q[4];
+    unpack_word(ww[wi], magic, q);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) d = F16 ? dot2_f16(q[kk], av[4 * wi + kk], d) : dot2_bf16(q[kk], av[4 * wi + kk], d);
+  }
+  return d;
+}
+
+// Scale and bias of the 64-input group that holds this lane's 32 inputs,
+// packed as bf16 scale (low half) | bf16 bias (high half).
+//
+// Quad-shared form: the four lanes of a quad cover two consecutive groups;
+// lane A of the quad loaded one dword (both groups) of array A, so two
+// broadcasts and one byte permute give every lane its own pair.  `sel`
+// picks the low (even group) or high (odd group) halves.
+template <int AS, int AB>
+__device__ __forceinline__ uint32_t quad_scale_bias(uint32_t q, uint32_t sel) {
+  return __builtin_amdgcn_perm(quad_bcast<AB>(q), quad_bcast<AS>(q), sel);
+}
+
+// ---------------------------------------------------------------------------
+// fused gate + up
+// ---------------------------------------------------------------------------
+
+// Packed weights of one gate/up work unit held by one lane: PPL positions x
+// RG rows x {gate, up}, each a 16-byte load, plus scales and biases: with
+// quad-shared loads one dword per (position, row) (array = lane % 4: gate
+// scale, gate bias, up scale, up bias), otherwise one packed pair per
+// (position, row, matrix).
+template <int PPL, int RG>
+struct GuFrag {
+  uint4 w[PPL][RG][2];
+  uint32_t sb[PPL][RG][2];
+};
+
+template <int PPL, int RG>
+struct GuOffsets {
+  uint32_t w[PPL][RG];   // byte offsets into the unit's packed codes
+  uint32_t s[PPL][RG];   // byte offsets into the unit's scale / bias rows
+};
+
+// Loads unit `un` (or nothing, with zero-range descriptors, when !valid).
+// Loads the unit whose first row is row0 (plain loads from a wave-uniform
+// row base plus per-lane offsets).
+template <int PPL, int RG, bool FULL, bool QS>
+__device__ __forceinline__ void gu_load(const UnionArgs& a, size_t row0, int nrows, int KU, int KG, int li, int lpr,
+                                        const unsigned char* lane_sbase, const GuOffsets<PPL, RG>& o,
+                                        GuFrag<PPL, RG>& f) {
+  const uint32_t sbb = (uint32_t)(nrows * KG * 2);
+  const unsigned char* wg = reinterpret_cast<const unsigned char*>(a.wg) + row0 * KU * 16;
+  const unsigned char* wu = reinterpret_cast<const unsigned char*>(a.wu) + row0 * KU * 16;
+  const size_t soff = row0 * KG * 2;
+#pragma unroll
+  for (int p = 0; p < PPL; ++p) {
+    if (FULL || li + lpr * p < KU) {
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        f.w[p][r][0] = *reinterpret_cast<const uint4*>(wg + o.w[p][r]);
+        f.w[p][r][1] = *reinterpret_cast<const uint4*>(wu + o.w[p][r]);
+        if (QS) {
+          f.sb[p][r][0] = ld4(lane_sbase + soff, o.s[p][r]);
+        } else {
+          const rsrc_t sg = make_rsrc(reinterpret_cast<const unsigned char*>(a.sg) + row0 * KG * 2, sbb);
+          const rsrc_t bg = make_rsrc(reinterpret_cast<const unsigned char*>(a.bg) + row0 * KG * 2, sbb);
+          const rsrc_t su = make_rsrc(reinterpret_cast<const unsigned char*>(a.su) + row0 * KG * 2, sbb);
+          const rsrc_t bu = make_rsrc(reinterpret_cast<const unsigned char*>(a.bu) + row0 * KG * 2, sbb);
+          f.sb[p][r][0] = bld2(sg, o.s[p][r]) | (bld2(bg, o.s[p][r]) << 16);
+          f.sb[p][r][1] = bld2(su, o.s[p][r]) | (bld2(bu, o.s[p][r]) << 16);
+        }
+      }
+    }
+  }
+}
+
+// One unit: gate and up of RG hidden rows of one distinct expert for every
+// token routed to it, one token at a time (the unit's weights stay in
+// registers); h = silu(gate) * up goes to hbuf[(slot0 + token rank) * I + row].
+template <int LPR, int PPL, int RG, bool FULL, bool QS>
+__device__ __forceinline__ void gu_compute(const UnionArgs& a, const GuFrag<PPL, RG>& f, uint32_t mask, int slot0,
+                                           int row, int li, int KU, const uint4* act, const float* asum,
+                                           uint32_t sel) {
+#pragma unroll
+  for (int p = 0; p < PPL; ++p)
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      touch(f.w[p][r][0]);
+      touch(f.w[p][r][1]);
+      touch(f.sb[p][r][0]);
+      if (!QS) touch(f.sb[p][r][1]);
+    }
+  uint32_t sbv[PPL][RG][2];
+#pragma unroll
+  for (int p = 0; p < PPL; ++p)
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      if (QS) {
+        sbv[p][r][0] = quad_scale_bias<0, 1>(f.sb[p][r][0], sel);
+        sbv[p][r][1] = quad_scale_bias<2, 3>(f.sb[p][r][0], sel);
+      } else {
+        sbv[p][r][0] = f.sb[p][r][0];
+        sbv[p][r][1] = f.sb[p][r][1];
+      }
+    }
+  uint32_t m = mask;
+  for (int c = 0; m; ++c) {
+    const int t = __builtin_ctz(m);
+    m &= m - 1u;
+    float acc[RG][2];
+#pragma unroll
+    for (int r = 0; r < RG; ++r) acc[r][0] = acc[r][1] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < PPL; ++p) {
+      const int j = li + LPR * p;
+      if (FULL || j < KU) {
+        const uint4* xa = act + (size_t)t * 4 * KU + j;
+        const uint4 x0 = xa[0], x1 = xa[KU], x2 = xa[2 * KU], x3 = xa[3 * KU];
+        const uint32_t xv[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                                 x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+        const float xs = asum[(size_t)t * KU + j];
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm) {
+            const float d = dot32<false>(f.w[p][r][mm], xv, kMagicBytes, 0.0f);
+            const float sc = bf16_lo_to_f32(sbv[p][r][mm]);
+            const float bi = bf16_hi_to_f32(sbv[p][r][mm]) - 128.0f * sc;
+            acc[r][mm] += sc * d + bi * xs;
+          }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      const float gt = group_sum<LPR>(acc[r][0]);
+      const float up = group_sum<LPR>(acc[r][1]);
+      // every lane of the group holds the same value: all store it
+      a.hbuf[(size_t)(slot0 + c) * a.I + row + r] = gt / (1.0f + expf(-gt)) * up;
+    }
+  }
+}
+
+template <int LPR, int PPL, bool FULL, bool QS>
+__global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
+  constexpr int G = 64 / LPR;           // lane groups per wave
+  constexpr int RG = gateup_rows(PPL);
+  constexpr int WROWS = G * RG;         // hidden rows of one wave unit
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int H = a.H, I = a.I, k = a.k, L = a.L, E = a.E;
+  const int P = L * k;
+  const int KU = H >> 5, KG = H >> 6;
+  uint4* act = reinterpret_cast<uint4*>(smem + a.lds_act);      // [L][4][KU] bf16 pairs in code order
+  float* asum = reinterpret_cast<float*>(smem + a.lds_asum);     // [L][KU] sums of the 32 inputs
+  UnionLds s;
+  carve_union(smem + a.lds_union, E, P, s);
+
+  // stage all tokens' activations (independent of the union; overlaps it)
+  const int tid = threadIdx.x;
+  for (int it = tid; it < L * KU; it += blockDim.x) {
+    const int t = it / KU, j = it - t * KU;
+    const uint4* xs = reinterpret_cast<const uint4*>(a.x + (size_t)t * H) + 4 * j;
+    float sum = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 v = xs[c];
+      sum = sum8_bf16(v, sum);
+      act[((size_t)t * 4 + c) * KU + j] = pair_activations(v);
+    }
+    asum[(size_t)t * KU + j] = sum;
+  }
+  build_union(a.ids, P, k, E, s);  // ends with a barrier
+  const int u = s.scal[0];
+
+  if (blockIdx.x == 0) {
+    // tables for the down and combine kernels
+    if (tid == 0) {
+      a.hdr[0] = s.scal[1] ? MOE_Q4_DEV_BAD_ID : 0u;  // status of this call
+      a.hdr[1] = MOE_Q4_PATH_UNION;
+      a.hdr[2] = (uint32_t)u;
+    }
+    for (int i = tid; i < u; i += blockDim.x) {
+      a.utab[i] = make_int4(s.uniq[i], (int)s.mask[i], s.off[i], 0);
+      uint32_t m = s.mask[i];
+      for (int c = 0; m; ++c) {
+        const int t = __builtin_ctz(m);
+        m &= m - 1u;
+        a.slot_w[s.off[i] + c] = token_expert_weight(a.ids, a.tw, t, k, s.uniq[i]);
+      }
+    }
+    for (int t = tid; t < L; t += blockDim.x) {
+      int c = 0;
+      for (int i = 0; i < u; ++i) {
+        const uint32_t m = s.mask[i];
+        if ((m >> t) & 1u) a.tslot[t * k + c++] = s.off[i] + __popc(m & ((1u << t) - 1u));
+      }
+      a.tcount[t] = c;
+    }
+  }
+
+  const int lane = tid & 63;
+  const int wave = wave_uniform(tid >> 6);
+  const int g = lane / LPR, li = lane % LPR;
+  const int qa = li & 3;                  // this lane's array in the quad-shared scale loads
+  const unsigned char* lane_sbase = reinterpret_cast<const unsigned char*>(
+      qa == 0 ? (const void*)a.sg : qa == 1 ? (const void*)a.bg : qa == 2 ? (const void*)a.su : (const void*)a.bu);
+  const uint32_t sel = ((li >> 1) & 1) ? 0x07060302u : 0x05040100u;
+  GuOffsets<PPL, RG> o;
+#pragma unroll
+  for (int p = 0; p < PPL; ++p)
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      const int j = li + LPR * p;
+      o.w[p][r] = (uint32_t)(((g * RG + r) * KU + j) * 16);
+      const int grp = QS ? 2 * (li >> 2) + (LPR / 2) * p : (j >> 1);
+      o.s[p][r] = (uint32_t)(((g * RG + r) * KG + grp) * 2);
+    }
+  // units ub, ub + stride, ub + 2 stride, ... of this wave: consecutive units
+  // (adjacent rows) go to adjacent waves, so the chip sweeps each expert's
+  // rows in order.  They stream through a ring of three register fragments,
+  // two in flight while the third is computed; prefetches past the end
+  // repeat the last unit (cache-resident) so every load is unconditional.
+  const int upe = I / WROWS;                // wave units per expert
+  const int nunits = u * upe;
+  const int stride = gridDim.x * kWaves;
+  const int ub = blockIdx.x * kWaves + wave;
+  if (ub >= nunits) return;
+  const int klast = (nunits - 1 - ub) / stride;  // index of this wave's last unit
+  auto load = [&](int kk, GuFrag<PPL, RG>& f) {
+    const int un = ub + min(kk, klast) * stride;
+    const int i = un / upe;
+    gu_load<PPL, RG, FULL, QS>(a, (size_t)wave_uniform(s.uniq[i]) * I + (un - i * upe) * WROWS, WROWS, KU, KG, li,
+                               LPR, lane_sbase, o, f);
+  };
+  auto compute = [&](int kk, const GuFrag<PPL, RG>& f) {
+    const int un = ub + kk * stride;
+    const int i = un / upe;
+    gu_compute<LPR, PPL, RG, FULL, QS>(a, f, wave_uniform((int)s.mask[i]), wave_uniform(s.off[i]),
+                                       (un - i * upe) * WROWS + g * RG, li, KU, act, asum, sel);
+  };
+  GuFrag<PPL, RG> f0, f1, f2;
+  load(0, f0);
+  load(1, f1);
+  for (int kk = 0;; kk += 3) {
+    load(kk + 2, f2);
+    compute(kk, f0);
+    if (kk + 1 > klast) break;
+    load(kk + 3, f0);
+    compute(kk + 1, f1);
+    if (kk + 2 > klast) break;
+    load(kk + 4, f1);
+    compute(kk + 2, f2);
+    if (kk + 3 > klast) break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// down projection (per expert and token, router-weighted)
+// ---------------------------------------------------------------------------
+
+// RS rows x PPL positions of packed codes plus scales and biases: quad-shared
+// (lane % 4 = 0, 1: scale, bias of row 2k; 2, 3: of row 2k + 1) or one packed
+// pair per (row, position).
+template <int PPL, int RS>
+struct DnFrag {
+  uint4 w[RS][PPL];
+  uint32_t sb[RS][PPL];
+};
+
+template <int PPL, int RS>
+struct DnOffsets {
+  uint32_t w[RS][PPL];
+  uint32_t s[RS][PPL];
+};
+
+template <int PPL, int RS, bool FULL, bool QS>
+__device__ __forceinline__ void dn_load(const UnionArgs& a, size_t row0, bool valid, size_t row_fallback, int nrows,
+                                        int KU, int KG, int li, int lpr, const unsigned char* lane_sbase,
+                                        const DnOffsets<PPL, RS>& o, DnFrag<PPL, RS>& f) {
+  const rsrc_t wd = make_rsrc(reinterpret_cast<const unsigned char*>(a.wd) + row0 * KU * 16,
+                              valid ? (uint32_t)(nrows * KU * 16) : 0u);
+  const size_t soff = (valid ? row0 : row_fallback) * KG * 2;
+  const uint32_t sbb = valid ? (uint32_t)(nrows * KG * 2) : 0u;
+#pragma unroll
+  for (int r = 0; r < RS; ++r)
+#pragma unroll
+    for (int p = 0; p < PPL; ++p)
+      if (FULL || li + lpr * p < KU) {
+        f.w[r][p] = bld16(wd, o.w[r][p]);
+        if (QS) {
+          if ((r & 1) == 0) f.sb[r][p] = ld4(lane_sbase + soff, o.s[r][p]);
+        } else {
+          const rsrc_t sd = make_rsrc(reinterpret_cast<const unsigned char*>(a.sd) + row0 * KG * 2, sbb);
+          const rsrc_t bd = make_rsrc(reinterpret_cast<const unsigned char*>(a.bd) + row0 * KG * 2, sbb);
+          f.sb[r][p] = bld2(sd, o.s[r][p]) | (bld2(bd, o.s[r][p]) << 16);
+        }
+      }
+}
+
+// One step: RS rows of this lane group against the NT staged hidden vectors
+// (fp16 pairs scaled by 2^k per token); each (row, token) result, times the
+// token's router weight (and 2^-k), goes to its ys address (a dummy line for
+// token slots past the expert's count).
+template <int LPR, int PPL, int RS, int NT, bool FULL, bool QS>
+__device__ __forceinline__ void dn_step(const UnionArgs& a, const DnFrag<PPL, RS>& f, const uint32_t (&hv)[NT][PPL][16],
+                                       const float (&hs)[NT][PPL], const float (&tw)[NT], float* const (&dst)[NT],
+                                       int row0, int li, int KU, uint32_t sel) {
+#pragma unroll
+  for (int r = 0; r < RS; ++r)
+#pragma unroll
+    for (int p = 0; p < PPL; ++p) {
+      touch(f.w[r][p]);
+      if (!QS || (r & 1) == 0) touch(f.sb[r][p]);
+    }
+#pragma unroll
+  for (int r = 0; r < RS; ++r) {
+    float acc[NT];
+#pragma unroll
+    for (int c = 0; c < NT; ++c) acc[c] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < PPL; ++p) {
+      if (FULL || li + LPR * p < KU) {
+        uint32_t sb;
+        if (QS)
+          sb = (r & 1) ? quad_scale_bias<2, 3>(f.sb[r & ~1][p], sel) : quad_scale_bias<0, 1>(f.sb[r][p], sel);
+        else
+          sb = f.sb[r][p];
+        const float sc = bf16_lo_to_f32(sb);
+        const float bi = bf16_hi_to_f32(sb) - 1024.0f * sc;
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          const float d = dot32<true>(f.w[r][p], hv[c][p], kMagicBytesF16, 0.0f);
+          acc[c] += sc * d + bi * hs[c][p];
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NT; ++c) dst[c][row0 + r] = tw[c] * group_sum<LPR>(acc[c]);
+  }
+}
+
+// One (expert, token chunk) segment of a down wave: stage the chunk's hidden
+// vectors, then stream the wave's row steps gj, gj + wpe, ... (kk <= klast).
+template <int LPR, int PPL, bool FULL, bool QS, int NT, int RS, int WSTEP>
+__device__ __forceinline__ void dn_segment(const UnionArgs& a, int e, size_t ebase, int slot0, int nt, int gj, int wpe,
+                                       int klast, int li, int g, int KU, int KG, int I, int H,
+                                       const unsigned char* lane_sbase, const DnOffsets<PPL, RS>& o,
+                                       uint32_t sel) {
+  (void)e;
+  const int t0 = 0;
+  // prefetches past the last step are zero-range no-ops
+  auto load = [&](int kk, DnFrag<PPL, RS>& fr) {
+    const bool valid = kk <= klast;
+    const size_t row0 = ebase + (size_t)(gj + min(kk, klast) * wpe) * WSTEP;
+    dn_load<PPL, RS, FULL, QS>(a, row0, valid, row0, WSTEP, KU, KG, li, LPR, lane_sbase, o, fr);
+  };
+  DnFrag<PPL, RS> f0, f1, f2;
+  load(0, f0);
+  load(1, f1);
+
+  // hidden vectors of up to NT tokens, each scaled by a power of two so
+  // that its largest magnitude lies in [2^13, 2^14), rounded to fp16 pairs
+  // in code order; hs = sum of the fp16 values per 32-input position
+  uint32_t hv[NT][PPL][16];
+  float hs[NT][PPL], tw[NT];
+  float* dst[NT];
+#pragma unroll
+  for (int c = 0; c < NT; ++c) {
+    const bool live = c < nt;
+    const int slot = slot0 + t0 + (live ? c : 0);
+    float v[PPL][32];
+    float mx = 0.0f;
+#pragma unroll
+    for (int p = 0; p < PPL; ++p) {
+      const int j = li + LPR * p;
+      if (FULL || j < KU) {
+        const float4* src = reinterpret_cast<const float4*>(a.hbuf + (size_t)slot * I + 32 * j);
+#pragma unroll
+        for (int q4 = 0; q4 < 8; ++q4) {
+          const float4 f4 = src[q4];
+          v[p][4 * q4 + 0] = f4.x; v[p][4 * q4 + 1] = f4.y; v[p][4 * q4 + 2] = f4.z; v[p][4 * q4 + 3] = f4.w;
+        }
+      } else {
+#pragma unroll
+        for (int n = 0; n < 32; ++n) v[p][n] = 0.0f;
+      }
+#pragma unroll
+      for (int n = 0; n < 32; ++n) mx = fmaxf(mx, fabsf(v[p][n]));
+    }
+    mx = wave_max(mx);
+    const int ex = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) : 0;
+    const float up = __builtin_ldexpf(1.0f, 14 - ex);
+    tw[c] = live ? a.slot_w[slot] * __builtin_ldexpf(1.0f, ex - 14) : 0.0f;
+    dst[c] = live ? a.ys + (size_t)slot * H : a.ys_dummy;
+#pragma unroll
+    for (int p = 0; p < PPL; ++p) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int wi = 0; wi < 4; ++wi) {
+        _Float16 hb[8];
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          hb[n] = (_Float16)(v[p][8 * wi + n] * up);
+          sum += (float)hb[n];
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          hv[c][p][4 * wi + kk] = (uint32_t)__builtin_bit_cast(uint16_t, hb[pair_lo(kk)]) |
+                                  ((uint32_t)__builtin_bit_cast(uint16_t, hb[pair_hi(kk)]) << 16);
+      }
+      hs[c][p] = sum;
+    }
+  }
+
+  auto step = [&](int kk, const DnFrag<PPL, RS>& fr) {
+    dn_step<LPR, PPL, RS, NT, FULL, QS>(a, fr, hv, hs, tw, dst, (gj + kk * wpe) * WSTEP + g * RS, li, KU, sel);
+  };
+#pragma unroll 1
+  for (int kk = 0;; kk += 3) {
+    load(kk + 2, f2);
+    step(kk, f0);
+    if (kk + 1 > klast) break;
+    load(kk + 3, f0);
+    step(kk + 1, f1);
+    if (kk + 2 > klast) break;
+    load(kk + 4, f1);
+    step(kk + 2, f2);
+    if (kk + 3 > klast) break;
+  }
+}
+
+template <int LPR, int PPL, bool FULL, bool QS, int NT>
+__global__ __launch_bounds__(kDownThreads) void k_down(UnionArgs a) {
+  constexpr int G = 64 / LPR;
+  constexpr int RS = down_rows(G);       // a wave step covers G * RS rows
+  constexpr int WSTEP = G * RS;
+  constexpr int NW = kDownThreads / 64;
+  static_assert(!QS || RS % 2 == 0, "quad-shared scales pair rows");
+  extern __shared__ __align__(16) unsigned char smem[];
+  int4* utab = reinterpret_cast<int4*>(smem);
+  const int H = a.H, I = a.I;
+  const int KU = I >> 5, KG = I >> 6;
+  const int tid = threadIdx.x;
+  const int u = (int)a.hdr[2];
+  for (int i = tid; i < u; i += blockDim.x) utab[i] = a.utab[i];
+  __syncthreads();
+
+  const int lane = tid & 63;
+  const int wave = wave_uniform(tid >> 6);
+  const int g = lane / LPR, li = lane % LPR;
+  const int qa = li & 3;
+  const unsigned char* lane_sbase =
+      reinterpret_cast<const unsigned char*>((qa & 1) ? (const void*)a.bd : (const void*)a.sd);
+  const uint32_t sel = ((li >> 1) & 1) ? 0x07060302u : 0x05040100u;
+  DnOffsets<PPL, RS> o;
+#pragma unroll
+  for (int r = 0; r < RS; ++r)
+#pragma unroll
+    for (int p = 0; p < PPL; ++p) {
+      const int j = li + LPR * p;
+      o.w[r][p] = (uint32_t)(((g * RS + r) * KU + j) * 16);
+      const int srow = QS ? (r & ~1) + (qa >> 1) : r;
+      const int grp = QS ? 2 * (li >> 2) + (LPR / 2) * p : (j >> 1);
+      o.s[r][p] = (uint32_t)(((g * RS + srow) * KG + grp) * 2);
+    }
+
+  // Waves split into groups, one distinct expert per group at a time; inside
+  // a group the waves interleave over the expert's row steps (adjacent waves,
+  // adjacent rows), so each wave stages its expert's hidden vectors once and
+  // the chip sweeps each expert's rows in order.
+  const int spe = H / WSTEP;                     // row steps per expert
+  const int nwaves = gridDim.x * NW;
+  const int wpe = max(1, nwaves / max(u, 1));    // waves per group
+  const int ngroups = nwaves / wpe;
+  const int gw = blockIdx.x * NW + wave;
+  const int grp = gw / wpe, gj = gw - grp * wpe;
+  if (grp >= ngroups) return;
+
+  for (int i = grp; i < u; i += ngroups) {
+    if (gj >= spe) continue;
+    const int klast = (spe - 1 - gj) / wpe;      // this wave's steps: gj + kk * wpe, kk <= klast
+    const int4 ent = utab[i];
+    const int e = wave_uniform(ent.x), slot0 = wave_uniform(ent.z);
+    const int ntok = __popc((uint32_t)wave_uniform(ent.y));
+    const size_t ebase = (size_t)e * H;
+    for (int t0 = 0; t0 < ntok; t0 += NT) {
+      const int nt = min(NT, ntok - t0);
+      if (NT > 1 && nt == 1)
+        dn_segment<LPR, PPL, FULL, QS, 1, RS, WSTEP>(a, e, ebase, slot0 + t0, 1, gj, wpe, klast, li, g, KU, KG, I, H,
+                                                     lane_sbase, o, sel);
+      else
+        dn_segment<LPR, PPL, FULL, QS, NT, RS, WSTEP>(a, e, ebase, slot0 + t0, nt, gj, wpe, klast, li, g, KU, KG, I,
+                                                      H, lane_sbase, o, sel);
+    }
+  }
+}
+
+}  // namespace moeq4
