@@ -99,7 +99,21 @@ def main():
     ap.add_argument("--Ls", default="1,2,4,8")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the baseline sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (reference for hardware "
+                         "byte counters) and exit")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration * 2**20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -223,6 +237,19 @@ def main():
         log(f"L={L}: {us_layer:.2f} us/layer, {gbps:.0f} GB/s effective ({gbps / PEAK_HBM_GBPS * 100:.1f}% of 8 TB/s);"
             f" gate+up {per_L[str(L)]['gateup_us']:.1f} us, down+combine {per_L[str(L)]['down_combine_us']:.1f} us")
 
+    # streaming reference: a plain device copy (read + write bytes / time)
+    ref_src = torch.empty(2 * 2**30, dtype=torch.uint8, device=dev).fill_(1)
+    ref_dst = torch.empty_like(ref_src)
+    ref_dst.copy_(ref_src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        ref_dst.copy_(ref_src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * ref_src.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del ref_src, ref_dst
+
     value = tot_bytes / (tot_ms * 1e-3) / 1e9
     ms_per_step = tot_ms / len(recs)
     result = {
@@ -233,6 +260,7 @@ def main():
                    "I": I, "group_size": 64, "bits": 4, "L": Ls, "layers": args.layers,
                    "bytes_per_expert": eb, "timing": "GPU events, chains enqueued back to back"},
         "per_L": per_L,
+        "stream_ref_copy_GBps": round(copy_gbps, 1),
     }
     if "1" in per_L and "2" in per_L:
         result["L2_over_L1_time"] = round(per_L["2"]["us_per_layer"] / per_L["1"]["us_per_layer"], 3)
