@@ -72,8 +72,8 @@ extern "C" {
 #define MOE_Q4_MAX_E 16384
 
 /* ---- forward stages (moe_swiglu_q4_forward_stages) ---- */
-#define MOE_Q4_STAGE_GATEUP 1u   /* route union + fused gate/up GEMV + silu(gate)*up -> workspace */
-#define MOE_Q4_STAGE_DOWN 2u     /* down GEMV + router-weighted combine -> out                    */
+#define MOE_Q4_STAGE_GATEUP 1u   /* union (or sort) + fused gate/up + silu(gate)*up -> workspace  */
+#define MOE_Q4_STAGE_DOWN 2u     /* down projection + router-weighted combine -> out              */
 #define MOE_Q4_STAGE_ALL 3u
 
 /*
@@ -86,6 +86,9 @@ size_t moe_swiglu_q4_workspace_bytes(int L, int k, int E, int H, int I);
 /*
  * Path the forward call takes for this shape (MOE_Q4_PATH_*), or a negative
  * status (-MOE_Q4_ERR_*) if the shape is invalid or unsupported.  Host only.
+ * The union path serves L <= MOE_Q4_UNION_MAX_L with L * k <= MOE_Q4_MAX_PAIRS
+ * (and its LDS limits); every other valid shape with L <= 65535,
+ * E <= MOE_Q4_MAX_E and L * k < 2^30 takes the sorted path.
  */
 int moe_swiglu_q4_select_path(int L, int k, int E, int H, int I);
 
@@ -111,9 +114,12 @@ int moe_swiglu_q4_select_path(int L, int k, int E, int H, int I);
  *                same time
  *
  * out[t, :] = sum_j topk_weights[t, j] * Wd[e] (silu(Wg[e] x_t) * (Wu[e] x_t)),
- * e = topk_ids[t, j].  Accumulation is fp32; the hidden vector h stays fp32.
- * Results are deterministic (no floating-point atomics).  L == 0 returns
- * MOE_Q4_OK without touching the GPU.
+ * e = topk_ids[t, j].  Accumulation is fp32.  The hidden vector h is never
+ * rounded to bf16: the union path keeps it in fp32 and feeds the down
+ * products an fp16 copy after an exact power-of-two rescale; the sorted path
+ * carries it as a bf16 hi + lo pair (16 significant bits).  Results are
+ * deterministic (no floating-point atomics).  L == 0 returns MOE_Q4_OK
+ * without touching the GPU.
  */
 int moe_swiglu_q4_forward(const void *x, const int32_t *topk_ids, const float *topk_weights,
                           const uint32_t *wg, const void *sg, const void *bg,
@@ -151,6 +157,34 @@ int moe_swiglu_q4_forward_stages(const void *x, const int32_t *topk_ids, const f
 int moe_route_union(const int32_t *topk_ids, const float *topk_weights, int L, int k, int E,
                     int32_t *u, int32_t *uniq_ids, uint32_t *tok_mask, float *uniq_w,
                     int32_t *slot_to_uniq, hipStream_t stream);
+
+/*
+ * Capacity (in tiles) that moe_sort_pairs needs for `tiles` with row tiles of
+ * bm rows: L*k / bm + min(E, L*k) + 1.  Negative status for invalid arguments.
+ */
+int moe_sort_pairs_tiles_max(int L, int k, int E, int bm);
+
+/*
+ * Expert sort of the sorted path, as its own call so it can be checked bit for
+ * bit.  Pair p = t * k + j (route j of token t).  Outputs (device):
+ *   offsets  int32 [E+1]          first sorted position of each expert's pairs;
+ *                                 offsets[E] = number of pairs with a valid id
+ *   perm     int32 [L*k]          sorted position -> pair: valid pairs ordered by
+ *                                 (expert, pair), then pairs with invalid ids by pair
+ *   inv      int32 [L*k]          pair -> sorted position (inverse of perm)
+ *   tiles    int32 [tiles_cap][4] row tiles (expert, first position, rows, 0):
+ *                                 ceil(n_e / bm) tiles per expert, cut at expert
+ *                                 boundaries, ascending expert; 16-byte aligned
+ *   info     uint32 [4]           [0] MOE_Q4_DEV_* status, [1] MOE_Q4_PATH_SORTED,
+ *                                 [2] valid pairs, [3] number of tiles
+ *   scratch  int32 [L*k]          device scratch, contents undefined afterwards
+ * tiles_cap must be at least moe_sort_pairs_tiles_max(L, k, E, bm).  The tile
+ * schedule is the expert-offset one of PR 4567 described on the page "MoE
+ * GatherQMM small-M verify cost" (Facts); the sort is stable in the pair index.
+ */
+int moe_sort_pairs(const int32_t *topk_ids, int L, int k, int E, int bm, int32_t *offsets,
+                   int32_t *perm, int32_t *inv, int32_t *tiles, int tiles_cap, uint32_t *info,
+                   int32_t *scratch, hipStream_t stream);
 
 /*
  * Reads the device status word (MOE_Q4_DEV_* bits) that the last forward

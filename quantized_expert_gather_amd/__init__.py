@@ -43,6 +43,8 @@ EXPORTS = (
     "moe_swiglu_q4_forward",
     "moe_swiglu_q4_forward_stages",
     "moe_route_union",
+    "moe_sort_pairs_tiles_max",
+    "moe_sort_pairs",
     "moe_q4_read_device_status",
     "moe_q4_clear_device_status",
     "moe_q4_status_string",
@@ -78,6 +80,10 @@ def lib() -> ctypes.CDLL:
     L.moe_swiglu_q4_forward_stages.restype = I32
     L.moe_route_union.argtypes = [P, P, I32, I32, I32, P, P, P, P, P, P]
     L.moe_route_union.restype = I32
+    L.moe_sort_pairs_tiles_max.argtypes = [I32] * 4
+    L.moe_sort_pairs_tiles_max.restype = I32
+    L.moe_sort_pairs.argtypes = [P, I32, I32, I32, I32, P, P, P, P, I32, P, P, P]
+    L.moe_sort_pairs.restype = I32
     L.moe_q4_read_device_status.argtypes = [P, P, P, P]
     L.moe_q4_read_device_status.restype = I32
     L.moe_q4_clear_device_status.argtypes = [P, P]
@@ -206,6 +212,36 @@ def moe_route_union(topk_ids: torch.Tensor, topk_weights: torch.Tensor, E: int, 
                                L, k, E, res["u"].data_ptr(), res["uniq_ids"].data_ptr(), res["tok_mask"].data_ptr(),
                                res["uniq_w"].data_ptr(), res["slot_to_uniq"].data_ptr(), _stream_ptr(stream))
     _check(st, "moe_route_union")
+    return res
+
+
+def moe_sort_pairs_tiles_max(L: int, k: int, E: int, bm: int) -> int:
+    n = int(lib().moe_sort_pairs_tiles_max(L, k, E, bm))
+    if n < 0:
+        raise MoeQ4Error(-n, "moe_sort_pairs_tiles_max")
+    return n
+
+
+def moe_sort_pairs(topk_ids: torch.Tensor, E: int, bm: int, stream=None) -> Dict[str, torch.Tensor]:
+    """Expert sort of the pairs and the row-tile list (see include/moe_q4.h).  Returns device tensors;
+    ``tiles`` holds all ``tiles_max`` rows, of which ``info[3]`` are written."""
+    L, k = topk_ids.shape
+    P = L * k
+    cap = moe_sort_pairs_tiles_max(L, k, E, bm)
+    dev = topk_ids.device
+    res = {
+        "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+        "perm": torch.empty(max(P, 1), dtype=torch.int32, device=dev),
+        "inv": torch.empty(max(P, 1), dtype=torch.int32, device=dev),
+        "tiles": torch.empty((cap, 4), dtype=torch.int32, device=dev),
+        "info": torch.empty(4, dtype=torch.int32, device=dev),
+    }
+    scratch = torch.empty(max(P, 1), dtype=torch.int32, device=dev)
+    st = lib().moe_sort_pairs(_dev_ptr(topk_ids, _I32, "topk_ids"), L, k, E, bm, res["offsets"].data_ptr(),
+                              res["perm"].data_ptr(), res["inv"].data_ptr(), res["tiles"].data_ptr(), cap,
+                              res["info"].data_ptr(), scratch.data_ptr(), _stream_ptr(stream))
+    _check(st, "moe_sort_pairs")
+    res["_scratch"] = scratch  # kept alive until the caller has synchronised
     return res
 
 

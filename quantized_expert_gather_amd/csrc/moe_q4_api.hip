@@ -52,6 +52,7 @@ static int select_path(int L, int k, int E, int H, int I) {
   if (L == 0) return MOE_Q4_PATH_NONE;
   if (L <= MOE_Q4_UNION_MAX_L && (long)L * k <= MOE_Q4_MAX_PAIRS && union_shape_supported(L, k, E, H, I))
     return MOE_Q4_PATH_UNION;
+  if (sorted_shape_supported(L, k, E, H, I)) return MOE_Q4_PATH_SORTED;
   return -MOE_Q4_ERR_UNSUPPORTED;
 }
 
@@ -82,6 +83,7 @@ extern "C" {
 size_t moe_swiglu_q4_workspace_bytes(int L, int k, int E, int H, int I) {
   const int path = select_path(L, k, E, H, I);
   if (path <= 0) return 0;
+  if (path == MOE_Q4_PATH_SORTED) return sorted_workspace_layout(L, k, E, H, I).total;
   return union_workspace_layout(L, k, E, H, I).total;
 }
 
@@ -108,8 +110,9 @@ int moe_swiglu_q4_forward_stages(const void* x, const int32_t* topk_ids, const f
       !aligned(topk_ids, 4) || !aligned(topk_weights, 4) || !aligned(sg, 4) || !aligned(bg, 4) ||
       !aligned(su, 4) || !aligned(bu, 4) || !aligned(sd, 4) || !aligned(bd, 4) || !aligned(workspace, 256))
     return MOE_Q4_ERR_ALIGN;
-  const UnionWorkspace lay = union_workspace_layout(L, k, E, H, I);
-  if (workspace_bytes < lay.total) return MOE_Q4_ERR_WORKSPACE;
+  const size_t ws_need = path == MOE_Q4_PATH_SORTED ? sorted_workspace_layout(L, k, E, H, I).total
+                                                     : union_workspace_layout(L, k, E, H, I).total;
+  if (workspace_bytes < ws_need) return MOE_Q4_ERR_WORKSPACE;
 
   const size_t out_bytes = (size_t)L * H * (out_dtype == MOE_Q4_OUT_F32 ? 4 : 2);
   const size_t gu_codes = (size_t)E * I * (H / 8) * 4, gu_sb = (size_t)E * I * (H / 64) * 2;
@@ -117,13 +120,43 @@ int moe_swiglu_q4_forward_stages(const void* x, const int32_t* topk_ids, const f
   const struct { const void* p; size_t n; } ins[] = {
       {x, (size_t)L * H * 2}, {topk_ids, (size_t)L * k * 4}, {topk_weights, (size_t)L * k * 4},
       {wg, gu_codes}, {sg, gu_sb}, {bg, gu_sb}, {wu, gu_codes}, {su, gu_sb}, {bu, gu_sb},
-      {wd, d_codes}, {sd, d_sb}, {bd, d_sb}, {workspace, lay.total}};
+      {wd, d_codes}, {sd, d_sb}, {bd, d_sb}, {workspace, ws_need}};
   for (const auto& in : ins)
     if (overlaps(out, out_bytes, in.p, in.n)) return MOE_Q4_ERR_ALIAS;
+
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  if (path == MOE_Q4_PATH_SORTED) {
+    const SortedWorkspace sw = sorted_workspace_layout(L, k, E, H, I);
+    SortedArgs a{};
+    a.x = static_cast<const uint16_t*>(x);
+    a.ids = topk_ids;
+    a.tw = topk_weights;
+    a.wg = wg; a.sg = static_cast<const uint16_t*>(sg); a.bg = static_cast<const uint16_t*>(bg);
+    a.wu = wu; a.su = static_cast<const uint16_t*>(su); a.bu = static_cast<const uint16_t*>(bu);
+    a.wd = wd; a.sd = static_cast<const uint16_t*>(sd); a.bd = static_cast<const uint16_t*>(bd);
+    a.out = out;
+    a.out_f32 = out_dtype == MOE_Q4_OUT_F32;
+    a.T = L; a.k = k; a.E = E; a.H = H; a.I = I;
+    a.bm = 32 * sorted_row_blocks(L, k, E);
+    a.tiles_max = sorted_tiles_max(L, k, E, a.bm);
+    a.hdr = reinterpret_cast<uint32_t*>(ws + sw.hdr);
+    a.offsets = reinterpret_cast<int32_t*>(ws + sw.offsets);
+    a.perm = reinterpret_cast<int32_t*>(ws + sw.perm);
+    a.inv = reinterpret_cast<int32_t*>(ws + sw.inv);
+    a.rank_tmp = reinterpret_cast<int32_t*>(ws + sw.rank_tmp);
+    a.tiles = reinterpret_cast<int4*>(ws + sw.tiles);
+    a.asum = reinterpret_cast<float*>(ws + sw.asum);
+    a.hhi = reinterpret_cast<uint16_t*>(ws + sw.hhi);
+    a.hlo = reinterpret_cast<uint16_t*>(ws + sw.hlo);
+    a.hsum2 = reinterpret_cast<float*>(ws + sw.hsum2);
+    a.ys = reinterpret_cast<float*>(ws + sw.ys);
+    return sorted_forward_launch(a, stages, stream);
+  }
 
   const int ncu = num_cus();
   if (ncu <= 0) return MOE_Q4_ERR_LAUNCH;
 
+  const UnionWorkspace lay = union_workspace_layout(L, k, E, H, I);
   UnionArgs a{};
   a.x = static_cast<const uint16_t*>(x);
   a.ids = topk_ids;
@@ -134,7 +167,6 @@ int moe_swiglu_q4_forward_stages(const void* x, const int32_t* topk_ids, const f
   a.out = out;
   a.out_f32 = out_dtype == MOE_Q4_OUT_F32;
   a.L = L; a.k = k; a.E = E; a.H = H; a.I = I;
-  unsigned char* ws = static_cast<unsigned char*>(workspace);
   a.hdr = reinterpret_cast<uint32_t*>(ws + lay.hdr);
   a.utab = reinterpret_cast<int4*>(ws + lay.utab);
   a.slot_w = reinterpret_cast<float*>(ws + lay.slot_w);
@@ -167,6 +199,35 @@ int moe_route_union(const int32_t* topk_ids, const float* topk_weights, int L, i
       !aligned(tok_mask, 4) || !aligned(uniq_w, 4) || !aligned(slot_to_uniq, 4))
     return MOE_Q4_ERR_ALIGN;
   return route_union_launch(topk_ids, topk_weights, L, k, E, u, uniq_ids, tok_mask, uniq_w, slot_to_uniq, stream);
+}
+
+int moe_sort_pairs_tiles_max(int L, int k, int E, int bm) {
+  if (L < 0 || k < 1 || E < 1 || bm < 1) return -MOE_Q4_ERR_SHAPE;
+  return sorted_tiles_max(L, k, E, bm);
+}
+
+int moe_sort_pairs(const int32_t* topk_ids, int L, int k, int E, int bm, int32_t* offsets, int32_t* perm,
+                   int32_t* inv, int32_t* tiles, int tiles_cap, uint32_t* info, int32_t* scratch,
+                   hipStream_t stream) {
+  if (L < 1 || k < 1 || E < 1 || k > E || bm < 1) return MOE_Q4_ERR_SHAPE;
+  if (E > MOE_Q4_MAX_E || (long)L * k >= (1L << 30)) return MOE_Q4_ERR_UNSUPPORTED;
+  if (!topk_ids || !offsets || !perm || !inv || !tiles || !info || !scratch) return MOE_Q4_ERR_NULL;
+  if (tiles_cap < sorted_tiles_max(L, k, E, bm)) return MOE_Q4_ERR_WORKSPACE;
+  if (!aligned(topk_ids, 4) || !aligned(offsets, 4) || !aligned(perm, 4) || !aligned(inv, 4) ||
+      !aligned(tiles, 16) || !aligned(info, 4) || !aligned(scratch, 4))
+    return MOE_Q4_ERR_ALIGN;
+  SortedArgs a{};
+  a.ids = topk_ids;
+  a.T = L; a.k = k; a.E = E;
+  a.bm = bm;
+  a.tiles_max = tiles_cap;
+  a.hdr = info;
+  a.offsets = offsets;
+  a.perm = perm;
+  a.inv = inv;
+  a.rank_tmp = scratch;
+  a.tiles = reinterpret_cast<int4*>(tiles);
+  return sort_launch(a, stream);
 }
 
 int moe_q4_read_device_status(const void* workspace, uint32_t* status, uint32_t* last_path, hipStream_t stream) {

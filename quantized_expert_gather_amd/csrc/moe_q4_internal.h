@@ -50,4 +50,47 @@ int route_union_launch(const int32_t* ids, const float* tw, int L, int k, int E,
                        uint32_t* tok_mask, float* uniq_w, int32_t* slot_to_uniq, hipStream_t stream);
 int clear_status_launch(uint32_t* hdr, hipStream_t stream);
 
+// Arguments of one sorted-path forward (T tokens, P = T * k pairs).
+struct SortedArgs {
+  const uint16_t* x;
+  const int32_t* ids;
+  const float* tw;
+  const uint32_t* wg;
+  const uint16_t* sg;
+  const uint16_t* bg;
+  const uint32_t* wu;
+  const uint16_t* su;
+  const uint16_t* bu;
+  const uint32_t* wd;
+  const uint16_t* sd;
+  const uint16_t* bd;
+  void* out;
+  int out_f32;
+  int T, k, E, H, I;
+  int bm;             // rows per tile (32, 64 or 128)
+  int tiles_max;      // capacity of `tiles`
+  uint32_t* hdr;      // [0] status, [1] path, [2] valid pairs, [3] tiles
+  int32_t* offsets;   // [E+1] first sorted row of each expert; [E] = valid pairs
+  int32_t* perm;      // [P] sorted row -> pair (valid pairs by (expert, pair), then invalid ones)
+  int32_t* inv;       // [P] pair -> sorted row
+  int32_t* rank_tmp;  // [P] pairs scattered into their expert's segment, unordered
+  int4* tiles;        // [tiles_max] (expert, first sorted row, rows, 0)
+  float* asum;        // [T][H/64] per-token sums of x over each 64-input group
+  uint16_t* hhi;      // [P][I] bf16 hi of h, columns in code order inside each 8
+  uint16_t* hlo;      // [P][I] bf16 lo of h (h - hi, rounded)
+  float* hsum2;       // [P][I/32] sum of hi + lo over each 32 columns
+  float* ys;          // [P][H] per-pair down outputs, unweighted
+};
+
+struct SortedWorkspace {
+  size_t hdr, offsets, perm, inv, rank_tmp, tiles, asum, hhi, hlo, hsum2, ys, total;
+};
+
+int sorted_row_blocks(int T, int k, int E);
+int sorted_tiles_max(int T, int k, int E, int bm);
+SortedWorkspace sorted_workspace_layout(int T, int k, int E, int H, int I);
+bool sorted_shape_supported(int T, int k, int E, int H, int I);
+int sort_launch(const SortedArgs& a, hipStream_t stream);
+int sorted_forward_launch(const SortedArgs& a, unsigned stages, hipStream_t stream);
+
 }  // namespace moeq4

@@ -1,0 +1,629 @@
+// Sorted grouped path of the SwitchGLU-q4 MoE layer for gfx950 (MI355X), used
+// when the token count is too large for the union path (prefill).
+//
+// Sources (web pages): sorting the (token, expert) pairs by expert and running
+// a grouped matmul over expert-contiguous rows is the sorted gather path of the
+// page "MoE GatherQMM small-M verify cost" (Facts: the gather_qmm_rhs
+// dispatch and its sorted_indices condition); cutting row tiles at expert
+// boundaries, ceil(n_e / BM) tiles per expert, is the tile scheduler of PR
+// 4567 / PR 4572 described on the same page; the SwitchGLU order (up, gate,
+// silu(gate) * up, down) follows the moe_bench script of the mlx issue
+// "gather_qmm at M=1 streams 4-bit expert weights at ~half the bandwidth of
+// M=4".
+//
+// One forward = six launches on one stream:
+//   k_sort_scan      one workgroup: per-expert counts, exclusive scan ->
+//                    offsets[E+1], the tile list, and an unordered scatter of
+//                    the pairs into their expert's segment.
+//   k_sort_rank      one thread per pair: its rank by pair index inside its
+//                    expert's segment, which makes the order stable (sorted by
+//                    (expert, pair)) -> perm and inv.
+//   k_token_gsum     per token and 64-input group, the fp32 sum of x.
+//   k_sorted_gateup  per (tile, 128 hidden columns): the tile's gathered x rows
+//                    staged in LDS per 64-input group; gate and up codes go
+//                    straight from HBM into registers and become exact bf16
+//                    (128 + q) MFMA operands; one v_mfma_f32_32x32x16_bf16
+//                    chain per group and 32x32 block, then the group's affine
+//                    correction in fp32:
+//                        sum_c x_c (s q_c + b) = s * D + (b - 128 s) * A,
+//                        D = sum_c x_c (128 + q_c),  A = sum_c x_c;
+//                    h = silu(gate) * up is written as a bf16 hi + lo pair
+//                    (h - hi rounded again), plus per-32-column sums of hi + lo.
+//   k_sorted_down    per (tile, 256 output columns): A = h hi and h lo (two
+//                    MFMA passes on the same codes), same affine correction
+//                    with the staged sums of hi + lo -> one fp32 output row per
+//                    pair.
+//   k_sorted_combine out[t] = sum over t's slots j (ascending) of w[t, j] *
+//                    y[inv(t, j)]: deterministic, no floating-point atomics.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_q4.h"
+#include "moe_q4_device.h"
+#include "moe_q4_internal.h"
+
+namespace moeq4 {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kSortThreads = 1024;
+constexpr int kMmThreads = 256;       // 4 waves per GEMM workgroup
+constexpr int kRowTile = 32;          // rows of one MFMA block
+constexpr int kGuCols = 128;          // hidden columns of one gate/up workgroup (32 per wave)
+constexpr int kDnCols = 256;          // output columns of one down workgroup (64 per wave)
+constexpr int kRowBytes = 144;        // LDS bytes per staged row: 8 x 16 B of one group + 16 B pad
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ uint4 unpack_codes(uint32_t w) {
+  uint32_t q[4];
+  unpack_word(w, kMagicBytes, q);
+  return make_uint4(q[0], q[1], q[2], q[3]);
+}
+
+__device__ __forceinline__ f32x16_t mfma_bf16(uint4 a, uint4 b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// sort
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kSortThreads) void k_sort_scan(SortedArgs a) {
+  extern __shared__ __align__(16) int32_t sl[];
+  const int P = a.T * a.k, E = a.E, tid = threadIdx.x;
+  int32_t* cnt = sl;                    // [E+1] counts, then scatter cursors
+  int32_t* part = sl + E + 1;           // [1024] per-thread pair sums
+  int32_t* tpart = part + kSortThreads; // [1024] per-thread tile sums
+  __shared__ int bad;
+  for (int e = tid; e <= E; e += kSortThreads) cnt[e] = 0;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += kSortThreads) {
+    const int e = a.ids[p];
+    const bool ok = e >= 0 && e < E;
+    if (!ok) bad = 1;
+    atomicAdd(&cnt[ok ? e : E], 1);
+  }
+  __syncthreads();
+  // each thread scans a contiguous run of keys (key E collects invalid ids)
+  const int n = E + 1;
+  const int per = (n + kSortThreads - 1) / kSortThreads;
+  const int c0 = min(n, tid * per), c1 = min(n, c0 + per);
+  int s = 0, ts = 0;
+  for (int e = c0; e < c1; ++e) {
+    s += cnt[e];
+    if (e < E) ts += (cnt[e] + a.bm - 1) / a.bm;
+  }
+  part[tid] = s;
+  tpart[tid] = ts;
+  __syncthreads();
+  for (int d = 1; d < kSortThreads; d <<= 1) {
+    int v = 0, tv = 0;
+    if (tid >= d) {
+      v = part[tid - d];
+      tv = tpart[tid - d];
+    }
+    __syncthreads();
+    if (tid >= d) {
+      part[tid] += v;
+      tpart[tid] += tv;
+    }
+    __syncthreads();
+  }
+  int run = tid ? part[tid - 1] : 0;
+  int trun = tid ? tpart[tid - 1] : 0;
+  for (int e = c0; e < c1; ++e) {
+    const int c = cnt[e];
+    a.offsets[e] = run;  // offsets[E] = number of valid pairs
+    if (e < E)
+      for (int r = 0; r < c; r += a.bm) a.tiles[trun++] = make_int4(e, run + r, min(a.bm, c - r), 0);
+    cnt[e] = run;
+    run += c;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    a.hdr[0] = bad ? MOE_Q4_DEV_BAD_ID : 0u;
+    a.hdr[1] = MOE_Q4_PATH_SORTED;
+    a.hdr[2] = (uint32_t)cnt[E];
+    a.hdr[3] = (uint32_t)tpart[kSortThreads - 1];
+  }
+  __syncthreads();  // cnt[E] read above before the scatter moves the cursors
+  for (int p = tid; p < P; p += kSortThreads) {
+    const int e = a.ids[p];
+    const int key = (e >= 0 && e < E) ? e : E;
+    a.rank_tmp[atomicAdd(&cnt[key], 1)] = p;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_sort_rank(SortedArgs a) {
+  const int P = a.T * a.k;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= P) return;
+  const int p = a.rank_tmp[i];
+  const int e = a.ids[p];
+  const bool ok = e >= 0 && e < a.E;
+  const int lo = ok ? a.offsets[e] : a.offsets[a.E];
+  const int hi = ok ? a.offsets[e + 1] : P;
+  int r = 0;
+  for (int j = lo; j < hi; ++j) r += a.rank_tmp[j] < p;
+  a.perm[lo + r] = p;
+  a.inv[p] = lo + r;
+}
+
+__global__ __launch_bounds__(256) void k_token_gsum(SortedArgs a) {
+  const int t = blockIdx.x;
+  const int G = a.H / 64;
+  for (int g = threadIdx.x; g < G; g += 256) {
+    const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)t * a.H + 64 * g);
+    float acc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc = sum8_bf16(src[c], acc);
+    a.asum[(size_t)t * G + g] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// block index -> (tile, column block): the column blocks of one tile run on
+// one XCD back to back (block b lands on XCD b % 8), so the tile's staged rows
+// are read from that XCD's L2 after the first block.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void tile_of_block(int ncb, int& tile, int& cb) {
+  const int b = blockIdx.x;
+  const int x = b & 7, j = b >> 3;
+  tile = x + 8 * (j / ncb);
+  cb = j % ncb;
+}
+
+// Row of the 32x32 MFMA result held in element i of lane half hh.
+__device__ __forceinline__ int c_row(int i, int hh) { return 8 * (i >> 2) + 4 * hh + (i & 3); }
+
+// ---------------------------------------------------------------------------
+// gate + up
+// ---------------------------------------------------------------------------
+
+struct GuFragS {
+  uint4 g, u;       // this lane's 4 code words of gate and up (one half of the group)
+  uint32_t sb[4];   // bf16 sg, bg, su, bu of this lane's column
+};
+
+template <int MT>
+__global__ __launch_bounds__(kMmThreads, 2) void k_sorted_gateup(SortedArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int H = a.H, I = a.I, G = H / 64;
+  const int ncb = (I + kGuCols - 1) / kGuCols;
+  int tile, cb;
+  tile_of_block(ncb, tile, cb);
+  if (tile >= (int)a.hdr[3]) return;
+  const int4 td = a.tiles[tile];
+  const int e = td.x, r0 = td.y, nrows = td.z;
+  const int nrt = (nrows + kRowTile - 1) / kRowTile;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, hh = lane >> 5, lc = lane & 31;
+  const int col0 = cb * kGuCols + 32 * wid;
+  const bool wave_on = col0 < I;
+  const int col = wave_on ? col0 + lc : 0;
+
+  constexpr int kRows = MT * kRowTile;
+  unsigned char* abuf = smem;                                      // [2][kRows][kRowBytes]
+  float* sbuf = reinterpret_cast<float*>(smem + 2 * kRows * kRowBytes);  // [2][kRows]
+  int32_t* tok = reinterpret_cast<int32_t*>(sbuf + 2 * kRows);    // [kRows]
+
+  for (int r = tid; r < kRows; r += kMmThreads) tok[r] = a.perm[r0 + min(r, nrows - 1)] / a.k;
+  __syncthreads();
+
+  // staging of one group of the tile's x rows (codes order) and their sums
+  constexpr int kPer = kRows * 8 / kMmThreads;  // uint4 per thread
+  uint4 st[kPer];
+  float sst = 0.0f;
+  // every thread loads unconditionally (rows past the tile repeat its last
+  // row: same addresses, no extra HBM traffic), so the waits stay exact
+  auto stage_load = [&](int g) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int idx = tid + kMmThreads * i, r = idx >> 3, w = idx & 7;
+      st[i] = *reinterpret_cast<const uint4*>(a.x + (size_t)tok[r] * H + 64 * g + 8 * w);
+    }
+    sst = a.asum[(size_t)tok[min(tid, kRows - 1)] * G + g];
+  };
+  auto stage_store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int idx = tid + kMmThreads * i, r = idx >> 3, w = idx & 7;
+      *reinterpret_cast<uint4*>(abuf + (size_t)(buf * kRows + r) * kRowBytes + 16 * w) = pair_activations(st[i]);
+    }
+    if (tid < kRows) sbuf[buf * kRows + tid] = sst;
+  };
+
+  const size_t rowg = ((size_t)e * I + col) * (size_t)(H / 8);
+  const size_t rows = ((size_t)e * I + col) * (size_t)G;
+  auto frag_load = [&](int g) {
+    GuFragS f;
+    f.g = *reinterpret_cast<const uint4*>(a.wg + rowg + 8 * g + 4 * hh);
+    f.u = *reinterpret_cast<const uint4*>(a.wu + rowg + 8 * g + 4 * hh);
+    f.sb[0] = a.sg[rows + g];
+    f.sb[1] = a.bg[rows + g];
+    f.sb[2] = a.su[rows + g];
+    f.sb[3] = a.bu[rows + g];
+    return f;
+  };
+
+  f32x16_t og[MT], ou[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) og[m][i] = ou[m][i] = 0.0f;
+
+  GuFragS f0 = frag_load(0), f1 = frag_load(min(1, G - 1));
+  stage_load(0);
+  stage_store(0);
+  __syncthreads();
+
+  for (int g = 0; g < G; ++g) {
+    const int buf = g & 1;
+    const GuFragS f2 = frag_load(min(g + 2, G - 1));
+    stage_load(min(g + 1, G - 1));
+    if (wave_on) {
+      const uint32_t wg4[4] = {f0.g.x, f0.g.y, f0.g.z, f0.g.w};
+      const uint32_t wu4[4] = {f0.u.x, f0.u.y, f0.u.z, f0.u.w};
+      uint4 bg_[4], bu_[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bg_[s] = unpack_codes(wg4[s]);
+        bu_[s] = unpack_codes(wu4[s]);
+      }
+      const float s_g = bf16_to_f32((uint16_t)f0.sb[0]), b_g = bf16_to_f32((uint16_t)f0.sb[1]) - 128.0f * s_g;
+      const float s_u = bf16_to_f32((uint16_t)f0.sb[2]), b_u = bf16_to_f32((uint16_t)f0.sb[3]) - 128.0f * s_u;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m < nrt) {
+          const unsigned char* arow = abuf + (size_t)(buf * kRows + m * kRowTile + lc) * kRowBytes + 64 * hh;
+          uint4 av[4];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) av[s] = *reinterpret_cast<const uint4*>(arow + 16 * s);
+          f32x16_t pg = {}, pu = {};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            pg = mfma_bf16(av[s], bg_[s], pg);
+            pu = mfma_bf16(av[s], bu_[s], pu);
+          }
+          const float* srow = sbuf + buf * kRows + m * kRowTile + 4 * hh;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 sa = *reinterpret_cast<const float4*>(srow + 8 * q);
+            const float sv[4] = {sa.x, sa.y, sa.z, sa.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int i = 4 * q + r;
+              og[m][i] = fmaf(b_g, sv[r], fmaf(s_g, pg[i], og[m][i]));
+              ou[m][i] = fmaf(b_u, sv[r], fmaf(s_u, pu[i], ou[m][i]));
+            }
+          }
+        }
+      }
+    }
+    stage_store(buf ^ 1);
+    __syncthreads();
+    f0 = f1;
+    f1 = f2;
+  }
+
+  if (!wave_on) return;
+  // h = silu(gate) * up; stored as bf16 hi + lo in code order within each 8 columns
+  const int scol = (col & ~7) | ((col & 7) >> 1) | ((col & 1) << 2);
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    if (m < nrt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = m * kRowTile + c_row(i, hh);
+        const float gv = og[m][i];
+        const float hv = gv / (1.0f + __expf(-gv)) * ou[m][i];
+        const uint32_t hi = f32_to_bf16_rne(hv);
+        const float hif = __uint_as_float(hi << 16);
+        const uint32_t lo = f32_to_bf16_rne(hv - hif);
+        const float v = group_sum<32>(hif + __uint_as_float(lo << 16));
+        if (r < nrows) {
+          const size_t o = (size_t)(r0 + r) * I;
+          a.hhi[o + scol] = (uint16_t)hi;
+          a.hlo[o + scol] = (uint16_t)lo;
+          if (lc == 0) a.hsum2[(size_t)(r0 + r) * (I / 32) + col0 / 32] = v;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// down
+// ---------------------------------------------------------------------------
+
+struct DnFragS {
+  uint4 w0, w1;     // this lane's 4 code words for each of its two 32-column blocks
+  uint32_t s0, b0, s1, b1;  // bf16 sd, bd of both columns
+};
+
+template <int MT>
+__global__ __launch_bounds__(kMmThreads, 2) void k_sorted_down(SortedArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int H = a.H, I = a.I, G = I / 64;
+  const int ncb = (H + kDnCols - 1) / kDnCols;
+  int tile, cb;
+  tile_of_block(ncb, tile, cb);
+  if (tile >= (int)a.hdr[3]) return;
+  const int4 td = a.tiles[tile];
+  const int e = td.x, r0 = td.y, nrows = td.z;
+  const int nrt = (nrows + kRowTile - 1) / kRowTile;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, hh = lane >> 5, lc = lane & 31;
+  const int colw = cb * kDnCols + 64 * wid;  // first column of this wave
+  bool on[2];
+  int col[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    on[c] = colw + 32 * c < H;
+    col[c] = on[c] ? colw + 32 * c + lc : 0;
+  }
+
+  constexpr int kRows = MT * kRowTile;
+  unsigned char* abuf = smem;  // [2 buffers][2 planes][kRows][kRowBytes]
+  float* sbuf = reinterpret_cast<float*>(smem + 4 * kRows * kRowBytes);  // [2][kRows]
+
+  constexpr int kPer = kRows * 8 / kMmThreads;  // uint4 per thread and plane
+  uint4 sth[kPer], stl[kPer];
+  float sst = 0.0f;
+  // unconditional loads (rows past the tile repeat its last row), exact waits
+  auto stage_load = [&](int g) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int idx = tid + kMmThreads * i, r = min(idx >> 3, nrows - 1), w = idx & 7;
+      const size_t o = (size_t)(r0 + r) * I + 64 * g + 8 * w;
+      sth[i] = *reinterpret_cast<const uint4*>(a.hhi + o);
+      stl[i] = *reinterpret_cast<const uint4*>(a.hlo + o);
+    }
+    const float* hs = a.hsum2 + (size_t)(r0 + min(tid, nrows - 1)) * (I / 32) + 2 * g;
+    sst = hs[0] + hs[1];
+  };
+  auto stage_store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int idx = tid + kMmThreads * i, r = idx >> 3, w = idx & 7;
+      *reinterpret_cast<uint4*>(abuf + (size_t)((buf * 2 + 0) * kRows + r) * kRowBytes + 16 * w) = sth[i];
+      *reinterpret_cast<uint4*>(abuf + (size_t)((buf * 2 + 1) * kRows + r) * kRowBytes + 16 * w) = stl[i];
+    }
+    if (tid < kRows) sbuf[buf * kRows + tid] = sst;
+  };
+
+  size_t rw[2], rs[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    rw[c] = ((size_t)e * H + col[c]) * (size_t)(I / 8);
+    rs[c] = ((size_t)e * H + col[c]) * (size_t)G;
+  }
+  auto frag_load = [&](int g) {
+    DnFragS f;
+    f.w0 = *reinterpret_cast<const uint4*>(a.wd + rw[0] + 8 * g + 4 * hh);
+    f.w1 = *reinterpret_cast<const uint4*>(a.wd + rw[1] + 8 * g + 4 * hh);
+    f.s0 = a.sd[rs[0] + g];
+    f.b0 = a.bd[rs[0] + g];
+    f.s1 = a.sd[rs[1] + g];
+    f.b1 = a.bd[rs[1] + g];
+    return f;
+  };
+
+  f32x16_t acc[MT][2];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[m][c][i] = 0.0f;
+
+  DnFragS f0 = frag_load(0), f1 = frag_load(min(1, G - 1));
+  stage_load(0);
+  stage_store(0);
+  __syncthreads();
+
+  for (int g = 0; g < G; ++g) {
+    const int buf = g & 1;
+    const DnFragS f2 = frag_load(min(g + 2, G - 1));
+    stage_load(min(g + 1, G - 1));
+    uint4 bw[2][4];
+    float sc[2], bc[2];
+    {
+      const uint32_t w8[8] = {f0.w0.x, f0.w0.y, f0.w0.z, f0.w0.w, f0.w1.x, f0.w1.y, f0.w1.z, f0.w1.w};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bw[0][s] = unpack_codes(w8[s]);
+        bw[1][s] = unpack_codes(w8[4 + s]);
+      }
+      sc[0] = bf16_to_f32((uint16_t)f0.s0);
+      bc[0] = bf16_to_f32((uint16_t)f0.b0) - 128.0f * sc[0];
+      sc[1] = bf16_to_f32((uint16_t)f0.s1);
+      bc[1] = bf16_to_f32((uint16_t)f0.b1) - 128.0f * sc[1];
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m < nrt) {
+        uint4 ahi[4], alo[4];
+        const unsigned char* ph = abuf + (size_t)((buf * 2 + 0) * kRows + m * kRowTile + lc) * kRowBytes + 64 * hh;
+        const unsigned char* pl = abuf + (size_t)((buf * 2 + 1) * kRows + m * kRowTile + lc) * kRowBytes + 64 * hh;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          ahi[s] = *reinterpret_cast<const uint4*>(ph + 16 * s);
+          alo[s] = *reinterpret_cast<const uint4*>(pl + 16 * s);
+        }
+        const float* srow = sbuf + buf * kRows + m * kRowTile + 4 * hh;
+        float sv[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 sa = *reinterpret_cast<const float4*>(srow + 8 * q);
+          sv[4 * q] = sa.x; sv[4 * q + 1] = sa.y; sv[4 * q + 2] = sa.z; sv[4 * q + 3] = sa.w;
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          if (on[c]) {
+            f32x16_t p = {};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              p = mfma_bf16(ahi[s], bw[c][s], p);
+              p = mfma_bf16(alo[s], bw[c][s], p);
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[m][c][i] = fmaf(bc[c], sv[i], fmaf(sc[c], p[i], acc[m][c][i]));
+          }
+        }
+      }
+    }
+    stage_store(buf ^ 1);
+    __syncthreads();
+    f0 = f1;
+    f1 = f2;
+  }
+
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    if (m < nrt) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        if (on[c]) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = m * kRowTile + c_row(i, hh);
+            if (r < nrows) a.ys[(size_t)(r0 + r) * H + col[c]] = acc[m][c][i];
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// combine
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void k_sorted_combine(SortedArgs a) {
+  const int H = a.H, k = a.k, n4 = H >> 2;
+  const int it = blockIdx.x * 256 + threadIdx.x;
+  const int t = blockIdx.y;
+  if (it >= n4) return;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int j = 0; j < k; ++j) {
+    const int p = t * k + j;
+    const int e = a.ids[p];
+    if (e < 0 || e >= a.E) continue;
+    const float w = a.tw[p];
+    const float4 v = reinterpret_cast<const float4*>(a.ys + (size_t)a.inv[p] * H)[it];
+    acc.x = fmaf(w, v.x, acc.x);
+    acc.y = fmaf(w, v.y, acc.y);
+    acc.z = fmaf(w, v.z, acc.z);
+    acc.w = fmaf(w, v.w, acc.w);
+  }
+  if (a.out_f32) {
+    reinterpret_cast<float4*>(a.out)[(size_t)t * n4 + it] = acc;
+  } else {
+    const uint32_t lo = f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16);
+    const uint32_t hi = f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16);
+    reinterpret_cast<uint2*>(a.out)[(size_t)t * n4 + it] = make_uint2(lo, hi);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+namespace {
+
+size_t r256(size_t v) { return (v + 255) & ~size_t(255); }
+
+size_t sort_lds(int E) { return (size_t)4 * (E + 1 + 2 * kSortThreads); }
+size_t gateup_lds(int mt) { return (size_t)2 * mt * kRowTile * kRowBytes + 3 * mt * kRowTile * 4; }
+size_t down_lds(int mt) { return (size_t)4 * mt * kRowTile * kRowBytes + 2 * mt * kRowTile * 4; }
+
+}  // namespace
+
+int sorted_row_blocks(int T, int k, int E) {
+  const double per = (double)T * k / (double)E;  // mean pairs per expert
+  return per <= 24.0 ? 1 : (per <= 48.0 ? 2 : (per <= 72.0 ? 3 : 4));
+}
+
+int sorted_tiles_max(int T, int k, int E, int bm) {
+  const long P = (long)T * k;
+  return (int)(P / bm + (P < E ? P : E) + 1);
+}
+
+SortedWorkspace sorted_workspace_layout(int T, int k, int E, int H, int I) {
+  SortedWorkspace w{};
+  const size_t P = (size_t)T * k;
+  size_t off = 0;
+  w.hdr = off;      off = r256(off + 256);
+  w.offsets = off;  off = r256(off + (size_t)(E + 1) * 4);
+  w.perm = off;     off = r256(off + P * 4);
+  w.inv = off;      off = r256(off + P * 4);
+  w.rank_tmp = off; off = r256(off + P * 4);
+  w.tiles = off;    off = r256(off + (size_t)sorted_tiles_max(T, k, E, kRowTile) * 16);
+  w.asum = off;     off = r256(off + (size_t)T * (H / 64) * 4);
+  w.hhi = off;      off = r256(off + P * I * 2);
+  w.hlo = off;      off = r256(off + P * I * 2);
+  w.hsum2 = off;    off = r256(off + P * (I / 32) * 4);
+  w.ys = off;       off = r256(off + P * H * 4);
+  w.total = off;
+  return w;
+}
+
+bool sorted_shape_supported(int T, int k, int E, int H, int I) {
+  (void)H; (void)I;
+  const long P = (long)T * k;
+  // T <= 65535: the combine grid's second dimension is the token
+  return T <= 65535 && E <= MOE_Q4_MAX_E && P < (1L << 30) && sort_lds(E) <= 160 * 1024;
+}
+
+int sort_launch(const SortedArgs& a, hipStream_t stream) {
+  const int P = a.T * a.k;
+  hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(kSortThreads), sort_lds(a.E), stream, a);
+  if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;
+  hipLaunchKernelGGL(k_sort_rank, dim3((P + 255) / 256), dim3(256), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? MOE_Q4_OK : MOE_Q4_ERR_LAUNCH;
+}
+
+template <int MT>
+int gemm_launch(const SortedArgs& a, bool down, hipStream_t stream) {
+  const int tiles8 = (a.tiles_max + 7) / 8 * 8;
+  if (!down) {
+    const int ncb = (a.I + kGuCols - 1) / kGuCols;
+    hipLaunchKernelGGL(k_sorted_gateup<MT>, dim3(tiles8 * ncb), dim3(kMmThreads), gateup_lds(MT), stream, a);
+  } else {
+    const int ncb = (a.H + kDnCols - 1) / kDnCols;
+    hipLaunchKernelGGL(k_sorted_down<MT>, dim3(tiles8 * ncb), dim3(kMmThreads), down_lds(MT), stream, a);
+  }
+  return hipGetLastError() == hipSuccess ? MOE_Q4_OK : MOE_Q4_ERR_LAUNCH;
+}
+
+int gemm_dispatch(const SortedArgs& a, bool down, hipStream_t stream) {
+  switch (a.bm / kRowTile) {
+    case 1: return gemm_launch<1>(a, down, stream);
+    case 2: return gemm_launch<2>(a, down, stream);
+    case 3: return gemm_launch<3>(a, down, stream);
+    case 4: return gemm_launch<4>(a, down, stream);
+    default: return MOE_Q4_ERR_UNSUPPORTED;
+  }
+}
+
+int sorted_forward_launch(const SortedArgs& a, unsigned stages, hipStream_t stream) {
+  if (stages & MOE_Q4_STAGE_GATEUP) {
+    int st = sort_launch(a, stream);
+    if (st) return st;
+    hipLaunchKernelGGL(k_token_gsum, dim3(a.T), dim3(256), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;
+    st = gemm_dispatch(a, false, stream);
+    if (st) return st;
+  }
+  if (stages & MOE_Q4_STAGE_DOWN) {
+    const int st = gemm_dispatch(a, true, stream);
+    if (st) return st;
+    hipLaunchKernelGGL(k_sorted_combine, dim3((a.H / 4 + 255) / 256, a.T), dim3(256), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;
+  }
+  return MOE_Q4_OK;
+}
+
+}  // namespace moeq4

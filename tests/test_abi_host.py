@@ -121,6 +121,49 @@ def test_path_selection_and_limits():
     assert q.moe_swiglu_q4_select_path(2, 2, 8, 256, 128) == q.MOE_Q4_PATH_UNION
     assert q.moe_swiglu_q4_select_path(3, 2, 8, 200, 128) == -q.MOE_Q4_ERR_UNSUPPORTED
     assert q.moe_swiglu_q4_select_path(2, 9, 8, 256, 128) == -q.MOE_Q4_ERR_SHAPE
+    # past the 32-bit token masks (or the pair limit) the sorted path takes over
+    assert q.moe_swiglu_q4_select_path(33, 8, 256, 2048, 512) == q.MOE_Q4_PATH_SORTED
+    assert q.moe_swiglu_q4_select_path(512, 8, 256, 4096, 2048) == q.MOE_Q4_PATH_SORTED
+    assert q.moe_swiglu_q4_select_path(2048, 8, 256, 4096, 2048) == q.MOE_Q4_PATH_SORTED
+    assert q.moe_swiglu_q4_select_path(200, 2, 8, 256, 128) == q.MOE_Q4_PATH_SORTED
+    assert q.moe_swiglu_q4_select_path(64, 8, 16385, 256, 128) == -q.MOE_Q4_ERR_UNSUPPORTED
+
+
+def test_sorted_workspace_holds_its_scratch():
+    for T, k, E, H, I in [(512, 8, 256, 4096, 2048), (2048, 8, 256, 4096, 2048), (100, 4, 16, 256, 128)]:
+        P = T * k
+        n = q.moe_swiglu_q4_workspace_bytes(T, k, E, H, I)
+        assert n % 256 == 0
+        # h as bf16 hi + lo, per-pair outputs in fp32, index arrays, per-token group sums
+        assert n >= P * I * 4 + P * H * 4 + 3 * P * 4 + (E + 1) * 4 + T * (H // 64) * 4
+
+
+def test_sort_tiles_max_bounds_every_schedule():
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(5)
+    for L, k, E, bm in [(7, 3, 5, 2), (64, 8, 16, 32), (33, 8, 256, 32), (512, 8, 256, 32), (40, 4, 8, 128)]:
+        cap = q.moe_sort_pairs_tiles_max(L, k, E, bm)
+        assert cap == L * k // bm + min(E, L * k) + 1
+        for _ in range(20):
+            ids = rng.integers(0, E, size=(L, k))
+            if rng.random() < 0.3:
+                ids[:] = rng.integers(0, E)  # everything on one expert
+            tiles = oracle.expert_tiles(oracle.sorted_pairs(ids, E)["offsets"], bm)
+            assert len(tiles) <= cap
+
+
+def test_sort_pairs_host_validation():
+    f = q.lib().moe_sort_pairs
+    p = [fake(i) for i in range(7)]
+    cap = q.moe_sort_pairs_tiles_max(64, 8, 256, 32)
+    assert f(p[0], 0, 8, 256, 32, p[1], p[2], p[3], p[4], cap, p[5], p[6], None) == q.MOE_Q4_ERR_SHAPE
+    assert f(p[0], 64, 8, 256, 0, p[1], p[2], p[3], p[4], cap, p[5], p[6], None) == q.MOE_Q4_ERR_SHAPE
+    assert f(p[0], 64, 9, 8, 32, p[1], p[2], p[3], p[4], cap, p[5], p[6], None) == q.MOE_Q4_ERR_SHAPE
+    assert f(0, 64, 8, 256, 32, p[1], p[2], p[3], p[4], cap, p[5], p[6], None) == q.MOE_Q4_ERR_NULL
+    assert f(p[0], 64, 8, 256, 32, p[1], p[2], p[3], p[4], cap - 1, p[5], p[6], None) == q.MOE_Q4_ERR_WORKSPACE
+    assert f(p[0], 64, 8, 256, 32, p[1], p[2], p[3], p[4] + 4, cap, p[5], p[6], None) == q.MOE_Q4_ERR_ALIGN
+    assert f(p[0], 64, 8, 16385, 32, p[1], p[2], p[3], p[4], cap, p[5], p[6], None) == q.MOE_Q4_ERR_UNSUPPORTED
 
 
 def test_workspace_size_grows_with_pairs():
