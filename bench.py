@@ -71,6 +71,77 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def bench_sorted(args, Ts, q, synth, torch, np, dev, stream, sleep_cycles_for):
+    """Chains of distinct prefill layers (E=256 top-8 H=4096 I=2048, uniform routes)
+    through the sorted path: full forward, then gate+up and down stages alone."""
+    w = synth.WORKLOADS["prefill"]
+    H, I, E, k = w.H, w.I, w.E, w.k
+    eb = expert_bytes(H, I)
+    out = {"workload": f"{w.name}: uniform top-{k}, {args.sorted_layers} distinct layers per chain",
+           "per_T": {}}
+    for T in Ts:
+        layers = []
+        for layer in range(args.sorted_layers):
+            lay = synth.make_layer(w, T, layer, seed=0, device=dev)
+            ids = torch.from_numpy(lay.ids).to(dev)
+            tw = torch.from_numpy(lay.weights).to(dev)
+            o = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+            ws = q.new_workspace(T, k, E, H, I, dev)
+            bt = lay.bank.tensors()
+            layers.append({"u": int(lay.bank.E), "keep": (lay, ids, tw, o, ws),
+                           "calls": {st: q.PreparedForward(lay.x, ids, tw, bt, o, ws, code, stream)
+                                     for st, code in (("all", q.MOE_Q4_STAGE_ALL), ("gateup", q.MOE_Q4_STAGE_GATEUP),
+                                                      ("down", q.MOE_Q4_STAGE_DOWN))}})
+        assert q.moe_swiglu_q4_select_path(T, k, E, H, I) == q.MOE_Q4_PATH_SORTED
+        torch.cuda.synchronize()
+
+        def chain(which, delay):
+            torch.cuda._sleep(delay)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            th = time.perf_counter()
+            for lay in layers:
+                lay["calls"][which]()
+            e1.record()
+            return e0, e1, (time.perf_counter() - th) * 1e3
+
+        warm = chain("all", 0)
+        torch.cuda.synchronize()
+        delay = sleep_cycles_for(1.5 * warm[2] + 1.0)
+        chain("all", delay)
+        torch.cuda.synchronize()
+        recs = {wh: [chain(wh, delay) for _ in range(max(3, args.steps // 2))] for wh in ("all", "gateup", "down")}
+        torch.cuda.synchronize()
+        nl = len(layers)
+        med = {wh: float(np.median([a.elapsed_time(b) for a, b, _ in v])) / nl for wh, v in recs.items()}
+        u_sum = sum(l["u"] for l in layers)
+        P = T * k
+        flops = 6.0 * P * I * H                          # gate, up, down: 2 flops per weight per pair
+        gu_bytes = (u_sum / nl) * gateup_bytes(H, I) + 2 * T * H + 8 * T * k
+        dn_bytes = (u_sum / nl) * down_bytes(H, I)
+        gb = (u_sum / nl) * eb / (med["all"] * 1e-3) / 1e9
+        tf = flops / (med["all"] * 1e-3) / 1e12
+        gu_ms, dn_ms = med["gateup"], med["down"]
+        out["per_T"][str(T)] = {
+            "us_per_layer": round(med["all"] * 1e3, 1), "u_mean": round(u_sum / nl, 1),
+            "eff_GBps": round(gb, 1), "frac_hbm_peak": round(gb / PEAK_HBM_GBPS, 4),
+            "TFLOPs": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "gateup_us": round(gu_ms * 1e3, 1), "down_combine_us": round(dn_ms * 1e3, 1),
+            "gateup_GBps": round(gu_bytes / (gu_ms * 1e-3) / 1e9, 1),
+            "gateup_TFLOPs": round(4.0 * P * I * H / (gu_ms * 1e-3) / 1e12, 1),
+            "down_GBps": round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1),
+            "down_TFLOPs": round(2.0 * P * I * H / (dn_ms * 1e-3) / 1e12, 1),
+        }
+        log(f"sorted T={T}: {med['all'] * 1e3:.1f} us/layer, {gb:.0f} GB/s, {tf:.0f} TFLOP/s; "
+            f"gate+up {gu_ms * 1e3:.1f} us, down+combine {dn_ms * 1e3:.1f} us")
+        del layers
+        torch.cuda.empty_cache()
+    return out
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -103,6 +174,9 @@ def main():
     ap.add_argument("--layers", type=int, default=75)
     ap.add_argument("--Ls", default="1,2,3,4,8",
                     help="window sizes timed; value aggregates those of the metric (1, 2, 4, 8)")
+    ap.add_argument("--sorted-Ts", default="512,2048",
+                    help="token counts of the prefill (sorted-path) measurement; empty to skip")
+    ap.add_argument("--sorted-layers", type=int, default=4, help="distinct layers per prefill chain")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the baseline sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -288,6 +362,12 @@ def main():
         result["down_kernel"] = {"kernel": "k_down + k_combine",
                                  "achieved_GBps": round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1),
                                  "avg_launch_us": round(dn_ms * 1e3 / dn_n, 3)}
+
+    # ---- prefill workload through the sorted path (grouped MFMA GEMMs) ----
+    sorted_Ts = [int(v) for v in args.sorted_Ts.split(",") if v.strip()]
+    if sorted_Ts:
+        result["sorted_path"] = bench_sorted(args, sorted_Ts, q, synth, torch, np, dev, stream,
+                                             lambda ms: sleep_cycles_for(ms))
 
     # ---- CPU oracle baseline on a bounded sample, and parity of the same layers ----
     if not args.no_cpu:

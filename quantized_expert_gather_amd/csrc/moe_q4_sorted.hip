@@ -46,6 +46,7 @@ namespace moeq4 {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kSortThreads = 1024;
 constexpr int kMmThreads = 256;       // 4 waves per GEMM workgroup
@@ -368,8 +369,8 @@ __global__ __launch_bounds__(kMmThreads, 2) void k_sorted_down(SortedArgs a) {
   unsigned char* abuf = smem;  // [2 buffers][2 planes][kRows][kRowBytes]
   float* sbuf = reinterpret_cast<float*>(smem + 4 * kRows * kRowBytes);  // [2][kRows]
 
-  constexpr int kPer = kRows * 8 / kMmThreads;  // uint4 per thread and plane
-  uint4 sth[kPer], stl[kPer];
+  constexpr int kPer = kRows * 8 / kMmThreads;  // 16-byte pieces per thread and plane
+  u32x4_t sth[kPer], stl[kPer];
   float sst = 0.0f;
   // unconditional loads (rows past the tile repeat its last row), exact waits
   auto stage_load = [&](int g) {
@@ -377,8 +378,8 @@ __global__ __launch_bounds__(kMmThreads, 2) void k_sorted_down(SortedArgs a) {
     for (int i = 0; i < kPer; ++i) {
       const int idx = tid + kMmThreads * i, r = min(idx >> 3, nrows - 1), w = idx & 7;
       const size_t o = (size_t)(r0 + r) * I + 64 * g + 8 * w;
-      sth[i] = *reinterpret_cast<const uint4*>(a.hhi + o);
-      stl[i] = *reinterpret_cast<const uint4*>(a.hlo + o);
+      sth[i] = *reinterpret_cast<const u32x4_t*>(a.hhi + o);
+      stl[i] = *reinterpret_cast<const u32x4_t*>(a.hlo + o);
     }
     const float* hs = a.hsum2 + (size_t)(r0 + min(tid, nrows - 1)) * (I / 32) + 2 * g;
     sst = hs[0] + hs[1];
@@ -387,8 +388,8 @@ __global__ __launch_bounds__(kMmThreads, 2) void k_sorted_down(SortedArgs a) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int idx = tid + kMmThreads * i, r = idx >> 3, w = idx & 7;
-      *reinterpret_cast<uint4*>(abuf + (size_t)((buf * 2 + 0) * kRows + r) * kRowBytes + 16 * w) = sth[i];
-      *reinterpret_cast<uint4*>(abuf + (size_t)((buf * 2 + 1) * kRows + r) * kRowBytes + 16 * w) = stl[i];
+      *reinterpret_cast<u32x4_t*>(abuf + (size_t)((buf * 2 + 0) * kRows + r) * kRowBytes + 16 * w) = sth[i];
+      *reinterpret_cast<u32x4_t*>(abuf + (size_t)((buf * 2 + 1) * kRows + r) * kRowBytes + 16 * w) = stl[i];
     }
     if (tid < kRows) sbuf[buf * kRows + tid] = sst;
   };
@@ -498,6 +499,326 @@ __global__ __launch_bounds__(kMmThreads, 2) void k_sorted_down(SortedArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// streaming variants for the common shapes (H, I multiples of 1024)
+//
+// The kernels above give each lane 16 bytes of one weight row per 64-input
+// group and 2 bytes of its scale row, so every 128-byte line is touched many
+// times, far apart in time, by 128 columns in flight per workgroup -- more
+// lines than L2 holds, and each touch refetches the line.  These variants
+// consume whole lines at once: an iteration covers 4 groups (the two halves
+// of a 32-lane column group read a row's full 128-byte code line), scales and
+// biases arrive 16 groups (32 bytes) per load, and gate and up run on
+// separate waves, which halves each wave's registers.  x (or h) staging loads
+// are issued before the weight prefetch of the same iteration, so the wait
+// for the staged rows never waits for weights still in flight.
+// ---------------------------------------------------------------------------
+
+constexpr int kV2Threads = 512;              // 8 waves
+constexpr int kV2GuCols = 128;               // gate/up: waves 0-3 gate, 4-7 up, 32 columns each
+constexpr int kV2DnCols = 256;               // down: 8 waves x 32 columns
+constexpr int kV2Row = 4 * 128 + 16;         // LDS bytes per staged row: 4 groups + pad
+
+struct Chunk16 {
+  uint4 s0, s1, b0, b1;  // 16 consecutive bf16 scales and biases of one row
+};
+
+__device__ __forceinline__ Chunk16 load_chunk16(const uint16_t* S, const uint16_t* B, size_t off) {
+  Chunk16 c;
+  c.s0 = *reinterpret_cast<const uint4*>(S + off);
+  c.s1 = *reinterpret_cast<const uint4*>(S + off + 8);
+  c.b0 = *reinterpret_cast<const uint4*>(B + off);
+  c.b1 = *reinterpret_cast<const uint4*>(B + off + 8);
+  return c;
+}
+
+// bf16 element j (compile-time after unrolling) of 16 packed in two uint4
+__device__ __forceinline__ float chunk_elem(const uint4& lo, const uint4& hi, int j) {
+  const uint4& v = j < 8 ? lo : hi;
+  const int d = (j & 7) >> 1;
+  const uint32_t w = d == 0 ? v.x : (d == 1 ? v.y : (d == 2 ? v.z : v.w));
+  return (j & 1) ? bf16_hi_to_f32(w) : bf16_lo_to_f32(w);
+}
+
+struct Codes4 {
+  uint4 q[4];  // this lane's half (4 words) of each of 4 consecutive groups
+};
+
+__device__ __forceinline__ Codes4 load_codes4(const uint32_t* W, size_t rowc, int g0, int hh) {
+  Codes4 c;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) c.q[q] = *reinterpret_cast<const uint4*>(W + rowc + 8 * (g0 + q) + 4 * hh);
+  return c;
+}
+
+template <int MT>
+__global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int H = a.H, I = a.I, G = H / 64;
+  const int nit = G / 4, nch = G / 16;
+  const int ncb = (I + kV2GuCols - 1) / kV2GuCols;
+  int tile, cb;
+  tile_of_block(ncb, tile, cb);
+  if (tile >= (int)a.hdr[3]) return;
+  const int4 td = a.tiles[tile];
+  const int e = td.x, r0 = td.y, nrows = td.z;
+  const int nrt = (nrows + kRowTile - 1) / kRowTile;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, hh = lane >> 5, lc = lane & 31;
+  const int mat = wid >> 2, cw = wid & 3;
+  const int col0 = cb * kV2GuCols + 32 * cw;
+  const bool wave_on = col0 < I;
+  const int col = wave_on ? col0 + lc : 0;
+
+  constexpr int kRows = MT * kRowTile;
+  unsigned char* abuf = smem;                                          // [kRows][kV2Row]
+  float* sbuf = reinterpret_cast<float*>(smem + kRows * kV2Row);      // [4][kRows]
+  int32_t* tok = reinterpret_cast<int32_t*>(sbuf + 4 * kRows);        // [kRows]
+  for (int r = tid; r < kRows; r += kV2Threads) tok[r] = a.perm[r0 + min(r, nrows - 1)] / a.k;
+  __syncthreads();
+
+  constexpr int kPer = kRows * 32 / kV2Threads;  // uint4 of x per thread and iteration
+  uint4 st[kPer];
+  float sst = 0.0f;
+  auto stage_load = [&](int it) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int idx = tid + kV2Threads * j, r = idx >> 5, w = idx & 31;
+      st[j] = *reinterpret_cast<const uint4*>(a.x + (size_t)tok[r] * H + 256 * it + 8 * w);
+    }
+    const int si = min(tid, 4 * kRows - 1), q = si / kRows, r = si % kRows;
+    sst = a.asum[(size_t)tok[r] * G + 4 * it + q];
+  };
+  auto stage_store = [&]() {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int idx = tid + kV2Threads * j, r = idx >> 5, w = idx & 31;
+      *reinterpret_cast<uint4*>(abuf + (size_t)r * kV2Row + 16 * w) = pair_activations(st[j]);
+    }
+    if (tid < 4 * kRows) sbuf[tid] = sst;  // [q][r] with q = tid / kRows
+  };
+
+  const uint32_t* W = mat ? a.wu : a.wg;
+  const uint16_t* S = mat ? a.su : a.sg;
+  const uint16_t* B = mat ? a.bu : a.bg;
+  const size_t rowc = ((size_t)e * I + col) * (size_t)(H / 8);
+  const size_t rows = ((size_t)e * I + col) * (size_t)G;
+
+  f32x16_t acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[m][i] = 0.0f;
+
+  Codes4 cur = load_codes4(W, rowc, 0, hh);
+  Chunk16 ch = load_chunk16(S, B, rows);
+  stage_load(0);
+  stage_store();
+  __syncthreads();
+
+  for (int c = 0; c < nch; ++c) {
+    Chunk16 chn;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int it = 4 * c + ii;
+      stage_load(min(it + 1, nit - 1));
+      const Codes4 nx = load_codes4(W, rowc, 4 * min(it + 1, nit - 1), hh);
+      if (ii == 0) chn = load_chunk16(S, B, rows + 16 * min(c + 1, nch - 1));
+      if (wave_on) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t w4[4] = {cur.q[q].x, cur.q[q].y, cur.q[q].z, cur.q[q].w};
+          uint4 bq[4];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) bq[s] = unpack_codes(w4[s]);
+          const float sc = chunk_elem(ch.s0, ch.s1, 4 * ii + q);
+          const float bc = chunk_elem(ch.b0, ch.b1, 4 * ii + q) - 128.0f * sc;
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            if (m < nrt) {
+              const unsigned char* arow = abuf + (size_t)(m * kRowTile + lc) * kV2Row + 128 * q + 64 * hh;
+              f32x16_t p = {};
+#pragma unroll
+              for (int s = 0; s < 4; ++s) p = mfma_bf16(*reinterpret_cast<const uint4*>(arow + 16 * s), bq[s], p);
+              const float* srow = sbuf + q * kRows + m * kRowTile + 4 * hh;
+#pragma unroll
+              for (int qq = 0; qq < 4; ++qq) {
+                const float4 sa = *reinterpret_cast<const float4*>(srow + 8 * qq);
+                acc[m][4 * qq + 0] = fmaf(bc, sa.x, fmaf(sc, p[4 * qq + 0], acc[m][4 * qq + 0]));
+                acc[m][4 * qq + 1] = fmaf(bc, sa.y, fmaf(sc, p[4 * qq + 1], acc[m][4 * qq + 1]));
+                acc[m][4 * qq + 2] = fmaf(bc, sa.z, fmaf(sc, p[4 * qq + 2], acc[m][4 * qq + 2]));
+                acc[m][4 * qq + 3] = fmaf(bc, sa.w, fmaf(sc, p[4 * qq + 3], acc[m][4 * qq + 3]));
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();
+      stage_store();
+      __syncthreads();
+      cur = nx;
+    }
+    ch = chn;
+  }
+
+  // up waves hand their sums to the gate waves through LDS (the staging area is free now)
+  float* xch = reinterpret_cast<float*>(smem);  // [kRows][128]
+  if (mat == 1 && wave_on) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      if (m < nrt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xch[(m * kRowTile + c_row(i, hh)) * kV2GuCols + 32 * cw + lc] = acc[m][i];
+  }
+  __syncthreads();
+  if (mat == 1 || !wave_on) return;
+  const int scol = (col & ~7) | ((col & 7) >> 1) | ((col & 1) << 2);
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    if (m < nrt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = m * kRowTile + c_row(i, hh);
+        const float gv = acc[m][i];
+        const float uv = xch[r * kV2GuCols + 32 * cw + lc];
+        const float hv = gv / (1.0f + __expf(-gv)) * uv;
+        const uint32_t hi = f32_to_bf16_rne(hv);
+        const float hif = __uint_as_float(hi << 16);
+        const uint32_t lo = f32_to_bf16_rne(hv - hif);
+        const float v = group_sum<32>(hif + __uint_as_float(lo << 16));
+        if (r < nrows) {
+          const size_t o = (size_t)(r0 + r) * I;
+          a.hhi[o + scol] = (uint16_t)hi;
+          a.hlo[o + scol] = (uint16_t)lo;
+          if (lc == 0) a.hsum2[(size_t)(r0 + r) * (I / 32) + col0 / 32] = v;
+        }
+      }
+    }
+  }
+}
+
+template <int MT>
+__global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int H = a.H, I = a.I, G = I / 64;
+  const int nit = G / 4, nch = G / 16;
+  const int ncb = (H + kV2DnCols - 1) / kV2DnCols;
+  int tile, cb;
+  tile_of_block(ncb, tile, cb);
+  if (tile >= (int)a.hdr[3]) return;
+  const int4 td = a.tiles[tile];
+  const int e = td.x, r0 = td.y, nrows = td.z;
+  const int nrt = (nrows + kRowTile - 1) / kRowTile;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, hh = lane >> 5, lc = lane & 31;
+  const int col0 = cb * kV2DnCols + 32 * wid;
+  const bool wave_on = col0 < H;
+  const int col = wave_on ? col0 + lc : 0;
+
+  constexpr int kRows = MT * kRowTile;
+  unsigned char* abuf = smem;                                                // [2 planes][kRows][kV2Row]
+  float* sbuf = reinterpret_cast<float*>(smem + 2 * kRows * kV2Row);        // [4][kRows]
+
+  constexpr int kPer = kRows * 32 / kV2Threads;  // 16-byte pieces per thread, iteration and plane
+  u32x4_t sth[kPer], stl[kPer];
+  float sst = 0.0f;
+  auto stage_load = [&](int it) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int idx = tid + kV2Threads * j, r = min(idx >> 5, nrows - 1), w = idx & 31;
+      const size_t o = (size_t)(r0 + r) * I + 256 * it + 8 * w;
+      sth[j] = *reinterpret_cast<const u32x4_t*>(a.hhi + o);
+      stl[j] = *reinterpret_cast<const u32x4_t*>(a.hlo + o);
+    }
+    const int si = min(tid, 4 * kRows - 1), q = si / kRows, r = min(si % kRows, nrows - 1);
+    const float* hs = a.hsum2 + (size_t)(r0 + r) * (I / 32) + 2 * (4 * it + q);
+    sst = hs[0] + hs[1];
+  };
+  auto stage_store = [&]() {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int idx = tid + kV2Threads * j, r = idx >> 5, w = idx & 31;
+      *reinterpret_cast<u32x4_t*>(abuf + (size_t)r * kV2Row + 16 * w) = sth[j];
+      *reinterpret_cast<u32x4_t*>(abuf + (size_t)(kRows + r) * kV2Row + 16 * w) = stl[j];
+    }
+    if (tid < 4 * kRows) sbuf[tid] = sst;
+  };
+
+  const size_t rowc = ((size_t)e * H + col) * (size_t)(I / 8);
+  const size_t rows = ((size_t)e * H + col) * (size_t)G;
+
+  f32x16_t acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[m][i] = 0.0f;
+
+  Codes4 cur = load_codes4(a.wd, rowc, 0, hh);
+  Chunk16 ch = load_chunk16(a.sd, a.bd, rows);
+  stage_load(0);
+  stage_store();
+  __syncthreads();
+
+  for (int c = 0; c < nch; ++c) {
+    Chunk16 chn;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int it = 4 * c + ii;
+      stage_load(min(it + 1, nit - 1));
+      const Codes4 nx = load_codes4(a.wd, rowc, 4 * min(it + 1, nit - 1), hh);
+      if (ii == 0) chn = load_chunk16(a.sd, a.bd, rows + 16 * min(c + 1, nch - 1));
+      if (wave_on) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t w4[4] = {cur.q[q].x, cur.q[q].y, cur.q[q].z, cur.q[q].w};
+          uint4 bq[4];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) bq[s] = unpack_codes(w4[s]);
+          const float sc = chunk_elem(ch.s0, ch.s1, 4 * ii + q);
+          const float bc = chunk_elem(ch.b0, ch.b1, 4 * ii + q) - 128.0f * sc;
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            if (m < nrt) {
+              const unsigned char* ph = abuf + (size_t)(m * kRowTile + lc) * kV2Row + 128 * q + 64 * hh;
+              const unsigned char* pl = ph + (size_t)kRows * kV2Row;
+              f32x16_t p = {};
+#pragma unroll
+              for (int s = 0; s < 4; ++s) {
+                p = mfma_bf16(*reinterpret_cast<const uint4*>(ph + 16 * s), bq[s], p);
+                p = mfma_bf16(*reinterpret_cast<const uint4*>(pl + 16 * s), bq[s], p);
+              }
+              const float* srow = sbuf + q * kRows + m * kRowTile + 4 * hh;
+#pragma unroll
+              for (int qq = 0; qq < 4; ++qq) {
+                const float4 sa = *reinterpret_cast<const float4*>(srow + 8 * qq);
+                acc[m][4 * qq + 0] = fmaf(bc, sa.x, fmaf(sc, p[4 * qq + 0], acc[m][4 * qq + 0]));
+                acc[m][4 * qq + 1] = fmaf(bc, sa.y, fmaf(sc, p[4 * qq + 1], acc[m][4 * qq + 1]));
+                acc[m][4 * qq + 2] = fmaf(bc, sa.z, fmaf(sc, p[4 * qq + 2], acc[m][4 * qq + 2]));
+                acc[m][4 * qq + 3] = fmaf(bc, sa.w, fmaf(sc, p[4 * qq + 3], acc[m][4 * qq + 3]));
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();
+      stage_store();
+      __syncthreads();
+      cur = nx;
+    }
+    ch = chn;
+  }
+
+  if (!wave_on) return;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    if (m < nrt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = m * kRowTile + c_row(i, hh);
+        if (r < nrows) a.ys[(size_t)(r0 + r) * H + col] = acc[m][i];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // combine
 // ---------------------------------------------------------------------------
 
@@ -585,10 +906,19 @@ int sort_launch(const SortedArgs& a, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? MOE_Q4_OK : MOE_Q4_ERR_LAUNCH;
 }
 
+size_t gateup2_lds(int mt) { return (size_t)mt * kRowTile * kV2Row + 5 * mt * kRowTile * 4; }
+size_t down2_lds(int mt) { return (size_t)2 * mt * kRowTile * kV2Row + 4 * mt * kRowTile * 4; }
+
 template <int MT>
 int gemm_launch(const SortedArgs& a, bool down, hipStream_t stream) {
   const int tiles8 = (a.tiles_max + 7) / 8 * 8;
-  if (!down) {
+  if (!down && a.H % 1024 == 0) {
+    const int ncb = (a.I + kV2GuCols - 1) / kV2GuCols;
+    hipLaunchKernelGGL(k_sorted_gateup2<MT>, dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT), stream, a);
+  } else if (down && a.I % 1024 == 0) {
+    const int ncb = (a.H + kV2DnCols - 1) / kV2DnCols;
+    hipLaunchKernelGGL(k_sorted_down2<MT>, dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT), stream, a);
+  } else if (!down) {
     const int ncb = (a.I + kGuCols - 1) / kGuCols;
     hipLaunchKernelGGL(k_sorted_gateup<MT>, dim3(tiles8 * ncb), dim3(kMmThreads), gateup_lds(MT), stream, a);
   } else {

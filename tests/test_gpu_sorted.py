@@ -151,6 +151,12 @@ SMALL = [
     (203, 4, 8, 512, 128, False),    # ~100 -> 4 blocks (tiles of 128 rows, some experts split)
     (64, 8, 16, 256, 128, True),     # duplicate ids within a token
     (300, 2, 4, 192, 64, False),     # 150 per expert: several tiles per expert
+    # H and I multiples of 1024 take the streaming kernels (4 groups per iteration)
+    (40, 4, 8, 1024, 1024, False),   # 1 block
+    (80, 4, 8, 1024, 1088, False),   # 2 blocks; gate/up column block with idle waves; down on the general kernel
+    (121, 4, 8, 2048, 1024, False),  # 3 blocks
+    (203, 4, 8, 1024, 2048, False),  # 4 blocks
+    (150, 4, 6, 1088, 1024, True),   # gate/up on the general kernel, down on the streaming one
 ]
 
 
