@@ -150,6 +150,7 @@ __device__ __forceinline__ int nth_set_bit(uint32_t m, int n) {
 //   uniq[P]     distinct ids ascending          mask[P]   token mask per distinct id
 //   off[P+1]    exclusive prefix of popcount(mask): first pair slot of each distinct id
 //   scal[0] = u (distinct ids), scal[1] = 1 if an id fell outside [0, E)
+//   ids[P], tw[P]  the routes and their router weights, staged by stage_routes
 struct UnionLds {
   uint32_t* bitmap;
   int32_t* scan;
@@ -157,11 +158,23 @@ struct UnionLds {
   uint32_t* mask;
   int32_t* off;
   int32_t* scal;
+  int32_t* ids;
+  float* tw;
 };
 
-// Every thread of the workgroup must call this (it contains barriers).
-// Requires blockDim.x >= 64, L <= 32, P = L * k.
-__device__ inline void build_union(const int32_t* __restrict__ ids, int P, int k, int E, const UnionLds& s) {
+// Copies the routes into LDS (no barrier; build_union's first barrier
+// publishes them).  Issued first so the loads overlap whatever follows.
+__device__ __forceinline__ void stage_routes(const int32_t* __restrict__ ids, const float* __restrict__ tw, int P,
+                                             const UnionLds& s) {
+  for (int p = threadIdx.x; p < P; p += blockDim.x) {
+    s.ids[p] = ids[p];
+    s.tw[p] = tw[p];
+  }
+}
+
+// Every thread of the workgroup must call this (it contains barriers), after
+// stage_routes.  Requires blockDim.x >= 64, L <= 32, P = L * k.
+__device__ inline void build_union(int P, int k, int E, const UnionLds& s) {
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int EW = (E + 31) >> 5;
   for (int w = tid; w < EW; w += nthr) s.bitmap[w] = 0u;
@@ -169,7 +182,7 @@ __device__ inline void build_union(const int32_t* __restrict__ ids, int P, int k
   if (tid == 0) s.scal[1] = 0;
   __syncthreads();
   for (int p = tid; p < P; p += nthr) {
-    const int e = ids[p];
+    const int e = s.ids[p];
     if (e >= 0 && e < E)
       atomicOr(&s.bitmap[e >> 5], 1u << (e & 31));
     else
@@ -189,7 +202,7 @@ __device__ inline void build_union(const int32_t* __restrict__ ids, int P, int k
   }
   __syncthreads();
   for (int p = tid; p < P; p += nthr) {
-    const int e = ids[p];
+    const int e = s.ids[p];
     if (e >= 0 && e < E) {
       const uint32_t word = s.bitmap[e >> 5];
       const int r = s.scan[e >> 5] + __popc(word & ((1u << (e & 31)) - 1u));
@@ -214,12 +227,12 @@ __device__ inline void build_union(const int32_t* __restrict__ ids, int P, int k
 }
 
 // Router weight of token t for expert e: the fp32 sum of t's weights over
-// its routes to e, added in ascending slot order starting from 0.
-__device__ __forceinline__ float token_expert_weight(const int32_t* __restrict__ ids, const float* __restrict__ tw,
-                                                     int t, int k, int e) {
+// its routes to e, added in ascending slot order starting from 0 (routes
+// read from the LDS copy).
+__device__ __forceinline__ float token_expert_weight(const UnionLds& s, int t, int k, int e) {
   float acc = 0.0f;
   for (int j = 0; j < k; ++j)
-    if (ids[t * k + j] == e) acc += tw[t * k + j];
+    if (s.ids[t * k + j] == e) acc += s.tw[t * k + j];
   return acc;
 }
 

@@ -20,7 +20,8 @@ __global__ __launch_bounds__(256) void k_route_union(const int32_t* __restrict__
   const int P = L * k;
   UnionLds s;
   carve_union(smem, E, P, s);
-  build_union(ids, P, k, E, s);
+  stage_routes(ids, tw, P, s);
+  build_union(P, k, E, s);
   const int u = s.scal[0];
   const int tid = threadIdx.x;
   if (tid == 0) *u_out = u;
@@ -31,7 +32,7 @@ __global__ __launch_bounds__(256) void k_route_union(const int32_t* __restrict__
   for (int it = tid; it < u_max * L; it += blockDim.x) {
     const int i = it / L, t = it % L;
     float v = 0.0f;
-    if (i < u && ((s.mask[i] >> t) & 1u)) v = token_expert_weight(ids, tw, t, k, s.uniq[i]);
+    if (i < u && ((s.mask[i] >> t) & 1u)) v = token_expert_weight(s, t, k, s.uniq[i]);
     uniq_w[it] = v;
   }
   for (int p = tid; p < P; p += blockDim.x) {
@@ -96,7 +97,7 @@ int positions_per_lane(int KU, int lpr, bool down) {
 
 size_t align16(size_t v) { return (v + 15) & ~size_t(15); }
 
-size_t union_lds(int E, int P) { return (size_t)4 * (2 * ((E + 31) >> 5) + 3 * P + 1 + 2); }
+size_t union_lds(int E, int P) { return (size_t)4 * (2 * ((E + 31) >> 5) + 5 * P + 1 + 2); }
 
 // gate/up LDS: activations of all L tokens | their 32-input sums | route union
 size_t gateup_lds_layout(UnionArgs& a) {
@@ -177,18 +178,12 @@ int union_forward_launch(const UnionArgs& base, unsigned stages, int num_cu, hip
     const size_t lds = align16((size_t)16 * P);
     const bool qs = (a.I / 64) % 2 == 0;
     // one token per register pass when every expert has exactly one token (L = 1)
-    const void* fn = down_kernel(lpr, ppl, lpr * ppl == KU, qs, a.L == 1 ? 1 : 2);
+    const int nt = a.L == 1 ? 1 : 2;
+    const void* fn = down_kernel(lpr, ppl, lpr * ppl == KU, qs, nt);
     if (!fn || lds > kMaxLds) return MOE_Q4_ERR_UNSUPPORTED;
-    const int groups = 64 / lpr;
-    const int wstep = groups * down_rows(groups);
-    const int steps = u_max * (a.H / wstep);
-    constexpr int nw = kDownThreads / 64;
-    int grid = num_cu * blocks_per_cu(fn, kDownThreads, lds);
-    const int need = (steps + nw - 1) / nw;
-    if (grid > need) grid = need;
-    if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(reinterpret_cast<void (*)(UnionArgs)>(const_cast<void*>(fn)), dim3(grid),
-                       dim3(kDownThreads), lds, stream, a);
+    // one block per CU: the CU's waves share the block's work counter
+    hipLaunchKernelGGL(reinterpret_cast<void (*)(UnionArgs)>(const_cast<void*>(fn)), dim3(num_cu),
+                       dim3(down_threads(nt)), lds, stream, a);
     if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;
     dim3 cgrid((a.H / 4 + 255) / 256, a.L);
     hipLaunchKernelGGL(k_combine, cgrid, dim3(256), 0, stream, a);

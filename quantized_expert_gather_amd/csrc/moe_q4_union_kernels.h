@@ -50,7 +50,6 @@ namespace moeq4 {
 
 constexpr int kThreads = 512;        // gate/up blocks: 8 waves sharing the staged activations
 constexpr int kWaves = kThreads / 64;
-constexpr int kDownThreads = 256;    // down blocks: 4 independent waves
 constexpr int kDownUnitRows = 64;    // output rows of one down work unit
 constexpr int kDownTokChunk = 2;     // tokens per register pass in down
 
@@ -69,6 +68,8 @@ __device__ __forceinline__ void carve_union(unsigned char* base, int E, int P, U
   s.mask = reinterpret_cast<uint32_t*>(s.uniq + P);
   s.off = reinterpret_cast<int32_t*>(s.mask + P);
   s.scal = s.off + P + 1;
+  s.ids = s.scal + 2;
+  s.tw = reinterpret_cast<float*>(s.ids + P);
 }
 
 // ---------------------------------------------------------------------------
@@ -254,6 +255,42 @@ __device__ __forceinline__ void gu_compute(const UnionArgs& a, const GuFrag<PPL,
   }
 }
 
+// Tables for the down and combine kernels (one workgroup; no barriers, so
+// each wave writes its share whenever it gets here):
+//   hdr[0..2]   status of this call, path, distinct experts u
+//   utab[i]     (expert id, token mask, first pair slot, 0) of distinct expert i
+//   slot_w[s]   router weight of pair slot s (token t's weights summed over its
+//               routes to that expert, ascending route order)
+//   tslot/tcount  each token's pair slots, ascending expert
+__device__ inline void write_union_tables(const UnionArgs& a, const UnionLds& s, int u, int L, int k) {
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    a.hdr[0] = s.scal[1] ? MOE_Q4_DEV_BAD_ID : 0u;  // status of this call
+    a.hdr[1] = MOE_Q4_PATH_UNION;
+    a.hdr[2] = (uint32_t)u;
+  }
+  for (int i = tid; i < u; i += blockDim.x) a.utab[i] = make_int4(s.uniq[i], (int)s.mask[i], s.off[i], 0);
+  // one thread per pair slot
+  const int npairs = s.off[u];
+  for (int sl = tid; sl < npairs; sl += blockDim.x) {
+    int lo = 0, hi = u - 1;  // distinct expert owning slot sl: last i with off[i] <= sl
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s.off[mid] <= sl) lo = mid; else hi = mid - 1;
+    }
+    const int t = nth_set_bit(s.mask[lo], sl - s.off[lo]);
+    a.slot_w[sl] = token_expert_weight(s, t, k, s.uniq[lo]);
+  }
+  for (int t = tid; t < L; t += blockDim.x) {
+    int c = 0;
+    for (int i = 0; i < u; ++i) {
+      const uint32_t m = s.mask[i];
+      if ((m >> t) & 1u) a.tslot[t * k + c++] = s.off[i] + __popc(m & ((1u << t) - 1u));
+    }
+    a.tcount[t] = c;
+  }
+}
+
 template <int LPR, int PPL, bool FULL, bool QS>
 __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
   constexpr int G = 64 / LPR;           // lane groups per wave
@@ -267,49 +304,43 @@ __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
   float* asum = reinterpret_cast<float*>(smem + a.lds_asum);     // [L][KU] sums of the 32 inputs
   UnionLds s;
   carve_union(smem + a.lds_union, E, P, s);
-
-  // stage all tokens' activations (independent of the union; overlaps it)
   const int tid = threadIdx.x;
-  for (int it = tid; it < L * KU; it += blockDim.x) {
-    const int t = it / KU, j = it - t * KU;
-    const uint4* xs = reinterpret_cast<const uint4*>(a.x + (size_t)t * H) + 4 * j;
-    float sum = 0.0f;
+  __shared__ int unit_q;  // next dynamically assigned unit of this block
+  if (tid == 0) unit_q = 2 * kWaves;
+  stage_routes(a.ids, a.tw, P, s);  // first loads of the kernel
+  // stage all tokens' activations (independent of the union; overlaps it):
+  // three 32-input positions per thread per round, all loads issued first
+  {
+    constexpr int XB = 3;
+    const int nx = L * KU;
+    for (int base = tid; base < nx; base += XB * kThreads) {
+      uint4 v[XB][4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint4 v = xs[c];
-      sum = sum8_bf16(v, sum);
-      act[((size_t)t * 4 + c) * KU + j] = pair_activations(v);
+      for (int b = 0; b < XB; ++b) {
+        const int it = min(base + b * kThreads, nx - 1);
+        const int t = it / KU, j = it - t * KU;
+        const uint4* xs = reinterpret_cast<const uint4*>(a.x + (size_t)t * H) + 4 * j;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[b][c] = xs[c];
+      }
+#pragma unroll
+      for (int b = 0; b < XB; ++b) {
+        const int it = base + b * kThreads;
+        if (it < nx) {
+          const int t = it / KU, j = it - t * KU;
+          float sum = 0.0f;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            sum = sum8_bf16(v[b][c], sum);
+            act[((size_t)t * 4 + c) * KU + j] = pair_activations(v[b][c]);
+          }
+          asum[(size_t)t * KU + j] = sum;
+        }
+      }
     }
-    asum[(size_t)t * KU + j] = sum;
   }
-  build_union(a.ids, P, k, E, s);  // ends with a barrier
+  build_union(P, k, E, s);  // ends with a barrier
   const int u = s.scal[0];
-
-  if (blockIdx.x == 0) {
-    // tables for the down and combine kernels
-    if (tid == 0) {
-      a.hdr[0] = s.scal[1] ? MOE_Q4_DEV_BAD_ID : 0u;  // status of this call
-      a.hdr[1] = MOE_Q4_PATH_UNION;
-      a.hdr[2] = (uint32_t)u;
-    }
-    for (int i = tid; i < u; i += blockDim.x) {
-      a.utab[i] = make_int4(s.uniq[i], (int)s.mask[i], s.off[i], 0);
-      uint32_t m = s.mask[i];
-      for (int c = 0; m; ++c) {
-        const int t = __builtin_ctz(m);
-        m &= m - 1u;
-        a.slot_w[s.off[i] + c] = token_expert_weight(a.ids, a.tw, t, k, s.uniq[i]);
-      }
-    }
-    for (int t = tid; t < L; t += blockDim.x) {
-      int c = 0;
-      for (int i = 0; i < u; ++i) {
-        const uint32_t m = s.mask[i];
-        if ((m >> t) & 1u) a.tslot[t * k + c++] = s.off[i] + __popc(m & ((1u << t) - 1u));
-      }
-      a.tcount[t] = c;
-    }
-  }
 
   const int lane = tid & 63;
   const int wave = wave_uniform(tid >> 6);
@@ -328,43 +359,62 @@ __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
       const int grp = QS ? 2 * (li >> 2) + (LPR / 2) * p : (j >> 1);
       o.s[p][r] = (uint32_t)(((g * RG + r) * KG + grp) * 2);
     }
-  // units ub, ub + stride, ub + 2 stride, ... of this wave: consecutive units
-  // (adjacent rows) go to adjacent waves, so the chip sweeps each expert's
-  // rows in order.  They stream through a ring of three register fragments,
-  // two in flight while the third is computed; prefetches past the end
-  // repeat the last unit (cache-resident) so every load is unconditional.
+  // Work units: (distinct expert, WROWS hidden rows).  Block b owns units
+  // b, b + nblk, b + 2 nblk, ... (adjacent blocks take adjacent rows, so the
+  // chip sweeps each expert's rows in order).  Inside the block the waves
+  // take the block's units from an LDS counter: the two waves sharing a SIMD
+  // do not progress at the same rate (issue arbitration favours the older
+  // one), and a fixed split would leave the younger ones as the kernel's
+  // tail.  Each wave streams its units through a ring of three register
+  // fragments, two in flight while the third is computed; a unit index past
+  // the block's share loads the share's last unit again (cache-resident), so
+  // every load is unconditional.
   const int upe = I / WROWS;                // wave units per expert
   const int nunits = u * upe;
-  const int stride = gridDim.x * kWaves;
-  const int ub = blockIdx.x * kWaves + wave;
-  if (ub >= nunits) return;
-  const int klast = (nunits - 1 - ub) / stride;  // index of this wave's last unit
-  auto load = [&](int kk, GuFrag<PPL, RG>& f) {
-    const int un = ub + min(kk, klast) * stride;
-    const int i = un / upe;
-    gu_load<PPL, RG, FULL, QS>(a, (size_t)wave_uniform(s.uniq[i]) * I + (un - i * upe) * WROWS, WROWS, KU, KG, li,
-                               LPR, lane_sbase, o, f);
-  };
-  auto compute = [&](int kk, const GuFrag<PPL, RG>& f) {
-    const int un = ub + kk * stride;
-    const int i = un / upe;
-    gu_compute<LPR, PPL, RG, FULL, QS>(a, f, wave_uniform((int)s.mask[i]), wave_uniform(s.off[i]),
-                                       (un - i * upe) * WROWS + g * RG, li, KU, act, asum, sel);
-  };
-  GuFrag<PPL, RG> f0, f1, f2;
-  load(0, f0);
-  load(1, f1);
-  for (int kk = 0;; kk += 3) {
-    load(kk + 2, f2);
-    compute(kk, f0);
-    if (kk + 1 > klast) break;
-    load(kk + 3, f0);
-    compute(kk + 1, f1);
-    if (kk + 2 > klast) break;
-    load(kk + 4, f1);
-    compute(kk + 2, f2);
-    if (kk + 3 > klast) break;
+  const int nblk = gridDim.x, b = blockIdx.x;
+  const int nub = nunits > b ? (nunits - 1 - b) / nblk + 1 : 0;  // units of this block
+  if (wave < nub) {
+    auto load = [&](int j, GuFrag<PPL, RG>& f) {
+      const int un = b + min(j, nub - 1) * nblk;
+      const int i = un / upe;
+      gu_load<PPL, RG, FULL, QS>(a, (size_t)wave_uniform(s.uniq[i]) * I + (un - i * upe) * WROWS, WROWS, KU, KG, li,
+                                 LPR, lane_sbase, o, f);
+    };
+    auto compute = [&](int j, const GuFrag<PPL, RG>& f) {
+      const int un = b + j * nblk;
+      const int i = un / upe;
+      gu_compute<LPR, PPL, RG, FULL, QS>(a, f, wave_uniform((int)s.mask[i]), wave_uniform(s.off[i]),
+                                         (un - i * upe) * WROWS + g * RG, li, KU, act, asum, sel);
+    };
+    auto grab = [&]() {
+      int v = 0;
+      if (lane == 0) v = atomicAdd(&unit_q, 1);
+      return __builtin_amdgcn_readfirstlane(v);
+    };
+    // j0, j1, j2: the units in f0, f1, f2 (increasing: the counter only grows)
+    GuFrag<PPL, RG> f0, f1, f2;
+    int j0 = wave, j1 = wave + kWaves, j2;
+    load(j0, f0);
+    load(j1, f1);
+    int jn = grab();  // next unit to load, taken one step ahead
+    for (;;) {
+      j2 = jn; jn = grab();
+      load(j2, f2);
+      compute(j0, f0);
+      if (j1 >= nub) break;
+      j0 = jn; jn = grab();
+      load(j0, f0);
+      compute(j1, f1);
+      if (j2 >= nub) break;
+      j1 = jn; jn = grab();
+      load(j1, f1);
+      compute(j2, f2);
+      if (j0 >= nub) break;
+    }
   }
+  // block 0 writes the tables the down and combine kernels read, after its
+  // own units so the table work stays off the start of its weight stream
+  if (blockIdx.x == 0) write_union_tables(a, s, u, L, k);
 }
 
 // ---------------------------------------------------------------------------
@@ -542,20 +592,27 @@ __device__ __forceinline__ void dn_segment(const UnionArgs& a, int e, size_t eba
   }
 }
 
+// threads of a down block: one block per CU, as many waves as the registers
+// allow (the waves of a CU share one LDS work counter)
+constexpr int down_threads(int nt) { return nt == 1 ? 1024 : 768; }
+constexpr int kDownUnitSteps = 4;  // row steps per down work unit
+
 template <int LPR, int PPL, bool FULL, bool QS, int NT>
-__global__ __launch_bounds__(kDownThreads) void k_down(UnionArgs a) {
+__global__ __launch_bounds__(down_threads(NT)) void k_down(UnionArgs a) {
   constexpr int G = 64 / LPR;
   constexpr int RS = down_rows(G);       // a wave step covers G * RS rows
   constexpr int WSTEP = G * RS;
-  constexpr int NW = kDownThreads / 64;
+  constexpr int NW = down_threads(NT) / 64;
   static_assert(!QS || RS % 2 == 0, "quad-shared scales pair rows");
   extern __shared__ __align__(16) unsigned char smem[];
   int4* utab = reinterpret_cast<int4*>(smem);
+  __shared__ int unit_q;  // next dynamically assigned unit of this block
   const int H = a.H, I = a.I;
   const int KU = I >> 5, KG = I >> 6;
   const int tid = threadIdx.x;
   const int u = (int)a.hdr[2];
   for (int i = tid; i < u; i += blockDim.x) utab[i] = a.utab[i];
+  if (tid == 0) unit_q = NW;
   __syncthreads();
 
   const int lane = tid & 63;
@@ -577,32 +634,38 @@ __global__ __launch_bounds__(kDownThreads) void k_down(UnionArgs a) {
       o.s[r][p] = (uint32_t)(((g * RS + srow) * KG + grp) * 2);
     }
 
-  // Waves split into groups, one distinct expert per group at a time; inside
-  // a group the waves interleave over the expert's row steps (adjacent waves,
-  // adjacent rows), so each wave stages its expert's hidden vectors once and
-  // the chip sweeps each expert's rows in order.
-  const int spe = H / WSTEP;                     // row steps per expert
-  const int nwaves = gridDim.x * NW;
-  const int wpe = max(1, nwaves / max(u, 1));    // waves per group
-  const int ngroups = nwaves / wpe;
-  const int gw = blockIdx.x * NW + wave;
-  const int grp = gw / wpe, gj = gw - grp * wpe;
-  if (grp >= ngroups) return;
-
-  for (int i = grp; i < u; i += ngroups) {
-    if (gj >= spe) continue;
-    const int klast = (spe - 1 - gj) / wpe;      // this wave's steps: gj + kk * wpe, kk <= klast
+  // Work units: (distinct expert, kDownUnitSteps row steps), expert-major.
+  // Block b owns units b, b + nblk, ... (adjacent blocks, adjacent rows of
+  // the same expert); its waves take them from an LDS counter (first unit of
+  // each wave fixed), so waves that get fewer issue slots do less of the
+  // block's share.  A unit runs every token of its expert, NT at a time,
+  // each chunk staging those tokens' hidden vectors once.
+  const int spe = H / WSTEP;                                 // row steps per expert
+  const int nrb = (spe + kDownUnitSteps - 1) / kDownUnitSteps;
+  const int nunits = u * nrb;
+  const int nblk = gridDim.x, b = blockIdx.x;
+  const int nub = nunits > b ? (nunits - 1 - b) / nblk + 1 : 0;
+  auto grab = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&unit_q, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  for (int j = wave; j < nub; j = grab()) {
+    const int un = b + j * nblk;
+    const int i = un / nrb, rb = un - i * nrb;
     const int4 ent = utab[i];
     const int e = wave_uniform(ent.x), slot0 = wave_uniform(ent.z);
     const int ntok = __popc((uint32_t)wave_uniform(ent.y));
     const size_t ebase = (size_t)e * H;
+    const int gj = rb * kDownUnitSteps;
+    const int klast = min(kDownUnitSteps, spe - gj) - 1;
     for (int t0 = 0; t0 < ntok; t0 += NT) {
       const int nt = min(NT, ntok - t0);
       if (NT > 1 && nt == 1)
-        dn_segment<LPR, PPL, FULL, QS, 1, RS, WSTEP>(a, e, ebase, slot0 + t0, 1, gj, wpe, klast, li, g, KU, KG, I, H,
+        dn_segment<LPR, PPL, FULL, QS, 1, RS, WSTEP>(a, e, ebase, slot0 + t0, 1, gj, 1, klast, li, g, KU, KG, I, H,
                                                      lane_sbase, o, sel);
       else
-        dn_segment<LPR, PPL, FULL, QS, NT, RS, WSTEP>(a, e, ebase, slot0 + t0, nt, gj, wpe, klast, li, g, KU, KG, I,
+        dn_segment<LPR, PPL, FULL, QS, NT, RS, WSTEP>(a, e, ebase, slot0 + t0, nt, gj, 1, klast, li, g, KU, KG, I,
                                                       H, lane_sbase, o, sel);
     }
   }
