@@ -137,6 +137,7 @@ def moe_swiglu_q4_select_path(L: int, k: int, E: int, H: int, I: int) -> int:
 
 
 def new_workspace(L: int, k: int, E: int, H: int, I: int, device=None) -> torch.Tensor:
+    """A workspace for this shape (its contents need no initialisation)."""
     n = moe_swiglu_q4_workspace_bytes(L, k, E, H, I)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device or "cuda")
 

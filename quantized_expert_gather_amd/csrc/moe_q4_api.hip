@@ -21,7 +21,7 @@ UnionWorkspace union_workspace_layout(int L, int k, int E, int H, int I) {
   w.hdr = off;    off = round256(off + 256);
   w.utab = off;   off = round256(off + pairs * 16);
   w.slot_w = off; off = round256(off + pairs * 4);
-  w.tslot = off;  off = round256(off + pairs * 4);
+  w.slot_dst = off; off = round256(off + pairs * 4);
   w.tcount = off; off = round256(off + (size_t)L * 4);
   w.hbuf = off;   off = round256(off + pairs * (size_t)I * 4);
   w.ys = off;     off = round256(off + pairs * (size_t)H * 4);
@@ -170,7 +170,7 @@ int moe_swiglu_q4_forward_stages(const void* x, const int32_t* topk_ids, const f
   a.hdr = reinterpret_cast<uint32_t*>(ws + lay.hdr);
   a.utab = reinterpret_cast<int4*>(ws + lay.utab);
   a.slot_w = reinterpret_cast<float*>(ws + lay.slot_w);
-  a.tslot = reinterpret_cast<int32_t*>(ws + lay.tslot);
+  a.slot_dst = reinterpret_cast<int32_t*>(ws + lay.slot_dst);
   a.tcount = reinterpret_cast<int32_t*>(ws + lay.tcount);
   a.hbuf = reinterpret_cast<float*>(ws + lay.hbuf);
   a.ys = reinterpret_cast<float*>(ws + lay.ys);

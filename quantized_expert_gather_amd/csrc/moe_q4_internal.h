@@ -28,10 +28,10 @@ struct UnionArgs {
   uint32_t* hdr;    // [0] status of the last call, [1] its path, [2] its distinct experts u
   int4* utab;       // [u] (expert id, token mask, first pair slot, 0) per distinct expert
   float* slot_w;    // [pairs] router weight of each (expert, token) pair
-  int32_t* tslot;   // [L][k] pair slots of each token, ascending expert
+  int32_t* slot_dst;  // [pairs] output row of each pair slot in ys: t * k + c, c = rank of its expert among t's
   int32_t* tcount;  // [L] number of pair slots of each token
   float* hbuf;      // [pairs][I] hidden vectors h = silu(gate) * up, fp32
-  float* ys;        // [pairs][H] router-weighted down outputs per (expert, token)
+  float* ys;        // [L * k][H] router-weighted down outputs, token-major (row t * k + c)
   float* ys_dummy;  // [H] write sink for token slots past an expert's count
   // dynamic LDS layout of the gate/up kernel
   size_t lds_act, lds_asum, lds_union;
@@ -39,7 +39,7 @@ struct UnionArgs {
 
 // Workspace layout (byte offsets from the workspace base, 256-aligned regions).
 struct UnionWorkspace {
-  size_t hdr, utab, slot_w, tslot, tcount, hbuf, ys, ys_dummy, total;
+  size_t hdr, utab, slot_w, slot_dst, tcount, hbuf, ys, ys_dummy, total;
 };
 
 UnionWorkspace union_workspace_layout(int L, int k, int E, int H, int I);

@@ -44,7 +44,9 @@ __global__ __launch_bounds__(256) void k_route_union(const int32_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// combine: out[t, m] = sum over t's pairs (ascending expert) of ys[pair, m]
+// combine: out[t, m] = sum over c < tcount[t] (ascending expert) of ys[t * k + c, m]
+// All k rows are loaded at once (rows past the count are ignored), so the
+// kernel waits for memory once.
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void k_combine(UnionArgs a) {
@@ -54,9 +56,22 @@ __global__ __launch_bounds__(256) void k_combine(UnionArgs a) {
   const int t = blockIdx.y;
   if (it >= n4) return;
   const int cnt = a.tcount[t];
+  const float4* rows = reinterpret_cast<const float4*>(a.ys + (size_t)t * k * H) + it;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  for (int c = 0; c < cnt; ++c) {
-    const float4 v = reinterpret_cast<const float4*>(a.ys + (size_t)a.tslot[t * k + c] * H)[it];
+  int c = 0;
+  for (; c + 8 <= k; c += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = rows[(size_t)(c + q) * n4];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      // rows past the count hold stale data: select, never add them
+      const float4 w = c + q < cnt ? v[q] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      acc.x += w.x; acc.y += w.y; acc.z += w.z; acc.w += w.w;
+    }
+  }
+  for (; c < cnt; ++c) {
+    const float4 v = rows[(size_t)c * n4];
     acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
   }
   if (a.out_f32) {

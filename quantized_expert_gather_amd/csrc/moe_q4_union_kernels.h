@@ -261,7 +261,8 @@ __device__ __forceinline__ void gu_compute(const UnionArgs& a, const GuFrag<PPL,
 //   utab[i]     (expert id, token mask, first pair slot, 0) of distinct expert i
 //   slot_w[s]   router weight of pair slot s (token t's weights summed over its
 //               routes to that expert, ascending route order)
-//   tslot/tcount  each token's pair slots, ascending expert
+//   slot_dst[s]   output row t * k + c of pair slot s in ys (c = rank of the
+//                 slot's expert among token t's distinct experts); tcount[t] = c's
 __device__ inline void write_union_tables(const UnionArgs& a, const UnionLds& s, int u, int L, int k) {
   const int tid = threadIdx.x;
   if (tid == 0) {
@@ -285,7 +286,7 @@ __device__ inline void write_union_tables(const UnionArgs& a, const UnionLds& s,
     int c = 0;
     for (int i = 0; i < u; ++i) {
       const uint32_t m = s.mask[i];
-      if ((m >> t) & 1u) a.tslot[t * k + c++] = s.off[i] + __popc(m & ((1u << t) - 1u));
+      if ((m >> t) & 1u) a.slot_dst[s.off[i] + __popc(m & ((1u << t) - 1u))] = t * k + c++;
     }
     a.tcount[t] = c;
   }
@@ -554,7 +555,7 @@ __device__ __forceinline__ void dn_segment(const UnionArgs& a, int e, size_t eba
     const int ex = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) : 0;
     const float up = __builtin_ldexpf(1.0f, 14 - ex);
     tw[c] = live ? a.slot_w[slot] * __builtin_ldexpf(1.0f, ex - 14) : 0.0f;
-    dst[c] = live ? a.ys + (size_t)slot * H : a.ys_dummy;
+    dst[c] = live ? a.ys + (size_t)a.slot_dst[slot] * H : a.ys_dummy;
 #pragma unroll
     for (int p = 0; p < PPL; ++p) {
       float sum = 0.0f;

@@ -199,6 +199,29 @@ def test_workspace_reuse_across_shapes():
         assert rel_err_rows(out.cpu().numpy(), ref).max() <= ARITH
 
 
+def test_garbage_workspace_and_repeated_calls():
+    # a workspace holding garbage needs no set-up; repeated calls and
+    # repeated stage-only calls on it all give the oracle's result
+    q = _q()
+    x, ids, tw, bank = synth.random_problem(4, 8, 64, 1024, 256, seed=13)
+    ref = oracle.forward_pairs(x, ids, tw, bank)
+    xd, idd, twd, bk = x.cuda(), torch.from_numpy(ids).cuda(), torch.from_numpy(tw).cuda(), bank.to("cuda")
+    n = q.moe_swiglu_q4_workspace_bytes(4, 8, 64, 1024, 256)
+    ws = torch.full((n,), 0xAB, dtype=torch.uint8, device="cuda")
+    say("garbage workspace")
+    outs = []
+    for _ in range(3):
+        outs.append(q.forward_bank(xd, idd, twd, bk, out_dtype=torch.float32, workspace=ws))
+    out = torch.empty((4, 1024), dtype=torch.float32, device="cuda")
+    for st in (q.MOE_Q4_STAGE_GATEUP, q.MOE_Q4_STAGE_GATEUP, q.MOE_Q4_STAGE_DOWN, q.MOE_Q4_STAGE_DOWN):
+        q.forward_bank(xd, idd, twd, bk, out=out, out_dtype=torch.float32, workspace=ws, stages=st)
+    outs.append(out)
+    torch.cuda.synchronize()
+    assert rel_err_rows(outs[0].cpu().numpy(), ref).max() <= ARITH
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
 def test_invalid_ids_set_status_and_drop_routes():
     q = _q()
     x, ids, tw, bank = synth.random_problem(3, 2, 6, 256, 128, seed=7)
