@@ -177,6 +177,9 @@ def main():
     ap.add_argument("--sorted-Ts", default="512,2048",
                     help="token counts of the prefill (sorted-path) measurement; empty to skip")
     ap.add_argument("--sorted-layers", type=int, default=4, help="distinct layers per prefill chain")
+    ap.add_argument("--pair-layers", type=int, default=20,
+                    help="layers of each chain timed again as a per-pair baseline (one call per token, so "
+                         "an expert shared by tokens is streamed once per token); 0 to skip")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the baseline sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -318,6 +321,53 @@ def main():
         log(f"L={L}: {us_layer:.2f} us/layer, {gbps:.0f} GB/s effective ({gbps / PEAK_HBM_GBPS * 100:.1f}% of 8 TB/s);"
             f" gate+up {per_L[str(L)]['gateup_us']:.1f} us, down+combine {per_L[str(L)]['down_combine_us']:.1f} us")
 
+    # per-pair baseline: the same layers with one call per token (L = 1 each),
+    # i.e. every (token, expert) route streams its expert's weights -- the
+    # traffic of a per-pair gather without deduplication across tokens
+    if args.pair_layers > 0:
+        pair = {}
+        for L in Ls:
+            if L == 1:
+                continue
+            layers = chains[L]["layers"][: args.pair_layers]
+            calls = []
+            for lay in layers:
+                ws1 = q.new_workspace(1, k, E, H, I, dev)
+                lay["pair_ws"] = ws1
+                for t in range(L):
+                    calls.append(q.PreparedForward(lay["x"][t:t + 1], lay["ids"][t:t + 1], lay["tw"][t:t + 1],
+                                                   lay["bank"].tensors(), lay["out"][t:t + 1], ws1,
+                                                   q.MOE_Q4_STAGE_ALL, stream))
+
+            ucalls = [lay["calls"]["all"] for lay in layers]
+
+            def chain_of(cs):
+                torch.cuda._sleep(sleep_cycles)
+                e0_, e1_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0_.record()
+                for c in cs:
+                    c()
+                e1_.record()
+                return e0_, e1_
+
+            chain_of(calls)
+            torch.cuda.synchronize()
+            nrep = max(3, args.steps // 2)
+            recs_p = [chain_of(calls) for _ in range(nrep)]
+            recs_u = [chain_of(ucalls) for _ in range(nrep)]  # the union path on the same layers
+            torch.cuda.synchronize()
+            us = float(np.median([a_.elapsed_time(b_) for a_, b_ in recs_p])) * 1e3 / len(layers)
+            uu = float(np.median([a_.elapsed_time(b_) for a_, b_ in recs_u])) * 1e3 / len(layers)
+            pair[str(L)] = {"us_per_layer": round(us, 2), "layers": len(layers),
+                            "union_us_per_layer_same_layers": round(uu, 2),
+                            "per_pair_over_union": round(us / uu, 3),
+                            "slot_bytes_GBps": round(L * k * eb / (us * 1e-6) / 1e9, 1)}
+            log(f"per-pair L={L}: {us:.1f} us/layer vs union {uu:.1f} us/layer on the same {len(layers)} layers "
+                f"({us / uu:.2f}x)")
+        pair_result = pair
+    else:
+        pair_result = None
+
     # streaming reference: a plain device copy (read + write bytes / time)
     ref_src = torch.empty(2 * 2**30, dtype=torch.uint8, device=dev).fill_(1)
     ref_dst = torch.empty_like(ref_src)
@@ -342,6 +392,7 @@ def main():
                    "value_over_L": [v for v in Ls if v in METRIC_LS] or Ls, "layers": args.layers,
                    "bytes_per_expert": eb, "timing": "GPU events, chains enqueued back to back"},
         "per_L": per_L,
+        "per_pair_baseline": pair_result,
         "stream_ref_copy_GBps": round(copy_gbps, 1),
     }
     if "1" in per_L and "2" in per_L:
