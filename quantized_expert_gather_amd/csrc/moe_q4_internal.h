@@ -35,6 +35,7 @@ struct UnionArgs {
   float* ys_dummy;  // [H] write sink for token slots past an expert's count
   // dynamic LDS layout of the gate/up kernel
   size_t lds_act, lds_asum, lds_union;
+  int dn_slots;  // pair slots the down kernel stages in LDS at a time
 };
 
 // Workspace layout (byte offsets from the workspace base, 256-aligned regions).

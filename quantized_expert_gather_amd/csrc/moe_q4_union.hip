@@ -2,6 +2,8 @@
 // route-union kernel, the combine kernel and the launchers.  The gate/up and
 // down kernel templates live in moe_q4_union_kernels.h and are instantiated
 // in the moe_q4_inst_*.hip units (compiled in parallel).
+#include <algorithm>
+
 #include "moe_q4_union_kernels.h"
 #include "moe_q4_inst.h"
 
@@ -155,7 +157,7 @@ bool union_shape_supported(int L, int k, int E, int H, int I) {
   const int lg = lanes_per_row(H / 32), ld = lanes_per_row(I / 32);
   if (!positions_per_lane(H / 32, lg, false) || !positions_per_lane(I / 32, ld, true)) return false;
   if ((I % (gateup_rows(positions_per_lane(H / 32, lg, false)) * (64 / lg))) != 0) return false;
-  return union_lds_bytes_max(L, k, E, H, I) <= kMaxLds && (size_t)4 * 16 * (L * k) <= kMaxLds;
+  return union_lds_bytes_max(L, k, E, H, I) <= kMaxLds && down_lds_head(L * k) + down_slot_bytes(I / 32) + 256 <= kMaxLds;
 }
 
 int route_union_launch(const int32_t* ids, const float* tw, int L, int k, int E, int32_t* u, int32_t* uniq_ids,
@@ -190,13 +192,18 @@ int union_forward_launch(const UnionArgs& base, unsigned stages, int num_cu, hip
     UnionArgs a = base;
     const int KU = a.I / 32;
     const int lpr = lanes_per_row(KU), ppl = positions_per_lane(KU, lpr, true);
-    const size_t lds = align16((size_t)16 * P);
+    // as many pair slots staged at once as the LDS holds, up to all of them
+    const size_t base_lds = down_lds_head(P);
+    if (base_lds + down_slot_bytes(KU) + 256 > kMaxLds) return MOE_Q4_ERR_UNSUPPORTED;
+    a.dn_slots = (int)std::min<size_t>((size_t)P, (kMaxLds - 256 - base_lds) / down_slot_bytes(KU));
+    const size_t lds = base_lds + (size_t)a.dn_slots * down_slot_bytes(KU);
     const bool qs = (a.I / 64) % 2 == 0;
     // one token per register pass when every expert has exactly one token (L = 1)
     const int nt = a.L == 1 ? 1 : 2;
     const void* fn = down_kernel(lpr, ppl, lpr * ppl == KU, qs, nt);
     if (!fn || lds > kMaxLds) return MOE_Q4_ERR_UNSUPPORTED;
-    // one block per CU: the CU's waves share the block's work counter
+    // one block per CU: the CU's waves share the block's converted hidden
+    // vectors and its work counter
     hipLaunchKernelGGL(reinterpret_cast<void (*)(UnionArgs)>(const_cast<void*>(fn)), dim3(num_cu),
                        dim3(down_threads(nt)), lds, stream, a);
     if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;

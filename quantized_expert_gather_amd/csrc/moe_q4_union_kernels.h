@@ -50,8 +50,7 @@ namespace moeq4 {
 
 constexpr int kThreads = 512;        // gate/up blocks: 8 waves sharing the staged activations
 constexpr int kWaves = kThreads / 64;
-constexpr int kDownUnitRows = 64;    // output rows of one down work unit
-constexpr int kDownTokChunk = 2;     // tokens per register pass in down
+constexpr int kDownUnitRows = 64;    // output rows of one down step, at most
 
 // hidden rows per lane group in one gate/up unit (fewer when a row needs
 // several 16-byte positions per lane, to keep two units in registers)
@@ -461,10 +460,129 @@ __device__ __forceinline__ void dn_load(const UnionArgs& a, size_t row0, bool va
       }
 }
 
-// One step: RS rows of this lane group against the NT staged hidden vectors
-// (fp16 pairs scaled by 2^k per token); each (row, token) result, times the
-// token's router weight (and 2^-k), goes to its ys address (a dummy line for
-// token slots past the expert's count).
+// Totals of RS rows whose partial sums are spread over the LPR lanes of each
+// lane group (v[r]: this lane's part of row r).  Reduce-scatter over the
+// quad (each exchange halves the values a lane carries), then an all-reduce
+// over the lanes that carry the same row.  Lane li of a group returns the
+// total of row li % RS; every lane with that residue holds the same value.
+template <int LPR, int RS>
+__device__ __forceinline__ float reduce_rows(const float (&v)[RS]) {
+  static_assert(RS == 2 || RS == 4, "rows per group");
+  static_assert(LPR >= RS && LPR <= 64, "lanes per group");
+  const int lane = threadIdx.x & 63;
+  const bool b0 = lane & 1, b1 = lane & 2;
+  float k;
+  if constexpr (RS == 4) {
+    float k0 = b0 ? v[1] : v[0];
+    float k1 = b0 ? v[3] : v[2];
+    k0 += dpp_f32<0xB1>(b0 ? v[0] : v[1]);  // quad_perm(1,0,3,2): lane ^ 1
+    k1 += dpp_f32<0xB1>(b0 ? v[2] : v[3]);
+    k = b1 ? k1 : k0;
+    k += dpp_f32<0x4E>(b1 ? k0 : k1);      // quad_perm(2,3,0,1): lane ^ 2
+  } else {
+    k = b0 ? v[1] : v[0];
+    k += dpp_f32<0xB1>(b0 ? v[0] : v[1]);
+    if constexpr (LPR >= 4) k += dpp_f32<0x4E>(k);
+  }
+  if constexpr (LPR == 8) k += __shfl_xor(k, 4, 64);
+  if constexpr (LPR >= 16) {
+    k += dpp_f32<0x124>(k);  // row_ror:4 (the 4 quads of a 16-lane row)
+    k += dpp_f32<0x128>(k);  // row_ror:8
+  }
+  if constexpr (LPR >= 32) {
+    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(k), __float_as_uint(k), false, false);
+    k = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // rows 0 + 1, rows 2 + 3
+  }
+  if constexpr (LPR == 64) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(k), __float_as_uint(k), false, false);
+    k = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // lanes 0-31 + lanes 32-63
+  }
+  return k;
+}
+
+// LDS of a down block: the union table, the work prefix per expert, then
+// per staged pair slot its hidden vector as fp16 pairs in code order
+// [4][KU] (uint4), the sums of the 32 fp16 values per position [KU], the
+// router weight times the slot's 2^-k and the slot's ys row.
+__host__ __device__ constexpr size_t down_slot_bytes(int KU) { return (size_t)KU * 68 + 8; }
+__host__ __device__ constexpr size_t down_lds_base(int P) { return ((size_t)16 * P + 15) & ~size_t(15); }
+// bytes before the staged slots: the union table and the work prefix
+__host__ __device__ constexpr size_t down_lds_head(int P) {
+  return down_lds_base(P) + (((size_t)4 * (P + 1) + 15) & ~size_t(15));
+}
+
+// Converts pair slot `slot` (h of one (expert, token) pair, fp32) into staged
+// slot `ls`: scaled by the power of two that puts its largest magnitude in
+// [2^13, 2^14), rounded to fp16.  One wave per slot.
+__device__ __forceinline__ void down_stage_slot(const UnionArgs& a, int ls, int slot, int KU, uint4* hvs, float* hss,
+                                                float* stw, int* sdst) {
+  const int lane = threadIdx.x & 63;
+  const float* hrow = a.hbuf + (size_t)slot * a.I;
+  auto load32 = [&](int j, float (&v)[32]) {
+    const float4* src = reinterpret_cast<const float4*>(hrow + 32 * j);
+#pragma unroll
+    for (int q4 = 0; q4 < 8; ++q4) {
+      const float4 f4 = src[q4];
+      v[4 * q4 + 0] = f4.x; v[4 * q4 + 1] = f4.y; v[4 * q4 + 2] = f4.z; v[4 * q4 + 3] = f4.w;
+    }
+  };
+  auto convert = [&](int j, const float (&v)[32], float up) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int wi = 0; wi < 4; ++wi) {
+      _Float16 hb[8];
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        hb[n] = (_Float16)(v[8 * wi + n] * up);
+        sum += (float)hb[n];
+      }
+      uint4 pk;
+      uint32_t* pw = reinterpret_cast<uint32_t*>(&pk);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        pw[kk] = (uint32_t)__builtin_bit_cast(uint16_t, hb[pair_lo(kk)]) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, hb[pair_hi(kk)]) << 16);
+      hvs[((size_t)ls * 4 + wi) * KU + j] = pk;
+    }
+    hss[(size_t)ls * KU + j] = sum;
+  };
+  float mx = 0.0f;
+  int ex;
+  if (KU <= 64) {  // one position per lane: a single pass over registers
+    float v[32];
+    const bool on = lane < KU;
+    load32(on ? lane : 0, v);
+#pragma unroll
+    for (int n = 0; n < 32; ++n) mx = fmaxf(mx, on ? fabsf(v[n]) : 0.0f);
+    mx = wave_max(mx);
+    ex = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) : 0;
+    if (on) convert(lane, v, __builtin_ldexpf(1.0f, 14 - ex));
+  } else {  // several positions per lane: the maximum first, then a second read
+    for (int j = lane; j < KU; j += 64) {
+      float v[32];
+      load32(j, v);
+#pragma unroll
+      for (int n = 0; n < 32; ++n) mx = fmaxf(mx, fabsf(v[n]));
+    }
+    mx = wave_max(mx);
+    ex = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) : 0;
+    const float up = __builtin_ldexpf(1.0f, 14 - ex);
+    for (int j = lane; j < KU; j += 64) {
+      float v[32];
+      load32(j, v);
+      convert(j, v, up);
+    }
+  }
+  if (lane == 0) {
+    stw[ls] = a.slot_w[slot] * __builtin_ldexpf(1.0f, ex - 14);
+    sdst[ls] = a.slot_dst[slot];
+  }
+}
+
+// One step: RS rows of this lane group against NT converted hidden vectors;
+// each token's RS row totals, times its router weight (and 2^-k), go to its
+// ys row in one store (every lane stores its residue's row; token slots past
+// the expert's count write to the sink).
 template <int LPR, int PPL, int RS, int NT, bool FULL, bool QS>
 __device__ __forceinline__ void dn_step(const UnionArgs& a, const DnFrag<PPL, RS>& f, const uint32_t (&hv)[NT][PPL][16],
                                        const float (&hs)[NT][PPL], const float (&tw)[NT], float* const (&dst)[NT],
@@ -476,11 +594,13 @@ __device__ __forceinline__ void dn_step(const UnionArgs& a, const DnFrag<PPL, RS
       touch(f.w[r][p]);
       if (!QS || (r & 1) == 0) touch(f.sb[r][p]);
     }
+  float acc[NT][RS];
+#pragma unroll
+  for (int c = 0; c < NT; ++c)
+#pragma unroll
+    for (int r = 0; r < RS; ++r) acc[c][r] = 0.0f;
 #pragma unroll
   for (int r = 0; r < RS; ++r) {
-    float acc[NT];
-#pragma unroll
-    for (int c = 0; c < NT; ++c) acc[c] = 0.0f;
 #pragma unroll
     for (int p = 0; p < PPL; ++p) {
       if (FULL || li + LPR * p < KU) {
@@ -494,90 +614,65 @@ __device__ __forceinline__ void dn_step(const UnionArgs& a, const DnFrag<PPL, RS
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
           const float d = dot32<true>(f.w[r][p], hv[c][p], kMagicBytesF16, 0.0f);
-          acc[c] += sc * d + bi * hs[c][p];
+          acc[c][r] += sc * d + bi * hs[c][p];
         }
       }
     }
-#pragma unroll
-    for (int c = 0; c < NT; ++c) dst[c][row0 + r] = tw[c] * group_sum<LPR>(acc[c]);
   }
+  const int rr = li & (RS - 1);
+#pragma unroll
+  for (int c = 0; c < NT; ++c) dst[c][row0 + rr] = tw[c] * reduce_rows<LPR, RS>(acc[c]);
 }
 
-// One (expert, token chunk) segment of a down wave: stage the chunk's hidden
-// vectors, then stream the wave's row steps gj, gj + wpe, ... (kk <= klast).
+// One (expert, token chunk) segment of a down wave: read the chunk's
+// converted hidden vectors from LDS, then stream the unit's row steps gj ..
+// gj + klast through a ring of three register fragments (two in flight).
 template <int LPR, int PPL, bool FULL, bool QS, int NT, int RS, int WSTEP>
-__device__ __forceinline__ void dn_segment(const UnionArgs& a, int e, size_t ebase, int slot0, int nt, int gj, int wpe,
-                                       int klast, int li, int g, int KU, int KG, int I, int H,
-                                       const unsigned char* lane_sbase, const DnOffsets<PPL, RS>& o,
-                                       uint32_t sel) {
-  (void)e;
-  const int t0 = 0;
+__device__ __forceinline__ void dn_segment(const UnionArgs& a, size_t ebase, int ls0, int nt, int gj, int klast,
+                                           int li, int g, int KU, int KG, int H, const unsigned char* lane_sbase,
+                                           const DnOffsets<PPL, RS>& o, uint32_t sel, const uint4* hvs,
+                                           const float* hss, const float* stw, const int* sdst) {
   // prefetches past the last step are zero-range no-ops
   auto load = [&](int kk, DnFrag<PPL, RS>& fr) {
     const bool valid = kk <= klast;
-    const size_t row0 = ebase + (size_t)(gj + min(kk, klast) * wpe) * WSTEP;
+    const size_t row0 = ebase + (size_t)(gj + min(kk, klast)) * WSTEP;
     dn_load<PPL, RS, FULL, QS>(a, row0, valid, row0, WSTEP, KU, KG, li, LPR, lane_sbase, o, fr);
   };
   DnFrag<PPL, RS> f0, f1, f2;
   load(0, f0);
   load(1, f1);
 
-  // hidden vectors of up to NT tokens, each scaled by a power of two so
-  // that its largest magnitude lies in [2^13, 2^14), rounded to fp16 pairs
-  // in code order; hs = sum of the fp16 values per 32-input position
   uint32_t hv[NT][PPL][16];
   float hs[NT][PPL], tw[NT];
   float* dst[NT];
 #pragma unroll
   for (int c = 0; c < NT; ++c) {
     const bool live = c < nt;
-    const int slot = slot0 + t0 + (live ? c : 0);
-    float v[PPL][32];
-    float mx = 0.0f;
+    const int ls = ls0 + (live ? c : 0);
 #pragma unroll
     for (int p = 0; p < PPL; ++p) {
       const int j = li + LPR * p;
       if (FULL || j < KU) {
-        const float4* src = reinterpret_cast<const float4*>(a.hbuf + (size_t)slot * I + 32 * j);
+        const uint4* hp = hvs + (size_t)ls * 4 * KU + j;
 #pragma unroll
-        for (int q4 = 0; q4 < 8; ++q4) {
-          const float4 f4 = src[q4];
-          v[p][4 * q4 + 0] = f4.x; v[p][4 * q4 + 1] = f4.y; v[p][4 * q4 + 2] = f4.z; v[p][4 * q4 + 3] = f4.w;
+        for (int wi = 0; wi < 4; ++wi) {
+          const uint4 h4 = hp[wi * KU];
+          hv[c][p][4 * wi + 0] = h4.x; hv[c][p][4 * wi + 1] = h4.y;
+          hv[c][p][4 * wi + 2] = h4.z; hv[c][p][4 * wi + 3] = h4.w;
         }
+        hs[c][p] = hss[(size_t)ls * KU + j];
       } else {
 #pragma unroll
-        for (int n = 0; n < 32; ++n) v[p][n] = 0.0f;
+        for (int n = 0; n < 16; ++n) hv[c][p][n] = 0u;
+        hs[c][p] = 0.0f;
       }
-#pragma unroll
-      for (int n = 0; n < 32; ++n) mx = fmaxf(mx, fabsf(v[p][n]));
     }
-    mx = wave_max(mx);
-    const int ex = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) : 0;
-    const float up = __builtin_ldexpf(1.0f, 14 - ex);
-    tw[c] = live ? a.slot_w[slot] * __builtin_ldexpf(1.0f, ex - 14) : 0.0f;
-    dst[c] = live ? a.ys + (size_t)a.slot_dst[slot] * H : a.ys_dummy;
-#pragma unroll
-    for (int p = 0; p < PPL; ++p) {
-      float sum = 0.0f;
-#pragma unroll
-      for (int wi = 0; wi < 4; ++wi) {
-        _Float16 hb[8];
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-          hb[n] = (_Float16)(v[p][8 * wi + n] * up);
-          sum += (float)hb[n];
-        }
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          hv[c][p][4 * wi + kk] = (uint32_t)__builtin_bit_cast(uint16_t, hb[pair_lo(kk)]) |
-                                  ((uint32_t)__builtin_bit_cast(uint16_t, hb[pair_hi(kk)]) << 16);
-      }
-      hs[c][p] = sum;
-    }
+    tw[c] = live ? stw[ls] : 0.0f;
+    dst[c] = live ? a.ys + (size_t)wave_uniform(sdst[ls]) * H : a.ys_dummy;
   }
 
   auto step = [&](int kk, const DnFrag<PPL, RS>& fr) {
-    dn_step<LPR, PPL, RS, NT, FULL, QS>(a, fr, hv, hs, tw, dst, (gj + kk * wpe) * WSTEP + g * RS, li, KU, sel);
+    dn_step<LPR, PPL, RS, NT, FULL, QS>(a, fr, hv, hs, tw, dst, (gj + kk) * WSTEP + g * RS, li, KU, sel);
   };
 #pragma unroll 1
   for (int kk = 0;; kk += 3) {
@@ -594,27 +689,81 @@ __device__ __forceinline__ void dn_segment(const UnionArgs& a, int e, size_t eba
 }
 
 // threads of a down block: one block per CU, as many waves as the registers
-// allow (the waves of a CU share one LDS work counter)
-constexpr int down_threads(int nt) { return nt == 1 ? 1024 : 768; }
+// allow (the waves of a CU share the converted hidden vectors and one LDS
+// work counter)
+constexpr int down_threads(int nt) { return nt == 1 ? 1024 : 512; }
 constexpr int kDownUnitSteps = 4;  // row steps per down work unit
 
+// Down projection and router weighting of every (distinct expert, token)
+// pair.  Work units: (distinct expert, kDownUnitSteps row steps), numbered
+// expert-major; block b takes a contiguous range of them, so it touches one
+// or two experts and converts only their tokens' hidden vectors (into LDS,
+// once).  Its waves take the units from an LDS counter (the first unit of
+// each wave fixed), so waves that get fewer issue slots do less of the
+// block's share.  A unit runs every token of its expert, NT at a time.
 template <int LPR, int PPL, bool FULL, bool QS, int NT>
 __global__ __launch_bounds__(down_threads(NT)) void k_down(UnionArgs a) {
   constexpr int G = 64 / LPR;
-  constexpr int RS = down_rows(G);       // a wave step covers G * RS rows
+  constexpr int RS = down_rows(G);  // a wave step covers G * RS rows
   constexpr int WSTEP = G * RS;
   constexpr int NW = down_threads(NT) / 64;
   static_assert(!QS || RS % 2 == 0, "quad-shared scales pair rows");
   extern __shared__ __align__(16) unsigned char smem[];
-  int4* utab = reinterpret_cast<int4*>(smem);
-  __shared__ int unit_q;  // next dynamically assigned unit of this block
-  const int H = a.H, I = a.I;
+  const int H = a.H, I = a.I, P = a.L * a.k;
   const int KU = I >> 5, KG = I >> 6;
+  const int SM = a.dn_slots;  // pair slots converted at a time
+  int4* utab = reinterpret_cast<int4*>(smem);
+  int* wpre = reinterpret_cast<int*>(smem + down_lds_base(P));     // [P + 1] work prefix per expert
+  uint4* hvs = reinterpret_cast<uint4*>(smem + down_lds_head(P));  // [SM][4][KU]
+  float* hss = reinterpret_cast<float*>(hvs + (size_t)SM * 4 * KU);  // [SM][KU]
+  float* stw = hss + (size_t)SM * KU;                                 // [SM]
+  int* sdst = reinterpret_cast<int*>(stw + SM);                       // [SM]
+  __shared__ int unit_q;  // next dynamically assigned unit (block-relative)
   const int tid = threadIdx.x;
-  const int u = (int)a.hdr[2];
-  for (int i = tid; i < u; i += blockDim.x) utab[i] = a.utab[i];
-  if (tid == 0) unit_q = NW;
+  const int umax = min(P, a.E);
+  const int u = min((int)a.hdr[2], umax);
+  const int spe = H / WSTEP;  // row steps per expert
+  const int nrb = (spe + kDownUnitSteps - 1) / kDownUnitSteps;  // units per expert
+  // Work of a unit: its token chunks (each streams the unit's rows once).
+  // wpre[i] = work of the units of experts before i (wave 0, straight from
+  // the table in memory); blocks take equal shares of the total, each share
+  // a contiguous range of units.
+  // (with at most NT tokens per token row set, every unit is one chunk and
+  // the shares are plain unit counts)
+  const bool uniform = a.L <= NT;
+  if (tid < 64 && !uniform) {
+    int carry = 0;
+    for (int base = 0; base < u; base += 64) {
+      const int i = base + tid;
+      const int w = i < u ? nrb * ((__popc((uint32_t)a.utab[i].y) + NT - 1) / NT) : 0;
+      const int incl = wave_incl_scan(w);
+      if (i < u) wpre[i] = carry + incl - w;
+      carry += __shfl(incl, 63, 64);
+    }
+    if (tid == 0) wpre[u] = carry;
+  }
+  for (int i = tid; i < umax; i += blockDim.x) utab[i] = a.utab[i];
   __syncthreads();
+  const int wtot = uniform ? u * nrb : wpre[u];
+  const int nblk = gridDim.x, b = blockIdx.x;
+  // first unit whose work starts at or after offset x
+  auto unit_at = [&](long long x) {
+    if (x >= wtot) return u * nrb;
+    if (uniform) return (int)x;
+    int lo = 0, hi = u - 1;  // last expert i with wpre[i] <= x
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (wpre[mid] <= x) lo = mid; else hi = mid - 1;
+    }
+    const int nch = (wpre[lo + 1] - wpre[lo]) / nrb;
+    return lo * nrb + (int)((x - wpre[lo] + nch - 1) / nch);
+  };
+  const int ub = unit_at((long long)wtot * b / nblk);
+  const int nub = unit_at((long long)wtot * (b + 1) / nblk) - ub;  // units of this block
+  if (nub <= 0) return;  // uniform over the block
+  const int s_lo = utab[ub / nrb].z;
+  const int4 ehi = utab[(ub + nub - 1) / nrb];
+  const int s_hi = ehi.z + __popc((uint32_t)ehi.y);  // pair slots of the block's experts
 
   const int lane = tid & 63;
   const int wave = wave_uniform(tid >> 6);
@@ -634,41 +783,40 @@ __global__ __launch_bounds__(down_threads(NT)) void k_down(UnionArgs a) {
       const int grp = QS ? 2 * (li >> 2) + (LPR / 2) * p : (j >> 1);
       o.s[r][p] = (uint32_t)(((g * RS + srow) * KG + grp) * 2);
     }
-
-  // Work units: (distinct expert, kDownUnitSteps row steps), expert-major.
-  // Block b owns units b, b + nblk, ... (adjacent blocks, adjacent rows of
-  // the same expert); its waves take them from an LDS counter (first unit of
-  // each wave fixed), so waves that get fewer issue slots do less of the
-  // block's share.  A unit runs every token of its expert, NT at a time,
-  // each chunk staging those tokens' hidden vectors once.
-  const int spe = H / WSTEP;                                 // row steps per expert
-  const int nrb = (spe + kDownUnitSteps - 1) / kDownUnitSteps;
-  const int nunits = u * nrb;
-  const int nblk = gridDim.x, b = blockIdx.x;
-  const int nub = nunits > b ? (nunits - 1 - b) / nblk + 1 : 0;
   auto grab = [&]() {
     int v = 0;
     if (lane == 0) v = atomicAdd(&unit_q, 1);
     return __builtin_amdgcn_readfirstlane(v);
   };
-  for (int j = wave; j < nub; j = grab()) {
-    const int un = b + j * nblk;
-    const int i = un / nrb, rb = un - i * nrb;
-    const int4 ent = utab[i];
-    const int e = wave_uniform(ent.x), slot0 = wave_uniform(ent.z);
-    const int ntok = __popc((uint32_t)wave_uniform(ent.y));
-    const size_t ebase = (size_t)e * H;
-    const int gj = rb * kDownUnitSteps;
-    const int klast = min(kDownUnitSteps, spe - gj) - 1;
-    for (int t0 = 0; t0 < ntok; t0 += NT) {
-      const int nt = min(NT, ntok - t0);
-      if (NT > 1 && nt == 1)
-        dn_segment<LPR, PPL, FULL, QS, 1, RS, WSTEP>(a, e, ebase, slot0 + t0, 1, gj, 1, klast, li, g, KU, KG, I, H,
-                                                     lane_sbase, o, sel);
-      else
-        dn_segment<LPR, PPL, FULL, QS, NT, RS, WSTEP>(a, e, ebase, slot0 + t0, nt, gj, 1, klast, li, g, KU, KG, I,
-                                                      H, lane_sbase, o, sel);
+
+
+  // Usually one pass; more when the block's experts have more pair slots
+  // than the LDS holds (each pass runs the block's units for its slots).
+  for (int c0 = s_lo; c0 < s_hi; c0 += SM) {
+    const int c1 = min(s_hi, c0 + SM);
+    if (tid == 0) unit_q = NW;
+    for (int sl = c0 + wave; sl < c1; sl += NW) down_stage_slot(a, sl - c0, sl, KU, hvs, hss, stw, sdst);
+    __syncthreads();
+    for (int j = wave; j < nub; j = grab()) {
+      const int un = ub + j;
+      const int i = un / nrb, rb = un - i * nrb;
+      const int4 ent = utab[i];
+      const int e = wave_uniform(ent.x), off = wave_uniform(ent.z);
+      const int t_lo = max(off, c0), t_hi = min(off + __popc((uint32_t)wave_uniform(ent.y)), c1);
+      const size_t ebase = (size_t)e * H;
+      const int gj = rb * kDownUnitSteps;
+      const int klast = min(kDownUnitSteps, spe - gj) - 1;
+      for (int t0 = t_lo; t0 < t_hi; t0 += NT) {
+        const int nt = min(NT, t_hi - t0);
+        if (NT > 1 && nt == 1)
+          dn_segment<LPR, PPL, FULL, QS, 1, RS, WSTEP>(a, ebase, t0 - c0, 1, gj, klast, li, g, KU, KG, H, lane_sbase,
+                                                       o, sel, hvs, hss, stw, sdst);
+        else
+          dn_segment<LPR, PPL, FULL, QS, NT, RS, WSTEP>(a, ebase, t0 - c0, nt, gj, klast, li, g, KU, KG, H,
+                                                        lane_sbase, o, sel, hvs, hss, stw, sdst);
+      }
     }
+    __syncthreads();  // the converted slots and the counter are reused
   }
 }
 
