@@ -118,6 +118,46 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 // Maximum over the 64 lanes of a wave; every lane receives it.
+// Totals of RS rows whose partial sums are spread over the LPR lanes of each
+// lane group (v[r]: this lane's part of row r).  Reduce-scatter over the
+// quad (each exchange halves the values a lane carries), then an all-reduce
+// over the lanes that carry the same row.  Lane li of a group returns the
+// total of row li % RS; every lane with that residue holds the same value.
+template <int LPR, int RS>
+__device__ __forceinline__ float reduce_rows(const float (&v)[RS]) {
+  static_assert(RS == 2 || RS == 4, "rows per group");
+  static_assert(LPR >= RS && LPR <= 64, "lanes per group");
+  const int lane = threadIdx.x & 63;
+  const bool b0 = lane & 1, b1 = lane & 2;
+  float k;
+  if constexpr (RS == 4) {
+    float k0 = b0 ? v[1] : v[0];
+    float k1 = b0 ? v[3] : v[2];
+    k0 += dpp_f32<0xB1>(b0 ? v[0] : v[1]);  // quad_perm(1,0,3,2): lane ^ 1
+    k1 += dpp_f32<0xB1>(b0 ? v[2] : v[3]);
+    k = b1 ? k1 : k0;
+    k += dpp_f32<0x4E>(b1 ? k0 : k1);      // quad_perm(2,3,0,1): lane ^ 2
+  } else {
+    k = b0 ? v[1] : v[0];
+    k += dpp_f32<0xB1>(b0 ? v[0] : v[1]);
+    if constexpr (LPR >= 4) k += dpp_f32<0x4E>(k);
+  }
+  if constexpr (LPR == 8) k += __shfl_xor(k, 4, 64);
+  if constexpr (LPR >= 16) {
+    k += dpp_f32<0x124>(k);  // row_ror:4 (the 4 quads of a 16-lane row)
+    k += dpp_f32<0x128>(k);  // row_ror:8
+  }
+  if constexpr (LPR >= 32) {
+    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(k), __float_as_uint(k), false, false);
+    k = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // rows 0 + 1, rows 2 + 3
+  }
+  if constexpr (LPR == 64) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(k), __float_as_uint(k), false, false);
+    k = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // lanes 0-31 + lanes 32-63
+  }
+  return k;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_f32<0xB1>(v));
   v = fmaxf(v, dpp_f32<0x4E>(v));

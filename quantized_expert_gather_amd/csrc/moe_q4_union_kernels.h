@@ -217,10 +217,8 @@ __device__ __forceinline__ void gu_compute(const UnionArgs& a, const GuFrag<PPL,
         sbv[p][r][1] = f.sb[p][r][1];
       }
     }
-  uint32_t m = mask;
-  for (int c = 0; m; ++c) {
-    const int t = __builtin_ctz(m);
-    m &= m - 1u;
+  // h of token t for this lane group's RG rows
+  auto token_h = [&](int t, float (&h)[RG]) {
     float acc[RG][2];
 #pragma unroll
     for (int r = 0; r < RG; ++r) acc[r][0] = acc[r][1] = 0.0f;
@@ -246,11 +244,44 @@ __device__ __forceinline__ void gu_compute(const UnionArgs& a, const GuFrag<PPL,
     }
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
-      const float gt = group_sum<LPR>(acc[r][0]);
-      const float up = group_sum<LPR>(acc[r][1]);
-      // every lane of the group holds the same value: all store it
-      a.hbuf[(size_t)(slot0 + c) * a.I + row + r] = gt / (1.0f + expf(-gt)) * up;
+      // gate total in even lanes, up total in odd lanes, then swapped in
+      const float k = reduce_rows<LPR, 2>(acc[r]);
+      const float o = dpp_f32<0xB1>(k);
+      const float gt = (li & 1) ? o : k, up = (li & 1) ? k : o;
+      h[r] = gt / (1.0f + expf(-gt)) * up;
     }
+  };
+  const int ntok = __popc(mask);
+  if (ntok <= LPR) {
+    // one store per row for all the unit's tokens: lane li stores token
+    // min(li, ntok - 1), so the count of stores does not depend on the
+    // tokens (the waits on the weight loads in flight stay static)
+    const int qsel = min(li, ntok - 1);
+    float hsel[RG];
+#pragma unroll
+    for (int r = 0; r < RG; ++r) hsel[r] = 0.0f;
+    uint32_t m = mask;
+    for (int c = 0; m; ++c) {
+      const int t = __builtin_ctz(m);
+      m &= m - 1u;
+      float h[RG];
+      token_h(t, h);
+#pragma unroll
+      for (int r = 0; r < RG; ++r) hsel[r] = qsel == c ? h[r] : hsel[r];
+    }
+#pragma unroll
+    for (int r = 0; r < RG; ++r) a.hbuf[(size_t)(slot0 + qsel) * a.I + row + r] = hsel[r];
+  } else {  // more tokens than lanes in a group: one store per token and row
+    uint32_t m = mask;
+    for (int c = 0; m; ++c) {
+      const int t = __builtin_ctz(m);
+      m &= m - 1u;
+      float h[RG];
+      token_h(t, h);
+#pragma unroll
+      for (int r = 0; r < RG; ++r) a.hbuf[(size_t)(slot0 + c) * a.I + row + r] = h[r];
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the loads in flight restart from a known count
   }
 }
 
@@ -458,46 +489,6 @@ __device__ __forceinline__ void dn_load(const UnionArgs& a, size_t row0, bool va
           f.sb[r][p] = bld2(sd, o.s[r][p]) | (bld2(bd, o.s[r][p]) << 16);
         }
       }
-}
-
-// Totals of RS rows whose partial sums are spread over the LPR lanes of each
-// lane group (v[r]: this lane's part of row r).  Reduce-scatter over the
-// quad (each exchange halves the values a lane carries), then an all-reduce
-// over the lanes that carry the same row.  Lane li of a group returns the
-// total of row li % RS; every lane with that residue holds the same value.
-template <int LPR, int RS>
-__device__ __forceinline__ float reduce_rows(const float (&v)[RS]) {
-  static_assert(RS == 2 || RS == 4, "rows per group");
-  static_assert(LPR >= RS && LPR <= 64, "lanes per group");
-  const int lane = threadIdx.x & 63;
-  const bool b0 = lane & 1, b1 = lane & 2;
-  float k;
-  if constexpr (RS == 4) {
-    float k0 = b0 ? v[1] : v[0];
-    float k1 = b0 ? v[3] : v[2];
-    k0 += dpp_f32<0xB1>(b0 ? v[0] : v[1]);  // quad_perm(1,0,3,2): lane ^ 1
-    k1 += dpp_f32<0xB1>(b0 ? v[2] : v[3]);
-    k = b1 ? k1 : k0;
-    k += dpp_f32<0x4E>(b1 ? k0 : k1);      // quad_perm(2,3,0,1): lane ^ 2
-  } else {
-    k = b0 ? v[1] : v[0];
-    k += dpp_f32<0xB1>(b0 ? v[0] : v[1]);
-    if constexpr (LPR >= 4) k += dpp_f32<0x4E>(k);
-  }
-  if constexpr (LPR == 8) k += __shfl_xor(k, 4, 64);
-  if constexpr (LPR >= 16) {
-    k += dpp_f32<0x124>(k);  // row_ror:4 (the 4 quads of a 16-lane row)
-    k += dpp_f32<0x128>(k);  // row_ror:8
-  }
-  if constexpr (LPR >= 32) {
-    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(k), __float_as_uint(k), false, false);
-    k = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // rows 0 + 1, rows 2 + 3
-  }
-  if constexpr (LPR == 64) {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(k), __float_as_uint(k), false, false);
-    k = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // lanes 0-31 + lanes 32-63
-  }
-  return k;
 }
 
 // LDS of a down block: the union table, the work prefix per expert, then
