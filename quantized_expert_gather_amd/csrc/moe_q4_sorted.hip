@@ -569,9 +569,11 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
   const int col = wave_on ? col0 + lc : 0;
 
   constexpr int kRows = MT * kRowTile;
-  unsigned char* abuf = smem;                                          // [kRows][kV2Row]
-  float* sbuf = reinterpret_cast<float*>(smem + kRows * kV2Row);      // [4][kRows]
-  int32_t* tok = reinterpret_cast<int32_t*>(sbuf + 4 * kRows);        // [kRows]
+  // two staging buffers: iteration it reads buffer it & 1 while the rows of
+  // it + 1 are written to the other, so one barrier per iteration suffices
+  unsigned char* abuf0 = smem;                                              // [2][kRows][kV2Row]
+  float* sbuf0 = reinterpret_cast<float*>(smem + 2 * kRows * kV2Row);      // [2][4][kRows]
+  int32_t* tok = reinterpret_cast<int32_t*>(sbuf0 + 8 * kRows);            // [kRows]
   for (int r = tid; r < kRows; r += kV2Threads) tok[r] = a.perm[r0 + min(r, nrows - 1)] / a.k;
   __syncthreads();
 
@@ -587,13 +589,14 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
     const int si = min(tid, 4 * kRows - 1), q = si / kRows, r = si % kRows;
     sst = a.asum[(size_t)tok[r] * G + 4 * it + q];
   };
-  auto stage_store = [&]() {
+  auto stage_store = [&](int buf) {
+    unsigned char* abuf = abuf0 + (size_t)buf * kRows * kV2Row;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int idx = tid + kV2Threads * j, r = idx >> 5, w = idx & 31;
       *reinterpret_cast<uint4*>(abuf + (size_t)r * kV2Row + 16 * w) = pair_activations(st[j]);
     }
-    if (tid < 4 * kRows) sbuf[tid] = sst;  // [q][r] with q = tid / kRows
+    if (tid < 4 * kRows) sbuf0[buf * 4 * kRows + tid] = sst;  // [q][r] with q = tid / kRows
   };
 
   const uint32_t* W = mat ? a.wu : a.wg;
@@ -609,9 +612,10 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
     for (int i = 0; i < 16; ++i) acc[m][i] = 0.0f;
 
   Codes4 cur = load_codes4(W, rowc, 0, hh);
+  Codes4 nx = load_codes4(W, rowc, 4 * min(1, nit - 1), hh);  // codes stay two iterations ahead
   Chunk16 ch = load_chunk16(S, B, rows);
   stage_load(0);
-  stage_store();
+  stage_store(0);
   __syncthreads();
 
   for (int c = 0; c < nch; ++c) {
@@ -619,8 +623,10 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int it = 4 * c + ii;
+      const unsigned char* abuf = abuf0 + (size_t)(ii & 1) * kRows * kV2Row;  // nit is a multiple of 4
+      const float* sbuf = sbuf0 + (ii & 1) * 4 * kRows;
       stage_load(min(it + 1, nit - 1));
-      const Codes4 nx = load_codes4(W, rowc, 4 * min(it + 1, nit - 1), hh);
+      const Codes4 nn = load_codes4(W, rowc, 4 * min(it + 2, nit - 1), hh);
       if (ii == 0) chn = load_chunk16(S, B, rows + 16 * min(c + 1, nch - 1));
       if (wave_on) {
 #pragma unroll
@@ -651,10 +657,10 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
           }
         }
       }
-      __syncthreads();
-      stage_store();
+      stage_store((ii + 1) & 1);
       __syncthreads();
       cur = nx;
+      nx = nn;
     }
     ch = chn;
   }
@@ -695,6 +701,9 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
   }
 }
 
+// staging buffers of the down streaming kernel: two while they fit the LDS
+constexpr int down2_buffers(int mt) { return (size_t)2 * 2 * mt * kRowTile * kV2Row + 8 * mt * kRowTile * 4 <= 160 * 1024 ? 2 : 1; }
+
 template <int MT>
 __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -713,8 +722,11 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
   const int col = wave_on ? col0 + lc : 0;
 
   constexpr int kRows = MT * kRowTile;
-  unsigned char* abuf = smem;                                                // [2 planes][kRows][kV2Row]
-  float* sbuf = reinterpret_cast<float*>(smem + 2 * kRows * kV2Row);        // [4][kRows]
+  // two staging buffers when they fit the LDS (one barrier per iteration),
+  // else one (a second barrier before the rows of the next iteration land)
+  constexpr int NB = down2_buffers(MT);
+  unsigned char* abuf0 = smem;                                                     // [NB][2 planes][kRows][kV2Row]
+  float* sbuf0 = reinterpret_cast<float*>(smem + (size_t)NB * 2 * kRows * kV2Row);  // [NB][4][kRows]
 
   constexpr int kPer = kRows * 32 / kV2Threads;  // 16-byte pieces per thread, iteration and plane
   u32x4_t sth[kPer], stl[kPer];
@@ -731,14 +743,15 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
     const float* hs = a.hsum2 + (size_t)(r0 + r) * (I / 32) + 2 * (4 * it + q);
     sst = hs[0] + hs[1];
   };
-  auto stage_store = [&]() {
+  auto stage_store = [&](int buf) {
+    unsigned char* abuf = abuf0 + (size_t)buf * 2 * kRows * kV2Row;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int idx = tid + kV2Threads * j, r = idx >> 5, w = idx & 31;
       *reinterpret_cast<u32x4_t*>(abuf + (size_t)r * kV2Row + 16 * w) = sth[j];
       *reinterpret_cast<u32x4_t*>(abuf + (size_t)(kRows + r) * kV2Row + 16 * w) = stl[j];
     }
-    if (tid < 4 * kRows) sbuf[tid] = sst;
+    if (tid < 4 * kRows) sbuf0[buf * 4 * kRows + tid] = sst;
   };
 
   const size_t rowc = ((size_t)e * H + col) * (size_t)(I / 8);
@@ -751,9 +764,10 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
     for (int i = 0; i < 16; ++i) acc[m][i] = 0.0f;
 
   Codes4 cur = load_codes4(a.wd, rowc, 0, hh);
+  Codes4 nx = load_codes4(a.wd, rowc, 4 * min(1, nit - 1), hh);  // codes stay two iterations ahead
   Chunk16 ch = load_chunk16(a.sd, a.bd, rows);
   stage_load(0);
-  stage_store();
+  stage_store(0);
   __syncthreads();
 
   for (int c = 0; c < nch; ++c) {
@@ -761,8 +775,11 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int it = 4 * c + ii;
+      const int cbuf = NB == 2 ? (ii & 1) : 0;  // nit is a multiple of 4
+      const unsigned char* abuf = abuf0 + (size_t)cbuf * 2 * kRows * kV2Row;
+      const float* sbuf = sbuf0 + cbuf * 4 * kRows;
       stage_load(min(it + 1, nit - 1));
-      const Codes4 nx = load_codes4(a.wd, rowc, 4 * min(it + 1, nit - 1), hh);
+      const Codes4 nn = load_codes4(a.wd, rowc, 4 * min(it + 2, nit - 1), hh);
       if (ii == 0) chn = load_chunk16(a.sd, a.bd, rows + 16 * min(c + 1, nch - 1));
       if (wave_on) {
 #pragma unroll
@@ -797,10 +814,11 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
           }
         }
       }
-      __syncthreads();
-      stage_store();
+      if (NB == 1) __syncthreads();
+      stage_store(NB == 2 ? ((ii + 1) & 1) : 0);
       __syncthreads();
       cur = nx;
+      nx = nn;
     }
     ch = chn;
   }
@@ -906,8 +924,11 @@ int sort_launch(const SortedArgs& a, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? MOE_Q4_OK : MOE_Q4_ERR_LAUNCH;
 }
 
-size_t gateup2_lds(int mt) { return (size_t)mt * kRowTile * kV2Row + 5 * mt * kRowTile * 4; }
-size_t down2_lds(int mt) { return (size_t)2 * mt * kRowTile * kV2Row + 4 * mt * kRowTile * 4; }
+size_t gateup2_lds(int mt) { return (size_t)2 * mt * kRowTile * kV2Row + 9 * mt * kRowTile * 4; }
+size_t down2_lds(int mt) {
+  const int nb = down2_buffers(mt);
+  return (size_t)nb * 2 * mt * kRowTile * kV2Row + (size_t)nb * 4 * mt * kRowTile * 4;
+}
 
 template <int MT>
 int gemm_launch(const SortedArgs& a, bool down, hipStream_t stream) {
