@@ -174,8 +174,9 @@ def main():
     ap.add_argument("--layers", type=int, default=75)
     ap.add_argument("--Ls", default="1,2,3,4,8",
                     help="window sizes timed; value aggregates those of the metric (1, 2, 4, 8)")
-    ap.add_argument("--sorted-Ts", default="512,2048",
-                    help="token counts of the prefill (sorted-path) measurement; empty to skip")
+    ap.add_argument("--sorted-Ts", default="512,2048,16384",
+                    help="token counts of the prefill (sorted-path) measurement (512 and 2048 are the "
+                         "prefill configuration; 16384 is the long-prefill regime); empty to skip")
     ap.add_argument("--sorted-layers", type=int, default=4, help="distinct layers per prefill chain")
     ap.add_argument("--pair-layers", type=int, default=20,
                     help="layers of each chain timed again as a per-pair baseline (one call per token, so "

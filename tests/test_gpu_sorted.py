@@ -201,7 +201,7 @@ def test_sorted_invalid_ids_dropped_and_reported():
 # prefill workload at full size: sampled tokens against the oracle
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("T", [512, 2048])
+@pytest.mark.parametrize("T", [512, 2048, 16384])
 def test_sorted_prefill_full_size_sampled(T):
     w = synth.WORKLOADS["prefill"]
     dev = torch.device("cuda")
@@ -221,3 +221,43 @@ def test_sorted_prefill_full_size_sampled(T):
     assert err.max() <= ARITH
     status, path = _q().moe_q4_read_device_status(ws)
     assert status == 0 and path == _q().MOE_Q4_PATH_SORTED
+
+
+# ---------------------------------------------------------------------------
+# long-prefill robustness: one expert with more than 32K rows, ragged widths
+# ---------------------------------------------------------------------------
+
+def _sampled_check(x, ids, tw, bank, sample, label):
+    say(label, "T=%d k=%d E=%d H=%d I=%d" % (ids.shape[0], ids.shape[1], bank.E, x.shape[1], bank.wg.shape[1]))
+    out, ws = run_layer(x, ids, tw, bank)
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    used = np.unique(ids[sample])
+    sub = bank.select(used).to("cpu")
+    ref = oracle.forward_pairs(x[sample].cpu(), np.searchsorted(used, ids[sample]).astype(np.int32),
+                               tw[sample], sub)
+    err = rel_err_rows(got[sample], ref)
+    print(f"  sampled rows {sample}: max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= ARITH
+    status, path = _q().moe_q4_read_device_status(ws)
+    assert status == 0 and path == _q().MOE_Q4_PATH_SORTED
+
+
+def test_sorted_one_expert_over_32k_rows():
+    # 5000 tokens, every slot routed to expert 5 (duplicates within a token
+    # are separate pairs on this path): 40,000 rows of one expert
+    T, k, E, H, I = 5000, 8, 8, 1024, 1024
+    x, _, tw, bank = synth.random_problem(T, k, E, H, I, seed=31)
+    ids = np.full((T, k), 5, np.int32)
+    rng = np.random.default_rng(31)
+    sample = sorted({0, T - 1, *rng.choice(T, size=6, replace=False).tolist()})
+    _sampled_check(x, ids, tw, bank, sample, "one expert, 40000 rows")
+
+
+def test_sorted_long_prefill_ragged_widths():
+    # H and I not multiples of the streaming kernels' 1024: the general kernels at T = 4096
+    T, k, E, H, I = 4096, 4, 16, 1088, 576
+    x, ids, tw, bank = synth.random_problem(T, k, E, H, I, seed=37)
+    rng = np.random.default_rng(37)
+    sample = sorted({0, T - 1, *rng.choice(T, size=6, replace=False).tolist()})
+    _sampled_check(x, ids, tw, bank, sample, "ragged widths")
