@@ -7,6 +7,9 @@ with it.
 * :func:`forward_pairs`, :func:`forward_union`, :func:`output_element`,
   :func:`dequant` wrap the plain C implementation in ``moe_oracle.c`` (IEEE
   double, each (token, expert) pair evaluated on its own).
+* :func:`forward_pairs_mx`, :func:`forward_union_mx`, :func:`output_element_mx`,
+  :func:`dequant_mx`: the same over mxfp4 gs32 banks (FP4 E2M1 elements, one
+  E8M0 power-of-two scale byte per 32 inputs).
 * :func:`route_union` and :func:`sorted_pairs` are plain Python: the
   bit-exact union outputs and the expert-sorted pair order with its
   expert-aligned tile list.
@@ -63,6 +66,14 @@ def _load():
     lib.oracle_output_element.restype = ctypes.c_double
     lib.oracle_dequant.argtypes = [P, P, P, Lg, Lg, P]
     lib.oracle_dequant.restype = ctypes.c_int
+    lib.oracle_forward_pairs_mx.argtypes = [P, P, P, Lg, Lg, Lg, Lg, Lg] + [P] * 6 + [P, P, P]
+    lib.oracle_forward_pairs_mx.restype = ctypes.c_int
+    lib.oracle_forward_union_mx.argtypes = [P, P, P, Lg, Lg, Lg, Lg, Lg] + [P] * 6 + [P]
+    lib.oracle_forward_union_mx.restype = ctypes.c_int
+    lib.oracle_output_element_mx.argtypes = [P, P, P, Lg, Lg, Lg, Lg, Lg] + [P] * 6 + [Lg, Lg]
+    lib.oracle_output_element_mx.restype = ctypes.c_double
+    lib.oracle_dequant_mx.argtypes = [P, P, Lg, Lg, P]
+    lib.oracle_dequant_mx.restype = ctypes.c_int
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
@@ -214,6 +225,95 @@ def output_element(x, ids, tw, bank, t: int, m: int) -> float:
                                       *[_ptr(a) for a in ba], int(t), int(m))
     if np.isnan(v):
         raise OracleError("oracle_output_element: invalid arguments")
+    return float(v)
+
+
+# --------------------------------------------------------------------------
+# mxfp4 gs32 banks (FP4 E2M1 elements, one E8M0 scale byte per 32 inputs)
+# --------------------------------------------------------------------------
+
+def _u8(a) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            assert a.dtype == torch.uint8
+            return np.ascontiguousarray(a.detach().cpu().contiguous().numpy())
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.asarray(a)
+    assert a.dtype == np.uint8
+    return np.ascontiguousarray(a)
+
+
+def _bank_arrays_mx(bank) -> List[np.ndarray]:
+    """(wg, eg, wu, eu, wd, ed): packed uint32 codes and uint8 scale bytes."""
+    ts = bank.tensors() if hasattr(bank, "tensors") else bank
+    return [_u32(t) if i % 2 == 0 else _u8(t) for i, t in enumerate(ts)]
+
+
+def dequant_mx(W, S) -> np.ndarray:
+    """Dense double copy of mxfp4 rows: W [..., N, K/8], S [..., N, K/32] -> [..., N, K]."""
+    w = _u32(W)
+    s = _u8(S)
+    *lead, n, k8 = w.shape
+    K = k8 * 8
+    rows = int(np.prod(lead, dtype=np.int64)) * n if lead else n
+    out = np.empty((rows, K), np.float64)
+    st = _load().oracle_dequant_mx(_ptr(w), _ptr(s), rows, K, _ptr(out))
+    if st:
+        raise OracleError(f"oracle_dequant_mx status {st}")
+    return out.reshape(*lead, n, K)
+
+
+def forward_pairs_mx(x, ids, tw, bank, want_hidden: bool = False) -> np.ndarray:
+    """Per-pair SwitchGLU + combine over an mxfp4 bank; out [L, H] float64."""
+    xa = _u16(x)
+    ia = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+    wa = np.ascontiguousarray(np.asarray(tw, dtype=np.float32))
+    ba = _bank_arrays_mx(bank)
+    L, k = ia.shape
+    E, I, h8 = ba[0].shape
+    H = h8 * 8
+    out = np.empty((L, H), np.float64)
+    hb = np.empty((L * k, I), np.float64) if want_hidden else None
+    st = _load().oracle_forward_pairs_mx(_ptr(xa), _ptr(ia), _ptr(wa), L, k, E, H, I,
+                                         *[_ptr(a) for a in ba], _ptr(out),
+                                         _ptr(hb) if hb is not None else None, None)
+    if st:
+        raise OracleError(f"oracle_forward_pairs_mx status {st}")
+    return (out, hb) if want_hidden else out
+
+
+def forward_union_mx(x, ids, tw, bank) -> np.ndarray:
+    """Union evaluation over an mxfp4 bank; must agree with :func:`forward_pairs_mx`."""
+    xa = _u16(x)
+    ia = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+    wa = np.ascontiguousarray(np.asarray(tw, dtype=np.float32))
+    ba = _bank_arrays_mx(bank)
+    L, k = ia.shape
+    E, I, h8 = ba[0].shape
+    H = h8 * 8
+    out = np.empty((L, H), np.float64)
+    st = _load().oracle_forward_union_mx(_ptr(xa), _ptr(ia), _ptr(wa), L, k, E, H, I,
+                                         *[_ptr(a) for a in ba], _ptr(out))
+    if st:
+        raise OracleError(f"oracle_forward_union_mx status {st}")
+    return out
+
+
+def output_element_mx(x, ids, tw, bank, t: int, m: int) -> float:
+    """out[t, m] alone over an mxfp4 bank."""
+    xa = _u16(x)
+    ia = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+    wa = np.ascontiguousarray(np.asarray(tw, dtype=np.float32))
+    ba = _bank_arrays_mx(bank)
+    L, k = ia.shape
+    E, I, h8 = ba[0].shape
+    H = h8 * 8
+    v = _load().oracle_output_element_mx(_ptr(xa), _ptr(ia), _ptr(wa), L, k, E, H, I,
+                                         *[_ptr(a) for a in ba], int(t), int(m))
+    if np.isnan(v):
+        raise OracleError("oracle_output_element_mx: invalid arguments")
     return float(v)
 
 

@@ -18,6 +18,16 @@
  *    with group 64, affine, bits 4).
  *  - Storage reading (not fixed by the pages): element c of an output row is
  *    nibble c % 8 of word c / 8, lowest nibble first.
+ *  - mxfp4 gs32 banks (the format of the pages' GLM-5.2 banks, mlx discussion
+ *    "Small-L fused expert gather for fine-grained MoE decode", "The data";
+ *    about 20 MB per expert): each 4-bit element is an FP4 E2M1 number and
+ *    each 32 consecutive inputs share one 8-bit power-of-two scale.  The
+ *    pages do not spell out the bit layouts; these follow the OCP
+ *    Microscaling Formats (MX) specification v1.0: E2M1 = sign bit 3,
+ *    exponent bits 2..1 with bias 1, mantissa bit 0, exponent 0 encoding
+ *    0 and +-0.5 (no infinities or NaN); the E8M0 scale byte e stands for
+ *    2^(e - 127), and e = 255 for NaN.  Packing of the elements as for the
+ *    affine banks.
  *  - Router-weighted combine out[t] = sum_j w[t, j] * y[t, j] (the pages'
  *    SwitchGLU returns per-pair outputs; the weighted sum is the plain MoE
  *    combine this layer adds, applied after the down projection).
@@ -63,6 +73,20 @@ static double weight_at(const uint32_t *W, const uint16_t *S, const uint16_t *B,
     return bf16_to_double(S[g]) * (double)code_at(W + row * (K / 8), c) + bf16_to_double(B[g]);
 }
 
+/* Value of a 4-bit FP4 E2M1 code (OCP MX v1.0 element encoding). */
+static double e2m1_value(unsigned code) {
+    unsigned sign = (code >> 3) & 1u, expo = (code >> 1) & 3u, mant = code & 1u;
+    double mag = expo == 0 ? 0.5 * (double)mant : ldexp(1.0 + 0.5 * (double)mant, (int)expo - 1);
+    return sign ? -mag : mag;
+}
+
+/* mxfp4 weight at (row, c): E2M1 element times the block's 2^(e - 127). */
+static double weight_at_mx(const uint32_t *W, const uint8_t *S, long row, long K, long c) {
+    unsigned e = S[row * (K / 32) + c / 32];
+    if (e == 255u) return NAN;
+    return ldexp(e2m1_value(code_at(W + row * (K / 8), c)), (int)e - 127);
+}
+
 static double silu(double v) { return v / (1.0 + exp(-v)); }
 
 int oracle_threads(void) {
@@ -93,7 +117,22 @@ typedef struct {
     const uint32_t *wg; const uint16_t *sg; const uint16_t *bg;
     const uint32_t *wu; const uint16_t *su; const uint16_t *bu;
     const uint32_t *wd; const uint16_t *sd; const uint16_t *bd;
+    /* mxfp4 banks: the scale bytes of gate, up, down (then sg..bd are unused) */
+    const uint8_t *eg, *eu, *ed;
+    int mx;
 } bank_t;
+
+/* Weight of matrix mat (0 gate, 1 up, 2 down) at (row, c). */
+static double bank_weight(const bank_t *bk, int mat, long row, long K, long c) {
+    if (bk->mx) {
+        const uint32_t *W = mat == 0 ? bk->wg : mat == 1 ? bk->wu : bk->wd;
+        const uint8_t *S = mat == 0 ? bk->eg : mat == 1 ? bk->eu : bk->ed;
+        return weight_at_mx(W, S, row, K, c);
+    }
+    if (mat == 0) return weight_at(bk->wg, bk->sg, bk->bg, row, K, c);
+    if (mat == 1) return weight_at(bk->wu, bk->su, bk->bu, row, K, c);
+    return weight_at(bk->wd, bk->sd, bk->bd, row, K, c);
+}
 
 /* Hidden activation of one (token, expert) pair: h[n] = silu(gate[n]) * up[n]. */
 static double pair_hidden_row(const bank_t *bk, const uint16_t *xrow, long e, long H, long I, long n) {
@@ -101,8 +140,8 @@ static double pair_hidden_row(const bank_t *bk, const uint16_t *xrow, long e, lo
     double g = 0.0, u = 0.0;
     for (long c = 0; c < H; ++c) {
         double xc = bf16_to_double(xrow[c]);
-        u += xc * weight_at(bk->wu, bk->su, bk->bu, row, H, c);
-        g += xc * weight_at(bk->wg, bk->sg, bk->bg, row, H, c);
+        u += xc * bank_weight(bk, 1, row, H, c);
+        g += xc * bank_weight(bk, 0, row, H, c);
     }
     return silu(g) * u;
 }
@@ -111,15 +150,19 @@ static double pair_hidden_row(const bank_t *bk, const uint16_t *xrow, long e, lo
 static double pair_down_row(const bank_t *bk, const double *h, long e, long H, long I, long m) {
     long row = e * H + m;
     double y = 0.0;
-    for (long n = 0; n < I; ++n) y += h[n] * weight_at(bk->wd, bk->sd, bk->bd, row, I, n);
+    for (long n = 0; n < I; ++n) y += h[n] * bank_weight(bk, 2, row, I, n);
     return y;
 }
 
-static int check_shapes(const int32_t *ids, long L, long k, long E, long H, long I) {
-    if (L < 0 || k <= 0 || E <= 0 || H <= 0 || I <= 0 || H % 64 || I % 64) return ORC_EINVAL;
+static int check_shapes_q(const int32_t *ids, long L, long k, long E, long H, long I, long q) {
+    if (L < 0 || k <= 0 || E <= 0 || H <= 0 || I <= 0 || H % q || I % q) return ORC_EINVAL;
     for (long p = 0; p < L * k; ++p)
         if (ids[p] < 0 || ids[p] >= E) return ORC_EINVAL;
     return ORC_OK;
+}
+
+static int check_shapes(const int32_t *ids, long L, long k, long E, long H, long I) {
+    return check_shapes_q(ids, L, k, E, H, I, 64);
 }
 
 /*
@@ -129,16 +172,10 @@ static int check_shapes(const int32_t *ids, long L, long k, long E, long H, long
  * every pair's hidden vector, h_out[(t * k + j) * I + n]; if y_out is not NULL,
  * every pair's down output y_out[(t * k + j) * H + m].
  */
-int oracle_forward_pairs(const uint16_t *x, const int32_t *ids, const float *tw,
-                         long L, long k, long E, long H, long I,
-                         const uint32_t *wg, const uint16_t *sg, const uint16_t *bg,
-                         const uint32_t *wu, const uint16_t *su, const uint16_t *bu,
-                         const uint32_t *wd, const uint16_t *sd, const uint16_t *bd,
-                         double *out, double *h_out, double *y_out) {
-    if (!out || (L > 0 && (!x || !ids || !tw))) return ORC_EINVAL;
-    int st = check_shapes(ids, L, k, E, H, I);
-    if (st) return st;
-    bank_t bk = {wg, sg, bg, wu, su, bu, wd, sd, bd};
+static int forward_pairs_bank(const uint16_t *x, const int32_t *ids, const float *tw,
+                              long L, long k, long H, long I, const bank_t *bkp,
+                              double *out, double *h_out, double *y_out) {
+    const bank_t bk = *bkp;
     long P = L * k;
     double *h = (double *)malloc(sizeof(double) * (size_t)(P > 0 ? P : 1) * (size_t)I);
     double *y = (double *)malloc(sizeof(double) * (size_t)(P > 0 ? P : 1) * (size_t)H);
@@ -170,22 +207,41 @@ int oracle_forward_pairs(const uint16_t *x, const int32_t *ids, const float *tw,
     return ORC_OK;
 }
 
+int oracle_forward_pairs(const uint16_t *x, const int32_t *ids, const float *tw,
+                         long L, long k, long E, long H, long I,
+                         const uint32_t *wg, const uint16_t *sg, const uint16_t *bg,
+                         const uint32_t *wu, const uint16_t *su, const uint16_t *bu,
+                         const uint32_t *wd, const uint16_t *sd, const uint16_t *bd,
+                         double *out, double *h_out, double *y_out) {
+    if (!out || (L > 0 && (!x || !ids || !tw))) return ORC_EINVAL;
+    int st = check_shapes(ids, L, k, E, H, I);
+    if (st) return st;
+    bank_t bk = {wg, sg, bg, wu, su, bu, wd, sd, bd, NULL, NULL, NULL, 0};
+    return forward_pairs_bank(x, ids, tw, L, k, H, I, &bk, out, h_out, y_out);
+}
+
+/* Per-pair evaluation over an mxfp4 bank: scales eg/eu/ed are uint8 [rows, K/32]. */
+int oracle_forward_pairs_mx(const uint16_t *x, const int32_t *ids, const float *tw,
+                            long L, long k, long E, long H, long I,
+                            const uint32_t *wg, const uint8_t *eg, const uint32_t *wu, const uint8_t *eu,
+                            const uint32_t *wd, const uint8_t *ed,
+                            double *out, double *h_out, double *y_out) {
+    if (!out || (L > 0 && (!x || !ids || !tw))) return ORC_EINVAL;
+    int st = check_shapes_q(ids, L, k, E, H, I, 32);
+    if (st) return st;
+    bank_t bk = {wg, NULL, NULL, wu, NULL, NULL, wd, NULL, NULL, eg, eu, ed, 1};
+    return forward_pairs_bank(x, ids, tw, L, k, H, I, &bk, out, h_out, y_out);
+}
+
 /*
  * Union evaluation: the distinct experts of all L * k routes, ascending; each
  * one's hidden and down vectors computed once per token routed to it, then
  * added with that token's summed router weight for the expert.  Same
  * arguments and output as oracle_forward_pairs.
  */
-int oracle_forward_union(const uint16_t *x, const int32_t *ids, const float *tw,
-                         long L, long k, long E, long H, long I,
-                         const uint32_t *wg, const uint16_t *sg, const uint16_t *bg,
-                         const uint32_t *wu, const uint16_t *su, const uint16_t *bu,
-                         const uint32_t *wd, const uint16_t *sd, const uint16_t *bd,
-                         double *out) {
-    if (!out || (L > 0 && (!x || !ids || !tw))) return ORC_EINVAL;
-    int st = check_shapes(ids, L, k, E, H, I);
-    if (st) return st;
-    bank_t bk = {wg, sg, bg, wu, su, bu, wd, sd, bd};
+static int forward_union_bank(const uint16_t *x, const int32_t *ids, const float *tw,
+                              long L, long k, long H, long I, const bank_t *bkp, double *out) {
+    const bank_t bk = *bkp;
     long P = L * k;
 
     /* distinct expert ids, ascending (insertion into a sorted list) */
@@ -235,11 +291,59 @@ int oracle_forward_union(const uint16_t *x, const int32_t *ids, const float *tw,
     return ORC_OK;
 }
 
+int oracle_forward_union(const uint16_t *x, const int32_t *ids, const float *tw,
+                         long L, long k, long E, long H, long I,
+                         const uint32_t *wg, const uint16_t *sg, const uint16_t *bg,
+                         const uint32_t *wu, const uint16_t *su, const uint16_t *bu,
+                         const uint32_t *wd, const uint16_t *sd, const uint16_t *bd,
+                         double *out) {
+    if (!out || (L > 0 && (!x || !ids || !tw))) return ORC_EINVAL;
+    int st = check_shapes(ids, L, k, E, H, I);
+    if (st) return st;
+    bank_t bk = {wg, sg, bg, wu, su, bu, wd, sd, bd, NULL, NULL, NULL, 0};
+    return forward_union_bank(x, ids, tw, L, k, H, I, &bk, out);
+}
+
+/* Union evaluation over an mxfp4 bank (arguments as oracle_forward_pairs_mx). */
+int oracle_forward_union_mx(const uint16_t *x, const int32_t *ids, const float *tw,
+                            long L, long k, long E, long H, long I,
+                            const uint32_t *wg, const uint8_t *eg, const uint32_t *wu, const uint8_t *eu,
+                            const uint32_t *wd, const uint8_t *ed, double *out) {
+    if (!out || (L > 0 && (!x || !ids || !tw))) return ORC_EINVAL;
+    int st = check_shapes_q(ids, L, k, E, H, I, 32);
+    if (st) return st;
+    bank_t bk = {wg, NULL, NULL, wu, NULL, NULL, wd, NULL, NULL, eg, eu, ed, 1};
+    return forward_union_bank(x, ids, tw, L, k, H, I, &bk, out);
+}
+
+/* Dense dequantized copy of mxfp4 rows: out[r * K + c] (K a multiple of 32). */
+int oracle_dequant_mx(const uint32_t *W, const uint8_t *S, long rows, long K, double *out) {
+    if (!W || !S || !out || rows < 0 || K <= 0 || K % 32) return ORC_EINVAL;
+    for (long r = 0; r < rows; ++r)
+        for (long c = 0; c < K; ++c) out[r * K + c] = weight_at_mx(W, S, r, K, c);
+    return ORC_OK;
+}
+
 /*
  * One output element computed on its own: out[t, m] for token t and output
  * row m, per-pair evaluation.  Lets tests sample single outputs of full-size
  * layers.  Returns NAN on invalid arguments.
  */
+static double output_element_bank(const uint16_t *x, const int32_t *ids, const float *tw, long k, long H, long I,
+                                  const bank_t *bk, long t, long m) {
+    double *h = (double *)malloc(sizeof(double) * (size_t)I);
+    if (!h) return NAN;
+    double acc = 0.0;
+    for (long j = 0; j < k; ++j) {
+        long e = ids[t * k + j];
+#pragma omp parallel for schedule(static)
+        for (long n = 0; n < I; ++n) h[n] = pair_hidden_row(bk, x + t * H, e, H, I, n);
+        acc += (double)tw[t * k + j] * pair_down_row(bk, h, e, H, I, m);
+    }
+    free(h);
+    return acc;
+}
+
 double oracle_output_element(const uint16_t *x, const int32_t *ids, const float *tw,
                              long L, long k, long E, long H, long I,
                              const uint32_t *wg, const uint16_t *sg, const uint16_t *bg,
@@ -247,16 +351,16 @@ double oracle_output_element(const uint16_t *x, const int32_t *ids, const float 
                              const uint32_t *wd, const uint16_t *sd, const uint16_t *bd,
                              long t, long m) {
     if (t < 0 || t >= L || m < 0 || m >= H || check_shapes(ids, L, k, E, H, I)) return NAN;
-    bank_t bk = {wg, sg, bg, wu, su, bu, wd, sd, bd};
-    double *h = (double *)malloc(sizeof(double) * (size_t)I);
-    if (!h) return NAN;
-    double acc = 0.0;
-    for (long j = 0; j < k; ++j) {
-        long e = ids[t * k + j];
-#pragma omp parallel for schedule(static)
-        for (long n = 0; n < I; ++n) h[n] = pair_hidden_row(&bk, x + t * H, e, H, I, n);
-        acc += (double)tw[t * k + j] * pair_down_row(&bk, h, e, H, I, m);
-    }
-    free(h);
-    return acc;
+    bank_t bk = {wg, sg, bg, wu, su, bu, wd, sd, bd, NULL, NULL, NULL, 0};
+    return output_element_bank(x, ids, tw, k, H, I, &bk, t, m);
+}
+
+/* One output element over an mxfp4 bank (arguments as oracle_forward_pairs_mx). */
+double oracle_output_element_mx(const uint16_t *x, const int32_t *ids, const float *tw,
+                                long L, long k, long E, long H, long I,
+                                const uint32_t *wg, const uint8_t *eg, const uint32_t *wu, const uint8_t *eu,
+                                const uint32_t *wd, const uint8_t *ed, long t, long m) {
+    if (t < 0 || t >= L || m < 0 || m >= H || check_shapes_q(ids, L, k, E, H, I, 32)) return NAN;
+    bank_t bk = {wg, NULL, NULL, wu, NULL, NULL, wd, NULL, NULL, eg, eu, ed, 1};
+    return output_element_bank(x, ids, tw, k, H, I, &bk, t, m);
 }

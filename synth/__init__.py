@@ -102,6 +102,42 @@ def pack_codes(q: torch.Tensor) -> torch.Tensor:
 
 
 # --------------------------------------------------------------------------
+# mxfp4 gs32 encoding (input preparation only)
+# --------------------------------------------------------------------------
+
+MX_GROUP = 32
+# magnitudes of the FP4 E2M1 codes 0..7 (codes 8..15 are their negatives)
+E2M1_MAGNITUDES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def quantize_mxfp4_g32(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Encode bf16 rows ``w[..., N, K]`` as packed FP4 E2M1 codes plus one
+    E8M0 scale byte per 32 inputs (the OCP MX recipe): the block exponent is
+    floor(log2(max|w|)) - 2 (E2M1's largest exponent), each element divided by
+    2^exponent goes to the nearest E2M1 magnitude (ties to the even code,
+    saturating at 6), and the sign becomes bit 3.  Only produces test data.
+
+    Returns (packed int32 [..., N, K/8], scale uint8 [..., N, K/32]).
+    """
+    assert w.dtype == torch.bfloat16
+    *lead, n, k = w.shape
+    assert k % MX_GROUP == 0
+    wf = w.float().reshape(*lead, n, k // MX_GROUP, MX_GROUP)
+    amax = wf.abs().amax(-1)
+    expo = torch.where(amax > 0, torch.floor(torch.log2(torch.where(amax > 0, amax, torch.ones_like(amax)))) - 2,
+                       torch.full_like(amax, -127.0))
+    e = (expo + 127).clamp(0, 254)
+    scaled = wf / torch.exp2(e - 127).unsqueeze(-1)
+    grid = torch.tensor(E2M1_MAGNITUDES, dtype=torch.float32, device=w.device)
+    dist = (scaled.abs().unsqueeze(-1) - grid).abs()
+    dist = dist + 1e-6 * (torch.arange(8, device=w.device) % 2)  # ties to the even code
+    mag = dist.argmin(-1)
+    code = mag + 8 * (scaled < 0).to(mag.dtype)
+    packed = pack_codes(code.reshape(*lead, n, k))
+    return packed, e.to(torch.uint8)
+
+
+# --------------------------------------------------------------------------
 # weights, activations, routes
 # --------------------------------------------------------------------------
 
@@ -153,6 +189,52 @@ def gen_bank(E: int, H: int, I: int, seed_parts, device="cpu", experts_per_chunk
     u = gen_matrix_q4(E, I, H, (*seed_parts, "up"), device, experts_per_chunk)
     d = gen_matrix_q4(E, H, I, (*seed_parts, "down"), device, experts_per_chunk)
     return Bank(*g, *u, *d)
+
+
+@dataclasses.dataclass
+class BankMX:
+    """One MoE layer's expert bank in mxfp4 gs32 form."""
+    wg: torch.Tensor  # int32 [E, I, H/8]
+    sg: torch.Tensor  # uint8 [E, I, H/32]
+    wu: torch.Tensor
+    su: torch.Tensor
+    wd: torch.Tensor  # int32 [E, H, I/8]
+    sd: torch.Tensor  # uint8 [E, H, I/32]
+
+    @property
+    def E(self) -> int:
+        return self.wg.shape[0]
+
+    def tensors(self):
+        return (self.wg, self.sg, self.wu, self.su, self.wd, self.sd)
+
+    def to(self, device) -> "BankMX":
+        return BankMX(*[t.to(device) for t in self.tensors()])
+
+    def select(self, experts) -> "BankMX":
+        idx = torch.as_tensor(experts, dtype=torch.long, device=self.wg.device)
+        return BankMX(*[t.index_select(0, idx) for t in self.tensors()])
+
+
+def gen_matrix_mx(E: int, N: int, K: int, seed_parts, device="cpu", experts_per_chunk: int = 8):
+    """E random N(0,1) matrices [N, K] -> bf16 -> mxfp4 gs32, generated in chunks."""
+    packed = torch.empty((E, N, K // 8), dtype=torch.int32, device=device)
+    scale = torch.empty((E, N, K // MX_GROUP), dtype=torch.uint8, device=device)
+    gen = torch_gen(device, *seed_parts)
+    for e0 in range(0, E, experts_per_chunk):
+        e1 = min(E, e0 + experts_per_chunk)
+        w = torch.randn((e1 - e0, N, K), generator=gen, device=device, dtype=torch.float32)
+        p, sc = quantize_mxfp4_g32(w.to(torch.bfloat16))
+        packed[e0:e1], scale[e0:e1] = p, sc
+        del w, p, sc
+    return packed, scale
+
+
+def gen_bank_mx(E: int, H: int, I: int, seed_parts, device="cpu", experts_per_chunk: int = 8) -> BankMX:
+    g = gen_matrix_mx(E, I, H, (*seed_parts, "gate"), device, experts_per_chunk)
+    u = gen_matrix_mx(E, I, H, (*seed_parts, "up"), device, experts_per_chunk)
+    d = gen_matrix_mx(E, H, I, (*seed_parts, "down"), device, experts_per_chunk)
+    return BankMX(*g, *u, *d)
 
 
 def gen_x(L: int, H: int, seed_parts, device="cpu") -> torch.Tensor:
@@ -374,4 +456,17 @@ def random_problem(L: int, k: int, E: int, H: int, I: int, seed: int, device="cp
     tw = router_weights(L, k, rng)
     x = gen_x(L, H, ("random_problem", seed, L, H), device)
     bank = gen_bank(E, H, I, ("random_problem", seed, E, H, I), device)
+    return x, ids, tw, bank
+
+
+def random_problem_mx(L: int, k: int, E: int, H: int, I: int, seed: int, device="cpu", dup: bool = False):
+    """As :func:`random_problem` with an mxfp4 gs32 bank."""
+    rng = np_rng("random_problem_mx", L, k, E, H, I, seed)
+    if dup:
+        ids = rng.integers(0, E, size=(L, k)).astype(np.int32)
+    else:
+        ids = routes_uniform(L, k, E, rng)
+    tw = router_weights(L, k, rng)
+    x = gen_x(L, H, ("random_problem_mx", seed, L, H), device)
+    bank = gen_bank_mx(E, H, I, ("random_problem_mx", seed, E, H, I), device)
     return x, ids, tw, bank

@@ -59,3 +59,44 @@ def test_mutant_is_caught(name, tmp_path):
     finally:
         oracle.restore_library(prev)
     assert failed, f"mutant {name} passed every pin"
+
+
+# planted mistakes in the mxfp4 decode, against the mxfp4 pins
+import test_oracle_mx_pins as mxpins  # noqa: E402
+
+MX_MUTANTS = {
+    "e2m1_exponent_bias_2": ("(int)expo - 1);", "(int)expo - 2);"),
+    "e2m1_mantissa_quarter": ("ldexp(1.0 + 0.5 * (double)mant", "ldexp(1.0 + 0.25 * (double)mant"),
+    "e2m1_sign_ignored": ("return sign ? -mag : mag;", "return mag;"),
+    "e2m1_subnormal_step_1": ("expo == 0 ? 0.5 * (double)mant", "expo == 0 ? 1.0 * (double)mant"),
+    "e8m0_bias_128": ("(int)e - 127);", "(int)e - 128);"),
+    "mx_block_of_64": ("S[row * (K / 32) + c / 32]", "S[row * (K / 32) + c / 64]"),
+}
+
+MX_PIN_TESTS = [
+    mxpins.test_code_table_closed_form_properties,
+    mxpins.test_scale_byte_is_a_power_of_two_per_block,
+    mxpins.test_grid_values_roundtrip_through_quantizer_and_decoder,
+]
+
+
+@pytest.mark.parametrize("name", sorted(MX_MUTANTS))
+def test_mx_mutant_is_caught(name, tmp_path):
+    old, new = MX_MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, name
+    mut = tmp_path / "mutant.c"
+    mut.write_text(src.replace(old, new))
+    so = str(tmp_path / "libmutant.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", so, str(mut), "-lm"], check=True)
+    prev = oracle.use_library(so)
+    failed = []
+    try:
+        for t in MX_PIN_TESTS:
+            try:
+                t()
+            except AssertionError:
+                failed.append(t.__name__)
+    finally:
+        oracle.restore_library(prev)
+    assert failed, f"mutant {name} passed every mxfp4 pin"
