@@ -144,6 +144,49 @@ int moe_swiglu_q4_forward_stages(const void *x, const int32_t *topk_ids, const f
                                  unsigned stages, hipStream_t stream);
 
 /*
+ * Workspace bytes moe_swiglu_mxfp4_forward needs for this shape; 0 if the
+ * shape is invalid or not served (see below).  Host only.
+ */
+size_t moe_swiglu_mxfp4_workspace_bytes(int L, int k, int E, int H, int I);
+
+/*
+ * The same SwitchGLU MoE layer over mxfp4 expert banks: 4-bit FP4 E2M1
+ * elements, one E8M0 power-of-two scale byte per 32 consecutive inputs of a
+ * row -- the format of the GLM-5.2 banks on the mlx discussion page
+ * "Small-L fused expert gather for fine-grained MoE decode" (section "The
+ * data").  The pages do not give bit layouts; the OCP Microscaling (MX) v1.0
+ * encodings are used: E2M1 = sign bit 3, exponent bits 2..1 (bias 1),
+ * mantissa bit 0, exponent 0 encoding 0 and 0.5; scale byte e stands for
+ * 2^(e - 127) and e = 255 for NaN (every product with that block is NaN).
+ * Elements are packed as for the affine banks (element c of a row is nibble
+ * c % 8 of word c / 8, lowest nibble first).
+ *
+ *   wg, wu       uint32 [E, I, H/8]      gate / up codes               (16-byte aligned)
+ *   sg, su       uint8  [E, I, H/32]     gate / up E8M0 scales         (any alignment)
+ *   wd           uint32 [E, H, I/8]      down codes                    (16-byte aligned)
+ *   sd           uint8  [E, H, I/32]     down E8M0 scales              (any alignment)
+ *   H, I         multiples of 32; with H <= 64, I a multiple of 64, and with
+ *                I <= 128, H a multiple of 64 (the kernels' row steps)
+ * All other arguments, the results' definition and the status codes are as
+ * for moe_swiglu_q4_forward.  Only the union path serves these banks:
+ * L <= MOE_Q4_UNION_MAX_L, L * k <= MOE_Q4_MAX_PAIRS and the union path's LDS
+ * limits, else MOE_Q4_ERR_UNSUPPORTED.  The workspace is sized by
+ * moe_swiglu_mxfp4_workspace_bytes.
+ */
+int moe_swiglu_mxfp4_forward(const void *x, const int32_t *topk_ids, const float *topk_weights,
+                             const uint32_t *wg, const uint8_t *sg, const uint32_t *wu, const uint8_t *su,
+                             const uint32_t *wd, const uint8_t *sd, int L, int k, int E, int H, int I,
+                             void *out, int out_dtype, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* moe_swiglu_mxfp4_forward restricted to `stages`, as moe_swiglu_q4_forward_stages. */
+int moe_swiglu_mxfp4_forward_stages(const void *x, const int32_t *topk_ids, const float *topk_weights,
+                                    const uint32_t *wg, const uint8_t *sg, const uint32_t *wu,
+                                    const uint8_t *su, const uint32_t *wd, const uint8_t *sd, int L, int k,
+                                    int E, int H, int I, void *out, int out_dtype, void *workspace,
+                                    size_t workspace_bytes, unsigned stages, hipStream_t stream);
+
+/*
  * Union of the L * k routes (the dedup step of the union path), as its own
  * call so it can be checked bit for bit.  Outputs (device, u_max = min(E, L*k)):
  *   u            int32 [1]           number of distinct valid expert ids

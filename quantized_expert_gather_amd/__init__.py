@@ -42,6 +42,9 @@ EXPORTS = (
     "moe_swiglu_q4_select_path",
     "moe_swiglu_q4_forward",
     "moe_swiglu_q4_forward_stages",
+    "moe_swiglu_mxfp4_workspace_bytes",
+    "moe_swiglu_mxfp4_forward",
+    "moe_swiglu_mxfp4_forward_stages",
     "moe_route_union",
     "moe_sort_pairs_tiles_max",
     "moe_sort_pairs",
@@ -78,6 +81,13 @@ def lib() -> ctypes.CDLL:
     L.moe_swiglu_q4_forward.restype = I32
     L.moe_swiglu_q4_forward_stages.argtypes = fwd + [U, P]
     L.moe_swiglu_q4_forward_stages.restype = I32
+    L.moe_swiglu_mxfp4_workspace_bytes.argtypes = [I32] * 5
+    L.moe_swiglu_mxfp4_workspace_bytes.restype = SZ
+    fwd_mx = [P] * 9 + [I32] * 5 + [P, I32, P, SZ]
+    L.moe_swiglu_mxfp4_forward.argtypes = fwd_mx + [P]
+    L.moe_swiglu_mxfp4_forward.restype = I32
+    L.moe_swiglu_mxfp4_forward_stages.argtypes = fwd_mx + [U, P]
+    L.moe_swiglu_mxfp4_forward_stages.restype = I32
     L.moe_route_union.argtypes = [P, P, I32, I32, I32, P, P, P, P, P, P]
     L.moe_route_union.restype = I32
     L.moe_sort_pairs_tiles_max.argtypes = [I32] * 4
@@ -195,6 +205,60 @@ def forward_bank(x, topk_ids, topk_weights, bank, **kw) -> torch.Tensor:
     """moe_swiglu_q4_forward with the nine bank tensors taken from an object
     exposing ``tensors()`` (wg, sg, bg, wu, su, bu, wd, sd, bd)."""
     return moe_swiglu_q4_forward(x, topk_ids, topk_weights, *bank.tensors(), **kw)
+
+
+def moe_swiglu_mxfp4_workspace_bytes(L: int, k: int, E: int, H: int, I: int) -> int:
+    return int(lib().moe_swiglu_mxfp4_workspace_bytes(L, k, E, H, I))
+
+
+_U8 = (torch.uint8,)
+
+
+def moe_swiglu_mxfp4_forward(x, topk_ids, topk_weights, wg, sg, wu, su, wd, sd, out=None,
+                             out_dtype=torch.bfloat16, workspace=None, stream=None,
+                             stages: int = MOE_Q4_STAGE_ALL) -> torch.Tensor:
+    """One SwitchGLU MoE layer over mxfp4 banks (see include/moe_q4.h).
+
+    x bf16 [L, H]; topk_ids int32 [L, k]; topk_weights fp32 [L, k];
+    wg/wu int32 (uint32 bits) [E, I, H/8]; sg/su uint8 E8M0 [E, I, H/32];
+    wd int32 [E, H, I/8]; sd uint8 [E, H, I/32].  Returns out [L, H].
+    """
+    if x.dim() != 2 or topk_ids.dim() != 2 or wg.dim() != 3 or wd.dim() != 3:
+        raise ValueError("x [L, H], topk_ids [L, k], wg [E, I, H/8] and wd [E, H, I/8] expected")
+    L, H = x.shape
+    k = topk_ids.shape[1]
+    E, I = wg.shape[0], wg.shape[1]
+    shapes = {
+        "topk_ids": (topk_ids, (L, k)), "topk_weights": (topk_weights, (L, k)),
+        "wg": (wg, (E, I, H // 8)), "wu": (wu, (E, I, H // 8)), "wd": (wd, (E, H, I // 8)),
+        "sg": (sg, (E, I, H // 32)), "su": (su, (E, I, H // 32)), "sd": (sd, (E, H, I // 32)),
+    }
+    for name, (t, shp) in shapes.items():
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    od = MOE_Q4_OUT_F32 if out_dtype == torch.float32 else MOE_Q4_OUT_BF16
+    if out is None:
+        out = torch.empty((L, H), dtype=torch.float32 if od == MOE_Q4_OUT_F32 else torch.bfloat16, device=x.device)
+    if tuple(out.shape) != (L, H):
+        raise ValueError("out must be [L, H]")
+    if workspace is None:
+        n = moe_swiglu_mxfp4_workspace_bytes(L, k, E, H, I)
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
+    st = lib().moe_swiglu_mxfp4_forward_stages(
+        _dev_ptr(x, _BF16, "x"), _dev_ptr(topk_ids, _I32, "topk_ids"), _dev_ptr(topk_weights, _F32, "topk_weights"),
+        _dev_ptr(wg, _U32, "wg"), _dev_ptr(sg, _U8, "sg"), _dev_ptr(wu, _U32, "wu"), _dev_ptr(su, _U8, "su"),
+        _dev_ptr(wd, _U32, "wd"), _dev_ptr(sd, _U8, "sd"), L, k, E, H, I,
+        _dev_ptr(out, (torch.float32,) if od == MOE_Q4_OUT_F32 else _BF16, "out"), od,
+        _dev_ptr(workspace, (torch.uint8,), "workspace"), workspace.numel(),
+        int(stages), _stream_ptr(stream))
+    _check(st, "moe_swiglu_mxfp4_forward")
+    return out
+
+
+def forward_bank_mx(x, topk_ids, topk_weights, bank, **kw) -> torch.Tensor:
+    """moe_swiglu_mxfp4_forward with the six bank tensors taken from an object
+    exposing ``tensors()`` (wg, sg, wu, su, wd, sd)."""
+    return moe_swiglu_mxfp4_forward(x, topk_ids, topk_weights, *bank.tensors(), **kw)
 
 
 def moe_route_union(topk_ids: torch.Tensor, topk_weights: torch.Tensor, E: int, stream=None) -> Dict[str, torch.Tensor]:

@@ -56,6 +56,16 @@ static int select_path(int L, int k, int E, int H, int I) {
   return -MOE_Q4_ERR_UNSUPPORTED;
 }
 
+// mxfp4 banks: union path only; H and I multiples of 32 (one E8M0 scale per 32 inputs)
+static int mx_shape_status(int L, int k, int E, int H, int I) {
+  if (L < 0 || k < 1 || E < 1 || H < 1 || I < 1 || k > E) return MOE_Q4_ERR_SHAPE;
+  if (H % 32 || I % 32 || E > MOE_Q4_MAX_E) return MOE_Q4_ERR_UNSUPPORTED;
+  if (L == 0) return MOE_Q4_OK;
+  if (L > MOE_Q4_UNION_MAX_L || (long)L * k > MOE_Q4_MAX_PAIRS || !union_shape_supported(L, k, E, H, I))
+    return MOE_Q4_ERR_UNSUPPORTED;
+  return MOE_Q4_OK;
+}
+
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -186,6 +196,72 @@ int moe_swiglu_q4_forward(const void* x, const int32_t* topk_ids, const float* t
   return moe_swiglu_q4_forward_stages(x, topk_ids, topk_weights, wg, sg, bg, wu, su, bu, wd, sd, bd, L, k, E, H, I,
                                       group_size, bits, out, out_dtype, workspace, workspace_bytes,
                                       MOE_Q4_STAGE_ALL, stream);
+}
+
+size_t moe_swiglu_mxfp4_workspace_bytes(int L, int k, int E, int H, int I) {
+  if (L == 0 || mx_shape_status(L, k, E, H, I)) return 0;
+  return union_workspace_layout(L, k, E, H, I).total;
+}
+
+int moe_swiglu_mxfp4_forward_stages(const void* x, const int32_t* topk_ids, const float* topk_weights,
+                                    const uint32_t* wg, const uint8_t* sg, const uint32_t* wu, const uint8_t* su,
+                                    const uint32_t* wd, const uint8_t* sd, int L, int k, int E, int H, int I,
+                                    void* out, int out_dtype, void* workspace, size_t workspace_bytes,
+                                    unsigned stages, hipStream_t stream) {
+  const int st = mx_shape_status(L, k, E, H, I);
+  if (st) return st;
+  if (out_dtype != MOE_Q4_OUT_BF16 && out_dtype != MOE_Q4_OUT_F32) return MOE_Q4_ERR_UNSUPPORTED;
+  if (stages == 0 || (stages & ~MOE_Q4_STAGE_ALL)) return MOE_Q4_ERR_UNSUPPORTED;
+  if (L == 0) return MOE_Q4_OK;
+  if (!x || !topk_ids || !topk_weights || !wg || !sg || !wu || !su || !wd || !sd || !out) return MOE_Q4_ERR_NULL;
+  if (!workspace) return MOE_Q4_ERR_WORKSPACE;
+  if (!aligned(x, 16) || !aligned(wg, 16) || !aligned(wu, 16) || !aligned(wd, 16) || !aligned(out, 16) ||
+      !aligned(topk_ids, 4) || !aligned(topk_weights, 4) || !aligned(workspace, 256))
+    return MOE_Q4_ERR_ALIGN;
+  const UnionWorkspace lay = union_workspace_layout(L, k, E, H, I);
+  if (workspace_bytes < lay.total) return MOE_Q4_ERR_WORKSPACE;
+
+  const size_t out_bytes = (size_t)L * H * (out_dtype == MOE_Q4_OUT_F32 ? 4 : 2);
+  const size_t gu_codes = (size_t)E * I * (H / 8) * 4, gu_e = (size_t)E * I * (H / 32);
+  const size_t d_codes = (size_t)E * H * (I / 8) * 4, d_e = (size_t)E * H * (I / 32);
+  const struct { const void* p; size_t n; } ins[] = {
+      {x, (size_t)L * H * 2}, {topk_ids, (size_t)L * k * 4}, {topk_weights, (size_t)L * k * 4},
+      {wg, gu_codes}, {sg, gu_e}, {wu, gu_codes}, {su, gu_e}, {wd, d_codes}, {sd, d_e}, {workspace, lay.total}};
+  for (const auto& in : ins)
+    if (overlaps(out, out_bytes, in.p, in.n)) return MOE_Q4_ERR_ALIAS;
+
+  const int ncu = num_cus();
+  if (ncu <= 0) return MOE_Q4_ERR_LAUNCH;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  UnionArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.ids = topk_ids;
+  a.tw = topk_weights;
+  // the E8M0 bytes travel in the scale slots; the bias slots stay NULL
+  a.wg = wg; a.sg = reinterpret_cast<const uint16_t*>(sg);
+  a.wu = wu; a.su = reinterpret_cast<const uint16_t*>(su);
+  a.wd = wd; a.sd = reinterpret_cast<const uint16_t*>(sd);
+  a.mx = 1;
+  a.out = out;
+  a.out_f32 = out_dtype == MOE_Q4_OUT_F32;
+  a.L = L; a.k = k; a.E = E; a.H = H; a.I = I;
+  a.hdr = reinterpret_cast<uint32_t*>(ws + lay.hdr);
+  a.utab = reinterpret_cast<int4*>(ws + lay.utab);
+  a.slot_w = reinterpret_cast<float*>(ws + lay.slot_w);
+  a.slot_dst = reinterpret_cast<int32_t*>(ws + lay.slot_dst);
+  a.tcount = reinterpret_cast<int32_t*>(ws + lay.tcount);
+  a.hbuf = reinterpret_cast<float*>(ws + lay.hbuf);
+  a.ys = reinterpret_cast<float*>(ws + lay.ys);
+  a.ys_dummy = reinterpret_cast<float*>(ws + lay.ys_dummy);
+  return union_forward_launch(a, stages, ncu, stream);
+}
+
+int moe_swiglu_mxfp4_forward(const void* x, const int32_t* topk_ids, const float* topk_weights, const uint32_t* wg,
+                             const uint8_t* sg, const uint32_t* wu, const uint8_t* su, const uint32_t* wd,
+                             const uint8_t* sd, int L, int k, int E, int H, int I, void* out, int out_dtype,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return moe_swiglu_mxfp4_forward_stages(x, topk_ids, topk_weights, wg, sg, wu, su, wd, sd, L, k, E, H, I, out,
+                                         out_dtype, workspace, workspace_bytes, MOE_Q4_STAGE_ALL, stream);
 }
 
 int moe_route_union(const int32_t* topk_ids, const float* topk_weights, int L, int k, int E, int32_t* u,

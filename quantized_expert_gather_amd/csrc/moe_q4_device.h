@@ -53,6 +53,50 @@ __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float acc) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), acc, false);
 }
 
+// mxfp4 gs32 (OCP MX: FP4 E2M1 elements, one E8M0 scale byte per 32 inputs).
+// gfx950 converts the two E2M1 codes of one byte (low nibble first) to a
+// bf16 or fp16 pair exactly (scale operand 1.0); the block's 2^(e - 127)
+// multiplies the fp32 partial sum of its 32 products afterwards.
+// Sum of the 32 products of one position: codes w (8 per word, element c in
+// nibble c of its word) against 16 bf16 pairs in natural element order.
+__device__ __forceinline__ float dot32_mx_bf16(const uint4 w, const uint32_t (&av)[16], float d) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(ws[i], 1.0f, 0),
+                                        __builtin_bit_cast(bf16x2_t, av[4 * i + 0]), d, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(ws[i], 1.0f, 1),
+                                        __builtin_bit_cast(bf16x2_t, av[4 * i + 1]), d, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(ws[i], 1.0f, 2),
+                                        __builtin_bit_cast(bf16x2_t, av[4 * i + 2]), d, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(ws[i], 1.0f, 3),
+                                        __builtin_bit_cast(bf16x2_t, av[4 * i + 3]), d, false);
+  }
+  return d;
+}
+
+// The same against 16 fp16 pairs in natural element order.
+__device__ __forceinline__ float dot32_mx_f16(const uint4 w, const uint32_t (&hv)[16], float d) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    d = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[i], 1.0f, 0),
+                               __builtin_bit_cast(half2_t, hv[4 * i + 0]), d, false);
+    d = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[i], 1.0f, 1),
+                               __builtin_bit_cast(half2_t, hv[4 * i + 1]), d, false);
+    d = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[i], 1.0f, 2),
+                               __builtin_bit_cast(half2_t, hv[4 * i + 2]), d, false);
+    d = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[i], 1.0f, 3),
+                               __builtin_bit_cast(half2_t, hv[4 * i + 3]), d, false);
+  }
+  return d;
+}
+
+// A block's partial sum times its E8M0 scale 2^(e - 127); e = 255 is NaN.
+__device__ __forceinline__ float mx_scaled(float d, uint32_t e) {
+  return e == 255u ? __builtin_nanf("") : __builtin_amdgcn_ldexpf(d, (int)e - 127);
+}
+
 // Value of lane 4*(lane/4) + A of the caller's quad (DPP quad_perm broadcast).
 template <int A>
 __device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {

@@ -36,6 +36,7 @@ struct UnionArgs {
   // dynamic LDS layout of the gate/up kernel
   size_t lds_act, lds_asum, lds_union;
   int dn_slots;  // pair slots the down kernel stages in LDS at a time
+  int mx;        // banks are mxfp4 (sg/su/sd hold E8M0 bytes; bg/bu/bd unused)
 };
 
 // Workspace layout (byte offsets from the workspace base, 256-aligned regions).

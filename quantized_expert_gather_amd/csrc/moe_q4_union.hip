@@ -157,6 +157,8 @@ bool union_shape_supported(int L, int k, int E, int H, int I) {
   const int lg = lanes_per_row(H / 32), ld = lanes_per_row(I / 32);
   if (!positions_per_lane(H / 32, lg, false) || !positions_per_lane(I / 32, ld, true)) return false;
   if ((I % (gateup_rows(positions_per_lane(H / 32, lg, false)) * (64 / lg))) != 0) return false;
+  // a down step covers whole row steps of every expert
+  if (H % ((64 / ld) * down_rows(64 / ld)) != 0) return false;
   return union_lds_bytes_max(L, k, E, H, I) <= kMaxLds && down_lds_head(L * k) + down_slot_bytes(I / 32) + 256 <= kMaxLds;
 }
 
@@ -177,7 +179,8 @@ int union_forward_launch(const UnionArgs& base, unsigned stages, int num_cu, hip
     const int KU = a.H / 32;
     const int lpr = lanes_per_row(KU), ppl = positions_per_lane(KU, lpr, false);
     const size_t lds = gateup_lds_layout(a);
-    const void* fn = gateup_kernel(lpr, ppl, lpr * ppl == KU, (a.H / 64) % 2 == 0);
+    const void* fn = a.mx ? gateup_kernel_mx(lpr, ppl, lpr * ppl == KU)
+                          : gateup_kernel(lpr, ppl, lpr * ppl == KU, (a.H / 64) % 2 == 0);
     if (!fn || lds > kMaxLds) return MOE_Q4_ERR_UNSUPPORTED;
     const int wunits = u_max * (a.I / (gateup_rows(ppl) * (64 / lpr)));
     int grid = num_cu * blocks_per_cu(fn, kThreads, lds);
@@ -200,7 +203,7 @@ int union_forward_launch(const UnionArgs& base, unsigned stages, int num_cu, hip
     const bool qs = (a.I / 64) % 2 == 0;
     // one token per register pass when every expert has exactly one token (L = 1)
     const int nt = a.L == 1 ? 1 : 2;
-    const void* fn = down_kernel(lpr, ppl, lpr * ppl == KU, qs, nt);
+    const void* fn = a.mx ? down_kernel_mx(lpr, ppl, lpr * ppl == KU, nt) : down_kernel(lpr, ppl, lpr * ppl == KU, qs, nt);
     if (!fn || lds > kMaxLds) return MOE_Q4_ERR_UNSUPPORTED;
     // one block per CU: the CU's waves share the block's converted hidden
     // vectors and its work counter
@@ -232,6 +235,16 @@ const void* down_kernel(int lpr, int ppl, bool full, bool qs, int nt) {
   if (!f) f = down_kernel_2(lpr, ppl, full, qs, nt);
   if (!f) f = down_kernel_3(lpr, ppl, full, qs, nt);
   return f;
+}
+
+const void* gateup_kernel_mx(int lpr, int ppl, bool full) {
+  const void* f = gateup_kernel_mx_0(lpr, ppl, full);
+  return f ? f : gateup_kernel_mx_1(lpr, ppl, full);
+}
+
+const void* down_kernel_mx(int lpr, int ppl, bool full, int nt) {
+  const void* f = down_kernel_mx_0(lpr, ppl, full, nt);
+  return f ? f : down_kernel_mx_1(lpr, ppl, full, nt);
 }
 
 }  // namespace moeq4

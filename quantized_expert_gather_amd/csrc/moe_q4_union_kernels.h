@@ -95,6 +95,9 @@ __device__ __forceinline__ uint4 bld16(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ uint32_t bld2(rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
+__device__ __forceinline__ uint32_t bld1(rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
 __device__ __forceinline__ uint32_t ld4(const unsigned char* base, uint32_t off) {
   return *reinterpret_cast<const uint32_t*>(base + off);
 }
@@ -158,10 +161,29 @@ struct GuOffsets {
 // Loads unit `un` (or nothing, with zero-range descriptors, when !valid).
 // Loads the unit whose first row is row0 (plain loads from a wave-uniform
 // row base plus per-lane offsets).
-template <int PPL, int RG, bool FULL, bool QS>
+template <int PPL, int RG, bool FULL, bool QS, bool MX = false>
 __device__ __forceinline__ void gu_load(const UnionArgs& a, size_t row0, int nrows, int KU, int KG, int li, int lpr,
                                         const unsigned char* lane_sbase, const GuOffsets<PPL, RG>& o,
                                         GuFrag<PPL, RG>& f) {
+  if constexpr (MX) {  // mxfp4: one scale byte per (row, 32-input position) of gate and of up
+    const unsigned char* wg = reinterpret_cast<const unsigned char*>(a.wg) + row0 * KU * 16;
+    const unsigned char* wu = reinterpret_cast<const unsigned char*>(a.wu) + row0 * KU * 16;
+    const unsigned char* eg = reinterpret_cast<const unsigned char*>(a.sg) + row0 * KU;
+    const unsigned char* eu = reinterpret_cast<const unsigned char*>(a.su) + row0 * KU;
+#pragma unroll
+    for (int p = 0; p < PPL; ++p) {
+      if (FULL || li + lpr * p < KU) {
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+          f.w[p][r][0] = *reinterpret_cast<const uint4*>(wg + o.w[p][r]);
+          f.w[p][r][1] = *reinterpret_cast<const uint4*>(wu + o.w[p][r]);
+          f.sb[p][r][0] = (uint32_t)eg[o.s[p][r]] | ((uint32_t)eu[o.s[p][r]] << 8);
+        }
+      }
+    }
+    (void)nrows; (void)KG; (void)lane_sbase;
+    return;
+  }
   const uint32_t sbb = (uint32_t)(nrows * KG * 2);
   const unsigned char* wg = reinterpret_cast<const unsigned char*>(a.wg) + row0 * KU * 16;
   const unsigned char* wu = reinterpret_cast<const unsigned char*>(a.wu) + row0 * KU * 16;
@@ -191,7 +213,7 @@ __device__ __forceinline__ void gu_load(const UnionArgs& a, size_t row0, int nro
 // One unit: gate and up of RG hidden rows of one distinct expert for every
 // token routed to it, one token at a time (the unit's weights stay in
 // registers); h = silu(gate) * up goes to hbuf[(slot0 + token rank) * I + row].
-template <int LPR, int PPL, int RG, bool FULL, bool QS>
+template <int LPR, int PPL, int RG, bool FULL, bool QS, bool MX = false>
 __device__ __forceinline__ void gu_compute(const UnionArgs& a, const GuFrag<PPL, RG>& f, uint32_t mask, int slot0,
                                            int row, int li, int KU, const uint4* act, const float* asum,
                                            uint32_t sel) {
@@ -202,14 +224,17 @@ __device__ __forceinline__ void gu_compute(const UnionArgs& a, const GuFrag<PPL,
       touch(f.w[p][r][0]);
       touch(f.w[p][r][1]);
       touch(f.sb[p][r][0]);
-      if (!QS) touch(f.sb[p][r][1]);
+      if (!QS && !MX) touch(f.sb[p][r][1]);
     }
   uint32_t sbv[PPL][RG][2];
 #pragma unroll
   for (int p = 0; p < PPL; ++p)
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
-      if (QS) {
+      if (MX) {
+        sbv[p][r][0] = f.sb[p][r][0] & 0xFFu;         // E8M0 byte of gate
+        sbv[p][r][1] = (f.sb[p][r][0] >> 8) & 0xFFu;  // and of up
+      } else if (QS) {
         sbv[p][r][0] = quad_scale_bias<0, 1>(f.sb[p][r][0], sel);
         sbv[p][r][1] = quad_scale_bias<2, 3>(f.sb[p][r][0], sel);
       } else {
@@ -230,16 +255,24 @@ __device__ __forceinline__ void gu_compute(const UnionArgs& a, const GuFrag<PPL,
         const uint4 x0 = xa[0], x1 = xa[KU], x2 = xa[2 * KU], x3 = xa[3 * KU];
         const uint32_t xv[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
                                  x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
-        const float xs = asum[(size_t)t * KU + j];
+        if constexpr (MX) {  // x staged in natural element order
 #pragma unroll
-        for (int r = 0; r < RG; ++r)
+          for (int r = 0; r < RG; ++r)
 #pragma unroll
-          for (int mm = 0; mm < 2; ++mm) {
-            const float d = dot32<false>(f.w[p][r][mm], xv, kMagicBytes, 0.0f);
-            const float sc = bf16_lo_to_f32(sbv[p][r][mm]);
-            const float bi = bf16_hi_to_f32(sbv[p][r][mm]) - 128.0f * sc;
-            acc[r][mm] += sc * d + bi * xs;
-          }
+            for (int mm = 0; mm < 2; ++mm)
+              acc[r][mm] += mx_scaled(dot32_mx_bf16(f.w[p][r][mm], xv, 0.0f), sbv[p][r][mm]);
+        } else {
+          const float xs = asum[(size_t)t * KU + j];
+#pragma unroll
+          for (int r = 0; r < RG; ++r)
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm) {
+              const float d = dot32<false>(f.w[p][r][mm], xv, kMagicBytes, 0.0f);
+              const float sc = bf16_lo_to_f32(sbv[p][r][mm]);
+              const float bi = bf16_hi_to_f32(sbv[p][r][mm]) - 128.0f * sc;
+              acc[r][mm] += sc * d + bi * xs;
+            }
+        }
       }
     }
 #pragma unroll
@@ -322,7 +355,7 @@ __device__ inline void write_union_tables(const UnionArgs& a, const UnionLds& s,
   }
 }
 
-template <int LPR, int PPL, bool FULL, bool QS>
+template <int LPR, int PPL, bool FULL, bool QS, bool MX = false>
 __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
   constexpr int G = 64 / LPR;           // lane groups per wave
   constexpr int RG = gateup_rows(PPL);
@@ -362,10 +395,11 @@ __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
           float sum = 0.0f;
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            sum = sum8_bf16(v[b][c], sum);
-            act[((size_t)t * 4 + c) * KU + j] = pair_activations(v[b][c]);
+            if (!MX) sum = sum8_bf16(v[b][c], sum);
+            // mxfp4 codes convert to pairs in natural element order
+            act[((size_t)t * 4 + c) * KU + j] = MX ? v[b][c] : pair_activations(v[b][c]);
           }
-          asum[(size_t)t * KU + j] = sum;
+          if (!MX) asum[(size_t)t * KU + j] = sum;
         }
       }
     }
@@ -388,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
       const int j = li + LPR * p;
       o.w[p][r] = (uint32_t)(((g * RG + r) * KU + j) * 16);
       const int grp = QS ? 2 * (li >> 2) + (LPR / 2) * p : (j >> 1);
-      o.s[p][r] = (uint32_t)(((g * RG + r) * KG + grp) * 2);
+      o.s[p][r] = MX ? (uint32_t)((g * RG + r) * KU + j) : (uint32_t)(((g * RG + r) * KG + grp) * 2);
     }
   // Work units: (distinct expert, WROWS hidden rows).  Block b owns units
   // b, b + nblk, b + 2 nblk, ... (adjacent blocks take adjacent rows, so the
@@ -408,13 +442,13 @@ __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
     auto load = [&](int j, GuFrag<PPL, RG>& f) {
       const int un = b + min(j, nub - 1) * nblk;
       const int i = un / upe;
-      gu_load<PPL, RG, FULL, QS>(a, (size_t)wave_uniform(s.uniq[i]) * I + (un - i * upe) * WROWS, WROWS, KU, KG, li,
-                                 LPR, lane_sbase, o, f);
+      gu_load<PPL, RG, FULL, QS, MX>(a, (size_t)wave_uniform(s.uniq[i]) * I + (un - i * upe) * WROWS, WROWS, KU, KG,
+                                     li, LPR, lane_sbase, o, f);
     };
     auto compute = [&](int j, const GuFrag<PPL, RG>& f) {
       const int un = b + j * nblk;
       const int i = un / upe;
-      gu_compute<LPR, PPL, RG, FULL, QS>(a, f, wave_uniform((int)s.mask[i]), wave_uniform(s.off[i]),
+      gu_compute<LPR, PPL, RG, FULL, QS, MX>(a, f, wave_uniform((int)s.mask[i]), wave_uniform(s.off[i]),
                                          (un - i * upe) * WROWS + g * RG, li, KU, act, asum, sel);
     };
     auto grab = [&]() {
@@ -467,10 +501,26 @@ struct DnOffsets {
   uint32_t s[RS][PPL];
 };
 
-template <int PPL, int RS, bool FULL, bool QS>
+template <int PPL, int RS, bool FULL, bool QS, bool MX = false>
 __device__ __forceinline__ void dn_load(const UnionArgs& a, size_t row0, bool valid, size_t row_fallback, int nrows,
                                         int KU, int KG, int li, int lpr, const unsigned char* lane_sbase,
                                         const DnOffsets<PPL, RS>& o, DnFrag<PPL, RS>& f) {
+  if constexpr (MX) {  // mxfp4: one scale byte per (row, 32-input position)
+    const rsrc_t wd = make_rsrc(reinterpret_cast<const unsigned char*>(a.wd) + row0 * KU * 16,
+                                valid ? (uint32_t)(nrows * KU * 16) : 0u);
+    const rsrc_t ed = make_rsrc(reinterpret_cast<const unsigned char*>(a.sd) + (valid ? row0 : row_fallback) * KU,
+                                valid ? (uint32_t)(nrows * KU) : 0u);
+#pragma unroll
+    for (int r = 0; r < RS; ++r)
+#pragma unroll
+      for (int p = 0; p < PPL; ++p)
+        if (FULL || li + lpr * p < KU) {
+          f.w[r][p] = bld16(wd, o.w[r][p]);
+          f.sb[r][p] = bld1(ed, o.s[r][p]);
+        }
+    (void)KG; (void)lane_sbase;
+    return;
+  }
   const rsrc_t wd = make_rsrc(reinterpret_cast<const unsigned char*>(a.wd) + row0 * KU * 16,
                               valid ? (uint32_t)(nrows * KU * 16) : 0u);
   const size_t soff = (valid ? row0 : row_fallback) * KG * 2;
@@ -506,7 +556,7 @@ __host__ __device__ constexpr size_t down_lds_head(int P) {
 // slot `ls`: scaled by the power of two that puts its largest magnitude in
 // [2^13, 2^14), rounded to fp16.  One wave per slot.
 __device__ __forceinline__ void down_stage_slot(const UnionArgs& a, int ls, int slot, int KU, uint4* hvs, float* hss,
-                                                float* stw, int* sdst) {
+                                                float* stw, int* sdst, bool natural) {
   const int lane = threadIdx.x & 63;
   const float* hrow = a.hbuf + (size_t)slot * a.I;
   auto load32 = [&](int j, float (&v)[32]) {
@@ -530,9 +580,11 @@ __device__ __forceinline__ void down_stage_slot(const UnionArgs& a, int ls, int 
       uint4 pk;
       uint32_t* pw = reinterpret_cast<uint32_t*>(&pk);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        pw[kk] = (uint32_t)__builtin_bit_cast(uint16_t, hb[pair_lo(kk)]) |
-                 ((uint32_t)__builtin_bit_cast(uint16_t, hb[pair_hi(kk)]) << 16);
+      for (int kk = 0; kk < 4; ++kk) {
+        // affine codes unpack to (e0,e2),(e4,e6),(e1,e3),(e5,e7); mxfp4 to natural pairs
+        const int lo = natural ? 2 * kk : pair_lo(kk), hi = natural ? 2 * kk + 1 : pair_hi(kk);
+        pw[kk] = (uint32_t)__builtin_bit_cast(uint16_t, hb[lo]) | ((uint32_t)__builtin_bit_cast(uint16_t, hb[hi]) << 16);
+      }
       hvs[((size_t)ls * 4 + wi) * KU + j] = pk;
     }
     hss[(size_t)ls * KU + j] = sum;
@@ -574,7 +626,7 @@ __device__ __forceinline__ void down_stage_slot(const UnionArgs& a, int ls, int 
 // each token's RS row totals, times its router weight (and 2^-k), go to its
 // ys row in one store (every lane stores its residue's row; token slots past
 // the expert's count write to the sink).
-template <int LPR, int PPL, int RS, int NT, bool FULL, bool QS>
+template <int LPR, int PPL, int RS, int NT, bool FULL, bool QS, bool MX = false>
 __device__ __forceinline__ void dn_step(const UnionArgs& a, const DnFrag<PPL, RS>& f, const uint32_t (&hv)[NT][PPL][16],
                                        const float (&hs)[NT][PPL], const float (&tw)[NT], float* const (&dst)[NT],
                                        int row0, int li, int KU, uint32_t sel) {
@@ -583,7 +635,7 @@ __device__ __forceinline__ void dn_step(const UnionArgs& a, const DnFrag<PPL, RS
 #pragma unroll
     for (int p = 0; p < PPL; ++p) {
       touch(f.w[r][p]);
-      if (!QS || (r & 1) == 0) touch(f.sb[r][p]);
+      if (MX || !QS || (r & 1) == 0) touch(f.sb[r][p]);
     }
   float acc[NT][RS];
 #pragma unroll
@@ -595,17 +647,22 @@ __device__ __forceinline__ void dn_step(const UnionArgs& a, const DnFrag<PPL, RS
 #pragma unroll
     for (int p = 0; p < PPL; ++p) {
       if (FULL || li + LPR * p < KU) {
-        uint32_t sb;
-        if (QS)
-          sb = (r & 1) ? quad_scale_bias<2, 3>(f.sb[r & ~1][p], sel) : quad_scale_bias<0, 1>(f.sb[r][p], sel);
-        else
-          sb = f.sb[r][p];
-        const float sc = bf16_lo_to_f32(sb);
-        const float bi = bf16_hi_to_f32(sb) - 1024.0f * sc;
+        if constexpr (MX) {  // hidden vectors staged as fp16 pairs in natural order
 #pragma unroll
-        for (int c = 0; c < NT; ++c) {
-          const float d = dot32<true>(f.w[r][p], hv[c][p], kMagicBytesF16, 0.0f);
-          acc[c][r] += sc * d + bi * hs[c][p];
+          for (int c = 0; c < NT; ++c) acc[c][r] += mx_scaled(dot32_mx_f16(f.w[r][p], hv[c][p], 0.0f), f.sb[r][p]);
+        } else {
+          uint32_t sb;
+          if (QS)
+            sb = (r & 1) ? quad_scale_bias<2, 3>(f.sb[r & ~1][p], sel) : quad_scale_bias<0, 1>(f.sb[r][p], sel);
+          else
+            sb = f.sb[r][p];
+          const float sc = bf16_lo_to_f32(sb);
+          const float bi = bf16_hi_to_f32(sb) - 1024.0f * sc;
+#pragma unroll
+          for (int c = 0; c < NT; ++c) {
+            const float d = dot32<true>(f.w[r][p], hv[c][p], kMagicBytesF16, 0.0f);
+            acc[c][r] += sc * d + bi * hs[c][p];
+          }
         }
       }
     }
@@ -618,7 +675,7 @@ __device__ __forceinline__ void dn_step(const UnionArgs& a, const DnFrag<PPL, RS
 // One (expert, token chunk) segment of a down wave: read the chunk's
 // converted hidden vectors from LDS, then stream the unit's row steps gj ..
 // gj + klast through a ring of three register fragments (two in flight).
-template <int LPR, int PPL, bool FULL, bool QS, int NT, int RS, int WSTEP>
+template <int LPR, int PPL, bool FULL, bool QS, int NT, int RS, int WSTEP, bool MX = false>
 __device__ __forceinline__ void dn_segment(const UnionArgs& a, size_t ebase, int ls0, int nt, int gj, int klast,
                                            int li, int g, int KU, int KG, int H, const unsigned char* lane_sbase,
                                            const DnOffsets<PPL, RS>& o, uint32_t sel, const uint4* hvs,
@@ -627,7 +684,7 @@ __device__ __forceinline__ void dn_segment(const UnionArgs& a, size_t ebase, int
   auto load = [&](int kk, DnFrag<PPL, RS>& fr) {
     const bool valid = kk <= klast;
     const size_t row0 = ebase + (size_t)(gj + min(kk, klast)) * WSTEP;
-    dn_load<PPL, RS, FULL, QS>(a, row0, valid, row0, WSTEP, KU, KG, li, LPR, lane_sbase, o, fr);
+    dn_load<PPL, RS, FULL, QS, MX>(a, row0, valid, row0, WSTEP, KU, KG, li, LPR, lane_sbase, o, fr);
   };
   DnFrag<PPL, RS> f0, f1, f2;
   load(0, f0);
@@ -663,7 +720,7 @@ __device__ __forceinline__ void dn_segment(const UnionArgs& a, size_t ebase, int
   }
 
   auto step = [&](int kk, const DnFrag<PPL, RS>& fr) {
-    dn_step<LPR, PPL, RS, NT, FULL, QS>(a, fr, hv, hs, tw, dst, (gj + kk) * WSTEP + g * RS, li, KU, sel);
+    dn_step<LPR, PPL, RS, NT, FULL, QS, MX>(a, fr, hv, hs, tw, dst, (gj + kk) * WSTEP + g * RS, li, KU, sel);
   };
 #pragma unroll 1
   for (int kk = 0;; kk += 3) {
@@ -692,7 +749,7 @@ constexpr int kDownUnitSteps = 4;  // row steps per down work unit
 // once).  Its waves take the units from an LDS counter (the first unit of
 // each wave fixed), so waves that get fewer issue slots do less of the
 // block's share.  A unit runs every token of its expert, NT at a time.
-template <int LPR, int PPL, bool FULL, bool QS, int NT>
+template <int LPR, int PPL, bool FULL, bool QS, int NT, bool MX = false>
 __global__ __launch_bounds__(down_threads(NT)) void k_down(UnionArgs a) {
   constexpr int G = 64 / LPR;
   constexpr int RS = down_rows(G);  // a wave step covers G * RS rows
@@ -772,7 +829,7 @@ __global__ __launch_bounds__(down_threads(NT)) void k_down(UnionArgs a) {
       o.w[r][p] = (uint32_t)(((g * RS + r) * KU + j) * 16);
       const int srow = QS ? (r & ~1) + (qa >> 1) : r;
       const int grp = QS ? 2 * (li >> 2) + (LPR / 2) * p : (j >> 1);
-      o.s[r][p] = (uint32_t)(((g * RS + srow) * KG + grp) * 2);
+      o.s[r][p] = MX ? (uint32_t)((g * RS + r) * KU + j) : (uint32_t)(((g * RS + srow) * KG + grp) * 2);
     }
   auto grab = [&]() {
     int v = 0;
@@ -786,7 +843,7 @@ __global__ __launch_bounds__(down_threads(NT)) void k_down(UnionArgs a) {
   for (int c0 = s_lo; c0 < s_hi; c0 += SM) {
     const int c1 = min(s_hi, c0 + SM);
     if (tid == 0) unit_q = NW;
-    for (int sl = c0 + wave; sl < c1; sl += NW) down_stage_slot(a, sl - c0, sl, KU, hvs, hss, stw, sdst);
+    for (int sl = c0 + wave; sl < c1; sl += NW) down_stage_slot(a, sl - c0, sl, KU, hvs, hss, stw, sdst, MX);
     __syncthreads();
     for (int j = wave; j < nub; j = grab()) {
       const int un = ub + j;
@@ -800,11 +857,11 @@ __global__ __launch_bounds__(down_threads(NT)) void k_down(UnionArgs a) {
       for (int t0 = t_lo; t0 < t_hi; t0 += NT) {
         const int nt = min(NT, t_hi - t0);
         if (NT > 1 && nt == 1)
-          dn_segment<LPR, PPL, FULL, QS, 1, RS, WSTEP>(a, ebase, t0 - c0, 1, gj, klast, li, g, KU, KG, H, lane_sbase,
-                                                       o, sel, hvs, hss, stw, sdst);
+          dn_segment<LPR, PPL, FULL, QS, 1, RS, WSTEP, MX>(a, ebase, t0 - c0, 1, gj, klast, li, g, KU, KG, H,
+                                                           lane_sbase, o, sel, hvs, hss, stw, sdst);
         else
-          dn_segment<LPR, PPL, FULL, QS, NT, RS, WSTEP>(a, ebase, t0 - c0, nt, gj, klast, li, g, KU, KG, H,
-                                                        lane_sbase, o, sel, hvs, hss, stw, sdst);
+          dn_segment<LPR, PPL, FULL, QS, NT, RS, WSTEP, MX>(a, ebase, t0 - c0, nt, gj, klast, li, g, KU, KG, H,
+                                                            lane_sbase, o, sel, hvs, hss, stw, sdst);
       }
     }
     __syncthreads();  // the converted slots and the counter are reused

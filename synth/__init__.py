@@ -428,6 +428,20 @@ def gen_bank_experts(w: Workload, experts, layer: int, seed: int, device="cpu", 
     return Bank(wg, sg, bg, wu, su, bu, wd, sd, bd)
 
 
+def make_layer_mx(w: Workload, L: int, layer: int, seed: int = 0, device="cpu") -> LayerInput:
+    """As :func:`make_layer` (compact) with an mxfp4 gs32 bank: same routes,
+    router weights and activations; expert e's bytes depend only on
+    (seed, layer, e)."""
+    ids, tw = layer_routes(w, L, layer, seed)
+    x = gen_x(L, w.H, (seed, w.name, L, layer), device)
+    used, remap = compact_ids(ids)
+    parts = []
+    for e in used.tolist():
+        parts.append(gen_bank_mx(1, w.H, w.I, (seed, w.name, layer, int(e), "mx"), device))
+    bank = BankMX(*[torch.cat([getattr(b, f) for b in parts]) for f in ("wg", "sg", "wu", "su", "wd", "sd")])
+    return LayerInput(x=x, ids=remap, weights=tw, bank=bank, global_ids=ids)
+
+
 def make_chain_layer(w: Workload, L: int, layer: int, seed: int = 0, device="cuda",
                      experts_per_chunk: int = 16) -> LayerInput:
     """One layer of a benchmark chain: compact bank of the used experts, each

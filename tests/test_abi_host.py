@@ -203,3 +203,56 @@ def test_binding_rejects_host_tensors_before_calling():
     with pytest.raises(ValueError):
         q.moe_swiglu_q4_forward(x, ids, w, *bank, workspace=torch.zeros(256, dtype=torch.uint8),
                                 out=torch.zeros((2, 256), dtype=torch.bfloat16))
+
+
+def call_mx(L=2, k=2, E=8, H=256, I=128, out_dtype=0, ws_bytes=1 << 30, stages=3, ptrs=None, ws=None, out=None):
+    p = [fake(i) for i in range(9)] if ptrs is None else ptrs
+    return q.lib().moe_swiglu_mxfp4_forward_stages(*p, L, k, E, H, I, fake(13) if out is None else out, out_dtype,
+                                                  fake(14) if ws is None else ws, ws_bytes, stages, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=-1), q.MOE_Q4_ERR_SHAPE),
+    (dict(k=9, E=8), q.MOE_Q4_ERR_SHAPE),
+    (dict(H=0), q.MOE_Q4_ERR_SHAPE),
+    (dict(H=240), q.MOE_Q4_ERR_UNSUPPORTED),
+    (dict(I=112), q.MOE_Q4_ERR_UNSUPPORTED),
+    (dict(L=33), q.MOE_Q4_ERR_UNSUPPORTED),       # the union path only
+    (dict(L=32, k=33, E=64), q.MOE_Q4_ERR_UNSUPPORTED),
+    (dict(out_dtype=5), q.MOE_Q4_ERR_UNSUPPORTED),
+    (dict(stages=4), q.MOE_Q4_ERR_UNSUPPORTED),
+    (dict(ws_bytes=64), q.MOE_Q4_ERR_WORKSPACE),
+])
+def test_mx_invalid_arguments_rejected_on_host(kw, status):
+    assert call_mx(**kw) == status
+
+
+def test_mx_host_checks():
+    assert call_mx(L=0) == q.MOE_Q4_OK
+    assert q.moe_swiglu_mxfp4_workspace_bytes(0, 2, 8, 256, 128) == 0
+    assert q.moe_swiglu_mxfp4_workspace_bytes(33, 8, 256, 2048, 512) == 0
+    # H and I multiples of 32 suffice; the layout is the union path's
+    assert q.moe_swiglu_mxfp4_workspace_bytes(2, 2, 4, 96, 256) > 0
+    assert q.moe_swiglu_mxfp4_workspace_bytes(2, 2, 4, 352, 224) > 0
+    # the kernels' row steps: H <= 64 needs I % 64 == 0, I <= 128 needs H % 64 == 0
+    assert q.moe_swiglu_mxfp4_workspace_bytes(2, 2, 4, 64, 32) == 0
+    assert q.moe_swiglu_mxfp4_workspace_bytes(2, 2, 4, 96, 96) == 0
+    assert q.moe_swiglu_mxfp4_workspace_bytes(2, 2, 4, 160, 128) == 0
+    assert q.moe_swiglu_mxfp4_workspace_bytes(2, 2, 4, 128, 128) > 0
+    assert q.moe_swiglu_mxfp4_workspace_bytes(8, 8, 256, 6144, 2048) == \
+        q.moe_swiglu_q4_workspace_bytes(8, 8, 256, 6144, 2048)
+    for i in range(9):
+        p = [fake(j) for j in range(9)]
+        p[i] = 0
+        assert call_mx(ptrs=p) == q.MOE_Q4_ERR_NULL, i
+    assert call_mx(ws=0) == q.MOE_Q4_ERR_WORKSPACE
+    for i, a in [(0, 8), (3, 8), (5, 4), (7, 8), (1, 2), (2, 2)]:
+        p = [fake(j) for j in range(9)]
+        p[i] += a
+        assert call_mx(ptrs=p) == q.MOE_Q4_ERR_ALIGN, i
+    p = [fake(j) for j in range(9)]
+    p[4] += 1  # scale bytes need no alignment
+    assert call_mx(ptrs=p, ws=0) == q.MOE_Q4_ERR_WORKSPACE
+    assert call_mx(out=fake(0)) == q.MOE_Q4_ERR_ALIAS
+    assert call_mx(out=fake(8) + 64) == q.MOE_Q4_ERR_ALIAS   # inside sd
+    assert call_mx(out=fake(14) + 256) == q.MOE_Q4_ERR_ALIAS
