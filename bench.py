@@ -21,6 +21,8 @@ adjacent-token overlap follows the measured depth-graded profile.
   chain first, so the events time the GPU, not Python.  Per-kernel durations
   come from chains of one stage alone (gate+up, or down+combine) over the
   same layers, timed the same way.
+* mxfp4: the same verify layers (routes, activations) over mxfp4 gs32 banks
+  (the pages' GLM-5.2 format), per L, with mxfp4 bytes per expert.
 * cpu_baseline: the CPU oracle (test infrastructure) timed on a bounded
   sample of the same layers on the host cores, with the same metric; the
   same layers are checked for parity (fp32 output before the bf16 cast,
@@ -142,6 +144,83 @@ def bench_sorted(args, Ts, q, synth, torch, np, dev, stream, sleep_cycles_for):
     return out
 
 
+def expert_bytes_mx(H: int, I: int) -> int:
+    """Bytes of one mxfp4 gs32 expert: 4-bit codes plus one E8M0 byte per 32
+    inputs, for gate, up and down (about 20 MB at H=6144, I=2048, the size the
+    mlx discussion "Small-L fused expert gather for fine-grained MoE decode"
+    gives for the GLM-5.2 experts)."""
+    return 3 * (H * I // 2 + H * I // 32)
+
+
+def bench_mx(args, Ls, q, synth, torch, np, dev, stream, sleep_cycles_for):
+    """The verify workload over mxfp4 gs32 banks: chains of layers spread over
+    the depth profile (so over the overlap range), full forward and gate+up
+    alone, per L."""
+    w = synth.WORKLOADS["verify"]
+    H, I, E, k = w.H, w.I, w.E, w.k
+    eb = expert_bytes_mx(H, I)
+    gub = 2 * (H * I // 2 + H * I // 32)
+    layer_ids = sorted(set(np.linspace(0, w.n_layers - 1, args.mx_layers).round().astype(int).tolist()))
+    out = {"workload": f"{w.name} in mxfp4 gs32 (E2M1 + E8M0 per 32), overlap chain of {len(layer_ids)} layers "
+                       f"spread over the {w.n_layers}-layer depth profile",
+           "bytes_per_expert": eb, "per_L": {}}
+    tot_b, tot_ms = 0.0, 0.0
+    for L in Ls:
+        layers = []
+        for layer in layer_ids:
+            lay = synth.make_chain_layer_mx(w, L, layer, seed=0, device=dev)
+            ids = torch.from_numpy(lay.ids).to(dev)
+            tw = torch.from_numpy(lay.weights).to(dev)
+            o = torch.empty((L, H), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(max(256, q.moe_swiglu_mxfp4_workspace_bytes(L, k, E, H, I)), dtype=torch.uint8,
+                             device=dev)
+            bt = lay.bank.tensors()
+            layers.append({"u": int(lay.bank.E), "keep": (lay, ids, tw, o, ws),
+                           "calls": {st: q.PreparedForwardMX(lay.x, ids, tw, bt, o, ws, code, stream)
+                                     for st, code in (("all", q.MOE_Q4_STAGE_ALL),
+                                                      ("gateup", q.MOE_Q4_STAGE_GATEUP))}})
+        torch.cuda.synchronize()
+
+        def chain(which, delay):
+            torch.cuda._sleep(delay)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            th = time.perf_counter()
+            for lay in layers:
+                lay["calls"][which]()
+            e1.record()
+            return e0, e1, (time.perf_counter() - th) * 1e3
+
+        warm = chain("all", 0)
+        torch.cuda.synchronize()
+        delay = sleep_cycles_for(1.5 * warm[2] + 1.0)
+        chain("all", delay)
+        torch.cuda.synchronize()
+        recs = {wh: [chain(wh, delay) for _ in range(max(3, args.steps))] for wh in ("all", "gateup")}
+        torch.cuda.synchronize()
+        nl = len(layers)
+        med = {wh: float(np.median([a.elapsed_time(b) for a, b, _ in v])) / nl for wh, v in recs.items()}
+        u_mean = sum(l["u"] for l in layers) / nl
+        gb = u_mean * eb / (med["all"] * 1e-3) / 1e9
+        gu_gb = (u_mean * gub + 2 * L * H + 8 * L * k) / (med["gateup"] * 1e-3) / 1e9
+        out["per_L"][str(L)] = {"us_per_layer": round(med["all"] * 1e3, 2), "u_mean": round(u_mean, 2),
+                                "eff_GBps": round(gb, 1), "frac_peak": round(gb / PEAK_HBM_GBPS, 4),
+                                "gateup_us": round(med["gateup"] * 1e3, 2), "gateup_GBps": round(gu_gb, 1)}
+        if L in METRIC_LS:
+            tot_b += u_mean * eb
+            tot_ms += med["all"]
+        log(f"mxfp4 L={L}: {med['all'] * 1e3:.2f} us/layer, {gb:.0f} GB/s effective; gate+up {gu_gb:.0f} GB/s")
+        del layers
+        torch.cuda.empty_cache()
+    if tot_ms > 0:
+        out["eff_GBps_over_L"] = round(tot_b / (tot_ms * 1e-3) / 1e9, 1)
+        out["frac_peak"] = round(out["eff_GBps_over_L"] / PEAK_HBM_GBPS, 4)
+    pl = out["per_L"]
+    if "1" in pl and "2" in pl:
+        out["L2_over_L1_time"] = round(pl["2"]["us_per_layer"] / pl["1"]["us_per_layer"], 3)
+    return out
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -181,6 +260,8 @@ def main():
     ap.add_argument("--pair-layers", type=int, default=20,
                     help="layers of each chain timed again as a per-pair baseline (one call per token, so "
                          "an expert shared by tokens is streamed once per token); 0 to skip")
+    ap.add_argument("--mx-layers", type=int, default=19,
+                    help="layers per L of the mxfp4 verify chains (spread over the depth profile); 0 to skip")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the baseline sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -420,6 +501,10 @@ def main():
     if sorted_Ts:
         result["sorted_path"] = bench_sorted(args, sorted_Ts, q, synth, torch, np, dev, stream,
                                              lambda ms: sleep_cycles_for(ms))
+
+    # ---- the same verify workload over mxfp4 banks ----
+    if args.mx_layers > 0:
+        result["mxfp4"] = bench_mx(args, Ls, q, synth, torch, np, dev, stream, lambda ms: sleep_cycles_for(ms))
 
     # ---- CPU oracle baseline on a bounded sample, and parity of the same layers ----
     if not args.no_cpu:

@@ -352,3 +352,28 @@ class PreparedForward:
         st = self._fn(*self._args)
         if st:
             raise MoeQ4Error(st, "moe_swiglu_q4_forward_stages")
+
+
+class PreparedForwardMX:
+    """:class:`PreparedForward` for mxfp4 banks (wg, sg, wu, su, wd, sd)."""
+
+    def __init__(self, x, topk_ids, topk_weights, bank_tensors, out, workspace, stages=MOE_Q4_STAGE_ALL,
+                 stream=None):
+        wg, sg, wu, su, wd, sd = bank_tensors
+        self._keep = (x, topk_ids, topk_weights, tuple(bank_tensors), out, workspace)
+        L, H = x.shape
+        k = topk_ids.shape[1]
+        E, I = wg.shape[0], wg.shape[1]
+        od = MOE_Q4_OUT_F32 if out.dtype == torch.float32 else MOE_Q4_OUT_BF16
+        kinds = (_BF16, _I32, _F32, _U32, _U8, _U32, _U8, _U32, _U8)
+        ptrs = [_dev_ptr(t, kd, "arg%d" % i)
+                for i, (t, kd) in enumerate(zip((x, topk_ids, topk_weights, wg, sg, wu, su, wd, sd), kinds))]
+        self._args = (*ptrs, L, k, E, H, I, _dev_ptr(out, (out.dtype,), "out"), od,
+                      _dev_ptr(workspace, (torch.uint8,), "workspace"), workspace.numel(), int(stages),
+                      _stream_ptr(stream))
+        self._fn = lib().moe_swiglu_mxfp4_forward_stages
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st:
+            raise MoeQ4Error(st, "moe_swiglu_mxfp4_forward_stages")

@@ -454,6 +454,17 @@ def make_chain_layer(w: Workload, L: int, layer: int, seed: int = 0, device="cud
     return LayerInput(x=x, ids=remap, weights=tw, bank=bank, global_ids=ids)
 
 
+def make_chain_layer_mx(w: Workload, L: int, layer: int, seed: int = 0, device="cuda",
+                        experts_per_chunk: int = 8) -> LayerInput:
+    """:func:`make_chain_layer` with an mxfp4 gs32 bank (same routes, router
+    weights and activations)."""
+    ids, tw = layer_routes(w, L, layer, seed)
+    x = gen_x(L, w.H, (seed, w.name, L, layer), device)
+    used, remap = compact_ids(ids)
+    bank = gen_bank_mx(len(used), w.H, w.I, (seed, w.name, L, layer, "chain-mx"), device, experts_per_chunk)
+    return LayerInput(x=x, ids=remap, weights=tw, bank=bank, global_ids=ids)
+
+
 def tiny_layer(device="cpu") -> LayerInput:
     """The tiny configuration exactly: E=8, top-2, H=256, I=128, L=2, seed 0, full bank."""
     w = WORKLOADS["tiny"]
