@@ -10,6 +10,9 @@ with it.
 * :func:`forward_pairs_mx`, :func:`forward_union_mx`, :func:`output_element_mx`,
   :func:`dequant_mx`: the same over mxfp4 gs32 banks (FP4 E2M1 elements, one
   E8M0 power-of-two scale byte per 32 inputs).
+* :func:`forward_pairs_q`, :func:`forward_union_q`, :func:`output_element_q`,
+  :func:`dequant_q`: any codec of :data:`CODECS` (affine 4/8-bit with group
+  32/64, mxfp4, nvfp4, mxfp8); :func:`e4m3_value` decodes one FP8 E4M3 byte.
 * :func:`route_union` and :func:`sorted_pairs` are plain Python: the
   bit-exact union outputs and the expert-sorted pair order with its
   expert-aligned tile list.
@@ -74,6 +77,17 @@ def _load():
     lib.oracle_output_element_mx.restype = ctypes.c_double
     lib.oracle_dequant_mx.argtypes = [P, P, Lg, Lg, P]
     lib.oracle_dequant_mx.restype = ctypes.c_int
+    I32 = ctypes.c_int
+    lib.oracle_forward_pairs_q.argtypes = [P, P, P, Lg, Lg, Lg, Lg, Lg, I32, I32, I32] + [P] * 9 + [P, P, P]
+    lib.oracle_forward_pairs_q.restype = ctypes.c_int
+    lib.oracle_forward_union_q.argtypes = [P, P, P, Lg, Lg, Lg, Lg, Lg, I32, I32, I32] + [P] * 9 + [P]
+    lib.oracle_forward_union_q.restype = ctypes.c_int
+    lib.oracle_output_element_q.argtypes = [P, P, P, Lg, Lg, Lg, Lg, Lg, I32, I32, I32] + [P] * 9 + [Lg, Lg]
+    lib.oracle_output_element_q.restype = ctypes.c_double
+    lib.oracle_dequant_q.argtypes = [I32, I32, I32, P, P, P, Lg, Lg, P]
+    lib.oracle_dequant_q.restype = ctypes.c_int
+    lib.oracle_e4m3_value.argtypes = [I32]
+    lib.oracle_e4m3_value.restype = ctypes.c_double
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
@@ -315,6 +329,118 @@ def output_element_mx(x, ids, tw, bank, t: int, m: int) -> float:
     if np.isnan(v):
         raise OracleError("oracle_output_element_mx: invalid arguments")
     return float(v)
+
+
+# --------------------------------------------------------------------------
+# any codec: affine 4/8-bit (group 32/64), mxfp4, nvfp4, mxfp8
+# --------------------------------------------------------------------------
+
+#: codec name -> (format code of moe_oracle.c, bits per element, inputs per scale group)
+CODECS = {
+    "affine4_g64": (0, 4, 64), "affine4_g32": (0, 4, 32),
+    "affine8_g64": (0, 8, 64), "affine8_g32": (0, 8, 32),
+    "mxfp4": (1, 4, 32), "nvfp4": (2, 4, 16), "mxfp8": (3, 8, 32),
+}
+
+
+def _codec_arrays(codec: str, bank) -> List[Optional[np.ndarray]]:
+    """(wg, sg, bg, wu, su, bu, wd, sd, bd) as uint32 codes, bf16 (affine) or
+    uint8 scales, and bf16 biases (None for the codecs without one)."""
+    fmt = CODECS[codec][0]
+    ts = bank.tensors() if hasattr(bank, "tensors") else bank
+    out = []
+    for i, t in enumerate(ts):
+        if t is None and (i % 3 != 2 or fmt == 0):
+            raise OracleError(f"{codec}: array {i} of the bank is missing")
+        try:
+            if i % 3 == 0:
+                out.append(_u32(t))
+            elif i % 3 == 1:
+                out.append(_u16(t) if fmt == 0 else _u8(t))
+            else:
+                out.append(_u16(t) if fmt == 0 else None)
+        except AssertionError:
+            raise OracleError(f"{codec}: array {i} of the bank has the wrong element type") from None
+    return out
+
+
+def _codec_shapes(codec: str, ia, ba):
+    bits = CODECS[codec][1]
+    L, k = ia.shape
+    E, I, hw = ba[0].shape
+    return L, k, E, hw * 32 // bits, I
+
+
+def _p(a):
+    return _ptr(a) if a is not None else None
+
+
+def forward_pairs_q(codec: str, x, ids, tw, bank, want_hidden: bool = False):
+    """Per-pair SwitchGLU + combine over a bank in ``codec``; out [L, H] float64."""
+    fmt, bits, gs = CODECS[codec]
+    xa = _u16(x)
+    ia = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+    wa = np.ascontiguousarray(np.asarray(tw, dtype=np.float32))
+    ba = _codec_arrays(codec, bank)
+    L, k, E, H, I = _codec_shapes(codec, ia, ba)
+    out = np.empty((L, H), np.float64)
+    hb = np.empty((L * k, I), np.float64) if want_hidden else None
+    st = _load().oracle_forward_pairs_q(_ptr(xa), _ptr(ia), _ptr(wa), L, k, E, H, I, fmt, bits, gs,
+                                        *[_p(a) for a in ba], _ptr(out), _p(hb), None)
+    if st:
+        raise OracleError(f"oracle_forward_pairs_q({codec}) status {st}")
+    return (out, hb) if want_hidden else out
+
+
+def forward_union_q(codec: str, x, ids, tw, bank) -> np.ndarray:
+    """Union evaluation over a bank in ``codec``; must agree with :func:`forward_pairs_q`."""
+    fmt, bits, gs = CODECS[codec]
+    xa = _u16(x)
+    ia = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+    wa = np.ascontiguousarray(np.asarray(tw, dtype=np.float32))
+    ba = _codec_arrays(codec, bank)
+    L, k, E, H, I = _codec_shapes(codec, ia, ba)
+    out = np.empty((L, H), np.float64)
+    st = _load().oracle_forward_union_q(_ptr(xa), _ptr(ia), _ptr(wa), L, k, E, H, I, fmt, bits, gs,
+                                        *[_p(a) for a in ba], _ptr(out))
+    if st:
+        raise OracleError(f"oracle_forward_union_q({codec}) status {st}")
+    return out
+
+
+def output_element_q(codec: str, x, ids, tw, bank, t: int, m: int) -> float:
+    """out[t, m] alone over a bank in ``codec``."""
+    fmt, bits, gs = CODECS[codec]
+    xa = _u16(x)
+    ia = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+    wa = np.ascontiguousarray(np.asarray(tw, dtype=np.float32))
+    ba = _codec_arrays(codec, bank)
+    L, k, E, H, I = _codec_shapes(codec, ia, ba)
+    if not (0 <= t < L and 0 <= m < H):
+        raise OracleError("output_element_q: index out of range")
+    return float(_load().oracle_output_element_q(_ptr(xa), _ptr(ia), _ptr(wa), L, k, E, H, I, fmt, bits, gs,
+                                                 *[_p(a) for a in ba], int(t), int(m)))
+
+
+def dequant_q(codec: str, W, S, B=None) -> np.ndarray:
+    """Dense double copy of rows in ``codec``: W [..., N, K*bits/32] -> [..., N, K]."""
+    fmt, bits, gs = CODECS[codec]
+    w = _u32(W)
+    s = _u16(S) if fmt == 0 else _u8(S)
+    b = _u16(B) if fmt == 0 else None
+    *lead, n, kw = w.shape
+    K = kw * 32 // bits
+    rows = int(np.prod(lead, dtype=np.int64)) * n if lead else n
+    out = np.empty((rows, K), np.float64)
+    st = _load().oracle_dequant_q(fmt, bits, gs, _ptr(w), _ptr(s), _p(b), rows, K, _ptr(out))
+    if st:
+        raise OracleError(f"oracle_dequant_q({codec}) status {st}")
+    return out.reshape(*lead, n, K)
+
+
+def e4m3_value(b: int) -> float:
+    """Value of one FP8 E4M3 byte."""
+    return float(_load().oracle_e4m3_value(int(b)))
 
 
 # --------------------------------------------------------------------------

@@ -28,6 +28,21 @@
  *    0 and +-0.5 (no infinities or NaN); the E8M0 scale byte e stands for
  *    2^(e - 127), and e = 255 for NaN.  Packing of the elements as for the
  *    affine banks.
+ *  - Further codecs named by the pages (mxfp8 in the dequant-mode comparison
+ *    of the mlx discussion above; nvfp4 and mxfp8 among the quantized modes of
+ *    PR 4572 on the page "MoE GatherQMM small-M verify cost", Facts; 8-bit
+ *    affine models in that page's correctness reports), without their bit
+ *    layouts.  The layouts taken here:
+ *      affine, bits 4 or 8, group 32 or 64: w = s * q + b with unsigned q and
+ *        one bf16 (s, b) per group; 8-bit codes are byte c % 4 of word c / 4,
+ *        lowest byte first;
+ *      nvfp4: FP4 E2M1 element (packed as the 4-bit codes) times an FP8 E4M3
+ *        scale per 16 consecutive inputs, no second-level scale;
+ *      mxfp8: FP8 E4M3 element (packed as the 8-bit codes) times the E8M0
+ *        scale 2^(e - 127) of its 32-input block (e = 255: NaN).
+ *    E4M3 follows the OCP 8-bit floating point specification: sign bit 7,
+ *    exponent bits 6..3 with bias 7, mantissa bits 2..0, exponent 0 encoding
+ *    subnormals m/8 * 2^-6, no infinities, and S.1111.111 the only NaN.
  *  - Router-weighted combine out[t] = sum_j w[t, j] * y[t, j] (the pages'
  *    SwitchGLU returns per-pair outputs; the weighted sum is the plain MoE
  *    combine this layer adds, applied after the down projection).
@@ -87,6 +102,66 @@ static double weight_at_mx(const uint32_t *W, const uint8_t *S, long row, long K
     return ldexp(e2m1_value(code_at(W + row * (K / 8), c)), (int)e - 127);
 }
 
+/* 8-bit code of input element c in a packed row. */
+static unsigned code8_at(const uint32_t *row_words, long c) {
+    return (row_words[c / 4] >> (8 * (c % 4))) & 0xFFu;
+}
+
+/* Value of an FP8 E4M3 number (OCP 8-bit floating point, E4M3 variant). */
+static double e4m3_value(unsigned b) {
+    unsigned sign = (b >> 7) & 1u, expo = (b >> 3) & 15u, mant = b & 7u;
+    if (expo == 15u && mant == 7u) return NAN;
+    double mag = expo == 0 ? ldexp((double)mant / 8.0, -6) : ldexp(1.0 + (double)mant / 8.0, (int)expo - 7);
+    return sign ? -mag : mag;
+}
+
+#define ORC_FMT_AFFINE 0
+#define ORC_FMT_MXFP4 1
+#define ORC_FMT_NVFP4 2
+#define ORC_FMT_MXFP8 3
+
+/* One quantized matrix of a codec: codes, per-group scales, per-group biases (affine only). */
+typedef struct {
+    int fmt, bits, gs;
+    const uint32_t *W;
+    const void *S;
+    const uint16_t *B;
+} qmat_t;
+
+/* Dequantized weight at (row, c) of a matrix with K inputs per row, any codec. */
+static double weight_at_q(const qmat_t *m, long row, long K, long c) {
+    const uint8_t *S8 = (const uint8_t *)m->S;
+    switch (m->fmt) {
+    case ORC_FMT_AFFINE: {
+        long g = row * (K / m->gs) + c / m->gs;
+        const uint32_t *rw = m->W + row * (K * m->bits / 32);
+        unsigned q = m->bits == 8 ? code8_at(rw, c) : code_at(rw, c);
+        return bf16_to_double(((const uint16_t *)m->S)[g]) * (double)q + bf16_to_double(m->B[g]);
+    }
+    case ORC_FMT_MXFP4:
+        return weight_at_mx(m->W, S8, row, K, c);
+    case ORC_FMT_NVFP4:
+        return e2m1_value(code_at(m->W + row * (K / 8), c)) * e4m3_value(S8[row * (K / 16) + c / 16]);
+    case ORC_FMT_MXFP8: {
+        unsigned e = S8[row * (K / 32) + c / 32];
+        if (e == 255u) return NAN;
+        return ldexp(e4m3_value(code8_at(m->W + row * (K / 4), c)), (int)e - 127);
+    }
+    }
+    return NAN;
+}
+
+/* Inputs per scale group of a codec, or 0 if the (fmt, bits, gs) triple is not one. */
+static long codec_group(int fmt, int bits, int gs) {
+    switch (fmt) {
+    case ORC_FMT_AFFINE: return (bits == 4 || bits == 8) && (gs == 32 || gs == 64) ? gs : 0;
+    case ORC_FMT_MXFP4: return bits == 4 && gs == 32 ? 32 : 0;
+    case ORC_FMT_NVFP4: return bits == 4 && gs == 16 ? 16 : 0;
+    case ORC_FMT_MXFP8: return bits == 8 && gs == 32 ? 32 : 0;
+    }
+    return 0;
+}
+
 static double silu(double v) { return v / (1.0 + exp(-v)); }
 
 int oracle_threads(void) {
@@ -120,10 +195,14 @@ typedef struct {
     /* mxfp4 banks: the scale bytes of gate, up, down (then sg..bd are unused) */
     const uint8_t *eg, *eu, *ed;
     int mx;
+    /* any codec: gate, up, down (used when q is set) */
+    int q;
+    qmat_t m[3];
 } bank_t;
 
 /* Weight of matrix mat (0 gate, 1 up, 2 down) at (row, c). */
 static double bank_weight(const bank_t *bk, int mat, long row, long K, long c) {
+    if (bk->q) return weight_at_q(&bk->m[mat], row, K, c);
     if (bk->mx) {
         const uint32_t *W = mat == 0 ? bk->wg : mat == 1 ? bk->wu : bk->wd;
         const uint8_t *S = mat == 0 ? bk->eg : mat == 1 ? bk->eu : bk->ed;
@@ -216,7 +295,7 @@ int oracle_forward_pairs(const uint16_t *x, const int32_t *ids, const float *tw,
     if (!out || (L > 0 && (!x || !ids || !tw))) return ORC_EINVAL;
     int st = check_shapes(ids, L, k, E, H, I);
     if (st) return st;
-    bank_t bk = {wg, sg, bg, wu, su, bu, wd, sd, bd, NULL, NULL, NULL, 0};
+    bank_t bk = {wg, sg, bg, wu, su, bu, wd, sd, bd, NULL, NULL, NULL, 0, 0, {{0}}};
     return forward_pairs_bank(x, ids, tw, L, k, H, I, &bk, out, h_out, y_out);
 }
 
@@ -229,7 +308,7 @@ int oracle_forward_pairs_mx(const uint16_t *x, const int32_t *ids, const float *
     if (!out || (L > 0 && (!x || !ids || !tw))) return ORC_EINVAL;
     int st = check_shapes_q(ids, L, k, E, H, I, 32);
     if (st) return st;
-    bank_t bk = {wg, NULL, NULL, wu, NULL, NULL, wd, NULL, NULL, eg, eu, ed, 1};
+    bank_t bk = {wg, NULL, NULL, wu, NULL, NULL, wd, NULL, NULL, eg, eu, ed, 1, 0, {{0}}};
     return forward_pairs_bank(x, ids, tw, L, k, H, I, &bk, out, h_out, y_out);
 }
 
@@ -300,7 +379,7 @@ int oracle_forward_union(const uint16_t *x, const int32_t *ids, const float *tw,
     if (!out || (L > 0 && (!x || !ids || !tw))) return ORC_EINVAL;
     int st = check_shapes(ids, L, k, E, H, I);
     if (st) return st;
-    bank_t bk = {wg, sg, bg, wu, su, bu, wd, sd, bd, NULL, NULL, NULL, 0};
+    bank_t bk = {wg, sg, bg, wu, su, bu, wd, sd, bd, NULL, NULL, NULL, 0, 0, {{0}}};
     return forward_union_bank(x, ids, tw, L, k, H, I, &bk, out);
 }
 
@@ -312,7 +391,7 @@ int oracle_forward_union_mx(const uint16_t *x, const int32_t *ids, const float *
     if (!out || (L > 0 && (!x || !ids || !tw))) return ORC_EINVAL;
     int st = check_shapes_q(ids, L, k, E, H, I, 32);
     if (st) return st;
-    bank_t bk = {wg, NULL, NULL, wu, NULL, NULL, wd, NULL, NULL, eg, eu, ed, 1};
+    bank_t bk = {wg, NULL, NULL, wu, NULL, NULL, wd, NULL, NULL, eg, eu, ed, 1, 0, {{0}}};
     return forward_union_bank(x, ids, tw, L, k, H, I, &bk, out);
 }
 
@@ -351,7 +430,7 @@ double oracle_output_element(const uint16_t *x, const int32_t *ids, const float 
                              const uint32_t *wd, const uint16_t *sd, const uint16_t *bd,
                              long t, long m) {
     if (t < 0 || t >= L || m < 0 || m >= H || check_shapes(ids, L, k, E, H, I)) return NAN;
-    bank_t bk = {wg, sg, bg, wu, su, bu, wd, sd, bd, NULL, NULL, NULL, 0};
+    bank_t bk = {wg, sg, bg, wu, su, bu, wd, sd, bd, NULL, NULL, NULL, 0, 0, {{0}}};
     return output_element_bank(x, ids, tw, k, H, I, &bk, t, m);
 }
 
@@ -361,6 +440,83 @@ double oracle_output_element_mx(const uint16_t *x, const int32_t *ids, const flo
                                 const uint32_t *wg, const uint8_t *eg, const uint32_t *wu, const uint8_t *eu,
                                 const uint32_t *wd, const uint8_t *ed, long t, long m) {
     if (t < 0 || t >= L || m < 0 || m >= H || check_shapes_q(ids, L, k, E, H, I, 32)) return NAN;
-    bank_t bk = {wg, NULL, NULL, wu, NULL, NULL, wd, NULL, NULL, eg, eu, ed, 1};
+    bank_t bk = {wg, NULL, NULL, wu, NULL, NULL, wd, NULL, NULL, eg, eu, ed, 1, 0, {{0}}};
     return output_element_bank(x, ids, tw, k, H, I, &bk, t, m);
 }
+
+/*
+ * Any codec (ORC_FMT_* with its bits and group size): the per-pair, union and
+ * single-element evaluations and a dense dequantized copy.  Codes are packed
+ * uint32 words [rows, K * bits / 32]; scales are bf16 (affine) or uint8 (the
+ * others) [rows, K / gs]; biases bf16 [rows, K / gs] for affine, else unused.
+ */
+static int make_bank_q(bank_t *bk, int fmt, int bits, int gs,
+                       const uint32_t *wg, const void *sg, const uint16_t *bg,
+                       const uint32_t *wu, const void *su, const uint16_t *bu,
+                       const uint32_t *wd, const void *sd, const uint16_t *bd) {
+    if (!codec_group(fmt, bits, gs)) return ORC_EINVAL;
+    if (!wg || !sg || !wu || !su || !wd || !sd) return ORC_EINVAL;
+    if (fmt == ORC_FMT_AFFINE && (!bg || !bu || !bd)) return ORC_EINVAL;
+    memset(bk, 0, sizeof *bk);
+    bk->q = 1;
+    const uint32_t *w[3] = {wg, wu, wd};
+    const void *sc[3] = {sg, su, sd};
+    const uint16_t *bi[3] = {bg, bu, bd};
+    for (int i = 0; i < 3; ++i) {
+        bk->m[i].fmt = fmt; bk->m[i].bits = bits; bk->m[i].gs = gs;
+        bk->m[i].W = w[i]; bk->m[i].S = sc[i]; bk->m[i].B = bi[i];
+    }
+    return ORC_OK;
+}
+
+int oracle_forward_pairs_q(const uint16_t *x, const int32_t *ids, const float *tw,
+                           long L, long k, long E, long H, long I, int fmt, int bits, int gs,
+                           const uint32_t *wg, const void *sg, const uint16_t *bg,
+                           const uint32_t *wu, const void *su, const uint16_t *bu,
+                           const uint32_t *wd, const void *sd, const uint16_t *bd,
+                           double *out, double *h_out, double *y_out) {
+    bank_t bk;
+    if (!out || (L > 0 && (!x || !ids || !tw))) return ORC_EINVAL;
+    if (make_bank_q(&bk, fmt, bits, gs, wg, sg, bg, wu, su, bu, wd, sd, bd)) return ORC_EINVAL;
+    int st = check_shapes_q(ids, L, k, E, H, I, codec_group(fmt, bits, gs));
+    if (st) return st;
+    return forward_pairs_bank(x, ids, tw, L, k, H, I, &bk, out, h_out, y_out);
+}
+
+int oracle_forward_union_q(const uint16_t *x, const int32_t *ids, const float *tw,
+                           long L, long k, long E, long H, long I, int fmt, int bits, int gs,
+                           const uint32_t *wg, const void *sg, const uint16_t *bg,
+                           const uint32_t *wu, const void *su, const uint16_t *bu,
+                           const uint32_t *wd, const void *sd, const uint16_t *bd, double *out) {
+    bank_t bk;
+    if (!out || (L > 0 && (!x || !ids || !tw))) return ORC_EINVAL;
+    if (make_bank_q(&bk, fmt, bits, gs, wg, sg, bg, wu, su, bu, wd, sd, bd)) return ORC_EINVAL;
+    int st = check_shapes_q(ids, L, k, E, H, I, codec_group(fmt, bits, gs));
+    if (st) return st;
+    return forward_union_bank(x, ids, tw, L, k, H, I, &bk, out);
+}
+
+double oracle_output_element_q(const uint16_t *x, const int32_t *ids, const float *tw,
+                               long L, long k, long E, long H, long I, int fmt, int bits, int gs,
+                               const uint32_t *wg, const void *sg, const uint16_t *bg,
+                               const uint32_t *wu, const void *su, const uint16_t *bu,
+                               const uint32_t *wd, const void *sd, const uint16_t *bd, long t, long m) {
+    bank_t bk;
+    if (make_bank_q(&bk, fmt, bits, gs, wg, sg, bg, wu, su, bu, wd, sd, bd)) return NAN;
+    if (t < 0 || t >= L || m < 0 || m >= H || check_shapes_q(ids, L, k, E, H, I, codec_group(fmt, bits, gs)))
+        return NAN;
+    return output_element_bank(x, ids, tw, k, H, I, &bk, t, m);
+}
+
+int oracle_dequant_q(int fmt, int bits, int gs, const uint32_t *W, const void *S, const uint16_t *B,
+                     long rows, long K, double *out) {
+    long g = codec_group(fmt, bits, gs);
+    if (!g || !W || !S || !out || (fmt == ORC_FMT_AFFINE && !B) || rows < 0 || K <= 0 || K % g) return ORC_EINVAL;
+    qmat_t m = {fmt, bits, gs, W, S, B};
+    for (long r = 0; r < rows; ++r)
+        for (long c = 0; c < K; ++c) out[r * K + c] = weight_at_q(&m, r, K, c);
+    return ORC_OK;
+}
+
+/* Value of one E4M3 byte (exported for the pins of the codec tables). */
+double oracle_e4m3_value(int b) { return e4m3_value((unsigned)b & 0xFFu); }

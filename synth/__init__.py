@@ -138,6 +138,191 @@ def quantize_mxfp4_g32(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
 
 
 # --------------------------------------------------------------------------
+# further codecs (input preparation only): affine 4/8-bit with group 32/64,
+# nvfp4 (E2M1 x E4M3 per 16), mxfp8 (E4M3 x E8M0 per 32)
+# --------------------------------------------------------------------------
+
+def e4m3_grid(device="cpu") -> torch.Tensor:
+    """Magnitudes of the FP8 E4M3 codes 0..126 (OCP: exponent bias 7, 3
+    mantissa bits, exponent 0 subnormal, code 127 NaN), increasing."""
+    vals = []
+    for c in range(127):
+        e, m = c >> 3, c & 7
+        vals.append(m / 8.0 * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return torch.tensor(vals, dtype=torch.float64, device=device)
+
+
+def encode_e4m3(v: torch.Tensor) -> torch.Tensor:
+    """Nearest E4M3 code of each value (ties to the even code, saturating at
+    448); uint8."""
+    grid = e4m3_grid(v.device)
+    a = v.double().abs().clamp(max=448.0)
+    hi = torch.searchsorted(grid, a).clamp(max=126)
+    lo = (hi - 1).clamp(min=0)
+    dlo = (a - grid[lo]).abs()
+    dhi = (grid[hi] - a).abs()
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = torch.where(pick_hi, hi, lo)
+    return (code + 128 * (v < 0).to(code.dtype)).to(torch.uint8)
+
+
+def decode_e4m3(code: torch.Tensor) -> torch.Tensor:
+    """Values of E4M3 codes (float64), for the encoders' own use."""
+    grid = torch.cat([e4m3_grid(code.device), torch.tensor([float("nan")], dtype=torch.float64,
+                                                          device=code.device)])
+    c = code.to(torch.int64)
+    mag = grid[c & 127]
+    return torch.where((c & 128) != 0, -mag, mag)
+
+
+def pack_codes8(q: torch.Tensor) -> torch.Tensor:
+    """Pack integer codes ``q[..., K]`` (0..255) into int32 words, lowest byte first."""
+    *lead, k = q.shape
+    assert k % 4 == 0
+    q = q.to(torch.int64).reshape(*lead, k // 4, 4)
+    shifts = torch.arange(0, 32, 8, device=q.device, dtype=torch.int64)
+    words = (q << shifts).sum(-1)
+    words = torch.where(words >= (1 << 31), words - (1 << 32), words)
+    return words.to(torch.int32)
+
+
+def quantize_affine(w: torch.Tensor, bits: int, gs: int):
+    """Affine encoding with ``bits`` (4 or 8) and group ``gs``: the recipe of
+    :func:`quantize_q4_g64` with 2^bits - 1 levels."""
+    assert w.dtype == torch.bfloat16 and bits in (4, 8)
+    *lead, n, k = w.shape
+    assert k % gs == 0
+    levels = float((1 << bits) - 1)
+    wf = w.float().reshape(*lead, n, k // gs, gs)
+    lo = wf.amin(-1)
+    hi = wf.amax(-1)
+    s = ((hi - lo) / levels).to(torch.bfloat16)
+    b = lo.to(torch.bfloat16)
+    sf = s.float().unsqueeze(-1)
+    bf = b.float().unsqueeze(-1)
+    safe = torch.where(sf > 0, sf, torch.ones_like(sf))
+    q = torch.round((wf - bf) / safe)
+    q = torch.where(sf > 0, q, torch.zeros_like(q)).clamp_(0, levels).to(torch.int64)
+    q = q.reshape(*lead, n, k)
+    return (pack_codes8(q) if bits == 8 else pack_codes(q)), s, b
+
+
+def _nearest_e2m1(scaled: torch.Tensor) -> torch.Tensor:
+    grid = torch.tensor(E2M1_MAGNITUDES, dtype=torch.float32, device=scaled.device)
+    dist = (scaled.abs().unsqueeze(-1) - grid).abs()
+    dist = dist + 1e-6 * (torch.arange(8, device=scaled.device) % 2)  # ties to the even code
+    mag = dist.argmin(-1)
+    return mag + 8 * (scaled < 0).to(mag.dtype)
+
+
+def quantize_nvfp4_g16(w: torch.Tensor):
+    """nvfp4: per 16 inputs an E4M3 scale nearest to max|w| / 6, then each
+    element divided by that scale goes to the nearest E2M1 value (ties to the
+    even code, saturating at 6).  Returns (packed int32 [..., N, K/8], scale
+    uint8 [..., N, K/16], None)."""
+    assert w.dtype == torch.bfloat16
+    *lead, n, k = w.shape
+    assert k % 16 == 0
+    wf = w.float().reshape(*lead, n, k // 16, 16)
+    sc = encode_e4m3(wf.abs().amax(-1).double() / 6.0)
+    sv = decode_e4m3(sc).float().unsqueeze(-1)
+    scaled = torch.where(sv > 0, wf / torch.where(sv > 0, sv, torch.ones_like(sv)), torch.zeros_like(wf))
+    code = _nearest_e2m1(scaled)
+    return pack_codes(code.reshape(*lead, n, k)), sc, None
+
+
+def quantize_mxfp8_g32(w: torch.Tensor):
+    """mxfp8 (OCP MX): block exponent floor(log2(max|w|)) - 8 (E4M3's largest
+    exponent), elements divided by 2^exponent go to the nearest E4M3 value
+    (ties to even, saturating at 448).  Returns (packed int32 [..., N, K/4],
+    scale uint8 [..., N, K/32], None)."""
+    assert w.dtype == torch.bfloat16
+    *lead, n, k = w.shape
+    assert k % 32 == 0
+    wf = w.float().reshape(*lead, n, k // 32, 32)
+    amax = wf.abs().amax(-1)
+    expo = torch.where(amax > 0, torch.floor(torch.log2(torch.where(amax > 0, amax, torch.ones_like(amax)))) - 8,
+                       torch.full_like(amax, -127.0))
+    e = (expo + 127).clamp(0, 254)
+    scaled = wf / torch.exp2(e - 127).unsqueeze(-1)
+    code = encode_e4m3(scaled)
+    return pack_codes8(code.reshape(*lead, n, k)), e.to(torch.uint8), None
+
+
+#: codec name -> (bits per element, inputs per scale group, has bias)
+CODECS = {
+    "affine4_g64": (4, 64, True), "affine4_g32": (4, 32, True),
+    "affine8_g64": (8, 64, True), "affine8_g32": (8, 32, True),
+    "mxfp4": (4, 32, False), "nvfp4": (4, 16, False), "mxfp8": (8, 32, False),
+}
+
+
+def quantize_codec(codec: str, w: torch.Tensor):
+    """(packed codes, scales, biases or None) of bf16 rows in ``codec``."""
+    bits, gs, _ = CODECS[codec]
+    if codec.startswith("affine"):
+        return quantize_affine(w, bits, gs)
+    if codec == "mxfp4":
+        p, sc = quantize_mxfp4_g32(w)
+        return p, sc, None
+    if codec == "nvfp4":
+        return quantize_nvfp4_g16(w)
+    if codec == "mxfp8":
+        return quantize_mxfp8_g32(w)
+    raise ValueError(codec)
+
+
+@dataclasses.dataclass
+class BankQ:
+    """One MoE layer's expert bank in any codec of :data:`CODECS` (biases None
+    for the codecs without one)."""
+    codec: str
+    wg: torch.Tensor
+    sg: torch.Tensor
+    bg: Optional[torch.Tensor]
+    wu: torch.Tensor
+    su: torch.Tensor
+    bu: Optional[torch.Tensor]
+    wd: torch.Tensor
+    sd: torch.Tensor
+    bd: Optional[torch.Tensor]
+
+    @property
+    def E(self) -> int:
+        return self.wg.shape[0]
+
+    def tensors(self):
+        return (self.wg, self.sg, self.bg, self.wu, self.su, self.bu, self.wd, self.sd, self.bd)
+
+    def to(self, device) -> "BankQ":
+        return BankQ(self.codec, *[None if t is None else t.to(device) for t in self.tensors()])
+
+    def select(self, experts) -> "BankQ":
+        idx = torch.as_tensor(experts, dtype=torch.long, device=self.wg.device)
+        return BankQ(self.codec, *[None if t is None else t.index_select(0, idx) for t in self.tensors()])
+
+
+def gen_matrix_q(codec: str, E: int, N: int, K: int, seed_parts, device="cpu", experts_per_chunk: int = 8):
+    """E random N(0,1) matrices [N, K] -> bf16 -> ``codec``, generated in chunks."""
+    parts = []
+    gen = torch_gen(device, *seed_parts)
+    for e0 in range(0, E, experts_per_chunk):
+        e1 = min(E, e0 + experts_per_chunk)
+        w = torch.randn((e1 - e0, N, K), generator=gen, device=device, dtype=torch.float32)
+        parts.append(quantize_codec(codec, w.to(torch.bfloat16)))
+        del w
+    cat = lambda i: None if parts[0][i] is None else torch.cat([p[i] for p in parts])  # noqa: E731
+    return cat(0), cat(1), cat(2)
+
+
+def gen_bank_q(codec: str, E: int, H: int, I: int, seed_parts, device="cpu", experts_per_chunk: int = 8) -> BankQ:
+    g = gen_matrix_q(codec, E, I, H, (*seed_parts, codec, "gate"), device, experts_per_chunk)
+    u = gen_matrix_q(codec, E, I, H, (*seed_parts, codec, "up"), device, experts_per_chunk)
+    d = gen_matrix_q(codec, E, H, I, (*seed_parts, codec, "down"), device, experts_per_chunk)
+    return BankQ(codec, *g, *u, *d)
+
+
+# --------------------------------------------------------------------------
 # weights, activations, routes
 # --------------------------------------------------------------------------
 
@@ -495,3 +680,38 @@ def random_problem_mx(L: int, k: int, E: int, H: int, I: int, seed: int, device=
     x = gen_x(L, H, ("random_problem_mx", seed, L, H), device)
     bank = gen_bank_mx(E, H, I, ("random_problem_mx", seed, E, H, I), device)
     return x, ids, tw, bank
+
+
+def random_problem_q(codec: str, L: int, k: int, E: int, H: int, I: int, seed: int, device="cpu",
+                     dup: bool = False):
+    """As :func:`random_problem` with a bank in ``codec``."""
+    rng = np_rng("random_problem_q", codec, L, k, E, H, I, seed)
+    if dup:
+        ids = rng.integers(0, E, size=(L, k)).astype(np.int32)
+    else:
+        ids = routes_uniform(L, k, E, rng)
+    tw = router_weights(L, k, rng)
+    x = gen_x(L, H, ("random_problem_q", seed, L, H), device)
+    bank = gen_bank_q(codec, E, H, I, ("random_problem_q", seed, E, H, I), device)
+    return x, ids, tw, bank
+
+
+def make_layer_q(codec: str, w: Workload, L: int, layer: int, seed: int = 0, device="cpu") -> LayerInput:
+    """As :func:`make_layer_mx` for any codec: expert e's bytes depend only on
+    (seed, layer, e, codec)."""
+    ids, tw = layer_routes(w, L, layer, seed)
+    x = gen_x(L, w.H, (seed, w.name, L, layer), device)
+    used, remap = compact_ids(ids)
+    parts = [gen_bank_q(codec, 1, w.H, w.I, (seed, w.name, layer, int(e)), device) for e in used.tolist()]
+    ts = [None if parts[0].tensors()[i] is None else torch.cat([b.tensors()[i] for b in parts]) for i in range(9)]
+    return LayerInput(x=x, ids=remap, weights=tw, bank=BankQ(codec, *ts), global_ids=ids)
+
+
+def make_chain_layer_q(codec: str, w: Workload, L: int, layer: int, seed: int = 0, device="cuda",
+                       experts_per_chunk: int = 8) -> LayerInput:
+    """:func:`make_chain_layer` with a bank in ``codec``."""
+    ids, tw = layer_routes(w, L, layer, seed)
+    x = gen_x(L, w.H, (seed, w.name, L, layer), device)
+    used, remap = compact_ids(ids)
+    bank = gen_bank_q(codec, len(used), w.H, w.I, (seed, w.name, L, layer, "chain"), device, experts_per_chunk)
+    return LayerInput(x=x, ids=remap, weights=tw, bank=bank, global_ids=ids)

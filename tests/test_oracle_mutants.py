@@ -100,3 +100,49 @@ def test_mx_mutant_is_caught(name, tmp_path):
     finally:
         oracle.restore_library(prev)
     assert failed, f"mutant {name} passed every mxfp4 pin"
+
+
+# planted mistakes in the further codecs, against the codec pins
+import test_oracle_codec_pins as cpins  # noqa: E402
+
+CODEC_MUTANTS = {
+    "e4m3_exponent_bias_8": ("(int)expo - 7);", "(int)expo - 8);"),
+    "e4m3_subnormal_step": ("ldexp((double)mant / 8.0, -6)", "ldexp((double)mant / 8.0, -7)"),
+    "e4m3_nan_lost": ("if (expo == 15u && mant == 7u) return NAN;", ""),
+    "byte_order_reversed": ("(8 * (c % 4))", "(8 * (3 - c % 4))"),
+    "nvfp4_block_of_32": ("S8[row * (K / 16) + c / 16]", "S8[row * (K / 16) + c / 32]"),
+    "affine_group_fixed_64": ("long g = row * (K / m->gs) + c / m->gs;", "long g = row * (K / m->gs) + c / 64;"),
+    "mxfp8_scale_bias_128": ("code8_at(m->W + row * (K / 4), c)), (int)e - 127);",
+                             "code8_at(m->W + row * (K / 4), c)), (int)e - 128);"),
+    "affine8_row_stride_of_4bit": ("m->W + row * (K * m->bits / 32)", "m->W + row * (K / 8)"),
+}
+
+CODEC_PIN_TESTS = [
+    cpins.test_e4m3_decoder_matches_library_float8,
+    cpins.test_known_code_patterns_decode_in_order,
+    cpins.test_affine_group32_is_group64_with_repeated_scales,
+    cpins.test_block_scales_act_on_their_own_block,
+    cpins.test_grid_values_roundtrip_through_encoders_and_decoder,
+]
+
+
+@pytest.mark.parametrize("name", sorted(CODEC_MUTANTS))
+def test_codec_mutant_is_caught(name, tmp_path):
+    old, new = CODEC_MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, name
+    mut = tmp_path / "mutant.c"
+    mut.write_text(src.replace(old, new))
+    so = str(tmp_path / "libmutant.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", so, str(mut), "-lm"], check=True)
+    prev = oracle.use_library(so)
+    failed = []
+    try:
+        for t in CODEC_PIN_TESTS:
+            try:
+                t()
+            except AssertionError:
+                failed.append(t.__name__)
+    finally:
+        oracle.restore_library(prev)
+    assert failed, f"mutant {name} passed every codec pin"
