@@ -71,6 +71,12 @@ extern "C" {
 #define MOE_Q4_MAX_PAIRS 1024    /* L * k on the union path                                    */
 #define MOE_Q4_MAX_E 16384
 
+/* ---- weight codecs (moe_swiglu_codec_forward) ---- */
+#define MOE_Q4_CODEC_AFFINE4_G64 0 /* 4-bit affine, bf16 scale + bias per 64 inputs (= moe_swiglu_q4_forward) */
+#define MOE_Q4_CODEC_AFFINE4_G32 1 /* 4-bit affine, bf16 scale + bias per 32 inputs                      */
+#define MOE_Q4_CODEC_MXFP4 2       /* FP4 E2M1 elements, one E8M0 scale byte per 32 inputs             */
+#define MOE_Q4_CODEC_NVFP4 3       /* FP4 E2M1 elements, one FP8 E4M3 scale byte per 16 inputs         */
+
 /* ---- forward stages (moe_swiglu_q4_forward_stages) ---- */
 #define MOE_Q4_STAGE_GATEUP 1u   /* union (or sort) + fused gate/up + silu(gate)*up -> workspace  */
 #define MOE_Q4_STAGE_DOWN 2u     /* down projection + router-weighted combine -> out              */
@@ -144,42 +150,71 @@ int moe_swiglu_q4_forward_stages(const void *x, const int32_t *topk_ids, const f
                                  unsigned stages, hipStream_t stream);
 
 /*
- * Workspace bytes moe_swiglu_mxfp4_forward needs for this shape; 0 if the
- * shape is invalid or not served (see below).  Host only.
+ * Workspace bytes moe_swiglu_codec_forward needs for this codec and shape; 0
+ * if the shape is invalid or not served (see below).  Host only.
  */
-size_t moe_swiglu_mxfp4_workspace_bytes(int L, int k, int E, int H, int I);
+size_t moe_swiglu_codec_workspace_bytes(int codec, int L, int k, int E, int H, int I);
 
 /*
- * The same SwitchGLU MoE layer over mxfp4 expert banks: 4-bit FP4 E2M1
- * elements, one E8M0 power-of-two scale byte per 32 consecutive inputs of a
- * row -- the format of the GLM-5.2 banks on the mlx discussion page
- * "Small-L fused expert gather for fine-grained MoE decode" (section "The
- * data").  The pages do not give bit layouts; the OCP Microscaling (MX) v1.0
- * encodings are used: E2M1 = sign bit 3, exponent bits 2..1 (bias 1),
- * mantissa bit 0, exponent 0 encoding 0 and 0.5; scale byte e stands for
- * 2^(e - 127) and e = 255 for NaN (every product with that block is NaN).
- * Elements are packed as for the affine banks (element c of a row is nibble
- * c % 8 of word c / 8, lowest nibble first).
+ * The same SwitchGLU MoE layer over expert banks in another weight codec
+ * (MOE_Q4_CODEC_*).  The pages name these storage modes without their bit
+ * layouts: mxfp4 gs32 is the format of the GLM-5.2 banks on the mlx
+ * discussion page "Small-L fused expert gather for fine-grained MoE decode"
+ * (section "The data", about 20 MB per expert), whose dequant-mode comparison
+ * also times affine group 32; nvfp4 is among the quantized modes of PR 4572
+ * on the page "MoE GatherQMM small-M verify cost" (Facts).  Layouts taken:
  *
- *   wg, wu       uint32 [E, I, H/8]      gate / up codes               (16-byte aligned)
- *   sg, su       uint8  [E, I, H/32]     gate / up E8M0 scales         (any alignment)
- *   wd           uint32 [E, H, I/8]      down codes                    (16-byte aligned)
- *   sd           uint8  [E, H, I/32]     down E8M0 scales              (any alignment)
- *   H, I         multiples of 32; with H <= 64, I a multiple of 64, and with
- *                I <= 128, H a multiple of 64 (the kernels' row steps)
+ *   codes (all)   element c of a row is nibble c % 8 of word c / 8, lowest
+ *                 nibble first (as for moe_swiglu_q4_forward)
+ *   AFFINE4_G32   w = s * q + b, q in 0..15, bf16 s and b per 32 inputs
+ *   MXFP4         w = e2m1(q) * 2^(e - 127), one E8M0 byte e per 32 inputs;
+ *                 e = 255 stands for NaN (every product with that block is NaN)
+ *   NVFP4         w = e2m1(q) * e4m3(s), one FP8 E4M3 byte s per 16 inputs, no
+ *                 second-level scale
+ *   E2M1 and E4M3 follow the OCP specifications (MX v1.0; 8-bit floating point
+ *   E4M3: exponent bias 7, subnormals, S.1111.111 NaN, no infinities).
+ *
+ *   wg, wu      uint32 [E, I, H/8]        codes                      (16-byte aligned)
+ *   sg, su      [E, I, H/gs]              scales: bf16 (AFFINE4_G32, 2-byte aligned),
+ *                                         uint8 E8M0 (MXFP4, any alignment),
+ *                                         uint8 E4M3 (NVFP4, gs = 16, 2-byte aligned)
+ *   bg, bu      bf16 [E, I, H/32]         biases (AFFINE4_G32 only, 2-byte aligned;
+ *                                         ignored and may be NULL otherwise)
+ *   wd, sd, bd  the same for down, [E, H, I/8] and [E, H, I/gs]
+ *   H, I        multiples of 32; with H <= 64, I a multiple of 64, and with
+ *               I <= 128, H a multiple of 64 (the kernels' row steps)
+ *
  * All other arguments, the results' definition and the status codes are as
- * for moe_swiglu_q4_forward.  Only the union path serves these banks:
- * L <= MOE_Q4_UNION_MAX_L, L * k <= MOE_Q4_MAX_PAIRS and the union path's LDS
- * limits, else MOE_Q4_ERR_UNSUPPORTED.  The workspace is sized by
- * moe_swiglu_mxfp4_workspace_bytes.
+ * for moe_swiglu_q4_forward.  MOE_Q4_CODEC_AFFINE4_G64 is exactly
+ * moe_swiglu_q4_forward (both paths).  The other codecs take the union path
+ * only: L <= MOE_Q4_UNION_MAX_L, L * k <= MOE_Q4_MAX_PAIRS and the union
+ * path's LDS limits, else MOE_Q4_ERR_UNSUPPORTED; so does an unknown codec.
  */
+int moe_swiglu_codec_forward(int codec, const void *x, const int32_t *topk_ids, const float *topk_weights,
+                             const uint32_t *wg, const void *sg, const void *bg,
+                             const uint32_t *wu, const void *su, const void *bu,
+                             const uint32_t *wd, const void *sd, const void *bd,
+                             int L, int k, int E, int H, int I, void *out, int out_dtype,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* moe_swiglu_codec_forward restricted to `stages`, as moe_swiglu_q4_forward_stages. */
+int moe_swiglu_codec_forward_stages(int codec, const void *x, const int32_t *topk_ids,
+                                    const float *topk_weights, const uint32_t *wg, const void *sg,
+                                    const void *bg, const uint32_t *wu, const void *su, const void *bu,
+                                    const uint32_t *wd, const void *sd, const void *bd, int L, int k,
+                                    int E, int H, int I, void *out, int out_dtype, void *workspace,
+                                    size_t workspace_bytes, unsigned stages, hipStream_t stream);
+
+/*
+ * mxfp4 shorthands: moe_swiglu_codec_* with MOE_Q4_CODEC_MXFP4 and no bias
+ * arrays (sg, su, sd uint8 E8M0 [.., K/32]).
+ */
+size_t moe_swiglu_mxfp4_workspace_bytes(int L, int k, int E, int H, int I);
 int moe_swiglu_mxfp4_forward(const void *x, const int32_t *topk_ids, const float *topk_weights,
                              const uint32_t *wg, const uint8_t *sg, const uint32_t *wu, const uint8_t *su,
                              const uint32_t *wd, const uint8_t *sd, int L, int k, int E, int H, int I,
                              void *out, int out_dtype, void *workspace, size_t workspace_bytes,
                              hipStream_t stream);
-
-/* moe_swiglu_mxfp4_forward restricted to `stages`, as moe_swiglu_q4_forward_stages. */
 int moe_swiglu_mxfp4_forward_stages(const void *x, const int32_t *topk_ids, const float *topk_weights,
                                     const uint32_t *wg, const uint8_t *sg, const uint32_t *wu,
                                     const uint8_t *su, const uint32_t *wd, const uint8_t *sd, int L, int k,

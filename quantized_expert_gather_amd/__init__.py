@@ -34,6 +34,13 @@ MOE_Q4_PATH_SORTED = 2
 MOE_Q4_STAGE_GATEUP = 1
 MOE_Q4_STAGE_DOWN = 2
 MOE_Q4_STAGE_ALL = 3
+MOE_Q4_CODEC_AFFINE4_G64 = 0
+MOE_Q4_CODEC_AFFINE4_G32 = 1
+MOE_Q4_CODEC_MXFP4 = 2
+MOE_Q4_CODEC_NVFP4 = 3
+#: codec names (as in the test-data generators) -> MOE_Q4_CODEC_* and inputs per scale group
+CODECS = {"affine4_g64": (MOE_Q4_CODEC_AFFINE4_G64, 64), "affine4_g32": (MOE_Q4_CODEC_AFFINE4_G32, 32),
+          "mxfp4": (MOE_Q4_CODEC_MXFP4, 32), "nvfp4": (MOE_Q4_CODEC_NVFP4, 16)}
 MOE_Q4_UNION_MAX_L = 32
 MOE_Q4_MAX_PAIRS = 1024
 
@@ -42,6 +49,9 @@ EXPORTS = (
     "moe_swiglu_q4_select_path",
     "moe_swiglu_q4_forward",
     "moe_swiglu_q4_forward_stages",
+    "moe_swiglu_codec_workspace_bytes",
+    "moe_swiglu_codec_forward",
+    "moe_swiglu_codec_forward_stages",
     "moe_swiglu_mxfp4_workspace_bytes",
     "moe_swiglu_mxfp4_forward",
     "moe_swiglu_mxfp4_forward_stages",
@@ -81,6 +91,13 @@ def lib() -> ctypes.CDLL:
     L.moe_swiglu_q4_forward.restype = I32
     L.moe_swiglu_q4_forward_stages.argtypes = fwd + [U, P]
     L.moe_swiglu_q4_forward_stages.restype = I32
+    L.moe_swiglu_codec_workspace_bytes.argtypes = [I32] * 6
+    L.moe_swiglu_codec_workspace_bytes.restype = SZ
+    fwd_c = [I32] + [P] * 12 + [I32] * 5 + [P, I32, P, SZ]
+    L.moe_swiglu_codec_forward.argtypes = fwd_c + [P]
+    L.moe_swiglu_codec_forward.restype = I32
+    L.moe_swiglu_codec_forward_stages.argtypes = fwd_c + [U, P]
+    L.moe_swiglu_codec_forward_stages.restype = I32
     L.moe_swiglu_mxfp4_workspace_bytes.argtypes = [I32] * 5
     L.moe_swiglu_mxfp4_workspace_bytes.restype = SZ
     fwd_mx = [P] * 9 + [I32] * 5 + [P, I32, P, SZ]
@@ -255,6 +272,75 @@ def moe_swiglu_mxfp4_forward(x, topk_ids, topk_weights, wg, sg, wu, su, wd, sd, 
     return out
 
 
+def moe_swiglu_codec_workspace_bytes(codec: int, L: int, k: int, E: int, H: int, I: int) -> int:
+    return int(lib().moe_swiglu_codec_workspace_bytes(int(codec), L, k, E, H, I))
+
+
+def _codec_id(codec) -> int:
+    return CODECS[codec][0] if isinstance(codec, str) else int(codec)
+
+
+def _codec_args(codec_name, x, topk_ids, topk_weights, wg, sg, bg, wu, su, bu, wd, sd, bd):
+    """Shape- and dtype-checked pointer list of a codec call."""
+    code = _codec_id(codec_name)
+    gs = {v[0]: v[1] for v in CODECS.values()}.get(code)
+    if gs is None:
+        raise ValueError(f"unknown codec {codec_name!r}")
+    if x.dim() != 2 or topk_ids.dim() != 2 or wg.dim() != 3 or wd.dim() != 3:
+        raise ValueError("x [L, H], topk_ids [L, k], wg [E, I, H/8] and wd [E, H, I/8] expected")
+    L, H = x.shape
+    k = topk_ids.shape[1]
+    E, I = wg.shape[0], wg.shape[1]
+    affine = code in (MOE_Q4_CODEC_AFFINE4_G64, MOE_Q4_CODEC_AFFINE4_G32)
+    shapes = {
+        "topk_ids": (topk_ids, (L, k)), "topk_weights": (topk_weights, (L, k)),
+        "wg": (wg, (E, I, H // 8)), "wu": (wu, (E, I, H // 8)), "wd": (wd, (E, H, I // 8)),
+        "sg": (sg, (E, I, H // gs)), "su": (su, (E, I, H // gs)), "sd": (sd, (E, H, I // gs)),
+    }
+    if affine:
+        shapes.update({"bg": (bg, (E, I, H // gs)), "bu": (bu, (E, I, H // gs)), "bd": (bd, (E, H, I // gs))})
+    for name, (t, shp) in shapes.items():
+        if t is None or tuple(t.shape) != shp:
+            raise ValueError(f"{name} has shape {None if t is None else tuple(t.shape)}, expected {shp}")
+    st = _BF16 if affine else _U8
+    ptrs = [_dev_ptr(x, _BF16, "x"), _dev_ptr(topk_ids, _I32, "topk_ids"),
+            _dev_ptr(topk_weights, _F32, "topk_weights"),
+            _dev_ptr(wg, _U32, "wg"), _dev_ptr(sg, st, "sg"), _dev_ptr(bg, _BF16, "bg") if affine else 0,
+            _dev_ptr(wu, _U32, "wu"), _dev_ptr(su, st, "su"), _dev_ptr(bu, _BF16, "bu") if affine else 0,
+            _dev_ptr(wd, _U32, "wd"), _dev_ptr(sd, st, "sd"), _dev_ptr(bd, _BF16, "bd") if affine else 0]
+    return code, ptrs, (L, k, E, H, I)
+
+
+def moe_swiglu_codec_forward(codec, x, topk_ids, topk_weights, wg, sg, bg, wu, su, bu, wd, sd, bd, out=None,
+                             out_dtype=torch.bfloat16, workspace=None, stream=None,
+                             stages: int = MOE_Q4_STAGE_ALL) -> torch.Tensor:
+    """One SwitchGLU MoE layer over a bank in ``codec`` (a name of :data:`CODECS`
+    or a MOE_Q4_CODEC_* value; see include/moe_q4.h).  Scales are bf16 for
+    the affine codecs and uint8 otherwise; biases are bf16 for the affine
+    codecs and ignored (may be None) otherwise."""
+    code, ptrs, (L, k, E, H, I) = _codec_args(codec, x, topk_ids, topk_weights, wg, sg, bg, wu, su, bu, wd, sd, bd)
+    od = MOE_Q4_OUT_F32 if out_dtype == torch.float32 else MOE_Q4_OUT_BF16
+    if out is None:
+        out = torch.empty((L, H), dtype=torch.float32 if od == MOE_Q4_OUT_F32 else torch.bfloat16, device=x.device)
+    if tuple(out.shape) != (L, H):
+        raise ValueError("out must be [L, H]")
+    if workspace is None:
+        n = moe_swiglu_codec_workspace_bytes(code, L, k, E, H, I)
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
+    st = lib().moe_swiglu_codec_forward_stages(
+        code, *ptrs, L, k, E, H, I, _dev_ptr(out, (torch.float32,) if od == MOE_Q4_OUT_F32 else _BF16, "out"), od,
+        _dev_ptr(workspace, (torch.uint8,), "workspace"), workspace.numel(), int(stages), _stream_ptr(stream))
+    _check(st, "moe_swiglu_codec_forward")
+    return out
+
+
+def forward_bank_codec(x, topk_ids, topk_weights, bank, **kw) -> torch.Tensor:
+    """moe_swiglu_codec_forward with the codec and the nine bank tensors taken
+    from an object exposing ``codec`` and ``tensors()`` (wg, sg, bg, wu, su,
+    bu, wd, sd, bd; biases None for the codecs without one)."""
+    return moe_swiglu_codec_forward(bank.codec, x, topk_ids, topk_weights, *bank.tensors(), **kw)
+
+
 def forward_bank_mx(x, topk_ids, topk_weights, bank, **kw) -> torch.Tensor:
     """moe_swiglu_mxfp4_forward with the six bank tensors taken from an object
     exposing ``tensors()`` (wg, sg, wu, su, wd, sd)."""
@@ -377,3 +463,23 @@ class PreparedForwardMX:
         st = self._fn(*self._args)
         if st:
             raise MoeQ4Error(st, "moe_swiglu_mxfp4_forward_stages")
+
+
+class PreparedForwardCodec:
+    """:class:`PreparedForward` for any codec (bank tensors as for
+    :func:`moe_swiglu_codec_forward`)."""
+
+    def __init__(self, codec, x, topk_ids, topk_weights, bank_tensors, out, workspace, stages=MOE_Q4_STAGE_ALL,
+                 stream=None):
+        self._keep = (x, topk_ids, topk_weights, tuple(bank_tensors), out, workspace)
+        code, ptrs, (L, k, E, H, I) = _codec_args(codec, x, topk_ids, topk_weights, *bank_tensors)
+        od = MOE_Q4_OUT_F32 if out.dtype == torch.float32 else MOE_Q4_OUT_BF16
+        self._args = (code, *ptrs, L, k, E, H, I, _dev_ptr(out, (out.dtype,), "out"), od,
+                      _dev_ptr(workspace, (torch.uint8,), "workspace"), workspace.numel(), int(stages),
+                      _stream_ptr(stream))
+        self._fn = lib().moe_swiglu_codec_forward_stages
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st:
+            raise MoeQ4Error(st, "moe_swiglu_codec_forward_stages")

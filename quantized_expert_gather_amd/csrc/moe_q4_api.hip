@@ -56,14 +56,26 @@ static int select_path(int L, int k, int E, int H, int I) {
   return -MOE_Q4_ERR_UNSUPPORTED;
 }
 
-// mxfp4 banks: union path only; H and I multiples of 32 (one E8M0 scale per 32 inputs)
-static int mx_shape_status(int L, int k, int E, int H, int I) {
+// Codecs other than 4-bit affine group 64 take the union path only, with H
+// and I multiples of 32 (the kernels' 32-input positions).
+static int codec_shape_status(int L, int k, int E, int H, int I) {
   if (L < 0 || k < 1 || E < 1 || H < 1 || I < 1 || k > E) return MOE_Q4_ERR_SHAPE;
   if (H % 32 || I % 32 || E > MOE_Q4_MAX_E) return MOE_Q4_ERR_UNSUPPORTED;
   if (L == 0) return MOE_Q4_OK;
   if (L > MOE_Q4_UNION_MAX_L || (long)L * k > MOE_Q4_MAX_PAIRS || !union_shape_supported(L, k, E, H, I))
     return MOE_Q4_ERR_UNSUPPORTED;
   return MOE_Q4_OK;
+}
+
+// Kernel format of a codec; -1 for an unknown codec.
+static int codec_fmt(int codec) {
+  switch (codec) {
+    case MOE_Q4_CODEC_AFFINE4_G64: return kFmtAffine;
+    case MOE_Q4_CODEC_AFFINE4_G32: return kFmtAffine32;
+    case MOE_Q4_CODEC_MXFP4: return kFmtMxfp4;
+    case MOE_Q4_CODEC_NVFP4: return kFmtNvfp4;
+  }
+  return -1;
 }
 
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -198,37 +210,53 @@ int moe_swiglu_q4_forward(const void* x, const int32_t* topk_ids, const float* t
                                       MOE_Q4_STAGE_ALL, stream);
 }
 
-size_t moe_swiglu_mxfp4_workspace_bytes(int L, int k, int E, int H, int I) {
-  if (L == 0 || mx_shape_status(L, k, E, H, I)) return 0;
+size_t moe_swiglu_codec_workspace_bytes(int codec, int L, int k, int E, int H, int I) {
+  if (codec == MOE_Q4_CODEC_AFFINE4_G64) return moe_swiglu_q4_workspace_bytes(L, k, E, H, I);
+  if (codec_fmt(codec) < 0 || L == 0 || codec_shape_status(L, k, E, H, I)) return 0;
   return union_workspace_layout(L, k, E, H, I).total;
 }
 
-int moe_swiglu_mxfp4_forward_stages(const void* x, const int32_t* topk_ids, const float* topk_weights,
-                                    const uint32_t* wg, const uint8_t* sg, const uint32_t* wu, const uint8_t* su,
-                                    const uint32_t* wd, const uint8_t* sd, int L, int k, int E, int H, int I,
-                                    void* out, int out_dtype, void* workspace, size_t workspace_bytes,
-                                    unsigned stages, hipStream_t stream) {
-  const int st = mx_shape_status(L, k, E, H, I);
+int moe_swiglu_codec_forward_stages(int codec, const void* x, const int32_t* topk_ids, const float* topk_weights,
+                                    const uint32_t* wg, const void* sg, const void* bg, const uint32_t* wu,
+                                    const void* su, const void* bu, const uint32_t* wd, const void* sd,
+                                    const void* bd, int L, int k, int E, int H, int I, void* out, int out_dtype,
+                                    void* workspace, size_t workspace_bytes, unsigned stages, hipStream_t stream) {
+  const int fmt = codec_fmt(codec);
+  if (fmt < 0) return MOE_Q4_ERR_UNSUPPORTED;
+  if (fmt == kFmtAffine)
+    return moe_swiglu_q4_forward_stages(x, topk_ids, topk_weights, wg, sg, bg, wu, su, bu, wd, sd, bd, L, k, E, H,
+                                        I, 64, 4, out, out_dtype, workspace, workspace_bytes, stages, stream);
+  const int st = codec_shape_status(L, k, E, H, I);
   if (st) return st;
   if (out_dtype != MOE_Q4_OUT_BF16 && out_dtype != MOE_Q4_OUT_F32) return MOE_Q4_ERR_UNSUPPORTED;
   if (stages == 0 || (stages & ~MOE_Q4_STAGE_ALL)) return MOE_Q4_ERR_UNSUPPORTED;
   if (L == 0) return MOE_Q4_OK;
+  const bool biased = fmt == kFmtAffine32;
   if (!x || !topk_ids || !topk_weights || !wg || !sg || !wu || !su || !wd || !sd || !out) return MOE_Q4_ERR_NULL;
+  if (biased && (!bg || !bu || !bd)) return MOE_Q4_ERR_NULL;
   if (!workspace) return MOE_Q4_ERR_WORKSPACE;
+  // scale (and bias) arrays: bf16 (affine), pairs of E4M3 bytes read as one
+  // 16-bit word (nvfp4) or single E8M0 bytes (mxfp4)
+  const size_t sa = fmt == kFmtMxfp4 ? 1 : 2;
   if (!aligned(x, 16) || !aligned(wg, 16) || !aligned(wu, 16) || !aligned(wd, 16) || !aligned(out, 16) ||
-      !aligned(topk_ids, 4) || !aligned(topk_weights, 4) || !aligned(workspace, 256))
+      !aligned(topk_ids, 4) || !aligned(topk_weights, 4) || !aligned(workspace, 256) || !aligned(sg, sa) ||
+      !aligned(su, sa) || !aligned(sd, sa) || (biased && (!aligned(bg, 2) || !aligned(bu, 2) || !aligned(bd, 2))))
     return MOE_Q4_ERR_ALIGN;
   const UnionWorkspace lay = union_workspace_layout(L, k, E, H, I);
   if (workspace_bytes < lay.total) return MOE_Q4_ERR_WORKSPACE;
 
+  // bytes of one scale array per 32 inputs of a row: bf16 (affine32), 2 E4M3 (nvfp4), 1 E8M0 (mxfp4)
+  const size_t per32 = fmt == kFmtMxfp4 ? 1 : 2;
   const size_t out_bytes = (size_t)L * H * (out_dtype == MOE_Q4_OUT_F32 ? 4 : 2);
-  const size_t gu_codes = (size_t)E * I * (H / 8) * 4, gu_e = (size_t)E * I * (H / 32);
-  const size_t d_codes = (size_t)E * H * (I / 8) * 4, d_e = (size_t)E * H * (I / 32);
+  const size_t gu_codes = (size_t)E * I * (H / 8) * 4, gu_s = (size_t)E * I * (H / 32) * per32;
+  const size_t d_codes = (size_t)E * H * (I / 8) * 4, d_s = (size_t)E * H * (I / 32) * per32;
   const struct { const void* p; size_t n; } ins[] = {
       {x, (size_t)L * H * 2}, {topk_ids, (size_t)L * k * 4}, {topk_weights, (size_t)L * k * 4},
-      {wg, gu_codes}, {sg, gu_e}, {wu, gu_codes}, {su, gu_e}, {wd, d_codes}, {sd, d_e}, {workspace, lay.total}};
+      {wg, gu_codes}, {sg, gu_s}, {wu, gu_codes}, {su, gu_s}, {wd, d_codes}, {sd, d_s},
+      {biased ? bg : nullptr, biased ? gu_s : 0}, {biased ? bu : nullptr, biased ? gu_s : 0},
+      {biased ? bd : nullptr, biased ? d_s : 0}, {workspace, lay.total}};
   for (const auto& in : ins)
-    if (overlaps(out, out_bytes, in.p, in.n)) return MOE_Q4_ERR_ALIAS;
+    if (in.p && overlaps(out, out_bytes, in.p, in.n)) return MOE_Q4_ERR_ALIAS;
 
   const int ncu = num_cus();
   if (ncu <= 0) return MOE_Q4_ERR_LAUNCH;
@@ -237,11 +265,11 @@ int moe_swiglu_mxfp4_forward_stages(const void* x, const int32_t* topk_ids, cons
   a.x = static_cast<const uint16_t*>(x);
   a.ids = topk_ids;
   a.tw = topk_weights;
-  // the E8M0 bytes travel in the scale slots; the bias slots stay NULL
-  a.wg = wg; a.sg = reinterpret_cast<const uint16_t*>(sg);
-  a.wu = wu; a.su = reinterpret_cast<const uint16_t*>(su);
-  a.wd = wd; a.sd = reinterpret_cast<const uint16_t*>(sd);
-  a.mx = 1;
+  // FP4 formats: the scale bytes travel in the scale slots, the bias slots stay NULL
+  a.wg = wg; a.sg = static_cast<const uint16_t*>(sg); a.bg = biased ? static_cast<const uint16_t*>(bg) : nullptr;
+  a.wu = wu; a.su = static_cast<const uint16_t*>(su); a.bu = biased ? static_cast<const uint16_t*>(bu) : nullptr;
+  a.wd = wd; a.sd = static_cast<const uint16_t*>(sd); a.bd = biased ? static_cast<const uint16_t*>(bd) : nullptr;
+  a.fmt = fmt;
   a.out = out;
   a.out_f32 = out_dtype == MOE_Q4_OUT_F32;
   a.L = L; a.k = k; a.E = E; a.H = H; a.I = I;
@@ -254,6 +282,30 @@ int moe_swiglu_mxfp4_forward_stages(const void* x, const int32_t* topk_ids, cons
   a.ys = reinterpret_cast<float*>(ws + lay.ys);
   a.ys_dummy = reinterpret_cast<float*>(ws + lay.ys_dummy);
   return union_forward_launch(a, stages, ncu, stream);
+}
+
+int moe_swiglu_codec_forward(int codec, const void* x, const int32_t* topk_ids, const float* topk_weights,
+                             const uint32_t* wg, const void* sg, const void* bg, const uint32_t* wu, const void* su,
+                             const void* bu, const uint32_t* wd, const void* sd, const void* bd, int L, int k, int E,
+                             int H, int I, void* out, int out_dtype, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  return moe_swiglu_codec_forward_stages(codec, x, topk_ids, topk_weights, wg, sg, bg, wu, su, bu, wd, sd, bd, L, k,
+                                         E, H, I, out, out_dtype, workspace, workspace_bytes, MOE_Q4_STAGE_ALL,
+                                         stream);
+}
+
+size_t moe_swiglu_mxfp4_workspace_bytes(int L, int k, int E, int H, int I) {
+  return moe_swiglu_codec_workspace_bytes(MOE_Q4_CODEC_MXFP4, L, k, E, H, I);
+}
+
+int moe_swiglu_mxfp4_forward_stages(const void* x, const int32_t* topk_ids, const float* topk_weights,
+                                    const uint32_t* wg, const uint8_t* sg, const uint32_t* wu, const uint8_t* su,
+                                    const uint32_t* wd, const uint8_t* sd, int L, int k, int E, int H, int I,
+                                    void* out, int out_dtype, void* workspace, size_t workspace_bytes,
+                                    unsigned stages, hipStream_t stream) {
+  return moe_swiglu_codec_forward_stages(MOE_Q4_CODEC_MXFP4, x, topk_ids, topk_weights, wg, sg, nullptr, wu, su,
+                                         nullptr, wd, sd, nullptr, L, k, E, H, I, out, out_dtype, workspace,
+                                         workspace_bytes, stages, stream);
 }
 
 int moe_swiglu_mxfp4_forward(const void* x, const int32_t* topk_ids, const float* topk_weights, const uint32_t* wg,

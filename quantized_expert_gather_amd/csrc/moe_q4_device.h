@@ -93,6 +93,55 @@ __device__ __forceinline__ float dot32_mx_f16(const uint4 w, const uint32_t (&hv
 }
 
 // A block's partial sum times its E8M0 scale 2^(e - 127); e = 255 is NaN.
+// nvfp4: the same products split at the 16-input scale boundary; elements
+// 0..15 sit in words 0 and 1, elements 16..31 in words 2 and 3.  Returns
+// s0 * (first 16 products) + s1 * (last 16 products).
+__device__ __forceinline__ float dot32_nv_bf16(const uint4 w, const uint32_t (&av)[16], float s0, float s1) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  float d[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float& e = d[i >> 1];
+    e = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(ws[i], 1.0f, 0),
+                                        __builtin_bit_cast(bf16x2_t, av[4 * i + 0]), e, false);
+    e = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(ws[i], 1.0f, 1),
+                                        __builtin_bit_cast(bf16x2_t, av[4 * i + 1]), e, false);
+    e = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(ws[i], 1.0f, 2),
+                                        __builtin_bit_cast(bf16x2_t, av[4 * i + 2]), e, false);
+    e = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(ws[i], 1.0f, 3),
+                                        __builtin_bit_cast(bf16x2_t, av[4 * i + 3]), e, false);
+  }
+  return __builtin_fmaf(d[1], s1, d[0] * s0);
+}
+
+__device__ __forceinline__ float dot32_nv_f16(const uint4 w, const uint32_t (&hv)[16], float s0, float s1) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  float d[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float& e = d[i >> 1];
+    e = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[i], 1.0f, 0),
+                               __builtin_bit_cast(half2_t, hv[4 * i + 0]), e, false);
+    e = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[i], 1.0f, 1),
+                               __builtin_bit_cast(half2_t, hv[4 * i + 1]), e, false);
+    e = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[i], 1.0f, 2),
+                               __builtin_bit_cast(half2_t, hv[4 * i + 2]), e, false);
+    e = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[i], 1.0f, 3),
+                               __builtin_bit_cast(half2_t, hv[4 * i + 3]), e, false);
+  }
+  return __builtin_fmaf(d[1], s1, d[0] * s0);
+}
+
+// Value of an FP8 E4M3 byte (OCP: exponent bias 7, three mantissa bits,
+// exponent 0 subnormal, S.1111.111 NaN), exact in fp32: a normal number's
+// fields move into the fp32 fields; a subnormal m/8 * 2^-6 is m * 2^-9.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  const float mag = e ? __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+  const float v = (b & 0x80u) ? -mag : mag;
+  return (e == 15u && m == 7u) ? __builtin_nanf("") : v;
+}
+
 __device__ __forceinline__ float mx_scaled(float d, uint32_t e) {
   return e == 255u ? __builtin_nanf("") : __builtin_amdgcn_ldexpf(d, (int)e - 127);
 }

@@ -8,9 +8,9 @@ namespace moeq4 {
 // loads `qs` (and tokens per register pass `nt`); nullptr if not built.
 const void* gateup_kernel(int lpr, int ppl, bool full, bool qs);
 const void* down_kernel(int lpr, int ppl, bool full, bool qs, int nt);
-// the same over mxfp4 banks (E2M1 codes, one E8M0 scale per 32 inputs)
-const void* gateup_kernel_mx(int lpr, int ppl, bool full);
-const void* down_kernel_mx(int lpr, int ppl, bool full, int nt);
+// the same for the other weight formats (kFmt*; no quad-shared scale loads)
+const void* gateup_kernel_fmt(int fmt, int lpr, int ppl, bool full);
+const void* down_kernel_fmt(int fmt, int lpr, int ppl, bool full, int nt);
 
 const void* gateup_kernel_0(int lpr, int ppl, bool full, bool qs);
 const void* gateup_kernel_1(int lpr, int ppl, bool full, bool qs);
@@ -20,9 +20,17 @@ const void* down_kernel_0(int lpr, int ppl, bool full, bool qs, int nt);
 const void* down_kernel_1(int lpr, int ppl, bool full, bool qs, int nt);
 const void* down_kernel_2(int lpr, int ppl, bool full, bool qs, int nt);
 const void* down_kernel_3(int lpr, int ppl, bool full, bool qs, int nt);
-const void* gateup_kernel_mx_0(int lpr, int ppl, bool full);
-const void* gateup_kernel_mx_1(int lpr, int ppl, bool full);
-const void* down_kernel_mx_0(int lpr, int ppl, bool full, int nt);
-const void* down_kernel_mx_1(int lpr, int ppl, bool full, int nt);
+const void* gateup_kernel_mxfp4_0(int lpr, int ppl, bool full);
+const void* gateup_kernel_mxfp4_1(int lpr, int ppl, bool full);
+const void* down_kernel_mxfp4_0(int lpr, int ppl, bool full, int nt);
+const void* down_kernel_mxfp4_1(int lpr, int ppl, bool full, int nt);
+const void* gateup_kernel_nvfp4_0(int lpr, int ppl, bool full);
+const void* gateup_kernel_nvfp4_1(int lpr, int ppl, bool full);
+const void* down_kernel_nvfp4_0(int lpr, int ppl, bool full, int nt);
+const void* down_kernel_nvfp4_1(int lpr, int ppl, bool full, int nt);
+const void* gateup_kernel_affine32_0(int lpr, int ppl, bool full);
+const void* gateup_kernel_affine32_1(int lpr, int ppl, bool full);
+const void* down_kernel_affine32_0(int lpr, int ppl, bool full, int nt);
+const void* down_kernel_affine32_1(int lpr, int ppl, bool full, int nt);
 
 }  // namespace moeq4

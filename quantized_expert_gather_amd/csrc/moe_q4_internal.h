@@ -7,6 +7,14 @@
 
 namespace moeq4 {
 
+// Weight formats of the union kernels (a template parameter of each kernel).
+constexpr int kFmtAffine = 0;    // 4-bit affine, bf16 scale and bias per 64 inputs
+constexpr int kFmtMxfp4 = 1;     // FP4 E2M1, E8M0 scale per 32 inputs
+constexpr int kFmtNvfp4 = 2;     // FP4 E2M1, FP8 E4M3 scale per 16 inputs
+constexpr int kFmtAffine32 = 3;  // 4-bit affine, bf16 scale and bias per 32 inputs
+// FP4 element formats: converted in hardware into natural-order pairs, no bias
+__host__ __device__ constexpr bool fmt_fp4(int f) { return f == kFmtMxfp4 || f == kFmtNvfp4; }
+
 // Arguments of one union-path forward (device pointers; LDS offsets in bytes).
 struct UnionArgs {
   const uint16_t* x;
@@ -36,7 +44,7 @@ struct UnionArgs {
   // dynamic LDS layout of the gate/up kernel
   size_t lds_act, lds_asum, lds_union;
   int dn_slots;  // pair slots the down kernel stages in LDS at a time
-  int mx;        // banks are mxfp4 (sg/su/sd hold E8M0 bytes; bg/bu/bd unused)
+  int fmt;       // weight format (kFmt*): for the FP4 formats sg/su/sd hold scale bytes, bg/bu/bd unused
 };
 
 // Workspace layout (byte offsets from the workspace base, 256-aligned regions).

@@ -179,8 +179,8 @@ int union_forward_launch(const UnionArgs& base, unsigned stages, int num_cu, hip
     const int KU = a.H / 32;
     const int lpr = lanes_per_row(KU), ppl = positions_per_lane(KU, lpr, false);
     const size_t lds = gateup_lds_layout(a);
-    const void* fn = a.mx ? gateup_kernel_mx(lpr, ppl, lpr * ppl == KU)
-                          : gateup_kernel(lpr, ppl, lpr * ppl == KU, (a.H / 64) % 2 == 0);
+    const void* fn = a.fmt != kFmtAffine ? gateup_kernel_fmt(a.fmt, lpr, ppl, lpr * ppl == KU)
+                                         : gateup_kernel(lpr, ppl, lpr * ppl == KU, (a.H / 64) % 2 == 0);
     if (!fn || lds > kMaxLds) return MOE_Q4_ERR_UNSUPPORTED;
     const int wunits = u_max * (a.I / (gateup_rows(ppl) * (64 / lpr)));
     int grid = num_cu * blocks_per_cu(fn, kThreads, lds);
@@ -203,7 +203,8 @@ int union_forward_launch(const UnionArgs& base, unsigned stages, int num_cu, hip
     const bool qs = (a.I / 64) % 2 == 0;
     // one token per register pass when every expert has exactly one token (L = 1)
     const int nt = a.L == 1 ? 1 : 2;
-    const void* fn = a.mx ? down_kernel_mx(lpr, ppl, lpr * ppl == KU, nt) : down_kernel(lpr, ppl, lpr * ppl == KU, qs, nt);
+    const void* fn = a.fmt != kFmtAffine ? down_kernel_fmt(a.fmt, lpr, ppl, lpr * ppl == KU, nt)
+                                         : down_kernel(lpr, ppl, lpr * ppl == KU, qs, nt);
     if (!fn || lds > kMaxLds) return MOE_Q4_ERR_UNSUPPORTED;
     // one block per CU: the CU's waves share the block's converted hidden
     // vectors and its work counter
@@ -237,14 +238,28 @@ const void* down_kernel(int lpr, int ppl, bool full, bool qs, int nt) {
   return f;
 }
 
-const void* gateup_kernel_mx(int lpr, int ppl, bool full) {
-  const void* f = gateup_kernel_mx_0(lpr, ppl, full);
-  return f ? f : gateup_kernel_mx_1(lpr, ppl, full);
+const void* gateup_kernel_fmt(int fmt, int lpr, int ppl, bool full) {
+  const void* f = nullptr;
+  switch (fmt) {
+    case kFmtMxfp4: f = gateup_kernel_mxfp4_0(lpr, ppl, full); return f ? f : gateup_kernel_mxfp4_1(lpr, ppl, full);
+    case kFmtNvfp4: f = gateup_kernel_nvfp4_0(lpr, ppl, full); return f ? f : gateup_kernel_nvfp4_1(lpr, ppl, full);
+    case kFmtAffine32:
+      f = gateup_kernel_affine32_0(lpr, ppl, full);
+      return f ? f : gateup_kernel_affine32_1(lpr, ppl, full);
+  }
+  return nullptr;
 }
 
-const void* down_kernel_mx(int lpr, int ppl, bool full, int nt) {
-  const void* f = down_kernel_mx_0(lpr, ppl, full, nt);
-  return f ? f : down_kernel_mx_1(lpr, ppl, full, nt);
+const void* down_kernel_fmt(int fmt, int lpr, int ppl, bool full, int nt) {
+  const void* f = nullptr;
+  switch (fmt) {
+    case kFmtMxfp4: f = down_kernel_mxfp4_0(lpr, ppl, full, nt); return f ? f : down_kernel_mxfp4_1(lpr, ppl, full, nt);
+    case kFmtNvfp4: f = down_kernel_nvfp4_0(lpr, ppl, full, nt); return f ? f : down_kernel_nvfp4_1(lpr, ppl, full, nt);
+    case kFmtAffine32:
+      f = down_kernel_affine32_0(lpr, ppl, full, nt);
+      return f ? f : down_kernel_affine32_1(lpr, ppl, full, nt);
+  }
+  return nullptr;
 }
 
 }  // namespace moeq4

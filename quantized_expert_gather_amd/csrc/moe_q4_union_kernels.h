@@ -161,15 +161,18 @@ struct GuOffsets {
 // Loads unit `un` (or nothing, with zero-range descriptors, when !valid).
 // Loads the unit whose first row is row0 (plain loads from a wave-uniform
 // row base plus per-lane offsets).
-template <int PPL, int RG, bool FULL, bool QS, bool MX = false>
+template <int PPL, int RG, bool FULL, bool QS, int FMT = kFmtAffine>
 __device__ __forceinline__ void gu_load(const UnionArgs& a, size_t row0, int nrows, int KU, int KG, int li, int lpr,
                                         const unsigned char* lane_sbase, const GuOffsets<PPL, RG>& o,
                                         GuFrag<PPL, RG>& f) {
-  if constexpr (MX) {  // mxfp4: one scale byte per (row, 32-input position) of gate and of up
+  if constexpr (fmt_fp4(FMT)) {
+    // scale bytes per (row, 32-input position): one E8M0 (mxfp4) or two E4M3
+    // (nvfp4) for gate and as many for up, packed gate low, up high
+    constexpr int SB = FMT == kFmtNvfp4 ? 2 : 1;
     const unsigned char* wg = reinterpret_cast<const unsigned char*>(a.wg) + row0 * KU * 16;
     const unsigned char* wu = reinterpret_cast<const unsigned char*>(a.wu) + row0 * KU * 16;
-    const unsigned char* eg = reinterpret_cast<const unsigned char*>(a.sg) + row0 * KU;
-    const unsigned char* eu = reinterpret_cast<const unsigned char*>(a.su) + row0 * KU;
+    const unsigned char* eg = reinterpret_cast<const unsigned char*>(a.sg) + row0 * KU * SB;
+    const unsigned char* eu = reinterpret_cast<const unsigned char*>(a.su) + row0 * KU * SB;
 #pragma unroll
     for (int p = 0; p < PPL; ++p) {
       if (FULL || li + lpr * p < KU) {
@@ -177,7 +180,11 @@ __device__ __forceinline__ void gu_load(const UnionArgs& a, size_t row0, int nro
         for (int r = 0; r < RG; ++r) {
           f.w[p][r][0] = *reinterpret_cast<const uint4*>(wg + o.w[p][r]);
           f.w[p][r][1] = *reinterpret_cast<const uint4*>(wu + o.w[p][r]);
-          f.sb[p][r][0] = (uint32_t)eg[o.s[p][r]] | ((uint32_t)eu[o.s[p][r]] << 8);
+          if constexpr (FMT == kFmtNvfp4)
+            f.sb[p][r][0] = (uint32_t)*reinterpret_cast<const uint16_t*>(eg + o.s[p][r]) |
+                            ((uint32_t)*reinterpret_cast<const uint16_t*>(eu + o.s[p][r]) << 16);
+          else
+            f.sb[p][r][0] = (uint32_t)eg[o.s[p][r]] | ((uint32_t)eu[o.s[p][r]] << 8);
         }
       }
     }
@@ -213,7 +220,7 @@ __device__ __forceinline__ void gu_load(const UnionArgs& a, size_t row0, int nro
 // One unit: gate and up of RG hidden rows of one distinct expert for every
 // token routed to it, one token at a time (the unit's weights stay in
 // registers); h = silu(gate) * up goes to hbuf[(slot0 + token rank) * I + row].
-template <int LPR, int PPL, int RG, bool FULL, bool QS, bool MX = false>
+template <int LPR, int PPL, int RG, bool FULL, bool QS, int FMT = kFmtAffine>
 __device__ __forceinline__ void gu_compute(const UnionArgs& a, const GuFrag<PPL, RG>& f, uint32_t mask, int slot0,
                                            int row, int li, int KU, const uint4* act, const float* asum,
                                            uint32_t sel) {
@@ -224,14 +231,19 @@ __device__ __forceinline__ void gu_compute(const UnionArgs& a, const GuFrag<PPL,
       touch(f.w[p][r][0]);
       touch(f.w[p][r][1]);
       touch(f.sb[p][r][0]);
-      if (!QS && !MX) touch(f.sb[p][r][1]);
+      if (!QS && !fmt_fp4(FMT)) touch(f.sb[p][r][1]);
     }
   uint32_t sbv[PPL][RG][2];
+  float nvs[PPL][RG][4];  // nvfp4: decoded scales (gate lo, gate hi, up lo, up hi)
 #pragma unroll
   for (int p = 0; p < PPL; ++p)
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
-      if (MX) {
+      if (FMT == kFmtNvfp4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) nvs[p][r][q] = e4m3_to_f32((f.sb[p][r][0] >> (8 * q)) & 0xFFu);
+        sbv[p][r][0] = sbv[p][r][1] = 0u;
+      } else if (FMT == kFmtMxfp4) {
         sbv[p][r][0] = f.sb[p][r][0] & 0xFFu;         // E8M0 byte of gate
         sbv[p][r][1] = (f.sb[p][r][0] >> 8) & 0xFFu;  // and of up
       } else if (QS) {
@@ -255,12 +267,18 @@ __device__ __forceinline__ void gu_compute(const UnionArgs& a, const GuFrag<PPL,
         const uint4 x0 = xa[0], x1 = xa[KU], x2 = xa[2 * KU], x3 = xa[3 * KU];
         const uint32_t xv[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
                                  x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
-        if constexpr (MX) {  // x staged in natural element order
+        if constexpr (FMT == kFmtMxfp4) {  // x staged in natural element order
 #pragma unroll
           for (int r = 0; r < RG; ++r)
 #pragma unroll
             for (int mm = 0; mm < 2; ++mm)
               acc[r][mm] += mx_scaled(dot32_mx_bf16(f.w[p][r][mm], xv, 0.0f), sbv[p][r][mm]);
+        } else if constexpr (FMT == kFmtNvfp4) {
+#pragma unroll
+          for (int r = 0; r < RG; ++r)
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm)
+              acc[r][mm] += dot32_nv_bf16(f.w[p][r][mm], xv, nvs[p][r][2 * mm], nvs[p][r][2 * mm + 1]);
         } else {
           const float xs = asum[(size_t)t * KU + j];
 #pragma unroll
@@ -355,7 +373,7 @@ __device__ inline void write_union_tables(const UnionArgs& a, const UnionLds& s,
   }
 }
 
-template <int LPR, int PPL, bool FULL, bool QS, bool MX = false>
+template <int LPR, int PPL, bool FULL, bool QS, int FMT = kFmtAffine>
 __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
   constexpr int G = 64 / LPR;           // lane groups per wave
   constexpr int RG = gateup_rows(PPL);
@@ -363,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int H = a.H, I = a.I, k = a.k, L = a.L, E = a.E;
   const int P = L * k;
-  const int KU = H >> 5, KG = H >> 6;
+  const int KU = H >> 5, KG = FMT == kFmtAffine32 ? KU : H >> 6;  // positions, affine groups
   uint4* act = reinterpret_cast<uint4*>(smem + a.lds_act);      // [L][4][KU] bf16 pairs in code order
   float* asum = reinterpret_cast<float*>(smem + a.lds_asum);     // [L][KU] sums of the 32 inputs
   UnionLds s;
@@ -395,11 +413,11 @@ __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
           float sum = 0.0f;
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            if (!MX) sum = sum8_bf16(v[b][c], sum);
-            // mxfp4 codes convert to pairs in natural element order
-            act[((size_t)t * 4 + c) * KU + j] = MX ? v[b][c] : pair_activations(v[b][c]);
+            if (!fmt_fp4(FMT)) sum = sum8_bf16(v[b][c], sum);
+            // FP4 codes convert to pairs in natural element order
+            act[((size_t)t * 4 + c) * KU + j] = fmt_fp4(FMT) ? v[b][c] : pair_activations(v[b][c]);
           }
-          if (!MX) asum[(size_t)t * KU + j] = sum;
+          if (!fmt_fp4(FMT)) asum[(size_t)t * KU + j] = sum;
         }
       }
     }
@@ -421,8 +439,9 @@ __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
     for (int r = 0; r < RG; ++r) {
       const int j = li + LPR * p;
       o.w[p][r] = (uint32_t)(((g * RG + r) * KU + j) * 16);
-      const int grp = QS ? 2 * (li >> 2) + (LPR / 2) * p : (j >> 1);
-      o.s[p][r] = MX ? (uint32_t)((g * RG + r) * KU + j) : (uint32_t)(((g * RG + r) * KG + grp) * 2);
+      const int grp = QS ? 2 * (li >> 2) + (LPR / 2) * p : FMT == kFmtAffine32 ? j : (j >> 1);
+      o.s[p][r] = fmt_fp4(FMT) ? (uint32_t)(((g * RG + r) * KU + j) * (FMT == kFmtNvfp4 ? 2 : 1))
+                               : (uint32_t)(((g * RG + r) * KG + grp) * 2);
     }
   // Work units: (distinct expert, WROWS hidden rows).  Block b owns units
   // b, b + nblk, b + 2 nblk, ... (adjacent blocks take adjacent rows, so the
@@ -442,13 +461,13 @@ __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
     auto load = [&](int j, GuFrag<PPL, RG>& f) {
       const int un = b + min(j, nub - 1) * nblk;
       const int i = un / upe;
-      gu_load<PPL, RG, FULL, QS, MX>(a, (size_t)wave_uniform(s.uniq[i]) * I + (un - i * upe) * WROWS, WROWS, KU, KG,
+      gu_load<PPL, RG, FULL, QS, FMT>(a, (size_t)wave_uniform(s.uniq[i]) * I + (un - i * upe) * WROWS, WROWS, KU, KG,
                                      li, LPR, lane_sbase, o, f);
     };
     auto compute = [&](int j, const GuFrag<PPL, RG>& f) {
       const int un = b + j * nblk;
       const int i = un / upe;
-      gu_compute<LPR, PPL, RG, FULL, QS, MX>(a, f, wave_uniform((int)s.mask[i]), wave_uniform(s.off[i]),
+      gu_compute<LPR, PPL, RG, FULL, QS, FMT>(a, f, wave_uniform((int)s.mask[i]), wave_uniform(s.off[i]),
                                          (un - i * upe) * WROWS + g * RG, li, KU, act, asum, sel);
     };
     auto grab = [&]() {
@@ -501,22 +520,23 @@ struct DnOffsets {
   uint32_t s[RS][PPL];
 };
 
-template <int PPL, int RS, bool FULL, bool QS, bool MX = false>
+template <int PPL, int RS, bool FULL, bool QS, int FMT = kFmtAffine>
 __device__ __forceinline__ void dn_load(const UnionArgs& a, size_t row0, bool valid, size_t row_fallback, int nrows,
                                         int KU, int KG, int li, int lpr, const unsigned char* lane_sbase,
                                         const DnOffsets<PPL, RS>& o, DnFrag<PPL, RS>& f) {
-  if constexpr (MX) {  // mxfp4: one scale byte per (row, 32-input position)
+  if constexpr (fmt_fp4(FMT)) {  // one E8M0 (mxfp4) or two E4M3 (nvfp4) bytes per (row, position)
+    constexpr int SB = FMT == kFmtNvfp4 ? 2 : 1;
     const rsrc_t wd = make_rsrc(reinterpret_cast<const unsigned char*>(a.wd) + row0 * KU * 16,
                                 valid ? (uint32_t)(nrows * KU * 16) : 0u);
-    const rsrc_t ed = make_rsrc(reinterpret_cast<const unsigned char*>(a.sd) + (valid ? row0 : row_fallback) * KU,
-                                valid ? (uint32_t)(nrows * KU) : 0u);
+    const rsrc_t ed = make_rsrc(reinterpret_cast<const unsigned char*>(a.sd) + (valid ? row0 : row_fallback) * KU * SB,
+                                valid ? (uint32_t)(nrows * KU * SB) : 0u);
 #pragma unroll
     for (int r = 0; r < RS; ++r)
 #pragma unroll
       for (int p = 0; p < PPL; ++p)
         if (FULL || li + lpr * p < KU) {
           f.w[r][p] = bld16(wd, o.w[r][p]);
-          f.sb[r][p] = bld1(ed, o.s[r][p]);
+          f.sb[r][p] = SB == 2 ? bld2(ed, o.s[r][p]) : bld1(ed, o.s[r][p]);
         }
     (void)KG; (void)lane_sbase;
     return;
@@ -626,7 +646,7 @@ __device__ __forceinline__ void down_stage_slot(const UnionArgs& a, int ls, int 
 // each token's RS row totals, times its router weight (and 2^-k), go to its
 // ys row in one store (every lane stores its residue's row; token slots past
 // the expert's count write to the sink).
-template <int LPR, int PPL, int RS, int NT, bool FULL, bool QS, bool MX = false>
+template <int LPR, int PPL, int RS, int NT, bool FULL, bool QS, int FMT = kFmtAffine>
 __device__ __forceinline__ void dn_step(const UnionArgs& a, const DnFrag<PPL, RS>& f, const uint32_t (&hv)[NT][PPL][16],
                                        const float (&hs)[NT][PPL], const float (&tw)[NT], float* const (&dst)[NT],
                                        int row0, int li, int KU, uint32_t sel) {
@@ -635,7 +655,7 @@ __device__ __forceinline__ void dn_step(const UnionArgs& a, const DnFrag<PPL, RS
 #pragma unroll
     for (int p = 0; p < PPL; ++p) {
       touch(f.w[r][p]);
-      if (MX || !QS || (r & 1) == 0) touch(f.sb[r][p]);
+      if (fmt_fp4(FMT) || !QS || (r & 1) == 0) touch(f.sb[r][p]);
     }
   float acc[NT][RS];
 #pragma unroll
@@ -647,9 +667,13 @@ __device__ __forceinline__ void dn_step(const UnionArgs& a, const DnFrag<PPL, RS
 #pragma unroll
     for (int p = 0; p < PPL; ++p) {
       if (FULL || li + LPR * p < KU) {
-        if constexpr (MX) {  // hidden vectors staged as fp16 pairs in natural order
+        if constexpr (FMT == kFmtMxfp4) {  // hidden vectors staged as fp16 pairs in natural order
 #pragma unroll
           for (int c = 0; c < NT; ++c) acc[c][r] += mx_scaled(dot32_mx_f16(f.w[r][p], hv[c][p], 0.0f), f.sb[r][p]);
+        } else if constexpr (FMT == kFmtNvfp4) {
+          const float s0 = e4m3_to_f32(f.sb[r][p] & 0xFFu), s1 = e4m3_to_f32((f.sb[r][p] >> 8) & 0xFFu);
+#pragma unroll
+          for (int c = 0; c < NT; ++c) acc[c][r] += dot32_nv_f16(f.w[r][p], hv[c][p], s0, s1);
         } else {
           uint32_t sb;
           if (QS)
@@ -675,7 +699,7 @@ __device__ __forceinline__ void dn_step(const UnionArgs& a, const DnFrag<PPL, RS
 // One (expert, token chunk) segment of a down wave: read the chunk's
 // converted hidden vectors from LDS, then stream the unit's row steps gj ..
 // gj + klast through a ring of three register fragments (two in flight).
-template <int LPR, int PPL, bool FULL, bool QS, int NT, int RS, int WSTEP, bool MX = false>
+template <int LPR, int PPL, bool FULL, bool QS, int NT, int RS, int WSTEP, int FMT = kFmtAffine>
 __device__ __forceinline__ void dn_segment(const UnionArgs& a, size_t ebase, int ls0, int nt, int gj, int klast,
                                            int li, int g, int KU, int KG, int H, const unsigned char* lane_sbase,
                                            const DnOffsets<PPL, RS>& o, uint32_t sel, const uint4* hvs,
@@ -684,7 +708,7 @@ __device__ __forceinline__ void dn_segment(const UnionArgs& a, size_t ebase, int
   auto load = [&](int kk, DnFrag<PPL, RS>& fr) {
     const bool valid = kk <= klast;
     const size_t row0 = ebase + (size_t)(gj + min(kk, klast)) * WSTEP;
-    dn_load<PPL, RS, FULL, QS, MX>(a, row0, valid, row0, WSTEP, KU, KG, li, LPR, lane_sbase, o, fr);
+    dn_load<PPL, RS, FULL, QS, FMT>(a, row0, valid, row0, WSTEP, KU, KG, li, LPR, lane_sbase, o, fr);
   };
   DnFrag<PPL, RS> f0, f1, f2;
   load(0, f0);
@@ -720,7 +744,7 @@ __device__ __forceinline__ void dn_segment(const UnionArgs& a, size_t ebase, int
   }
 
   auto step = [&](int kk, const DnFrag<PPL, RS>& fr) {
-    dn_step<LPR, PPL, RS, NT, FULL, QS, MX>(a, fr, hv, hs, tw, dst, (gj + kk) * WSTEP + g * RS, li, KU, sel);
+    dn_step<LPR, PPL, RS, NT, FULL, QS, FMT>(a, fr, hv, hs, tw, dst, (gj + kk) * WSTEP + g * RS, li, KU, sel);
   };
 #pragma unroll 1
   for (int kk = 0;; kk += 3) {
@@ -749,7 +773,7 @@ constexpr int kDownUnitSteps = 4;  // row steps per down work unit
 // once).  Its waves take the units from an LDS counter (the first unit of
 // each wave fixed), so waves that get fewer issue slots do less of the
 // block's share.  A unit runs every token of its expert, NT at a time.
-template <int LPR, int PPL, bool FULL, bool QS, int NT, bool MX = false>
+template <int LPR, int PPL, bool FULL, bool QS, int NT, int FMT = kFmtAffine>
 __global__ __launch_bounds__(down_threads(NT)) void k_down(UnionArgs a) {
   constexpr int G = 64 / LPR;
   constexpr int RS = down_rows(G);  // a wave step covers G * RS rows
@@ -758,7 +782,7 @@ __global__ __launch_bounds__(down_threads(NT)) void k_down(UnionArgs a) {
   static_assert(!QS || RS % 2 == 0, "quad-shared scales pair rows");
   extern __shared__ __align__(16) unsigned char smem[];
   const int H = a.H, I = a.I, P = a.L * a.k;
-  const int KU = I >> 5, KG = I >> 6;
+  const int KU = I >> 5, KG = FMT == kFmtAffine32 ? KU : I >> 6;  // positions, affine groups
   const int SM = a.dn_slots;  // pair slots converted at a time
   int4* utab = reinterpret_cast<int4*>(smem);
   int* wpre = reinterpret_cast<int*>(smem + down_lds_base(P));     // [P + 1] work prefix per expert
@@ -828,8 +852,9 @@ __global__ __launch_bounds__(down_threads(NT)) void k_down(UnionArgs a) {
       const int j = li + LPR * p;
       o.w[r][p] = (uint32_t)(((g * RS + r) * KU + j) * 16);
       const int srow = QS ? (r & ~1) + (qa >> 1) : r;
-      const int grp = QS ? 2 * (li >> 2) + (LPR / 2) * p : (j >> 1);
-      o.s[r][p] = MX ? (uint32_t)((g * RS + r) * KU + j) : (uint32_t)(((g * RS + srow) * KG + grp) * 2);
+      const int grp = QS ? 2 * (li >> 2) + (LPR / 2) * p : FMT == kFmtAffine32 ? j : (j >> 1);
+      o.s[r][p] = fmt_fp4(FMT) ? (uint32_t)(((g * RS + r) * KU + j) * (FMT == kFmtNvfp4 ? 2 : 1))
+                               : (uint32_t)(((g * RS + srow) * KG + grp) * 2);
     }
   auto grab = [&]() {
     int v = 0;
@@ -843,7 +868,7 @@ __global__ __launch_bounds__(down_threads(NT)) void k_down(UnionArgs a) {
   for (int c0 = s_lo; c0 < s_hi; c0 += SM) {
     const int c1 = min(s_hi, c0 + SM);
     if (tid == 0) unit_q = NW;
-    for (int sl = c0 + wave; sl < c1; sl += NW) down_stage_slot(a, sl - c0, sl, KU, hvs, hss, stw, sdst, MX);
+    for (int sl = c0 + wave; sl < c1; sl += NW) down_stage_slot(a, sl - c0, sl, KU, hvs, hss, stw, sdst, fmt_fp4(FMT));
     __syncthreads();
     for (int j = wave; j < nub; j = grab()) {
       const int un = ub + j;
@@ -857,10 +882,10 @@ __global__ __launch_bounds__(down_threads(NT)) void k_down(UnionArgs a) {
       for (int t0 = t_lo; t0 < t_hi; t0 += NT) {
         const int nt = min(NT, t_hi - t0);
         if (NT > 1 && nt == 1)
-          dn_segment<LPR, PPL, FULL, QS, 1, RS, WSTEP, MX>(a, ebase, t0 - c0, 1, gj, klast, li, g, KU, KG, H,
+          dn_segment<LPR, PPL, FULL, QS, 1, RS, WSTEP, FMT>(a, ebase, t0 - c0, 1, gj, klast, li, g, KU, KG, H,
                                                            lane_sbase, o, sel, hvs, hss, stw, sdst);
         else
-          dn_segment<LPR, PPL, FULL, QS, NT, RS, WSTEP, MX>(a, ebase, t0 - c0, nt, gj, klast, li, g, KU, KG, H,
+          dn_segment<LPR, PPL, FULL, QS, NT, RS, WSTEP, FMT>(a, ebase, t0 - c0, nt, gj, klast, li, g, KU, KG, H,
                                                             lane_sbase, o, sel, hvs, hss, stw, sdst);
       }
     }

@@ -256,3 +256,45 @@ def test_mx_host_checks():
     assert call_mx(out=fake(0)) == q.MOE_Q4_ERR_ALIAS
     assert call_mx(out=fake(8) + 64) == q.MOE_Q4_ERR_ALIAS   # inside sd
     assert call_mx(out=fake(14) + 256) == q.MOE_Q4_ERR_ALIAS
+
+
+def call_codec(codec, L=2, k=2, E=8, H=256, I=128, out_dtype=0, ws_bytes=1 << 30, stages=3, ptrs=None, ws=None,
+               out=None):
+    p = [fake(i) for i in range(12)] if ptrs is None else ptrs
+    return q.lib().moe_swiglu_codec_forward_stages(codec, *p, L, k, E, H, I, fake(13) if out is None else out,
+                                                  out_dtype, fake(14) if ws is None else ws, ws_bytes, stages, None)
+
+
+def test_codec_host_checks():
+    A32, MX, NV, A64 = q.MOE_Q4_CODEC_AFFINE4_G32, q.MOE_Q4_CODEC_MXFP4, q.MOE_Q4_CODEC_NVFP4, \
+        q.MOE_Q4_CODEC_AFFINE4_G64
+    assert call_codec(7) == q.MOE_Q4_ERR_UNSUPPORTED
+    assert q.moe_swiglu_codec_workspace_bytes(7, 2, 2, 8, 256, 128) == 0
+    for c in (A32, MX, NV):
+        assert call_codec(c, L=0) == q.MOE_Q4_OK
+        assert call_codec(c, H=240) == q.MOE_Q4_ERR_UNSUPPORTED
+        assert call_codec(c, L=33) == q.MOE_Q4_ERR_UNSUPPORTED
+        assert call_codec(c, k=9) == q.MOE_Q4_ERR_SHAPE
+        assert call_codec(c, ws_bytes=64) == q.MOE_Q4_ERR_WORKSPACE
+        assert q.moe_swiglu_codec_workspace_bytes(c, 2, 2, 4, 96, 256) > 0
+        assert q.moe_swiglu_codec_workspace_bytes(c, 8, 8, 256, 6144, 2048) == \
+            q.moe_swiglu_q4_workspace_bytes(8, 8, 256, 6144, 2048)
+    # codec 0 is moe_swiglu_q4_forward itself (H multiple of 64, sorted path above 32 tokens)
+    assert q.moe_swiglu_codec_workspace_bytes(A64, 64, 8, 256, 4096, 2048) == \
+        q.moe_swiglu_q4_workspace_bytes(64, 8, 256, 4096, 2048) > 0
+    assert call_codec(A64, H=96) == q.MOE_Q4_ERR_UNSUPPORTED
+    # biases: required for affine group 32, ignored by the FP4 codecs
+    for i in (5, 8, 11):
+        p = [fake(j) for j in range(12)]
+        p[i] = 0
+        assert call_codec(A32, ptrs=p) == q.MOE_Q4_ERR_NULL, i
+        assert call_codec(NV, ptrs=p, ws=0) == q.MOE_Q4_ERR_WORKSPACE, i
+    # scale alignment: 2 bytes for affine group 32 and nvfp4, none for mxfp4
+    for c, want in ((A32, q.MOE_Q4_ERR_ALIGN), (NV, q.MOE_Q4_ERR_ALIGN), (MX, q.MOE_Q4_ERR_WORKSPACE)):
+        p = [fake(j) for j in range(12)]
+        p[7] += 1
+        assert call_codec(c, ptrs=p, ws=0 if want != q.MOE_Q4_ERR_ALIGN else None) == want, c
+    # out inside a bias array aliases for affine group 32 only
+    assert call_codec(A32, out=fake(5) + 64) == q.MOE_Q4_ERR_ALIAS
+    assert call_codec(NV, out=fake(5) + 64, ws=0) == q.MOE_Q4_ERR_WORKSPACE
+    assert call_codec(NV, out=fake(10) + 64) == q.MOE_Q4_ERR_ALIAS
