@@ -21,8 +21,9 @@ adjacent-token overlap follows the measured depth-graded profile.
   chain first, so the events time the GPU, not Python.  Per-kernel durations
   come from chains of one stage alone (gate+up, or down+combine) over the
   same layers, timed the same way.
-* mxfp4: the same verify layers (routes, activations) over mxfp4 gs32 banks
-  (the pages' GLM-5.2 format), per L, with mxfp4 bytes per expert.
+* codecs: the same verify routes and activations over banks in other codecs
+  (mxfp4 gs32, the pages' GLM-5.2 format; nvfp4; 4-bit affine group 32),
+  at L = 1, 2, 4, 8, each with its own bytes per expert.
 * cpu_baseline: the CPU oracle (test infrastructure) timed on a bounded
   sample of the same layers on the host cores, with the same metric; the
   same layers are checked for parity (fp32 output before the bf16 cast,
@@ -144,41 +145,43 @@ def bench_sorted(args, Ts, q, synth, torch, np, dev, stream, sleep_cycles_for):
     return out
 
 
-def expert_bytes_mx(H: int, I: int) -> int:
-    """Bytes of one mxfp4 gs32 expert: 4-bit codes plus one E8M0 byte per 32
-    inputs, for gate, up and down (about 20 MB at H=6144, I=2048, the size the
-    mlx discussion "Small-L fused expert gather for fine-grained MoE decode"
-    gives for the GLM-5.2 experts)."""
-    return 3 * (H * I // 2 + H * I // 32)
+def expert_bytes_codec(codec: str, H: int, I: int) -> int:
+    """Bytes of one expert's gate, up and down in ``codec``: 4-bit codes plus
+    the scales (and biases) of each group -- mxfp4: one byte per 32 inputs
+    (about 20 MB at H=6144, I=2048, the size the mlx discussion "Small-L fused
+    expert gather for fine-grained MoE decode" gives for the GLM-5.2 experts);
+    nvfp4: one byte per 16; affine group 32: a bf16 scale and bias per 32."""
+    per = {"mxfp4": 1 / 32, "nvfp4": 1 / 16, "affine4_g32": 4 / 32}[codec]
+    return 3 * (H * I // 2 + round(H * I * per))
 
 
-def bench_mx(args, Ls, q, synth, torch, np, dev, stream, sleep_cycles_for):
-    """The verify workload over mxfp4 gs32 banks: chains of layers spread over
-    the depth profile (so over the overlap range), full forward and gate+up
-    alone, per L."""
+def bench_codec(codec, args, Ls, q, synth, torch, np, dev, stream, sleep_cycles_for):
+    """The verify workload over banks in another codec: chains of layers
+    spread over the depth profile (so over the overlap range), full forward
+    and gate+up alone, per L."""
     w = synth.WORKLOADS["verify"]
     H, I, E, k = w.H, w.I, w.E, w.k
-    eb = expert_bytes_mx(H, I)
-    gub = 2 * (H * I // 2 + H * I // 32)
-    layer_ids = sorted(set(np.linspace(0, w.n_layers - 1, args.mx_layers).round().astype(int).tolist()))
-    out = {"workload": f"{w.name} in mxfp4 gs32 (E2M1 + E8M0 per 32), overlap chain of {len(layer_ids)} layers "
-                       f"spread over the {w.n_layers}-layer depth profile",
-           "bytes_per_expert": eb, "per_L": {}}
+    code = q.CODECS[codec][0]
+    eb = expert_bytes_codec(codec, H, I)
+    gub = 2 * eb // 3
+    layer_ids = sorted(set(np.linspace(0, w.n_layers - 1, args.codec_layers).round().astype(int).tolist()))
+    out = {"workload": f"{w.name} in {codec}, overlap chain of {len(layer_ids)} layers spread over the "
+                       f"{w.n_layers}-layer depth profile", "bytes_per_expert": eb, "per_L": {}}
     tot_b, tot_ms = 0.0, 0.0
     for L in Ls:
         layers = []
         for layer in layer_ids:
-            lay = synth.make_chain_layer_mx(w, L, layer, seed=0, device=dev)
+            lay = synth.make_chain_layer_q(codec, w, L, layer, seed=0, device=dev)
             ids = torch.from_numpy(lay.ids).to(dev)
             tw = torch.from_numpy(lay.weights).to(dev)
             o = torch.empty((L, H), dtype=torch.bfloat16, device=dev)
-            ws = torch.empty(max(256, q.moe_swiglu_mxfp4_workspace_bytes(L, k, E, H, I)), dtype=torch.uint8,
+            ws = torch.empty(max(256, q.moe_swiglu_codec_workspace_bytes(code, L, k, E, H, I)), dtype=torch.uint8,
                              device=dev)
             bt = lay.bank.tensors()
             layers.append({"u": int(lay.bank.E), "keep": (lay, ids, tw, o, ws),
-                           "calls": {st: q.PreparedForwardMX(lay.x, ids, tw, bt, o, ws, code, stream)
-                                     for st, code in (("all", q.MOE_Q4_STAGE_ALL),
-                                                      ("gateup", q.MOE_Q4_STAGE_GATEUP))}})
+                           "calls": {st: q.PreparedForwardCodec(codec, lay.x, ids, tw, bt, o, ws, sc, stream)
+                                     for st, sc in (("all", q.MOE_Q4_STAGE_ALL),
+                                                    ("gateup", q.MOE_Q4_STAGE_GATEUP))}})
         torch.cuda.synchronize()
 
         def chain(which, delay):
@@ -209,7 +212,7 @@ def bench_mx(args, Ls, q, synth, torch, np, dev, stream, sleep_cycles_for):
         if L in METRIC_LS:
             tot_b += u_mean * eb
             tot_ms += med["all"]
-        log(f"mxfp4 L={L}: {med['all'] * 1e3:.2f} us/layer, {gb:.0f} GB/s effective; gate+up {gu_gb:.0f} GB/s")
+        log(f"{codec} L={L}: {med['all'] * 1e3:.2f} us/layer, {gb:.0f} GB/s effective; gate+up {gu_gb:.0f} GB/s")
         del layers
         torch.cuda.empty_cache()
     if tot_ms > 0:
@@ -260,8 +263,10 @@ def main():
     ap.add_argument("--pair-layers", type=int, default=20,
                     help="layers of each chain timed again as a per-pair baseline (one call per token, so "
                          "an expert shared by tokens is streamed once per token); 0 to skip")
-    ap.add_argument("--mx-layers", type=int, default=19,
-                    help="layers per L of the mxfp4 verify chains (spread over the depth profile); 0 to skip")
+    ap.add_argument("--codecs", default="mxfp4,nvfp4,affine4_g32",
+                    help="other weight codecs timed on the verify workload (comma list; empty to skip)")
+    ap.add_argument("--codec-layers", type=int, default=19,
+                    help="layers per L of each codec's verify chains (spread over the depth profile)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the baseline sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -502,9 +507,12 @@ def main():
         result["sorted_path"] = bench_sorted(args, sorted_Ts, q, synth, torch, np, dev, stream,
                                              lambda ms: sleep_cycles_for(ms))
 
-    # ---- the same verify workload over mxfp4 banks ----
-    if args.mx_layers > 0:
-        result["mxfp4"] = bench_mx(args, Ls, q, synth, torch, np, dev, stream, lambda ms: sleep_cycles_for(ms))
+    # ---- the same verify workload over banks in other codecs ----
+    codecs = [c for c in args.codecs.split(",") if c.strip()]
+    if codecs and args.codec_layers > 0:
+        cLs = [v for v in Ls if v in METRIC_LS] or Ls
+        result["codecs"] = {c: bench_codec(c, args, cLs, q, synth, torch, np, dev, stream,
+                                           lambda ms: sleep_cycles_for(ms)) for c in codecs}
 
     # ---- CPU oracle baseline on a bounded sample, and parity of the same layers ----
     if not args.no_cpu:
