@@ -201,15 +201,17 @@ int union_forward_launch(const UnionArgs& base, unsigned stages, int num_cu, hip
     a.dn_slots = (int)std::min<size_t>((size_t)P, (kMaxLds - 256 - base_lds) / down_slot_bytes(KU));
     const size_t lds = base_lds + (size_t)a.dn_slots * down_slot_bytes(KU);
     const bool qs = (a.I / 64) % 2 == 0;
-    // one token per register pass when every expert has exactly one token (L = 1)
-    const int nt = a.L == 1 ? 1 : 2;
+    // one token per register pass when every expert has exactly one token
+    // (L = 1), or when a lane holds several positions per row (a second
+    // token's hidden vectors would not fit in the registers beside the ring)
+    const int nt = (a.L == 1 || ppl >= 2) ? 1 : 2;
     const void* fn = a.fmt != kFmtAffine ? down_kernel_fmt(a.fmt, lpr, ppl, lpr * ppl == KU, nt)
                                          : down_kernel(lpr, ppl, lpr * ppl == KU, qs, nt);
     if (!fn || lds > kMaxLds) return MOE_Q4_ERR_UNSUPPORTED;
     // one block per CU: the CU's waves share the block's converted hidden
     // vectors and its work counter
     hipLaunchKernelGGL(reinterpret_cast<void (*)(UnionArgs)>(const_cast<void*>(fn)), dim3(num_cu),
-                       dim3(down_threads(nt)), lds, stream, a);
+                       dim3(down_threads(nt, ppl)), lds, stream, a);
     if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;
     dim3 cgrid((a.H / 4 + 255) / 256, a.L);
     hipLaunchKernelGGL(k_combine, cgrid, dim3(256), 0, stream, a);

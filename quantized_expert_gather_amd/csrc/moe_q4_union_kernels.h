@@ -109,6 +109,20 @@ __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_rea
 __device__ __forceinline__ void touch(const uint4& v) { asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w)); }
 __device__ __forceinline__ void touch(uint32_t v) { asm volatile("" ::"v"(v)); }
 
+// A copy of a weight fragment that the compiler cannot see through: the
+// values derived from it (unpacked codes, converted pairs) are recomputed at
+// each use instead of being kept live across a token loop.  With many
+// positions per lane those derived values would take more registers than
+// the load ring itself and spill.
+template <bool OPAQUE>
+__device__ __forceinline__ uint4 opaque(uint4 v) {
+  if constexpr (OPAQUE) asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+  return v;
+}
+// positions per lane from which the gate/up kernel recomputes unpacked codes
+// per token rather than keep them
+constexpr int kGuOpaquePpl = 4;
+
 // D = sum over the 32 inputs of one 16-byte load of a_c * (M + q_c), with the
 // activations a as 16 packed pairs in code order; M = 128 (bf16 pairs) or
 // 1024 (fp16 pairs).
@@ -272,20 +286,22 @@ __device__ __forceinline__ void gu_compute(const UnionArgs& a, const GuFrag<PPL,
           for (int r = 0; r < RG; ++r)
 #pragma unroll
             for (int mm = 0; mm < 2; ++mm)
-              acc[r][mm] += mx_scaled(dot32_mx_bf16(f.w[p][r][mm], xv, 0.0f), sbv[p][r][mm]);
+              acc[r][mm] += mx_scaled(dot32_mx_bf16(opaque<(PPL >= kGuOpaquePpl)>(f.w[p][r][mm]), xv, 0.0f),
+                                      sbv[p][r][mm]);
         } else if constexpr (FMT == kFmtNvfp4) {
 #pragma unroll
           for (int r = 0; r < RG; ++r)
 #pragma unroll
             for (int mm = 0; mm < 2; ++mm)
-              acc[r][mm] += dot32_nv_bf16(f.w[p][r][mm], xv, nvs[p][r][2 * mm], nvs[p][r][2 * mm + 1]);
+              acc[r][mm] += dot32_nv_bf16(opaque<(PPL >= kGuOpaquePpl)>(f.w[p][r][mm]), xv, nvs[p][r][2 * mm],
+                                          nvs[p][r][2 * mm + 1]);
         } else {
           const float xs = asum[(size_t)t * KU + j];
 #pragma unroll
           for (int r = 0; r < RG; ++r)
 #pragma unroll
             for (int mm = 0; mm < 2; ++mm) {
-              const float d = dot32<false>(f.w[p][r][mm], xv, kMagicBytes, 0.0f);
+              const float d = dot32<false>(opaque<(PPL >= kGuOpaquePpl)>(f.w[p][r][mm]), xv, kMagicBytes, 0.0f);
               const float sc = bf16_lo_to_f32(sbv[p][r][mm]);
               const float bi = bf16_hi_to_f32(sbv[p][r][mm]) - 128.0f * sc;
               acc[r][mm] += sc * d + bi * xs;
@@ -762,8 +778,9 @@ __device__ __forceinline__ void dn_segment(const UnionArgs& a, size_t ebase, int
 
 // threads of a down block: one block per CU, as many waves as the registers
 // allow (the waves of a CU share the converted hidden vectors and one LDS
-// work counter)
-constexpr int down_threads(int nt) { return nt == 1 ? 1024 : 512; }
+// work counter); 1024 (at most 128 registers a lane) only for one token per
+// pass and one position per lane, where the ring fits in them
+__host__ __device__ constexpr int down_threads(int nt, int ppl) { return nt == 1 && ppl == 1 ? 1024 : 512; }
 constexpr int kDownUnitSteps = 4;  // row steps per down work unit
 
 // Down projection and router weighting of every (distinct expert, token)
@@ -774,11 +791,11 @@ constexpr int kDownUnitSteps = 4;  // row steps per down work unit
 // each wave fixed), so waves that get fewer issue slots do less of the
 // block's share.  A unit runs every token of its expert, NT at a time.
 template <int LPR, int PPL, bool FULL, bool QS, int NT, int FMT = kFmtAffine>
-__global__ __launch_bounds__(down_threads(NT)) void k_down(UnionArgs a) {
+__global__ __launch_bounds__(down_threads(NT, PPL)) void k_down(UnionArgs a) {
   constexpr int G = 64 / LPR;
   constexpr int RS = down_rows(G);  // a wave step covers G * RS rows
   constexpr int WSTEP = G * RS;
-  constexpr int NW = down_threads(NT) / 64;
+  constexpr int NW = down_threads(NT, PPL) / 64;
   static_assert(!QS || RS % 2 == 0, "quad-shared scales pair rows");
   extern __shared__ __align__(16) unsigned char smem[];
   const int H = a.H, I = a.I, P = a.L * a.k;

@@ -98,6 +98,8 @@ SMALL_SHAPES = [
     (32, 2, 48, 256, 480, True),
     (6, 1, 3, 1056, 2048, False),
     (4, 4, 4, 8192, 192, False),
+    (3, 4, 4, 256, 4096, True),
+    (4, 8, 16, 7168, 256, False),
 ]
 
 

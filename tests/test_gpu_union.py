@@ -147,6 +147,11 @@ SMALL_SHAPES = [
     (6, 1, 3, 1024, 2048, False),
     (4, 4, 4, 8192, 192, False),
     (2, 2, 3, 16384, 64, False),
+    # down with 2 and 4 positions per lane, more than one token per expert
+    (3, 4, 4, 256, 4096, True),
+    (5, 3, 3, 128, 8192, True),
+    # gate/up with 4 positions per lane on a ragged row (H = 7168: 224 of 256)
+    (4, 8, 16, 7168, 256, False),
 ]
 
 
@@ -279,3 +284,13 @@ def test_full_bank_layer_id_range():
     say("full bank E=256 H=6144 I=2048 L=2")
     lay = synth.make_layer(w, 2, 11, seed=0, device="cuda", compact=False)
     check_layer(lay.x, lay.ids, lay.weights, lay.bank, "full-bank")
+
+
+@pytest.mark.parametrize("L", [1, 4])
+def test_deepseek_shaped_layer_full_size(L):
+    # E=256 top-8, hidden 7168, expert intermediate 2048 (four positions per
+    # lane on a row of 224), independent uniform routes, every output checked
+    w = synth.Workload("deepseek_shape_E256_k8_H7168_I2048", 256, 8, 7168, 2048, (1, 4), "uniform", 4)
+    say("full", w.name, "L", L)
+    lay = synth.make_layer(w, L, 1, seed=0, device="cuda")
+    check_layer(lay.x, lay.ids, lay.weights, lay.bank, w.name)
