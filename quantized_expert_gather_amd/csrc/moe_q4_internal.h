@@ -44,6 +44,7 @@ struct UnionArgs {
   // dynamic LDS layout of the gate/up kernel
   size_t lds_act, lds_asum, lds_union;
   int dn_slots;  // pair slots the down kernel stages in LDS at a time
+  int dn_rows;   // one token: down blocks own output rows of all experts and write out (no combine kernel)
   int fmt;       // weight format (kFmt*): for the FP4 formats sg/su/sd hold scale bytes, bg/bu/bd unused
 };
 

@@ -199,12 +199,23 @@ int union_forward_launch(const UnionArgs& base, unsigned stages, int num_cu, hip
     const size_t base_lds = down_lds_head(P);
     if (base_lds + down_slot_bytes(KU) + 256 > kMaxLds) return MOE_Q4_ERR_UNSUPPORTED;
     a.dn_slots = (int)std::min<size_t>((size_t)P, (kMaxLds - 256 - base_lds) / down_slot_bytes(KU));
-    const size_t lds = base_lds + (size_t)a.dn_slots * down_slot_bytes(KU);
-    const bool qs = (a.I / 64) % 2 == 0;
+    size_t lds = base_lds + (size_t)a.dn_slots * down_slot_bytes(KU);
+    const bool qs = a.fmt == kFmtAffine && (a.I / 64) % 2 == 0;
     // one token per register pass when every expert has exactly one token
     // (L = 1), or when a lane holds several positions per row (a second
     // token's hidden vectors would not fit in the registers beside the ring)
     const int nt = (a.L == 1 || ppl >= 2) ? 1 : 2;
+    // one token: each block owns whole output rows of every expert (all pair
+    // slots staged at once plus a row slice per slot) and writes out, so the
+    // combine kernel is not needed
+    const int wstep = (64 / lpr) * down_rows(64 / lpr);
+    const int blk_rows = ((a.H / wstep + num_cu - 1) / num_cu) * wstep;
+    const size_t rows_lds = base_lds + (size_t)P * down_slot_bytes(KU) + (size_t)P * blk_rows * 4;
+    a.dn_rows = a.L == 1 && rows_lds + 256 <= kMaxLds;
+    if (a.dn_rows) {
+      a.dn_slots = P;
+      lds = rows_lds;
+    }
     const void* fn = a.fmt != kFmtAffine ? down_kernel_fmt(a.fmt, lpr, ppl, lpr * ppl == KU, nt)
                                          : down_kernel(lpr, ppl, lpr * ppl == KU, qs, nt);
     if (!fn || lds > kMaxLds) return MOE_Q4_ERR_UNSUPPORTED;
@@ -213,6 +224,7 @@ int union_forward_launch(const UnionArgs& base, unsigned stages, int num_cu, hip
     hipLaunchKernelGGL(reinterpret_cast<void (*)(UnionArgs)>(const_cast<void*>(fn)), dim3(num_cu),
                        dim3(down_threads(nt, ppl)), lds, stream, a);
     if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;
+    if (a.dn_rows) return MOE_Q4_OK;
     dim3 cgrid((a.H / 4 + 255) / 256, a.L);
     hipLaunchKernelGGL(k_combine, cgrid, dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;

@@ -719,7 +719,8 @@ template <int LPR, int PPL, bool FULL, bool QS, int NT, int RS, int WSTEP, int F
 __device__ __forceinline__ void dn_segment(const UnionArgs& a, size_t ebase, int ls0, int nt, int gj, int klast,
                                            int li, int g, int KU, int KG, int H, const unsigned char* lane_sbase,
                                            const DnOffsets<PPL, RS>& o, uint32_t sel, const uint4* hvs,
-                                           const float* hss, const float* stw, const int* sdst) {
+                                           const float* hss, const float* stw, const int* sdst,
+                                           float* rows_dst = nullptr) {
   // prefetches past the last step are zero-range no-ops
   auto load = [&](int kk, DnFrag<PPL, RS>& fr) {
     const bool valid = kk <= klast;
@@ -757,6 +758,7 @@ __device__ __forceinline__ void dn_segment(const UnionArgs& a, size_t ebase, int
     }
     tw[c] = live ? stw[ls] : 0.0f;
     dst[c] = live ? a.ys + (size_t)wave_uniform(sdst[ls]) * H : a.ys_dummy;
+    if (rows_dst) dst[c] = rows_dst;  // one token: the block's row slice in LDS
   }
 
   auto step = [&](int kk, const DnFrag<PPL, RS>& fr) {
@@ -832,9 +834,69 @@ __global__ __launch_bounds__(down_threads(NT, PPL)) void k_down(UnionArgs a) {
     if (tid == 0) wpre[u] = carry;
   }
   for (int i = tid; i < umax; i += blockDim.x) utab[i] = a.utab[i];
+  if (tid == 0) unit_q = NW;
   __syncthreads();
-  const int wtot = uniform ? u * nrb : wpre[u];
   const int nblk = gridDim.x, b = blockIdx.x;
+  const int lane = tid & 63;
+  const int wave = wave_uniform(tid >> 6);
+  auto grab = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&unit_q, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  const int g = lane / LPR, li = lane % LPR;
+  const int qa = li & 3;
+  const unsigned char* lane_sbase =
+      reinterpret_cast<const unsigned char*>((qa & 1) ? (const void*)a.bd : (const void*)a.sd);
+  const uint32_t sel = ((li >> 1) & 1) ? 0x07060302u : 0x05040100u;
+  DnOffsets<PPL, RS> o;
+#pragma unroll
+  for (int r = 0; r < RS; ++r)
+#pragma unroll
+    for (int p = 0; p < PPL; ++p) {
+      const int j = li + LPR * p;
+      o.w[r][p] = (uint32_t)(((g * RS + r) * KU + j) * 16);
+      const int srow = QS ? (r & ~1) + (qa >> 1) : r;
+      const int grp = QS ? 2 * (li >> 2) + (LPR / 2) * p : FMT == kFmtAffine32 ? j : (j >> 1);
+      o.s[r][p] = fmt_fp4(FMT) ? (uint32_t)(((g * RS + r) * KU + j) * (FMT == kFmtNvfp4 ? 2 : 1))
+                               : (uint32_t)(((g * RS + srow) * KG + grp) * 2);
+    }
+
+  if (NT == 1 && a.dn_rows) {
+    // One token (so one pair slot per distinct expert, slot i of expert i):
+    // block b owns row steps [s0, s1) of every expert, stages all u hidden
+    // vectors, runs units (expert, chunk of its steps) into a row slice per
+    // expert in LDS, then adds the slices in ascending expert order -- the
+    // combine kernel's order -- and writes out itself.
+    const int s0 = (int)((long long)spe * b / nblk), s1 = (int)((long long)spe * (b + 1) / nblk);
+    const int ns = s1 - s0, nrows = ns * WSTEP;
+    if (ns <= 0) return;  // uniform over the block
+    float* part = reinterpret_cast<float*>(sdst + SM);  // [u][nrows]
+    for (int sl = wave; sl < u; sl += NW) down_stage_slot(a, sl, sl, KU, hvs, hss, stw, sdst, fmt_fp4(FMT));
+    __syncthreads();
+    const int nch = max(1, min(ns, NW / max(u, 1)));  // step chunks per expert
+    const int cs = (ns + nch - 1) / nch;
+    for (int j = wave; j < u * nch; j = grab()) {
+      const int i = j / nch, g0 = (j - i * nch) * cs, g1 = min(ns, g0 + cs);
+      if (g0 >= g1) continue;
+      const size_t ebase = (size_t)wave_uniform(utab[i].x) * H + (size_t)s0 * WSTEP;
+      dn_segment<LPR, PPL, FULL, QS, 1, RS, WSTEP, FMT>(a, ebase, i, 1, g0, g1 - g0 - 1, li, g, KU, KG, H, lane_sbase,
+                                                       o, sel, hvs, hss, stw, sdst, part + (size_t)i * nrows);
+    }
+    __syncthreads();
+    for (int r = tid; r < nrows; r += blockDim.x) {
+      float acc = 0.0f;
+      for (int i = 0; i < u; ++i) acc += part[i * nrows + r];
+      const size_t m = (size_t)s0 * WSTEP + r;
+      if (a.out_f32)
+        reinterpret_cast<float*>(a.out)[m] = acc;
+      else
+        reinterpret_cast<uint16_t*>(a.out)[m] = (uint16_t)f32_to_bf16_rne(acc);
+    }
+    return;
+  }
+
+  const int wtot = uniform ? u * nrb : wpre[u];
   // first unit whose work starts at or after offset x
   auto unit_at = [&](long long x) {
     if (x >= wtot) return u * nrb;
@@ -853,32 +915,6 @@ __global__ __launch_bounds__(down_threads(NT, PPL)) void k_down(UnionArgs a) {
   const int s_lo = utab[ub / nrb].z;
   const int4 ehi = utab[(ub + nub - 1) / nrb];
   const int s_hi = ehi.z + __popc((uint32_t)ehi.y);  // pair slots of the block's experts
-
-  const int lane = tid & 63;
-  const int wave = wave_uniform(tid >> 6);
-  const int g = lane / LPR, li = lane % LPR;
-  const int qa = li & 3;
-  const unsigned char* lane_sbase =
-      reinterpret_cast<const unsigned char*>((qa & 1) ? (const void*)a.bd : (const void*)a.sd);
-  const uint32_t sel = ((li >> 1) & 1) ? 0x07060302u : 0x05040100u;
-  DnOffsets<PPL, RS> o;
-#pragma unroll
-  for (int r = 0; r < RS; ++r)
-#pragma unroll
-    for (int p = 0; p < PPL; ++p) {
-      const int j = li + LPR * p;
-      o.w[r][p] = (uint32_t)(((g * RS + r) * KU + j) * 16);
-      const int srow = QS ? (r & ~1) + (qa >> 1) : r;
-      const int grp = QS ? 2 * (li >> 2) + (LPR / 2) * p : FMT == kFmtAffine32 ? j : (j >> 1);
-      o.s[r][p] = fmt_fp4(FMT) ? (uint32_t)(((g * RS + r) * KU + j) * (FMT == kFmtNvfp4 ? 2 : 1))
-                               : (uint32_t)(((g * RS + srow) * KG + grp) * 2);
-    }
-  auto grab = [&]() {
-    int v = 0;
-    if (lane == 0) v = atomicAdd(&unit_q, 1);
-    return __builtin_amdgcn_readfirstlane(v);
-  };
-
 
   // Usually one pass; more when the block's experts have more pair slots
   // than the LDS holds (each pass runs the block's units for its slots).
