@@ -70,6 +70,7 @@ extern "C" {
 #define MOE_Q4_UNION_MAX_L 32    /* token masks are 32-bit                                     */
 #define MOE_Q4_MAX_PAIRS 1024    /* L * k on the union path                                    */
 #define MOE_Q4_MAX_E 16384
+#define MOE_Q4_CODEC_MAX_L 65535 /* tokens of one moe_swiglu_codec_forward call          */
 
 /* ---- weight codecs (moe_swiglu_codec_forward) ---- */
 #define MOE_Q4_CODEC_AFFINE4_G64 0 /* 4-bit affine, bf16 scale + bias per 64 inputs (= moe_swiglu_q4_forward) */
@@ -186,9 +187,15 @@ size_t moe_swiglu_codec_workspace_bytes(int codec, int L, int k, int E, int H, i
  *
  * All other arguments, the results' definition and the status codes are as
  * for moe_swiglu_q4_forward.  MOE_Q4_CODEC_AFFINE4_G64 is exactly
- * moe_swiglu_q4_forward (both paths).  The other codecs take the union path
- * only: L <= MOE_Q4_UNION_MAX_L, L * k <= MOE_Q4_MAX_PAIRS and the union
- * path's LDS limits, else MOE_Q4_ERR_UNSUPPORTED; so does an unknown codec.
+ * moe_swiglu_q4_forward (both paths).  The other codecs run on the union
+ * kernels only.  Calls with more tokens than one union launch serves
+ * (L > MOE_Q4_UNION_MAX_L or L * k > MOE_Q4_MAX_PAIRS) run as consecutive
+ * chunks of min(MOE_Q4_UNION_MAX_L, MOE_Q4_MAX_PAIRS / k) tokens on the
+ * same workspace (sized by moe_swiglu_codec_workspace_bytes for one chunk);
+ * each chunk streams the distinct experts of its own tokens, so long inputs
+ * re-read the bank once per chunk.  Such calls need stages ==
+ * MOE_Q4_STAGE_ALL.  The device status word is the OR over the chunks.
+ * L <= MOE_Q4_CODEC_MAX_L.  An unknown codec gives MOE_Q4_ERR_UNSUPPORTED.
  */
 int moe_swiglu_codec_forward(int codec, const void *x, const int32_t *topk_ids, const float *topk_weights,
                              const uint32_t *wg, const void *sg, const void *bg,

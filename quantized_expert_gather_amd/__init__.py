@@ -43,6 +43,7 @@ CODECS = {"affine4_g64": (MOE_Q4_CODEC_AFFINE4_G64, 64), "affine4_g32": (MOE_Q4_
           "mxfp4": (MOE_Q4_CODEC_MXFP4, 32), "nvfp4": (MOE_Q4_CODEC_NVFP4, 16)}
 MOE_Q4_UNION_MAX_L = 32
 MOE_Q4_MAX_PAIRS = 1024
+MOE_Q4_CODEC_MAX_L = 65535
 
 EXPORTS = (
     "moe_swiglu_q4_workspace_bytes",

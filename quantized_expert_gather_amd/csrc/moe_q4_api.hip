@@ -3,6 +3,8 @@
 // before any GPU work, so invalid calls return a status without touching the
 // device.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stdint.h>
 #include <string.h>
 
@@ -56,14 +58,20 @@ static int select_path(int L, int k, int E, int H, int I) {
   return -MOE_Q4_ERR_UNSUPPORTED;
 }
 
-// Codecs other than 4-bit affine group 64 take the union path only, with H
-// and I multiples of 32 (the kernels' 32-input positions).
+// Codecs other than 4-bit affine group 64 run on the union kernels only, with
+// H and I multiples of 32 (the kernels' 32-input positions).  More tokens
+// than one union launch serves are run as consecutive token chunks.
+static int codec_chunk_tokens(int L, int k) {
+  const int cap = std::min(MOE_Q4_UNION_MAX_L, MOE_Q4_MAX_PAIRS / k);
+  return L < cap ? L : cap;
+}
+
 static int codec_shape_status(int L, int k, int E, int H, int I) {
   if (L < 0 || k < 1 || E < 1 || H < 1 || I < 1 || k > E) return MOE_Q4_ERR_SHAPE;
-  if (H % 32 || I % 32 || E > MOE_Q4_MAX_E) return MOE_Q4_ERR_UNSUPPORTED;
-  if (L == 0) return MOE_Q4_OK;
-  if (L > MOE_Q4_UNION_MAX_L || (long)L * k > MOE_Q4_MAX_PAIRS || !union_shape_supported(L, k, E, H, I))
+  if (H % 32 || I % 32 || E > MOE_Q4_MAX_E || k > MOE_Q4_MAX_PAIRS || L > MOE_Q4_CODEC_MAX_L)
     return MOE_Q4_ERR_UNSUPPORTED;
+  if (L == 0) return MOE_Q4_OK;
+  if (!union_shape_supported(codec_chunk_tokens(L, k), k, E, H, I)) return MOE_Q4_ERR_UNSUPPORTED;
   return MOE_Q4_OK;
 }
 
@@ -213,7 +221,7 @@ int moe_swiglu_q4_forward(const void* x, const int32_t* topk_ids, const float* t
 size_t moe_swiglu_codec_workspace_bytes(int codec, int L, int k, int E, int H, int I) {
   if (codec == MOE_Q4_CODEC_AFFINE4_G64) return moe_swiglu_q4_workspace_bytes(L, k, E, H, I);
   if (codec_fmt(codec) < 0 || L == 0 || codec_shape_status(L, k, E, H, I)) return 0;
-  return union_workspace_layout(L, k, E, H, I).total;
+  return union_workspace_layout(codec_chunk_tokens(L, k), k, E, H, I).total;
 }
 
 int moe_swiglu_codec_forward_stages(int codec, const void* x, const int32_t* topk_ids, const float* topk_weights,
@@ -231,6 +239,9 @@ int moe_swiglu_codec_forward_stages(int codec, const void* x, const int32_t* top
   if (out_dtype != MOE_Q4_OUT_BF16 && out_dtype != MOE_Q4_OUT_F32) return MOE_Q4_ERR_UNSUPPORTED;
   if (stages == 0 || (stages & ~MOE_Q4_STAGE_ALL)) return MOE_Q4_ERR_UNSUPPORTED;
   if (L == 0) return MOE_Q4_OK;
+  const int Lc = codec_chunk_tokens(L, k);
+  // stage-only calls hand the hidden vectors of one launch to the next
+  if (Lc < L && stages != MOE_Q4_STAGE_ALL) return MOE_Q4_ERR_UNSUPPORTED;
   const bool biased = fmt == kFmtAffine32;
   if (!x || !topk_ids || !topk_weights || !wg || !sg || !wu || !su || !wd || !sd || !out) return MOE_Q4_ERR_NULL;
   if (biased && (!bg || !bu || !bd)) return MOE_Q4_ERR_NULL;
@@ -242,7 +253,7 @@ int moe_swiglu_codec_forward_stages(int codec, const void* x, const int32_t* top
       !aligned(topk_ids, 4) || !aligned(topk_weights, 4) || !aligned(workspace, 256) || !aligned(sg, sa) ||
       !aligned(su, sa) || !aligned(sd, sa) || (biased && (!aligned(bg, 2) || !aligned(bu, 2) || !aligned(bd, 2))))
     return MOE_Q4_ERR_ALIGN;
-  const UnionWorkspace lay = union_workspace_layout(L, k, E, H, I);
+  const UnionWorkspace lay = union_workspace_layout(Lc, k, E, H, I);
   if (workspace_bytes < lay.total) return MOE_Q4_ERR_WORKSPACE;
 
   // bytes of one scale array per 32 inputs of a row: bf16 (affine32), 2 E4M3 (nvfp4), 1 E8M0 (mxfp4)
@@ -281,7 +292,20 @@ int moe_swiglu_codec_forward_stages(int codec, const void* x, const int32_t* top
   a.hbuf = reinterpret_cast<float*>(ws + lay.hbuf);
   a.ys = reinterpret_cast<float*>(ws + lay.ys);
   a.ys_dummy = reinterpret_cast<float*>(ws + lay.ys_dummy);
-  return union_forward_launch(a, stages, ncu, stream);
+  // token chunks of Lc, in order, on the same workspace
+  const size_t out_elt = out_dtype == MOE_Q4_OUT_F32 ? 4 : 2;
+  for (int t0 = 0; t0 < L; t0 += Lc) {
+    UnionArgs c = a;
+    c.L = std::min(Lc, L - t0);
+    c.x = a.x + (size_t)t0 * H;
+    c.ids = topk_ids + (size_t)t0 * k;
+    c.tw = topk_weights + (size_t)t0 * k;
+    c.out = static_cast<unsigned char*>(out) + (size_t)t0 * H * out_elt;
+    c.status_or = t0 > 0;
+    const int st2 = union_forward_launch(c, stages, ncu, stream);
+    if (st2) return st2;
+  }
+  return MOE_Q4_OK;
 }
 
 int moe_swiglu_codec_forward(int codec, const void* x, const int32_t* topk_ids, const float* topk_weights,

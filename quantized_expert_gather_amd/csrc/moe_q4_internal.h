@@ -45,6 +45,7 @@ struct UnionArgs {
   size_t lds_act, lds_asum, lds_union;
   int dn_slots;  // pair slots the down kernel stages in LDS at a time
   int dn_rows;   // one token: down blocks own output rows of all experts and write out (no combine kernel)
+  int status_or; // later token chunk of one call: OR this chunk's status into the call's status word
   int fmt;       // weight format (kFmt*): for the FP4 formats sg/su/sd hold scale bytes, bg/bu/bd unused
 };
 

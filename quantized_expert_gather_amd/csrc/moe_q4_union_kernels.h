@@ -368,7 +368,8 @@ __device__ __forceinline__ void gu_compute(const UnionArgs& a, const GuFrag<PPL,
 __device__ inline void write_union_tables(const UnionArgs& a, const UnionLds& s, int u, int L, int k) {
   const int tid = threadIdx.x;
   if (tid == 0) {
-    a.hdr[0] = s.scal[1] ? MOE_Q4_DEV_BAD_ID : 0u;  // status of this call
+    const uint32_t st = s.scal[1] ? MOE_Q4_DEV_BAD_ID : 0u;
+    a.hdr[0] = a.status_or ? (a.hdr[0] | st) : st;  // status of this call
     a.hdr[1] = MOE_Q4_PATH_UNION;
     a.hdr[2] = (uint32_t)u;
   }

@@ -217,8 +217,9 @@ def call_mx(L=2, k=2, E=8, H=256, I=128, out_dtype=0, ws_bytes=1 << 30, stages=3
     (dict(H=0), q.MOE_Q4_ERR_SHAPE),
     (dict(H=240), q.MOE_Q4_ERR_UNSUPPORTED),
     (dict(I=112), q.MOE_Q4_ERR_UNSUPPORTED),
-    (dict(L=33), q.MOE_Q4_ERR_UNSUPPORTED),       # the union path only
-    (dict(L=32, k=33, E=64), q.MOE_Q4_ERR_UNSUPPORTED),
+    (dict(L=33, stages=1), q.MOE_Q4_ERR_UNSUPPORTED),   # token chunks need all stages
+    (dict(L=65536), q.MOE_Q4_ERR_UNSUPPORTED),
+    (dict(k=1025, E=2048), q.MOE_Q4_ERR_UNSUPPORTED),
     (dict(out_dtype=5), q.MOE_Q4_ERR_UNSUPPORTED),
     (dict(stages=4), q.MOE_Q4_ERR_UNSUPPORTED),
     (dict(ws_bytes=64), q.MOE_Q4_ERR_WORKSPACE),
@@ -230,7 +231,13 @@ def test_mx_invalid_arguments_rejected_on_host(kw, status):
 def test_mx_host_checks():
     assert call_mx(L=0) == q.MOE_Q4_OK
     assert q.moe_swiglu_mxfp4_workspace_bytes(0, 2, 8, 256, 128) == 0
-    assert q.moe_swiglu_mxfp4_workspace_bytes(33, 8, 256, 2048, 512) == 0
+    # more tokens than one union launch: the workspace of one 32-token chunk
+    assert q.moe_swiglu_mxfp4_workspace_bytes(33, 8, 256, 2048, 512) == \
+        q.moe_swiglu_mxfp4_workspace_bytes(32, 8, 256, 2048, 512) > 0
+    assert q.moe_swiglu_mxfp4_workspace_bytes(5000, 8, 256, 2048, 512) == \
+        q.moe_swiglu_mxfp4_workspace_bytes(32, 8, 256, 2048, 512)
+    assert q.moe_swiglu_mxfp4_workspace_bytes(100, 32, 256, 2048, 512) == \
+        q.moe_swiglu_mxfp4_workspace_bytes(32, 32, 256, 2048, 512)
     # H and I multiples of 32 suffice; the layout is the union path's
     assert q.moe_swiglu_mxfp4_workspace_bytes(2, 2, 4, 96, 256) > 0
     assert q.moe_swiglu_mxfp4_workspace_bytes(2, 2, 4, 352, 224) > 0
@@ -273,7 +280,8 @@ def test_codec_host_checks():
     for c in (A32, MX, NV):
         assert call_codec(c, L=0) == q.MOE_Q4_OK
         assert call_codec(c, H=240) == q.MOE_Q4_ERR_UNSUPPORTED
-        assert call_codec(c, L=33) == q.MOE_Q4_ERR_UNSUPPORTED
+        assert call_codec(c, L=33, stages=2) == q.MOE_Q4_ERR_UNSUPPORTED
+        assert call_codec(c, L=65536) == q.MOE_Q4_ERR_UNSUPPORTED
         assert call_codec(c, k=9) == q.MOE_Q4_ERR_SHAPE
         assert call_codec(c, ws_bytes=64) == q.MOE_Q4_ERR_WORKSPACE
         assert q.moe_swiglu_codec_workspace_bytes(c, 2, 2, 4, 96, 256) > 0

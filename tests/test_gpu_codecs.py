@@ -179,6 +179,29 @@ def test_codec_full_size_verify_layers(codec, L, layer):
     check_layer(lay.x, lay.ids, lay.weights, lay.bank, w.name)
 
 
+@pytest.mark.parametrize("codec", CODECS)
+def test_codec_long_inputs_run_as_token_chunks(codec):
+    # 70 tokens at top-8: chunks of 32, 32 and 6 tokens on one workspace;
+    # an invalid id in the last chunk must reach the call's status word
+    q = _q()
+    L, k, E, H, I = 70, 8, 64, 512, 256
+    x, ids, tw, bank = synth.random_problem_q(codec, L, k, E, H, I, seed=21)
+    say(codec, "token chunks L=70")
+    ref = oracle.forward_pairs_q(codec, x, ids, tw, bank)
+    out, ws = run_layer(x, ids, tw, bank)
+    assert q.moe_swiglu_codec_workspace_bytes(q.CODECS[codec][0], L, k, E, H, I) == \
+        q.moe_swiglu_codec_workspace_bytes(q.CODECS[codec][0], 32, k, E, H, I)
+    assert rel_err_rows(out.cpu().numpy(), ref).max() <= ARITH
+    assert q.moe_q4_read_device_status(ws)[0] == 0
+    bad = ids.copy()
+    bad[66, 3] = E + 5
+    out2, ws2 = run_layer(x, bad, tw, bank)
+    assert q.moe_q4_read_device_status(ws2)[0] & q.MOE_Q4_DEV_BAD_ID
+    keep, tw0 = ids.copy(), tw.copy()
+    keep[66, 3], tw0[66, 3] = 0, 0
+    assert rel_err_rows(out2.cpu().numpy(), oracle.forward_pairs_q(codec, x, keep, tw0, bank)).max() <= ARITH
+
+
 def test_codec_entry_for_affine_group64_is_the_q4_forward():
     q = _q()
     x, ids, tw, bank = synth.random_problem(4, 4, 9, 1024, 512, seed=14)
