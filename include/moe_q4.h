@@ -77,6 +77,8 @@ extern "C" {
 #define MOE_Q4_CODEC_AFFINE4_G32 1 /* 4-bit affine, bf16 scale + bias per 32 inputs                      */
 #define MOE_Q4_CODEC_MXFP4 2       /* FP4 E2M1 elements, one E8M0 scale byte per 32 inputs             */
 #define MOE_Q4_CODEC_NVFP4 3       /* FP4 E2M1 elements, one FP8 E4M3 scale byte per 16 inputs         */
+#define MOE_Q4_CODEC_AFFINE8_G64 4 /* 8-bit affine, bf16 scale + bias per 64 inputs                      */
+#define MOE_Q4_CODEC_MXFP8 5       /* FP8 E4M3 elements, one E8M0 scale byte per 32 inputs             */
 
 /* ---- forward stages (moe_swiglu_q4_forward_stages) ---- */
 #define MOE_Q4_STAGE_GATEUP 1u   /* union (or sort) + fused gate/up + silu(gate)*up -> workspace  */
@@ -165,9 +167,12 @@ size_t moe_swiglu_codec_workspace_bytes(int codec, int L, int k, int E, int H, i
  * also times affine group 32; nvfp4 is among the quantized modes of PR 4572
  * on the page "MoE GatherQMM small-M verify cost" (Facts).  Layouts taken:
  *
- *   codes (all)   element c of a row is nibble c % 8 of word c / 8, lowest
- *                 nibble first (as for moe_swiglu_q4_forward)
+ *   codes         4-bit codecs: element c of a row is nibble c % 8 of word
+ *                 c / 8, lowest nibble first (as for moe_swiglu_q4_forward);
+ *                 8-bit codecs: byte c % 4 of word c / 4, lowest byte first
  *   AFFINE4_G32   w = s * q + b, q in 0..15, bf16 s and b per 32 inputs
+ *   AFFINE8_G64   w = s * q + b, q in 0..255, bf16 s and b per 64 inputs
+ *   MXFP8         w = e4m3(q) * 2^(e - 127), one E8M0 byte e per 32 inputs
  *   MXFP4         w = e2m1(q) * 2^(e - 127), one E8M0 byte e per 32 inputs;
  *                 e = 255 stands for NaN (every product with that block is NaN)
  *   NVFP4         w = e2m1(q) * e4m3(s), one FP8 E4M3 byte s per 16 inputs, no
@@ -175,15 +180,17 @@ size_t moe_swiglu_codec_workspace_bytes(int codec, int L, int k, int E, int H, i
  *   E2M1 and E4M3 follow the OCP specifications (MX v1.0; 8-bit floating point
  *   E4M3: exponent bias 7, subnormals, S.1111.111 NaN, no infinities).
  *
- *   wg, wu      uint32 [E, I, H/8]        codes                      (16-byte aligned)
- *   sg, su      [E, I, H/gs]              scales: bf16 (AFFINE4_G32, 2-byte aligned),
- *                                         uint8 E8M0 (MXFP4, any alignment),
- *                                         uint8 E4M3 (NVFP4, gs = 16, 2-byte aligned)
- *   bg, bu      bf16 [E, I, H/32]         biases (AFFINE4_G32 only, 2-byte aligned;
+ *   wg, wu      uint32 [E, I, H*bits/32]  codes                      (16-byte aligned)
+ *   sg, su      [E, I, H/gs]              scales: bf16 (AFFINE4_G32, AFFINE8_G64;
+ *                                         2-byte aligned), uint8 E8M0 (MXFP4, MXFP8;
+ *                                         any alignment), uint8 E4M3 (NVFP4, gs = 16,
+ *                                         2-byte aligned)
+ *   bg, bu      bf16 [E, I, H/gs]         biases (affine codecs only, 2-byte aligned;
  *                                         ignored and may be NULL otherwise)
- *   wd, sd, bd  the same for down, [E, H, I/8] and [E, H, I/gs]
- *   H, I        multiples of 32; with H <= 64, I a multiple of 64, and with
- *               I <= 128, H a multiple of 64 (the kernels' row steps)
+ *   wd, sd, bd  the same for down, [E, H, I*bits/32] and [E, H, I/gs]
+ *   H, I        multiples of 32 (of 64 for AFFINE8_G64); the kernels' row steps
+ *               add limits for very small H or I (a shape they cannot tile gives
+ *               MOE_Q4_ERR_UNSUPPORTED and moe_swiglu_codec_workspace_bytes 0)
  *
  * All other arguments, the results' definition and the status codes are as
  * for moe_swiglu_q4_forward.  MOE_Q4_CODEC_AFFINE4_G64 is exactly

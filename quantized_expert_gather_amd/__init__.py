@@ -38,9 +38,12 @@ MOE_Q4_CODEC_AFFINE4_G64 = 0
 MOE_Q4_CODEC_AFFINE4_G32 = 1
 MOE_Q4_CODEC_MXFP4 = 2
 MOE_Q4_CODEC_NVFP4 = 3
-#: codec names (as in the test-data generators) -> MOE_Q4_CODEC_* and inputs per scale group
-CODECS = {"affine4_g64": (MOE_Q4_CODEC_AFFINE4_G64, 64), "affine4_g32": (MOE_Q4_CODEC_AFFINE4_G32, 32),
-          "mxfp4": (MOE_Q4_CODEC_MXFP4, 32), "nvfp4": (MOE_Q4_CODEC_NVFP4, 16)}
+MOE_Q4_CODEC_AFFINE8_G64 = 4
+MOE_Q4_CODEC_MXFP8 = 5
+#: codec names (as in the test-data generators) -> MOE_Q4_CODEC_*, inputs per scale group, bits per code
+CODECS = {"affine4_g64": (MOE_Q4_CODEC_AFFINE4_G64, 64, 4), "affine4_g32": (MOE_Q4_CODEC_AFFINE4_G32, 32, 4),
+          "mxfp4": (MOE_Q4_CODEC_MXFP4, 32, 4), "nvfp4": (MOE_Q4_CODEC_NVFP4, 16, 4),
+          "affine8_g64": (MOE_Q4_CODEC_AFFINE8_G64, 64, 8), "mxfp8": (MOE_Q4_CODEC_MXFP8, 32, 8)}
 MOE_Q4_UNION_MAX_L = 32
 MOE_Q4_MAX_PAIRS = 1024
 MOE_Q4_CODEC_MAX_L = 65535
@@ -284,18 +287,22 @@ def _codec_id(codec) -> int:
 def _codec_args(codec_name, x, topk_ids, topk_weights, wg, sg, bg, wu, su, bu, wd, sd, bd):
     """Shape- and dtype-checked pointer list of a codec call."""
     code = _codec_id(codec_name)
-    gs = {v[0]: v[1] for v in CODECS.values()}.get(code)
-    if gs is None:
+    spec = {v[0]: v[1:] for v in CODECS.values()}.get(code)
+    if spec is None:
         raise ValueError(f"unknown codec {codec_name!r}")
+    gs, bits = spec
     if x.dim() != 2 or topk_ids.dim() != 2 or wg.dim() != 3 or wd.dim() != 3:
         raise ValueError("x [L, H], topk_ids [L, k], wg [E, I, H/8] and wd [E, H, I/8] expected")
     L, H = x.shape
     k = topk_ids.shape[1]
     E, I = wg.shape[0], wg.shape[1]
-    affine = code in (MOE_Q4_CODEC_AFFINE4_G64, MOE_Q4_CODEC_AFFINE4_G32)
+    affine = code in (MOE_Q4_CODEC_AFFINE4_G64, MOE_Q4_CODEC_AFFINE4_G32, MOE_Q4_CODEC_AFFINE8_G64)
+    per_word = 32 // bits
+    if wg.shape[2] * per_word != H:
+        raise ValueError(f"wg has {wg.shape[2]} words per row, expected {H // per_word}")
     shapes = {
         "topk_ids": (topk_ids, (L, k)), "topk_weights": (topk_weights, (L, k)),
-        "wg": (wg, (E, I, H // 8)), "wu": (wu, (E, I, H // 8)), "wd": (wd, (E, H, I // 8)),
+        "wg": (wg, (E, I, H // per_word)), "wu": (wu, (E, I, H // per_word)), "wd": (wd, (E, H, I // per_word)),
         "sg": (sg, (E, I, H // gs)), "su": (su, (E, I, H // gs)), "sd": (sd, (E, H, I // gs)),
     }
     if affine:

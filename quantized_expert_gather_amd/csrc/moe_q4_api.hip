@@ -59,19 +59,21 @@ static int select_path(int L, int k, int E, int H, int I) {
 }
 
 // Codecs other than 4-bit affine group 64 run on the union kernels only, with
-// H and I multiples of 32 (the kernels' 32-input positions).  More tokens
-// than one union launch serves are run as consecutive token chunks.
+// H and I multiples of 32 (one scale per 32 inputs at least; 64 for the
+// group-64 8-bit affine codes).  More tokens than one union launch serves
+// are run as consecutive token chunks.
 static int codec_chunk_tokens(int L, int k) {
   const int cap = std::min(MOE_Q4_UNION_MAX_L, MOE_Q4_MAX_PAIRS / k);
   return L < cap ? L : cap;
 }
 
-static int codec_shape_status(int L, int k, int E, int H, int I) {
+static int codec_shape_status(int L, int k, int E, int H, int I, int fmt) {
   if (L < 0 || k < 1 || E < 1 || H < 1 || I < 1 || k > E) return MOE_Q4_ERR_SHAPE;
-  if (H % 32 || I % 32 || E > MOE_Q4_MAX_E || k > MOE_Q4_MAX_PAIRS || L > MOE_Q4_CODEC_MAX_L)
+  const int grp = fmt == kFmtAffine8 ? 64 : 32;
+  if (H % grp || I % grp || E > MOE_Q4_MAX_E || k > MOE_Q4_MAX_PAIRS || L > MOE_Q4_CODEC_MAX_L)
     return MOE_Q4_ERR_UNSUPPORTED;
   if (L == 0) return MOE_Q4_OK;
-  if (!union_shape_supported(codec_chunk_tokens(L, k), k, E, H, I)) return MOE_Q4_ERR_UNSUPPORTED;
+  if (!union_shape_supported(codec_chunk_tokens(L, k), k, E, H, I, fmt)) return MOE_Q4_ERR_UNSUPPORTED;
   return MOE_Q4_OK;
 }
 
@@ -82,6 +84,8 @@ static int codec_fmt(int codec) {
     case MOE_Q4_CODEC_AFFINE4_G32: return kFmtAffine32;
     case MOE_Q4_CODEC_MXFP4: return kFmtMxfp4;
     case MOE_Q4_CODEC_NVFP4: return kFmtNvfp4;
+    case MOE_Q4_CODEC_AFFINE8_G64: return kFmtAffine8;
+    case MOE_Q4_CODEC_MXFP8: return kFmtMxfp8;
   }
   return -1;
 }
@@ -220,7 +224,7 @@ int moe_swiglu_q4_forward(const void* x, const int32_t* topk_ids, const float* t
 
 size_t moe_swiglu_codec_workspace_bytes(int codec, int L, int k, int E, int H, int I) {
   if (codec == MOE_Q4_CODEC_AFFINE4_G64) return moe_swiglu_q4_workspace_bytes(L, k, E, H, I);
-  if (codec_fmt(codec) < 0 || L == 0 || codec_shape_status(L, k, E, H, I)) return 0;
+  if (codec_fmt(codec) < 0 || L == 0 || codec_shape_status(L, k, E, H, I, codec_fmt(codec))) return 0;
   return union_workspace_layout(codec_chunk_tokens(L, k), k, E, H, I).total;
 }
 
@@ -234,7 +238,7 @@ int moe_swiglu_codec_forward_stages(int codec, const void* x, const int32_t* top
   if (fmt == kFmtAffine)
     return moe_swiglu_q4_forward_stages(x, topk_ids, topk_weights, wg, sg, bg, wu, su, bu, wd, sd, bd, L, k, E, H,
                                         I, 64, 4, out, out_dtype, workspace, workspace_bytes, stages, stream);
-  const int st = codec_shape_status(L, k, E, H, I);
+  const int st = codec_shape_status(L, k, E, H, I, fmt);
   if (st) return st;
   if (out_dtype != MOE_Q4_OUT_BF16 && out_dtype != MOE_Q4_OUT_F32) return MOE_Q4_ERR_UNSUPPORTED;
   if (stages == 0 || (stages & ~MOE_Q4_STAGE_ALL)) return MOE_Q4_ERR_UNSUPPORTED;
@@ -242,13 +246,14 @@ int moe_swiglu_codec_forward_stages(int codec, const void* x, const int32_t* top
   const int Lc = codec_chunk_tokens(L, k);
   // stage-only calls hand the hidden vectors of one launch to the next
   if (Lc < L && stages != MOE_Q4_STAGE_ALL) return MOE_Q4_ERR_UNSUPPORTED;
-  const bool biased = fmt == kFmtAffine32;
+  const bool biased = fmt == kFmtAffine32 || fmt == kFmtAffine8;
   if (!x || !topk_ids || !topk_weights || !wg || !sg || !wu || !su || !wd || !sd || !out) return MOE_Q4_ERR_NULL;
   if (biased && (!bg || !bu || !bd)) return MOE_Q4_ERR_NULL;
   if (!workspace) return MOE_Q4_ERR_WORKSPACE;
   // scale (and bias) arrays: bf16 (affine), pairs of E4M3 bytes read as one
-  // 16-bit word (nvfp4) or single E8M0 bytes (mxfp4)
-  const size_t sa = fmt == kFmtMxfp4 ? 1 : 2;
+  // 16-bit word (nvfp4) or single E8M0 bytes (mxfp4, mxfp8)
+  const bool e8m0 = fmt == kFmtMxfp4 || fmt == kFmtMxfp8;
+  const size_t sa = e8m0 ? 1 : 2;
   if (!aligned(x, 16) || !aligned(wg, 16) || !aligned(wu, 16) || !aligned(wd, 16) || !aligned(out, 16) ||
       !aligned(topk_ids, 4) || !aligned(topk_weights, 4) || !aligned(workspace, 256) || !aligned(sg, sa) ||
       !aligned(su, sa) || !aligned(sd, sa) || (biased && (!aligned(bg, 2) || !aligned(bu, 2) || !aligned(bd, 2))))
@@ -256,11 +261,13 @@ int moe_swiglu_codec_forward_stages(int codec, const void* x, const int32_t* top
   const UnionWorkspace lay = union_workspace_layout(Lc, k, E, H, I);
   if (workspace_bytes < lay.total) return MOE_Q4_ERR_WORKSPACE;
 
-  // bytes of one scale array per 32 inputs of a row: bf16 (affine32), 2 E4M3 (nvfp4), 1 E8M0 (mxfp4)
-  const size_t per32 = fmt == kFmtMxfp4 ? 1 : 2;
+  // bytes of one scale array per 32 inputs of a row: a bf16 per 32 (affine
+  // group 32) or per 64 (8-bit affine), two E4M3 (nvfp4), one E8M0 (mx)
+  const size_t per32 = e8m0 || fmt == kFmtAffine8 ? 1 : 2;
+  const size_t cb = fmt_8bit(fmt) ? 1 : 2;  // inputs per code byte: 1 (8-bit) or 2 (4-bit)
   const size_t out_bytes = (size_t)L * H * (out_dtype == MOE_Q4_OUT_F32 ? 4 : 2);
-  const size_t gu_codes = (size_t)E * I * (H / 8) * 4, gu_s = (size_t)E * I * (H / 32) * per32;
-  const size_t d_codes = (size_t)E * H * (I / 8) * 4, d_s = (size_t)E * H * (I / 32) * per32;
+  const size_t gu_codes = (size_t)E * I * H / cb, gu_s = (size_t)E * I * (H / 32) * per32;
+  const size_t d_codes = (size_t)E * H * I / cb, d_s = (size_t)E * H * (I / 32) * per32;
   const struct { const void* p; size_t n; } ins[] = {
       {x, (size_t)L * H * 2}, {topk_ids, (size_t)L * k * 4}, {topk_weights, (size_t)L * k * 4},
       {wg, gu_codes}, {sg, gu_s}, {wu, gu_codes}, {su, gu_s}, {wd, d_codes}, {sd, d_s},

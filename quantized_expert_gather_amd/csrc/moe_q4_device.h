@@ -132,6 +132,68 @@ __device__ __forceinline__ float dot32_nv_f16(const uint4 w, const uint32_t (&hv
   return __builtin_fmaf(d[1], s1, d[0] * s0);
 }
 
+// 8-bit codes: a 16-byte load holds 16 elements (element c is byte c % 4 of
+// word c / 4, lowest byte first), against 8 activation pairs in natural order.
+//
+// Affine 8-bit against bf16 pairs: each byte q = l + 16 h is split into its
+// nibbles, each placed under the bf16 128 exponent as for 4-bit codes, so
+// the sum of the 16 products comes out as sum_c a_c * (q_c + 2176) with
+// 2176 = 128 * (1 + 16), exact products and fp32 accumulation.
+__device__ __forceinline__ float dot16_a8_bf16(const uint4 w, const uint32_t (&av)[16], float d) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  float dl = 0.0f, dh = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t q[4];
+    unpack_word(ws[i], kMagicBytes, q);  // (l0,l1), (l2,l3), (h0,h1), (h2,h3) of the word's bytes
+    dl = dot2_bf16(q[0], av[2 * i], dl);
+    dl = dot2_bf16(q[1], av[2 * i + 1], dl);
+    dh = dot2_bf16(q[2], av[2 * i], dh);
+    dh = dot2_bf16(q[3], av[2 * i + 1], dh);
+  }
+  return __builtin_fmaf(16.0f, dh, dl + d);
+}
+
+// Affine 8-bit against fp16 pairs: a byte under the fp16 1024 exponent is
+// 1024 + q exactly, two per v_perm; sum_c h_c * (q_c + 1024).
+__device__ __forceinline__ float dot16_a8_f16(const uint4 w, const uint32_t (&hv)[16], float d) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // selector bytes 0-3 pick bytes of the second operand, 4-7 of the first
+    d = dot2_f16(__builtin_amdgcn_perm(kMagicBytesF16, ws[i], 0x04010400u), hv[2 * i], d);
+    d = dot2_f16(__builtin_amdgcn_perm(kMagicBytesF16, ws[i], 0x04030402u), hv[2 * i + 1], d);
+  }
+  return d;
+}
+
+// mxfp8 (OCP MX: FP8 E4M3 elements, E8M0 scale per 32 inputs): gfx950's
+// scaled FP8 conversions turn two E4M3 bytes (word_sel false: bytes 0 and 1,
+// true: bytes 2 and 3) into an exact bf16 / fp16 pair (scale operand 1.0).
+__device__ __forceinline__ float dot16_mx8_bf16(const uint4 w, const uint32_t (&av)[16], float d) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ws[i], 1.0f, false),
+                                        __builtin_bit_cast(bf16x2_t, av[2 * i]), d, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ws[i], 1.0f, true),
+                                        __builtin_bit_cast(bf16x2_t, av[2 * i + 1]), d, false);
+  }
+  return d;
+}
+
+__device__ __forceinline__ float dot16_mx8_f16(const uint4 w, const uint32_t (&hv)[16], float d) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    d = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ws[i], 1.0f, false),
+                               __builtin_bit_cast(half2_t, hv[2 * i]), d, false);
+    d = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ws[i], 1.0f, true),
+                               __builtin_bit_cast(half2_t, hv[2 * i + 1]), d, false);
+  }
+  return d;
+}
+
 // Value of an FP8 E4M3 byte (OCP: exponent bias 7, three mantissa bits,
 // exponent 0 subnormal, S.1111.111 NaN), exact in fp32: a normal number's
 // fields move into the fp32 fields; a subnormal m/8 * 2^-6 is m * 2^-9.

@@ -32,5 +32,13 @@ const void* gateup_kernel_affine32_0(int lpr, int ppl, bool full);
 const void* gateup_kernel_affine32_1(int lpr, int ppl, bool full);
 const void* down_kernel_affine32_0(int lpr, int ppl, bool full, int nt);
 const void* down_kernel_affine32_1(int lpr, int ppl, bool full, int nt);
+const void* gateup_kernel_affine8_0(int lpr, int ppl, bool full);
+const void* gateup_kernel_affine8_1(int lpr, int ppl, bool full);
+const void* down_kernel_affine8_0(int lpr, int ppl, bool full, int nt);
+const void* down_kernel_affine8_1(int lpr, int ppl, bool full, int nt);
+const void* gateup_kernel_mxfp8_0(int lpr, int ppl, bool full);
+const void* gateup_kernel_mxfp8_1(int lpr, int ppl, bool full);
+const void* down_kernel_mxfp8_0(int lpr, int ppl, bool full, int nt);
+const void* down_kernel_mxfp8_1(int lpr, int ppl, bool full, int nt);
 
 }  // namespace moeq4

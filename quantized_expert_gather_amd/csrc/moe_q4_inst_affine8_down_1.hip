@@ -1,0 +1,21 @@
+// Instantiations of the down kernel over 8-bit affine banks (group 64), part 1.
+#include "moe_q4_inst.h"
+#include "moe_q4_union_kernels.h"
+
+namespace moeq4 {
+
+#define MOEQ4_DN_F_NT(L_, P_, F_) \
+  (nt == 1 ? (const void*)&k_down<L_, P_, F_, false, 1, kFmtAffine8> : (const void*)&k_down<L_, P_, F_, false, 2, kFmtAffine8>)
+#define MOEQ4_DN_F(L_, P_) \
+  if (lpr == L_ && ppl == P_) return full ? MOEQ4_DN_F_NT(L_, P_, true) : MOEQ4_DN_F_NT(L_, P_, false);
+
+const void* down_kernel_affine8_1(int lpr, int ppl, bool full, int nt) {
+  MOEQ4_DN_F(32, 1)
+  MOEQ4_DN_F(16, 1)
+  MOEQ4_DN_F(8, 1)
+  MOEQ4_DN_F(4, 1)
+  MOEQ4_DN_F(2, 1)
+  return nullptr;
+}
+
+}  // namespace moeq4

@@ -12,8 +12,20 @@ constexpr int kFmtAffine = 0;    // 4-bit affine, bf16 scale and bias per 64 inp
 constexpr int kFmtMxfp4 = 1;     // FP4 E2M1, E8M0 scale per 32 inputs
 constexpr int kFmtNvfp4 = 2;     // FP4 E2M1, FP8 E4M3 scale per 16 inputs
 constexpr int kFmtAffine32 = 3;  // 4-bit affine, bf16 scale and bias per 32 inputs
+constexpr int kFmtAffine8 = 4;   // 8-bit affine, bf16 scale and bias per 64 inputs
+constexpr int kFmtMxfp8 = 5;     // FP8 E4M3, E8M0 scale per 32 inputs
 // FP4 element formats: converted in hardware into natural-order pairs, no bias
 __host__ __device__ constexpr bool fmt_fp4(int f) { return f == kFmtMxfp4 || f == kFmtNvfp4; }
+__host__ __device__ constexpr bool fmt_8bit(int f) { return f == kFmtAffine8 || f == kFmtMxfp8; }
+// staged activations / hidden vectors in natural element order (else the
+// 4-bit affine nibble-pair order)
+__host__ __device__ constexpr bool fmt_natural(int f) { return fmt_fp4(f) || fmt_8bit(f); }
+// a per-group bias (affine) and so per-position activation sums
+__host__ __device__ constexpr bool fmt_biased(int f) { return !fmt_fp4(f) && f != kFmtMxfp8; }
+// 16-byte loads per position of the activations; a position is the inputs of
+// one 16-byte weight load: 32 for 4-bit codes, 16 for 8-bit codes
+__host__ __device__ constexpr int fmt_na(int f) { return fmt_8bit(f) ? 2 : 4; }
+__host__ __device__ constexpr int fmt_pos_inputs(int f) { return 8 * fmt_na(f); }
 
 // Arguments of one union-path forward (device pointers; LDS offsets in bytes).
 struct UnionArgs {
@@ -55,8 +67,8 @@ struct UnionWorkspace {
 };
 
 UnionWorkspace union_workspace_layout(int L, int k, int E, int H, int I);
-bool union_shape_supported(int L, int k, int E, int H, int I);
-size_t union_lds_bytes_max(int L, int k, int E, int H, int I);
+bool union_shape_supported(int L, int k, int E, int H, int I, int fmt = kFmtAffine);
+size_t union_lds_bytes_max(int L, int k, int E, int H, int I, int fmt = kFmtAffine);
 int union_forward_launch(const UnionArgs& a, unsigned stages, int num_cu, hipStream_t stream);
 int route_union_launch(const int32_t* ids, const float* tw, int L, int k, int E, int32_t* u, int32_t* uniq_ids,
                        uint32_t* tok_mask, float* uniq_w, int32_t* slot_to_uniq, hipStream_t stream);

@@ -118,9 +118,9 @@ size_t union_lds(int E, int P) { return (size_t)4 * (2 * ((E + 31) >> 5) + 5 * P
 
 // gate/up LDS: activations of all L tokens | their 32-input sums | route union
 size_t gateup_lds_layout(UnionArgs& a) {
-  const int KU = a.H / 32;
+  const int KU = a.H / fmt_pos_inputs(a.fmt);  // positions; the activations take 2 H bytes per token
   size_t off = 0;
-  a.lds_act = off;   off = align16(off + (size_t)a.L * 4 * KU * 16);
+  a.lds_act = off;   off = align16(off + (size_t)a.L * fmt_na(a.fmt) * KU * 16);
   a.lds_asum = off;  off = align16(off + (size_t)a.L * KU * 4);
   a.lds_union = off; off = align16(off + union_lds(a.E, a.L * a.k));
   return off;
@@ -147,19 +147,21 @@ int blocks_per_cu(const void* fn, int threads, size_t lds) {
 
 }  // namespace
 
-size_t union_lds_bytes_max(int L, int k, int E, int H, int I) {
+size_t union_lds_bytes_max(int L, int k, int E, int H, int I, int fmt) {
   UnionArgs a{};
-  a.L = L; a.k = k; a.E = E; a.H = H; a.I = I;
+  a.L = L; a.k = k; a.E = E; a.H = H; a.I = I; a.fmt = fmt;
   return gateup_lds_layout(a);
 }
 
-bool union_shape_supported(int L, int k, int E, int H, int I) {
-  const int lg = lanes_per_row(H / 32), ld = lanes_per_row(I / 32);
-  if (!positions_per_lane(H / 32, lg, false) || !positions_per_lane(I / 32, ld, true)) return false;
-  if ((I % (gateup_rows(positions_per_lane(H / 32, lg, false)) * (64 / lg))) != 0) return false;
+bool union_shape_supported(int L, int k, int E, int H, int I, int fmt) {
+  const int pos = fmt_pos_inputs(fmt), KG = H / pos, KD = I / pos;
+  const int lg = lanes_per_row(KG), ld = lanes_per_row(KD);
+  if (!positions_per_lane(KG, lg, false) || !positions_per_lane(KD, ld, true)) return false;
+  if ((I % (gateup_rows(positions_per_lane(KG, lg, false)) * (64 / lg))) != 0) return false;
   // a down step covers whole row steps of every expert
   if (H % ((64 / ld) * down_rows(64 / ld)) != 0) return false;
-  return union_lds_bytes_max(L, k, E, H, I) <= kMaxLds && down_lds_head(L * k) + down_slot_bytes(I / 32) + 256 <= kMaxLds;
+  return union_lds_bytes_max(L, k, E, H, I, fmt) <= kMaxLds &&
+         down_lds_head(L * k) + down_slot_bytes(KD, fmt_na(fmt)) + 256 <= kMaxLds;
 }
 
 int route_union_launch(const int32_t* ids, const float* tw, int L, int k, int E, int32_t* u, int32_t* uniq_ids,
@@ -176,7 +178,7 @@ int union_forward_launch(const UnionArgs& base, unsigned stages, int num_cu, hip
   const int u_max = P < base.E ? P : base.E;
   if (stages & MOE_Q4_STAGE_GATEUP) {
     UnionArgs a = base;
-    const int KU = a.H / 32;
+    const int KU = a.H / fmt_pos_inputs(a.fmt);
     const int lpr = lanes_per_row(KU), ppl = positions_per_lane(KU, lpr, false);
     const size_t lds = gateup_lds_layout(a);
     const void* fn = a.fmt != kFmtAffine ? gateup_kernel_fmt(a.fmt, lpr, ppl, lpr * ppl == KU)
@@ -193,13 +195,14 @@ int union_forward_launch(const UnionArgs& base, unsigned stages, int num_cu, hip
   }
   if (stages & MOE_Q4_STAGE_DOWN) {
     UnionArgs a = base;
-    const int KU = a.I / 32;
+    const int KU = a.I / fmt_pos_inputs(a.fmt), NA = fmt_na(a.fmt);
     const int lpr = lanes_per_row(KU), ppl = positions_per_lane(KU, lpr, true);
     // as many pair slots staged at once as the LDS holds, up to all of them
     const size_t base_lds = down_lds_head(P);
-    if (base_lds + down_slot_bytes(KU) + 256 > kMaxLds) return MOE_Q4_ERR_UNSUPPORTED;
-    a.dn_slots = (int)std::min<size_t>((size_t)P, (kMaxLds - 256 - base_lds) / down_slot_bytes(KU));
-    size_t lds = base_lds + (size_t)a.dn_slots * down_slot_bytes(KU);
+    const size_t slot_bytes = down_slot_bytes(KU, NA);
+    if (base_lds + slot_bytes + 256 > kMaxLds) return MOE_Q4_ERR_UNSUPPORTED;
+    a.dn_slots = (int)std::min<size_t>((size_t)P, (kMaxLds - 256 - base_lds) / slot_bytes);
+    size_t lds = base_lds + (size_t)a.dn_slots * slot_bytes;
     const bool qs = a.fmt == kFmtAffine && (a.I / 64) % 2 == 0;
     // one token per register pass when every expert has exactly one token
     // (L = 1), or when a lane holds several positions per row (a second
@@ -210,7 +213,7 @@ int union_forward_launch(const UnionArgs& base, unsigned stages, int num_cu, hip
     // combine kernel is not needed
     const int wstep = (64 / lpr) * down_rows(64 / lpr);
     const int blk_rows = ((a.H / wstep + num_cu - 1) / num_cu) * wstep;
-    const size_t rows_lds = base_lds + (size_t)P * down_slot_bytes(KU) + (size_t)P * blk_rows * 4;
+    const size_t rows_lds = base_lds + (size_t)P * slot_bytes + (size_t)P * blk_rows * 4;
     a.dn_rows = a.L == 1 && rows_lds + 256 <= kMaxLds;
     if (a.dn_rows) {
       a.dn_slots = P;
@@ -260,6 +263,8 @@ const void* gateup_kernel_fmt(int fmt, int lpr, int ppl, bool full) {
     case kFmtAffine32:
       f = gateup_kernel_affine32_0(lpr, ppl, full);
       return f ? f : gateup_kernel_affine32_1(lpr, ppl, full);
+    case kFmtAffine8: f = gateup_kernel_affine8_0(lpr, ppl, full); return f ? f : gateup_kernel_affine8_1(lpr, ppl, full);
+    case kFmtMxfp8: f = gateup_kernel_mxfp8_0(lpr, ppl, full); return f ? f : gateup_kernel_mxfp8_1(lpr, ppl, full);
   }
   return nullptr;
 }
@@ -272,6 +277,10 @@ const void* down_kernel_fmt(int fmt, int lpr, int ppl, bool full, int nt) {
     case kFmtAffine32:
       f = down_kernel_affine32_0(lpr, ppl, full, nt);
       return f ? f : down_kernel_affine32_1(lpr, ppl, full, nt);
+    case kFmtAffine8:
+      f = down_kernel_affine8_0(lpr, ppl, full, nt);
+      return f ? f : down_kernel_affine8_1(lpr, ppl, full, nt);
+    case kFmtMxfp8: f = down_kernel_mxfp8_0(lpr, ppl, full, nt); return f ? f : down_kernel_mxfp8_1(lpr, ppl, full, nt);
   }
   return nullptr;
 }

@@ -179,14 +179,15 @@ template <int PPL, int RG, bool FULL, bool QS, int FMT = kFmtAffine>
 __device__ __forceinline__ void gu_load(const UnionArgs& a, size_t row0, int nrows, int KU, int KG, int li, int lpr,
                                         const unsigned char* lane_sbase, const GuOffsets<PPL, RG>& o,
                                         GuFrag<PPL, RG>& f) {
-  if constexpr (fmt_fp4(FMT)) {
-    // scale bytes per (row, 32-input position): one E8M0 (mxfp4) or two E4M3
-    // (nvfp4) for gate and as many for up, packed gate low, up high
-    constexpr int SB = FMT == kFmtNvfp4 ? 2 : 1;
+  if constexpr (fmt_fp4(FMT) || FMT == kFmtMxfp8) {
+    // scale bytes of a row: two E4M3 per position (nvfp4), one E8M0 per 32
+    // inputs (mxfp4: per position; mxfp8: per two positions); packed gate
+    // low, up high
+    const size_t srow = FMT == kFmtNvfp4 ? (size_t)KU * 2 : FMT == kFmtMxfp8 ? (size_t)(KU >> 1) : (size_t)KU;
     const unsigned char* wg = reinterpret_cast<const unsigned char*>(a.wg) + row0 * KU * 16;
     const unsigned char* wu = reinterpret_cast<const unsigned char*>(a.wu) + row0 * KU * 16;
-    const unsigned char* eg = reinterpret_cast<const unsigned char*>(a.sg) + row0 * KU * SB;
-    const unsigned char* eu = reinterpret_cast<const unsigned char*>(a.su) + row0 * KU * SB;
+    const unsigned char* eg = reinterpret_cast<const unsigned char*>(a.sg) + row0 * srow;
+    const unsigned char* eu = reinterpret_cast<const unsigned char*>(a.su) + row0 * srow;
 #pragma unroll
     for (int p = 0; p < PPL; ++p) {
       if (FULL || li + lpr * p < KU) {
@@ -245,7 +246,7 @@ __device__ __forceinline__ void gu_compute(const UnionArgs& a, const GuFrag<PPL,
       touch(f.w[p][r][0]);
       touch(f.w[p][r][1]);
       touch(f.sb[p][r][0]);
-      if (!QS && !fmt_fp4(FMT)) touch(f.sb[p][r][1]);
+      if (!QS && fmt_biased(FMT)) touch(f.sb[p][r][1]);
     }
   uint32_t sbv[PPL][RG][2];
   float nvs[PPL][RG][4];  // nvfp4: decoded scales (gate lo, gate hi, up lo, up hi)
@@ -257,7 +258,7 @@ __device__ __forceinline__ void gu_compute(const UnionArgs& a, const GuFrag<PPL,
 #pragma unroll
         for (int q = 0; q < 4; ++q) nvs[p][r][q] = e4m3_to_f32((f.sb[p][r][0] >> (8 * q)) & 0xFFu);
         sbv[p][r][0] = sbv[p][r][1] = 0u;
-      } else if (FMT == kFmtMxfp4) {
+      } else if (FMT == kFmtMxfp4 || FMT == kFmtMxfp8) {
         sbv[p][r][0] = f.sb[p][r][0] & 0xFFu;         // E8M0 byte of gate
         sbv[p][r][1] = (f.sb[p][r][0] >> 8) & 0xFFu;  // and of up
       } else if (QS) {
@@ -277,11 +278,33 @@ __device__ __forceinline__ void gu_compute(const UnionArgs& a, const GuFrag<PPL,
     for (int p = 0; p < PPL; ++p) {
       const int j = li + LPR * p;
       if (FULL || j < KU) {
-        const uint4* xa = act + (size_t)t * 4 * KU + j;
-        const uint4 x0 = xa[0], x1 = xa[KU], x2 = xa[2 * KU], x3 = xa[3 * KU];
-        const uint32_t xv[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
-                                 x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
-        if constexpr (FMT == kFmtMxfp4) {  // x staged in natural element order
+        constexpr int NA = fmt_na(FMT);
+        const uint4* xa = act + (size_t)t * NA * KU + j;
+        uint32_t xv[16];
+#pragma unroll
+        for (int c = 0; c < NA; ++c) {
+          const uint4 xc = xa[c * KU];
+          xv[4 * c + 0] = xc.x; xv[4 * c + 1] = xc.y; xv[4 * c + 2] = xc.z; xv[4 * c + 3] = xc.w;
+        }
+        if constexpr (FMT == kFmtMxfp8) {  // 16 inputs per position, natural order
+#pragma unroll
+          for (int r = 0; r < RG; ++r)
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm)
+              acc[r][mm] += mx_scaled(dot16_mx8_bf16(opaque<(PPL >= kGuOpaquePpl)>(f.w[p][r][mm]), xv, 0.0f),
+                                      sbv[p][r][mm]);
+        } else if constexpr (FMT == kFmtAffine8) {  // 16 inputs per position, natural order
+          const float xs = asum[(size_t)t * KU + j];
+#pragma unroll
+          for (int r = 0; r < RG; ++r)
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm) {
+              const float d = dot16_a8_bf16(opaque<(PPL >= kGuOpaquePpl)>(f.w[p][r][mm]), xv, 0.0f);
+              const float sc = bf16_lo_to_f32(sbv[p][r][mm]);
+              const float bi = bf16_hi_to_f32(sbv[p][r][mm]) - 2176.0f * sc;
+              acc[r][mm] += sc * d + bi * xs;
+            }
+        } else if constexpr (FMT == kFmtMxfp4) {  // x staged in natural element order
 #pragma unroll
           for (int r = 0; r < RG; ++r)
 #pragma unroll
@@ -403,9 +426,10 @@ __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int H = a.H, I = a.I, k = a.k, L = a.L, E = a.E;
   const int P = L * k;
-  const int KU = H >> 5, KG = FMT == kFmtAffine32 ? KU : H >> 6;  // positions, affine groups
-  uint4* act = reinterpret_cast<uint4*>(smem + a.lds_act);      // [L][4][KU] bf16 pairs in code order
-  float* asum = reinterpret_cast<float*>(smem + a.lds_asum);     // [L][KU] sums of the 32 inputs
+  constexpr int NA = fmt_na(FMT);
+  const int KU = H / fmt_pos_inputs(FMT), KG = FMT == kFmtAffine32 ? KU : H >> 6;  // positions, affine groups
+  uint4* act = reinterpret_cast<uint4*>(smem + a.lds_act);      // [L][NA][KU] bf16 pairs
+  float* asum = reinterpret_cast<float*>(smem + a.lds_asum);     // [L][KU] sums of each position's inputs
   UnionLds s;
   carve_union(smem + a.lds_union, E, P, s);
   const int tid = threadIdx.x;
@@ -413,19 +437,19 @@ __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
   if (tid == 0) unit_q = 2 * kWaves;
   stage_routes(a.ids, a.tw, P, s);  // first loads of the kernel
   // stage all tokens' activations (independent of the union; overlaps it):
-  // three 32-input positions per thread per round, all loads issued first
+  // three positions per thread per round, all loads issued first
   {
     constexpr int XB = 3;
     const int nx = L * KU;
     for (int base = tid; base < nx; base += XB * kThreads) {
-      uint4 v[XB][4];
+      uint4 v[XB][NA];
 #pragma unroll
       for (int b = 0; b < XB; ++b) {
         const int it = min(base + b * kThreads, nx - 1);
         const int t = it / KU, j = it - t * KU;
-        const uint4* xs = reinterpret_cast<const uint4*>(a.x + (size_t)t * H) + 4 * j;
+        const uint4* xs = reinterpret_cast<const uint4*>(a.x + (size_t)t * H) + NA * j;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v[b][c] = xs[c];
+        for (int c = 0; c < NA; ++c) v[b][c] = xs[c];
       }
 #pragma unroll
       for (int b = 0; b < XB; ++b) {
@@ -434,12 +458,12 @@ __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
           const int t = it / KU, j = it - t * KU;
           float sum = 0.0f;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            if (!fmt_fp4(FMT)) sum = sum8_bf16(v[b][c], sum);
-            // FP4 codes convert to pairs in natural element order
-            act[((size_t)t * 4 + c) * KU + j] = fmt_fp4(FMT) ? v[b][c] : pair_activations(v[b][c]);
+          for (int c = 0; c < NA; ++c) {
+            if (fmt_biased(FMT)) sum = sum8_bf16(v[b][c], sum);
+            // FP4 and 8-bit codes convert to pairs in natural element order
+            act[((size_t)t * NA + c) * KU + j] = fmt_natural(FMT) ? v[b][c] : pair_activations(v[b][c]);
           }
-          if (!fmt_fp4(FMT)) asum[(size_t)t * KU + j] = sum;
+          if (fmt_biased(FMT)) asum[(size_t)t * KU + j] = sum;
         }
       }
     }
@@ -461,9 +485,11 @@ __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
     for (int r = 0; r < RG; ++r) {
       const int j = li + LPR * p;
       o.w[p][r] = (uint32_t)(((g * RG + r) * KU + j) * 16);
-      const int grp = QS ? 2 * (li >> 2) + (LPR / 2) * p : FMT == kFmtAffine32 ? j : (j >> 1);
-      o.s[p][r] = fmt_fp4(FMT) ? (uint32_t)(((g * RG + r) * KU + j) * (FMT == kFmtNvfp4 ? 2 : 1))
-                               : (uint32_t)(((g * RG + r) * KG + grp) * 2);
+      const int grp = QS ? 2 * (li >> 2) + (LPR / 2) * p
+                         : FMT == kFmtAffine32 ? j : FMT == kFmtAffine8 ? (j >> 2) : (j >> 1);
+      o.s[p][r] = FMT == kFmtMxfp8 ? (uint32_t)((g * RG + r) * (KU >> 1) + (j >> 1))
+                  : fmt_fp4(FMT)   ? (uint32_t)(((g * RG + r) * KU + j) * (FMT == kFmtNvfp4 ? 2 : 1))
+                                   : (uint32_t)(((g * RG + r) * KG + grp) * 2);
     }
   // Work units: (distinct expert, WROWS hidden rows).  Block b owns units
   // b, b + nblk, b + 2 nblk, ... (adjacent blocks take adjacent rows, so the
@@ -546,12 +572,15 @@ template <int PPL, int RS, bool FULL, bool QS, int FMT = kFmtAffine>
 __device__ __forceinline__ void dn_load(const UnionArgs& a, size_t row0, bool valid, size_t row_fallback, int nrows,
                                         int KU, int KG, int li, int lpr, const unsigned char* lane_sbase,
                                         const DnOffsets<PPL, RS>& o, DnFrag<PPL, RS>& f) {
-  if constexpr (fmt_fp4(FMT)) {  // one E8M0 (mxfp4) or two E4M3 (nvfp4) bytes per (row, position)
+  if constexpr (fmt_fp4(FMT) || FMT == kFmtMxfp8) {
+    // two E4M3 bytes per position (nvfp4), one E8M0 byte per 32 inputs
+    // (mxfp4: per position; mxfp8: per two positions)
     constexpr int SB = FMT == kFmtNvfp4 ? 2 : 1;
+    const size_t srow = FMT == kFmtNvfp4 ? (size_t)KU * 2 : FMT == kFmtMxfp8 ? (size_t)(KU >> 1) : (size_t)KU;
     const rsrc_t wd = make_rsrc(reinterpret_cast<const unsigned char*>(a.wd) + row0 * KU * 16,
                                 valid ? (uint32_t)(nrows * KU * 16) : 0u);
-    const rsrc_t ed = make_rsrc(reinterpret_cast<const unsigned char*>(a.sd) + (valid ? row0 : row_fallback) * KU * SB,
-                                valid ? (uint32_t)(nrows * KU * SB) : 0u);
+    const rsrc_t ed = make_rsrc(reinterpret_cast<const unsigned char*>(a.sd) + (valid ? row0 : row_fallback) * srow,
+                                valid ? (uint32_t)(nrows * srow) : 0u);
 #pragma unroll
     for (int r = 0; r < RS; ++r)
 #pragma unroll
@@ -584,10 +613,10 @@ __device__ __forceinline__ void dn_load(const UnionArgs& a, size_t row0, bool va
 }
 
 // LDS of a down block: the union table, the work prefix per expert, then
-// per staged pair slot its hidden vector as fp16 pairs in code order
-// [4][KU] (uint4), the sums of the 32 fp16 values per position [KU], the
-// router weight times the slot's 2^-k and the slot's ys row.
-__host__ __device__ constexpr size_t down_slot_bytes(int KU) { return (size_t)KU * 68 + 8; }
+// per staged pair slot its hidden vector as fp16 pairs [NA][KU] (uint4; KU
+// positions of 8 NA inputs), the sums of each position's fp16 values [KU],
+// the router weight times the slot's 2^-k and the slot's ys row.
+__host__ __device__ constexpr size_t down_slot_bytes(int KU, int na = 4) { return (size_t)KU * (16 * na + 4) + 8; }
 __host__ __device__ constexpr size_t down_lds_base(int P) { return ((size_t)16 * P + 15) & ~size_t(15); }
 // bytes before the staged slots: the union table and the work prefix
 __host__ __device__ constexpr size_t down_lds_head(int P) {
@@ -596,7 +625,10 @@ __host__ __device__ constexpr size_t down_lds_head(int P) {
 
 // Converts pair slot `slot` (h of one (expert, token) pair, fp32) into staged
 // slot `ls`: scaled by the power of two that puts its largest magnitude in
-// [2^13, 2^14), rounded to fp16.  One wave per slot.
+// [2^13, 2^14), rounded to fp16.  One wave per slot; a lane converts 32
+// inputs at a time (one position of 4-bit codes, two of 8-bit codes).  KU
+// counts 32-input blocks.
+template <int NA>
 __device__ __forceinline__ void down_stage_slot(const UnionArgs& a, int ls, int slot, int KU, uint4* hvs, float* hss,
                                                 float* stw, int* sdst, bool natural) {
   const int lane = threadIdx.x & 63;
@@ -627,9 +659,17 @@ __device__ __forceinline__ void down_stage_slot(const UnionArgs& a, int ls, int 
         const int lo = natural ? 2 * kk : pair_lo(kk), hi = natural ? 2 * kk + 1 : pair_hi(kk);
         pw[kk] = (uint32_t)__builtin_bit_cast(uint16_t, hb[lo]) | ((uint32_t)__builtin_bit_cast(uint16_t, hb[hi]) << 16);
       }
-      hvs[((size_t)ls * 4 + wi) * KU + j] = pk;
+      if constexpr (NA == 4) {
+        hvs[((size_t)ls * 4 + wi) * KU + j] = pk;
+      } else {  // positions 2j and 2j + 1 of 16 inputs, two uint4 each
+        hvs[((size_t)ls * 2 + (wi & 1)) * (2 * KU) + 2 * j + (wi >> 1)] = pk;
+        if (wi & 1) {
+          hss[(size_t)ls * 2 * KU + 2 * j + (wi >> 1)] = sum;
+          sum = 0.0f;
+        }
+      }
     }
-    hss[(size_t)ls * KU + j] = sum;
+    if constexpr (NA == 4) hss[(size_t)ls * KU + j] = sum;
   };
   float mx = 0.0f;
   int ex;
@@ -689,7 +729,15 @@ __device__ __forceinline__ void dn_step(const UnionArgs& a, const DnFrag<PPL, RS
 #pragma unroll
     for (int p = 0; p < PPL; ++p) {
       if (FULL || li + LPR * p < KU) {
-        if constexpr (FMT == kFmtMxfp4) {  // hidden vectors staged as fp16 pairs in natural order
+        if constexpr (FMT == kFmtMxfp8) {  // 16 inputs per position, natural order
+#pragma unroll
+          for (int c = 0; c < NT; ++c) acc[c][r] += mx_scaled(dot16_mx8_f16(f.w[r][p], hv[c][p], 0.0f), f.sb[r][p]);
+        } else if constexpr (FMT == kFmtAffine8) {
+          const float sc = bf16_lo_to_f32(f.sb[r][p]);
+          const float bi = bf16_hi_to_f32(f.sb[r][p]) - 1024.0f * sc;
+#pragma unroll
+          for (int c = 0; c < NT; ++c) acc[c][r] += sc * dot16_a8_f16(f.w[r][p], hv[c][p], 0.0f) + bi * hs[c][p];
+        } else if constexpr (FMT == kFmtMxfp4) {  // hidden vectors staged as fp16 pairs in natural order
 #pragma unroll
           for (int c = 0; c < NT; ++c) acc[c][r] += mx_scaled(dot32_mx_f16(f.w[r][p], hv[c][p], 0.0f), f.sb[r][p]);
         } else if constexpr (FMT == kFmtNvfp4) {
@@ -748,9 +796,10 @@ __device__ __forceinline__ void dn_segment(const UnionArgs& a, size_t ebase, int
     for (int p = 0; p < PPL; ++p) {
       const int j = li + LPR * p;
       if (FULL || j < KU) {
-        const uint4* hp = hvs + (size_t)ls * 4 * KU + j;
+        constexpr int NA = fmt_na(FMT);
+        const uint4* hp = hvs + (size_t)ls * NA * KU + j;
 #pragma unroll
-        for (int wi = 0; wi < 4; ++wi) {
+        for (int wi = 0; wi < NA; ++wi) {
           const uint4 h4 = hp[wi * KU];
           hv[c][p][4 * wi + 0] = h4.x; hv[c][p][4 * wi + 1] = h4.y;
           hv[c][p][4 * wi + 2] = h4.z; hv[c][p][4 * wi + 3] = h4.w;
@@ -807,12 +856,13 @@ __global__ __launch_bounds__(down_threads(NT, PPL)) void k_down(UnionArgs a) {
   static_assert(!QS || RS % 2 == 0, "quad-shared scales pair rows");
   extern __shared__ __align__(16) unsigned char smem[];
   const int H = a.H, I = a.I, P = a.L * a.k;
-  const int KU = I >> 5, KG = FMT == kFmtAffine32 ? KU : I >> 6;  // positions, affine groups
+  constexpr int NA = fmt_na(FMT);
+  const int KU = I / fmt_pos_inputs(FMT), KG = FMT == kFmtAffine32 ? KU : I >> 6;  // positions, affine groups
   const int SM = a.dn_slots;  // pair slots converted at a time
   int4* utab = reinterpret_cast<int4*>(smem);
   int* wpre = reinterpret_cast<int*>(smem + down_lds_base(P));     // [P + 1] work prefix per expert
-  uint4* hvs = reinterpret_cast<uint4*>(smem + down_lds_head(P));  // [SM][4][KU]
-  float* hss = reinterpret_cast<float*>(hvs + (size_t)SM * 4 * KU);  // [SM][KU]
+  uint4* hvs = reinterpret_cast<uint4*>(smem + down_lds_head(P));  // [SM][NA][KU]
+  float* hss = reinterpret_cast<float*>(hvs + (size_t)SM * NA * KU);  // [SM][KU]
   float* stw = hss + (size_t)SM * KU;                                 // [SM]
   int* sdst = reinterpret_cast<int*>(stw + SM);                       // [SM]
   __shared__ int unit_q;  // next dynamically assigned unit (block-relative)
@@ -863,9 +913,11 @@ __global__ __launch_bounds__(down_threads(NT, PPL)) void k_down(UnionArgs a) {
       const int j = li + LPR * p;
       o.w[r][p] = (uint32_t)(((g * RS + r) * KU + j) * 16);
       const int srow = QS ? (r & ~1) + (qa >> 1) : r;
-      const int grp = QS ? 2 * (li >> 2) + (LPR / 2) * p : FMT == kFmtAffine32 ? j : (j >> 1);
-      o.s[r][p] = fmt_fp4(FMT) ? (uint32_t)(((g * RS + r) * KU + j) * (FMT == kFmtNvfp4 ? 2 : 1))
-                               : (uint32_t)(((g * RS + srow) * KG + grp) * 2);
+      const int grp = QS ? 2 * (li >> 2) + (LPR / 2) * p
+                         : FMT == kFmtAffine32 ? j : FMT == kFmtAffine8 ? (j >> 2) : (j >> 1);
+      o.s[r][p] = FMT == kFmtMxfp8 ? (uint32_t)((g * RS + r) * (KU >> 1) + (j >> 1))
+                  : fmt_fp4(FMT)   ? (uint32_t)(((g * RS + r) * KU + j) * (FMT == kFmtNvfp4 ? 2 : 1))
+                                   : (uint32_t)(((g * RS + srow) * KG + grp) * 2);
     }
 
   if (NT == 1 && a.dn_rows) {
@@ -878,7 +930,8 @@ __global__ __launch_bounds__(down_threads(NT, PPL)) void k_down(UnionArgs a) {
     const int ns = s1 - s0, nrows = ns * WSTEP;
     if (ns <= 0) return;  // uniform over the block
     float* part = reinterpret_cast<float*>(sdst + SM);  // [u][nrows]
-    for (int sl = wave; sl < u; sl += NW) down_stage_slot(a, sl, sl, KU, hvs, hss, stw, sdst, fmt_fp4(FMT));
+    for (int sl = wave; sl < u; sl += NW)
+      down_stage_slot<NA>(a, sl, sl, I >> 5, hvs, hss, stw, sdst, fmt_natural(FMT));
     __syncthreads();
     const int nch = max(1, min(ns, NW / max(u, 1)));  // step chunks per expert
     const int cs = (ns + nch - 1) / nch;
@@ -927,7 +980,8 @@ __global__ __launch_bounds__(down_threads(NT, PPL)) void k_down(UnionArgs a) {
   for (int c0 = s_lo; c0 < s_hi; c0 += SM) {
     const int c1 = min(s_hi, c0 + SM);
     if (tid == 0) unit_q = NW;
-    for (int sl = c0 + wave; sl < c1; sl += NW) down_stage_slot(a, sl - c0, sl, KU, hvs, hss, stw, sdst, fmt_fp4(FMT));
+    for (int sl = c0 + wave; sl < c1; sl += NW)
+      down_stage_slot<NA>(a, sl - c0, sl, I >> 5, hvs, hss, stw, sdst, fmt_natural(FMT));
     __syncthreads();
     for (int j = wave; j < nub; j = grab()) {
       const int un = ub + j;

@@ -306,3 +306,25 @@ def test_codec_host_checks():
     assert call_codec(A32, out=fake(5) + 64) == q.MOE_Q4_ERR_ALIAS
     assert call_codec(NV, out=fake(5) + 64, ws=0) == q.MOE_Q4_ERR_WORKSPACE
     assert call_codec(NV, out=fake(10) + 64) == q.MOE_Q4_ERR_ALIAS
+
+
+def test_codec_8bit_host_checks():
+    A8, MX8 = q.MOE_Q4_CODEC_AFFINE8_G64, q.MOE_Q4_CODEC_MXFP8
+    # group 64 for the 8-bit affine codes, 32 for mxfp8
+    assert call_codec(A8, H=288) == q.MOE_Q4_ERR_UNSUPPORTED
+    assert call_codec(A8, I=96) == q.MOE_Q4_ERR_UNSUPPORTED
+    assert q.moe_swiglu_codec_workspace_bytes(A8, 2, 2, 4, 320, 128) > 0
+    assert q.moe_swiglu_codec_workspace_bytes(MX8, 2, 2, 4, 96, 256) > 0
+    assert q.moe_swiglu_codec_workspace_bytes(A8, 8, 8, 256, 6144, 2048) == \
+        q.moe_swiglu_q4_workspace_bytes(8, 8, 256, 6144, 2048)
+    # biases required for the 8-bit affine codes only; E8M0 scales need no alignment
+    p = [fake(j) for j in range(12)]
+    p[5] = 0
+    assert call_codec(A8, ptrs=p) == q.MOE_Q4_ERR_NULL
+    assert call_codec(MX8, ptrs=p, ws=0) == q.MOE_Q4_ERR_WORKSPACE
+    p = [fake(j) for j in range(12)]
+    p[4] += 1
+    assert call_codec(A8, ptrs=p) == q.MOE_Q4_ERR_ALIGN
+    assert call_codec(MX8, ptrs=p, ws=0) == q.MOE_Q4_ERR_WORKSPACE
+    # 8-bit codes are twice the bytes: out just past the 4-bit size of wg still aliases
+    assert call_codec(A8, out=fake(3) + 8 * 128 * 256 // 2 + 64) == q.MOE_Q4_ERR_ALIAS

@@ -1,8 +1,9 @@
 """GPU parity of the union path over the further weight codecs (needs an MI355X).
 
 Codecs: 4-bit affine with group 32, nvfp4 (E2M1 elements, an FP8 E4M3 scale
-per 16 inputs) and mxfp4 through the generic codec entry point, each against
-the CPU oracle's evaluation of the same codec.  The pages name these storage
+per 16 inputs), mxfp4, 8-bit affine with group 64 and mxfp8 (E4M3 elements,
+an E8M0 scale per 32 inputs) through the generic codec entry point, each
+against the CPU oracle's evaluation of the same codec.  The pages name these storage
 modes (the dequant-mode comparison of the mlx discussion "Small-L fused
 expert gather for fine-grained MoE decode"; nvfp4 among the quantized modes
 of PR 4572 on the page "MoE GatherQMM small-M verify cost", Facts) without
@@ -26,7 +27,7 @@ pytestmark = pytest.mark.gpu
 
 CONTRACT = 1e-3
 ARITH = 6e-4
-CODECS = ["affine4_g32", "nvfp4", "mxfp4"]
+CODECS = ["affine4_g32", "nvfp4", "mxfp4", "affine8_g64", "mxfp8"]
 
 
 def _q():
@@ -103,8 +104,27 @@ SMALL_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("codec", CODECS)
-@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "L%d_k%d_E%d_H%d_I%d_dup%d" % s)
+# the same cases with H and I multiples of 64 (group-64 8-bit affine codes)
+SMALL_SHAPES_64 = [
+    (1, 2, 4, 64, 64, False),
+    (2, 2, 4, 128, 256, False),
+    (3, 2, 6, 384, 192, True),
+    (5, 3, 7, 320, 128, True),
+    (8, 4, 16, 2048, 256, False),
+    (4, 8, 12, 4096, 192, True),
+    (2, 8, 64, 6144, 128, False),
+    (16, 4, 40, 512, 512, False),
+    (32, 2, 48, 256, 512, True),
+    (6, 1, 3, 1088, 2048, False),
+    (4, 4, 4, 8192, 192, False),
+    (3, 4, 4, 256, 4096, True),
+    (4, 8, 16, 7168, 256, False),
+]
+SHAPE_CASES = [(c, sh) for c in CODECS for sh in (SMALL_SHAPES_64 if c == "affine8_g64" else SMALL_SHAPES)]
+
+
+@pytest.mark.parametrize("codec,shape", SHAPE_CASES,
+                         ids=[f"{c}-L%d_k%d_E%d_H%d_I%d_dup%d" % sh for c, sh in SHAPE_CASES])
 def test_codec_small_shapes(codec, shape):
     L, k, E, H, I, dup = shape
     x, ids, tw, bank = synth.random_problem_q(codec, L, k, E, H, I, seed=sum(shape), dup=dup)
