@@ -22,8 +22,9 @@ adjacent-token overlap follows the measured depth-graded profile.
   come from chains of one stage alone (gate+up, or down+combine) over the
   same layers, timed the same way.
 * codecs: the same verify routes and activations over banks in other codecs
-  (mxfp4 gs32, the pages' GLM-5.2 format; nvfp4; 4-bit affine group 32),
-  at L = 1, 2, 4, 8, each with its own bytes per expert.
+  (mxfp4 gs32, the pages' GLM-5.2 format; nvfp4; 4-bit affine group 32;
+  8-bit affine group 64; mxfp8), at L = 1, 2, 4, 8, each with its own bytes
+  per expert.
 * cpu_baseline: the CPU oracle (test infrastructure) timed on a bounded
   sample of the same layers on the host cores, with the same metric; the
   same layers are checked for parity (fp32 output before the bf16 cast,
@@ -150,9 +151,12 @@ def expert_bytes_codec(codec: str, H: int, I: int) -> int:
     the scales (and biases) of each group -- mxfp4: one byte per 32 inputs
     (about 20 MB at H=6144, I=2048, the size the mlx discussion "Small-L fused
     expert gather for fine-grained MoE decode" gives for the GLM-5.2 experts);
-    nvfp4: one byte per 16; affine group 32: a bf16 scale and bias per 32."""
-    per = {"mxfp4": 1 / 32, "nvfp4": 1 / 16, "affine4_g32": 4 / 32}[codec]
-    return 3 * (H * I // 2 + round(H * I * per))
+    nvfp4: one byte per 16; affine group 32: a bf16 scale and bias per 32;
+    8-bit codecs: one byte per element plus a bf16 scale and bias per 64
+    (affine) or one byte per 32 (mxfp8)."""
+    bits, per = {"mxfp4": (4, 1 / 32), "nvfp4": (4, 1 / 16), "affine4_g32": (4, 4 / 32),
+                 "affine8_g64": (8, 4 / 64), "mxfp8": (8, 1 / 32)}[codec]
+    return 3 * (H * I * bits // 8 + round(H * I * per))
 
 
 def bench_codec(codec, args, Ls, q, synth, torch, np, dev, stream, sleep_cycles_for):
@@ -263,7 +267,7 @@ def main():
     ap.add_argument("--pair-layers", type=int, default=20,
                     help="layers of each chain timed again as a per-pair baseline (one call per token, so "
                          "an expert shared by tokens is streamed once per token); 0 to skip")
-    ap.add_argument("--codecs", default="mxfp4,nvfp4,affine4_g32",
+    ap.add_argument("--codecs", default="mxfp4,nvfp4,affine4_g32,affine8_g64,mxfp8",
                     help="other weight codecs timed on the verify workload (comma list; empty to skip)")
     ap.add_argument("--codec-layers", type=int, default=19,
                     help="layers per L of each codec's verify chains (spread over the depth profile)")
