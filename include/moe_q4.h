@@ -195,13 +195,24 @@ size_t moe_swiglu_codec_workspace_bytes(int codec, int L, int k, int E, int H, i
  * All other arguments, the results' definition and the status codes are as
  * for moe_swiglu_q4_forward.  MOE_Q4_CODEC_AFFINE4_G64 is exactly
  * moe_swiglu_q4_forward (both paths).  The other codecs run on the union
- * kernels only.  Calls with more tokens than one union launch serves
- * (L > MOE_Q4_UNION_MAX_L or L * k > MOE_Q4_MAX_PAIRS) run as consecutive
- * chunks of min(MOE_Q4_UNION_MAX_L, MOE_Q4_MAX_PAIRS / k) tokens on the
- * same workspace (sized by moe_swiglu_codec_workspace_bytes for one chunk);
- * each chunk streams the distinct experts of its own tokens, so long inputs
- * re-read the bank once per chunk.  Such calls need stages ==
- * MOE_Q4_STAGE_ALL.  The device status word is the OR over the chunks.
+ * kernels, in chunks of at most min(MOE_Q4_UNION_MAX_L, MOE_Q4_MAX_PAIRS / k)
+ * tokens, fewer where that many tokens' activations do not fit one
+ * workgroup's LDS (large H).  Calls with more tokens than one chunk run the
+ * chunks one after another on the same workspace (sized by
+ * moe_swiglu_codec_workspace_bytes); each chunk streams the distinct experts
+ * of its own tokens, so long inputs re-read the bank once per chunk.  Such
+ * calls need stages == MOE_Q4_STAGE_ALL.  The device status word is the OR
+ * over the chunks.
+ *
+ * MXFP4 with L > min(MOE_Q4_UNION_MAX_L, MOE_Q4_MAX_PAIRS / k) and H and I
+ * multiples of 1024 takes the sorted path instead (expert-sorted pairs,
+ * grouped bf16 MFMA GEMMs, every bank byte read once per tile row block; the
+ * device path word reads MOE_Q4_PATH_SORTED; stage-split calls allowed).
+ * There the scale arrays sg, su and sd must be 8-byte aligned: unaligned
+ * ones run as token chunks where the shape allows that, else give
+ * MOE_Q4_ERR_ALIGN.  Results are as on the union path (NaN for e = 255,
+ * subnormal block scales honoured).
+ *
  * L <= MOE_Q4_CODEC_MAX_L.  An unknown codec gives MOE_Q4_ERR_UNSUPPORTED.
  */
 int moe_swiglu_codec_forward(int codec, const void *x, const int32_t *topk_ids, const float *topk_weights,

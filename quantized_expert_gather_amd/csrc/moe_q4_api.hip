@@ -58,13 +58,24 @@ static int select_path(int L, int k, int E, int H, int I) {
   return -MOE_Q4_ERR_UNSUPPORTED;
 }
 
-// Codecs other than 4-bit affine group 64 run on the union kernels only, with
-// H and I multiples of 32 (one scale per 32 inputs at least; 64 for the
+// Codecs other than 4-bit affine group 64 run on the union kernels, with H
+// and I multiples of 32 (one scale per 32 inputs at least; 64 for the
 // group-64 8-bit affine codes).  More tokens than one union launch serves
-// are run as consecutive token chunks.
-static int codec_chunk_tokens(int L, int k) {
-  const int cap = std::min(MOE_Q4_UNION_MAX_L, MOE_Q4_MAX_PAIRS / k);
-  return L < cap ? L : cap;
+// run as consecutive token chunks: at most 32 tokens and 256 pairs, fewer
+// where the chunk's activations would not fit the LDS.  mxfp4 inputs longer
+// than that take the sorted (MFMA) path where its streaming kernels cover
+// the shape.
+static int union_token_cap(int k) { return std::min(MOE_Q4_UNION_MAX_L, MOE_Q4_MAX_PAIRS / k); }
+
+// Tokens per union launch; 0 if not even one token fits.
+static int codec_chunk_tokens(int L, int k, int E, int H, int I, int fmt) {
+  int c = std::min(L, union_token_cap(k));
+  while (c > 0 && !union_shape_supported(c, k, E, H, I, fmt)) --c;
+  return c;
+}
+
+static bool codec_sorted(int fmt, int L, int k, int E, int H, int I) {
+  return fmt == kFmtMxfp4 && L > union_token_cap(k) && sorted_mx_shape_supported(L, k, E, H, I);
 }
 
 static int codec_shape_status(int L, int k, int E, int H, int I, int fmt) {
@@ -72,9 +83,28 @@ static int codec_shape_status(int L, int k, int E, int H, int I, int fmt) {
   const int grp = fmt == kFmtAffine8 ? 64 : 32;
   if (H % grp || I % grp || E > MOE_Q4_MAX_E || k > MOE_Q4_MAX_PAIRS || L > MOE_Q4_CODEC_MAX_L)
     return MOE_Q4_ERR_UNSUPPORTED;
-  if (L == 0) return MOE_Q4_OK;
-  if (!union_shape_supported(codec_chunk_tokens(L, k), k, E, H, I, fmt)) return MOE_Q4_ERR_UNSUPPORTED;
+  if (L == 0 || codec_sorted(fmt, L, k, E, H, I)) return MOE_Q4_OK;
+  if (codec_chunk_tokens(L, k, E, H, I, fmt) < 1) return MOE_Q4_ERR_UNSUPPORTED;
   return MOE_Q4_OK;
+}
+
+// Points the workspace arrays of a sorted-path call into `ws`.
+static void sorted_workspace_args(SortedArgs& a, unsigned char* ws, const SortedWorkspace& sw) {
+  a.bm = 32 * sorted_row_blocks(a.T, a.k, a.E);
+  a.tiles_max = sorted_tiles_max(a.T, a.k, a.E, a.bm);
+  a.hdr = reinterpret_cast<uint32_t*>(ws + sw.hdr);
+  a.offsets = reinterpret_cast<int32_t*>(ws + sw.offsets);
+  a.perm = reinterpret_cast<int32_t*>(ws + sw.perm);
+  a.inv = reinterpret_cast<int32_t*>(ws + sw.inv);
+  a.rank_tmp = reinterpret_cast<int32_t*>(ws + sw.rank_tmp);
+  a.tiles = reinterpret_cast<int4*>(ws + sw.tiles);
+  a.asum = reinterpret_cast<float*>(ws + sw.asum);
+  a.hhi = reinterpret_cast<uint16_t*>(ws + sw.hhi);
+  a.hlo = reinterpret_cast<uint16_t*>(ws + sw.hlo);
+  a.hsum2 = reinterpret_cast<float*>(ws + sw.hsum2);
+  a.ys = reinterpret_cast<float*>(ws + sw.ys);
+  a.mxflag_gu = reinterpret_cast<uint32_t*>(ws + sw.mxflag);
+  a.mxflag_dn = a.mxflag_gu + sorted_flag_count(a.T, a.k, a.E, a.H, a.I);
 }
 
 // Kernel format of a codec; -1 for an unknown codec.
@@ -171,19 +201,8 @@ int moe_swiglu_q4_forward_stages(const void* x, const int32_t* topk_ids, const f
     a.out = out;
     a.out_f32 = out_dtype == MOE_Q4_OUT_F32;
     a.T = L; a.k = k; a.E = E; a.H = H; a.I = I;
-    a.bm = 32 * sorted_row_blocks(L, k, E);
-    a.tiles_max = sorted_tiles_max(L, k, E, a.bm);
-    a.hdr = reinterpret_cast<uint32_t*>(ws + sw.hdr);
-    a.offsets = reinterpret_cast<int32_t*>(ws + sw.offsets);
-    a.perm = reinterpret_cast<int32_t*>(ws + sw.perm);
-    a.inv = reinterpret_cast<int32_t*>(ws + sw.inv);
-    a.rank_tmp = reinterpret_cast<int32_t*>(ws + sw.rank_tmp);
-    a.tiles = reinterpret_cast<int4*>(ws + sw.tiles);
-    a.asum = reinterpret_cast<float*>(ws + sw.asum);
-    a.hhi = reinterpret_cast<uint16_t*>(ws + sw.hhi);
-    a.hlo = reinterpret_cast<uint16_t*>(ws + sw.hlo);
-    a.hsum2 = reinterpret_cast<float*>(ws + sw.hsum2);
-    a.ys = reinterpret_cast<float*>(ws + sw.ys);
+    a.fmt = kFmtAffine;
+    sorted_workspace_args(a, ws, sw);
     return sorted_forward_launch(a, stages, stream);
   }
 
@@ -224,8 +243,12 @@ int moe_swiglu_q4_forward(const void* x, const int32_t* topk_ids, const float* t
 
 size_t moe_swiglu_codec_workspace_bytes(int codec, int L, int k, int E, int H, int I) {
   if (codec == MOE_Q4_CODEC_AFFINE4_G64) return moe_swiglu_q4_workspace_bytes(L, k, E, H, I);
-  if (codec_fmt(codec) < 0 || L == 0 || codec_shape_status(L, k, E, H, I, codec_fmt(codec))) return 0;
-  return union_workspace_layout(codec_chunk_tokens(L, k), k, E, H, I).total;
+  const int fmt = codec_fmt(codec);
+  if (fmt < 0 || L == 0 || codec_shape_status(L, k, E, H, I, fmt)) return 0;
+  const int Lc = codec_chunk_tokens(L, k, E, H, I, fmt);
+  const size_t un = Lc > 0 ? union_workspace_layout(Lc, k, E, H, I).total : 0;
+  // enough for the token chunks too, which serve scale arrays not aligned for the sorted path
+  return codec_sorted(fmt, L, k, E, H, I) ? std::max(un, sorted_workspace_layout(L, k, E, H, I).total) : un;
 }
 
 int moe_swiglu_codec_forward_stages(int codec, const void* x, const int32_t* topk_ids, const float* topk_weights,
@@ -243,9 +266,13 @@ int moe_swiglu_codec_forward_stages(int codec, const void* x, const int32_t* top
   if (out_dtype != MOE_Q4_OUT_BF16 && out_dtype != MOE_Q4_OUT_F32) return MOE_Q4_ERR_UNSUPPORTED;
   if (stages == 0 || (stages & ~MOE_Q4_STAGE_ALL)) return MOE_Q4_ERR_UNSUPPORTED;
   if (L == 0) return MOE_Q4_OK;
-  const int Lc = codec_chunk_tokens(L, k);
+  const int Lc = codec_chunk_tokens(L, k, E, H, I, fmt);
+  // the sorted path reads the scale bytes 8 at a time; unaligned ones run as token chunks
+  const bool mx_al = aligned(sg, 8) && aligned(su, 8) && aligned(sd, 8);
+  const bool srt = codec_sorted(fmt, L, k, E, H, I) && (mx_al || Lc < 1);
+  if (srt && !mx_al) return MOE_Q4_ERR_ALIGN;
   // stage-only calls hand the hidden vectors of one launch to the next
-  if (Lc < L && stages != MOE_Q4_STAGE_ALL) return MOE_Q4_ERR_UNSUPPORTED;
+  if (!srt && Lc < L && stages != MOE_Q4_STAGE_ALL) return MOE_Q4_ERR_UNSUPPORTED;
   const bool biased = fmt == kFmtAffine32 || fmt == kFmtAffine8;
   if (!x || !topk_ids || !topk_weights || !wg || !sg || !wu || !su || !wd || !sd || !out) return MOE_Q4_ERR_NULL;
   if (biased && (!bg || !bu || !bd)) return MOE_Q4_ERR_NULL;
@@ -258,8 +285,9 @@ int moe_swiglu_codec_forward_stages(int codec, const void* x, const int32_t* top
       !aligned(topk_ids, 4) || !aligned(topk_weights, 4) || !aligned(workspace, 256) || !aligned(sg, sa) ||
       !aligned(su, sa) || !aligned(sd, sa) || (biased && (!aligned(bg, 2) || !aligned(bu, 2) || !aligned(bd, 2))))
     return MOE_Q4_ERR_ALIGN;
-  const UnionWorkspace lay = union_workspace_layout(Lc, k, E, H, I);
-  if (workspace_bytes < lay.total) return MOE_Q4_ERR_WORKSPACE;
+  const UnionWorkspace lay = union_workspace_layout(srt ? 1 : Lc, k, E, H, I);
+  const size_t ws_need = srt ? sorted_workspace_layout(L, k, E, H, I).total : lay.total;
+  if (workspace_bytes < ws_need) return MOE_Q4_ERR_WORKSPACE;
 
   // bytes of one scale array per 32 inputs of a row: a bf16 per 32 (affine
   // group 32) or per 64 (8-bit affine), two E4M3 (nvfp4), one E8M0 (mx)
@@ -272,9 +300,26 @@ int moe_swiglu_codec_forward_stages(int codec, const void* x, const int32_t* top
       {x, (size_t)L * H * 2}, {topk_ids, (size_t)L * k * 4}, {topk_weights, (size_t)L * k * 4},
       {wg, gu_codes}, {sg, gu_s}, {wu, gu_codes}, {su, gu_s}, {wd, d_codes}, {sd, d_s},
       {biased ? bg : nullptr, biased ? gu_s : 0}, {biased ? bu : nullptr, biased ? gu_s : 0},
-      {biased ? bd : nullptr, biased ? d_s : 0}, {workspace, lay.total}};
+      {biased ? bd : nullptr, biased ? d_s : 0}, {workspace, ws_need}};
   for (const auto& in : ins)
     if (in.p && overlaps(out, out_bytes, in.p, in.n)) return MOE_Q4_ERR_ALIAS;
+
+  if (srt) {
+    SortedArgs a{};
+    a.x = static_cast<const uint16_t*>(x);
+    a.ids = topk_ids;
+    a.tw = topk_weights;
+    // E8M0 bytes travel in the scale slots; no biases
+    a.wg = wg; a.sg = static_cast<const uint16_t*>(sg);
+    a.wu = wu; a.su = static_cast<const uint16_t*>(su);
+    a.wd = wd; a.sd = static_cast<const uint16_t*>(sd);
+    a.out = out;
+    a.out_f32 = out_dtype == MOE_Q4_OUT_F32;
+    a.T = L; a.k = k; a.E = E; a.H = H; a.I = I;
+    a.fmt = fmt;
+    sorted_workspace_args(a, static_cast<unsigned char*>(workspace), sorted_workspace_layout(L, k, E, H, I));
+    return sorted_forward_launch(a, stages, stream);
+  }
 
   const int ncu = num_cus();
   if (ncu <= 0) return MOE_Q4_ERR_LAUNCH;

@@ -91,6 +91,7 @@ struct SortedArgs {
   void* out;
   int out_f32;
   int T, k, E, H, I;
+  int fmt;            // kFmtAffine, or kFmtMxfp4 (scale slots hold E8M0 bytes, no biases)
   int bm;             // rows per tile (32, 64 or 128)
   int tiles_max;      // capacity of `tiles`
   uint32_t* hdr;      // [0] status, [1] path, [2] valid pairs, [3] tiles
@@ -104,16 +105,21 @@ struct SortedArgs {
   uint16_t* hlo;      // [P][I] bf16 lo of h (h - hi, rounded)
   float* hsum2;       // [P][I/32] sum of hi + lo over each 32 columns
   float* ys;          // [P][H] per-pair down outputs, unweighted
+  uint32_t* mxflag_gu;  // mxfp4: per gate/up block, 1 if it needs the exact pass
+  uint32_t* mxflag_dn;  // mxfp4: per down block, likewise
 };
 
 struct SortedWorkspace {
-  size_t hdr, offsets, perm, inv, rank_tmp, tiles, asum, hhi, hlo, hsum2, ys, total;
+  size_t hdr, offsets, perm, inv, rank_tmp, tiles, asum, hhi, hlo, hsum2, ys, mxflag, total;
 };
 
 int sorted_row_blocks(int T, int k, int E);
 int sorted_tiles_max(int T, int k, int E, int bm);
+size_t sorted_flag_count(int T, int k, int E, int H, int I);
 SortedWorkspace sorted_workspace_layout(int T, int k, int E, int H, int I);
 bool sorted_shape_supported(int T, int k, int E, int H, int I);
+// mxfp4 banks on the sorted path: the streaming kernels, H and I multiples of 1024
+bool sorted_mx_shape_supported(int T, int k, int E, int H, int I);
 int sort_launch(const SortedArgs& a, hipStream_t stream);
 int sorted_forward_launch(const SortedArgs& a, unsigned stages, hipStream_t stream);
 

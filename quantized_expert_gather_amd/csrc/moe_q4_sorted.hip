@@ -550,15 +550,152 @@ __device__ __forceinline__ Codes4 load_codes4(const uint32_t* W, size_t rowc, in
   return c;
 }
 
-template <int MT>
+// mxfp4 banks (E2M1 codes in the same word layout, one E8M0 scale byte per
+// 32 inputs of a row).  The scale bytes of 4 consecutive 64-input groups of
+// one row: byte 2 q + hh is the 32-input block of lane half hh in group q.
+__device__ __forceinline__ uint2 load_mx_scales(const unsigned char* S, size_t rowb, int g0) {
+  return *reinterpret_cast<const uint2*>(S + rowb + 2 * g0);
+}
+
+__device__ __forceinline__ uint32_t mx_scale_byte(uint2 s, int q, int hh) {
+  return ((q < 2 ? s.x : s.y) >> (8 * (2 * (q & 1) + hh))) & 0xFFu;
+}
+
+// Exponent bytes for which every E2M1 magnitude (0.5 to 6) times 2^(e - 127)
+// is a normal, finite bf16: there the scaled conversion is exact and the
+// scale can be folded into the MFMA operand.
+__device__ __forceinline__ bool mx_fold_exact(uint32_t e) { return e >= 2u && e <= 252u; }
+
+// One code word (8 E2M1 codes, low nibble first) as 8 bf16 in element order,
+// each multiplied by `sc` in the conversion.
+__device__ __forceinline__ uint4 mx_word_bf16(uint32_t w, float sc) {
+  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3)));
+}
+
+// acc += A x B for one 64-input mxfp4 group: A = NPL staged planes of the
+// rows (natural element order), B = the lane's 4 code words of its column.
+//   folded: the block scale went into the conversion of bq (exact, see
+//           mx_fold_exact), so the MFMAs accumulate straight into acc.
+//   split:  bq was converted with unit scale; each 32-input block gets its
+//           own MFMA chain (the A operand of the other lane half zeroed) and is
+//           scaled in fp32 afterwards by s0 (inputs 0..31) or s1 (32..63),
+//           which also carries NaN (e = 255) and subnormal scales.
+template <int NPL>
+__device__ __forceinline__ void mx_mfma_folded(f32x16_t& acc, const uint4 (&bq)[4],
+                                               const unsigned char* const (&ap)[NPL]) {
+#pragma unroll
+  for (int pl = 0; pl < NPL; ++pl)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = mfma_bf16(*reinterpret_cast<const uint4*>(ap[pl] + 16 * s), bq[s], acc);
+}
+
+template <int NPL>
+__device__ __forceinline__ void mx_mfma_split(f32x16_t& acc, const uint4 (&bq)[4], const unsigned char* const (&ap)[NPL],
+                                              float s0, float s1, int hh) {
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+  f32x16_t p0 = {}, p1 = {};
+#pragma unroll
+  for (int pl = 0; pl < NPL; ++pl)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 av = *reinterpret_cast<const uint4*>(ap[pl] + 16 * s);
+      // the product over one 32-input block: the other lane half's A operand is zeroed
+      p0 = mfma_bf16(hh ? z : av, bq[s], p0);
+      p1 = mfma_bf16(hh ? av : z, bq[s], p1);
+    }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = fmaf(s1, p1[i], fmaf(s0, p0[i], acc[i]));
+  __builtin_amdgcn_sched_barrier(0);  // one row block at a time: no operand reads hoisted across blocks
+}
+
+// The scales of one group for the lane's column: s0 for inputs 0..31, s1 for
+// 32..63 (2^(e - 127), NaN for e = 255), and whether both halves of every
+// column of the wave can be folded.
+__device__ __forceinline__ void mx_group_scales(uint32_t e, int hh, float& s0, float& s1) {
+  const float own = mx_scaled(1.0f, e);
+  const float oth = __shfl_xor(own, 32);
+  s0 = hh ? oth : own;
+  s1 = hh ? own : oth;
+}
+
+// Kernel modes of the streaming kernels.  mxfp4 runs in two passes:
+// kSortMxFold folds every block scale into the conversions (the fast form,
+// exact while every exponent byte of the block's groups passes
+// mx_fold_exact) and flags blocks where one does not; kSortMxExact then
+// recomputes only the flagged blocks with per-32-input chains and fp32
+// scaling, and returns at once elsewhere.
+constexpr int kSortAffine = 0, kSortMxFold = 1, kSortMxExact = 2;
+
+// One iteration (4 groups of 64 inputs) of an mxfp4 column wave: acc[m] +=
+// rows of block m (NPL planes `plane` bytes apart, from `arows`) x this
+// lane's codes `cur` with exponent bytes `sc`.
+template <int MT, int MXM, int NPL>
+__device__ __forceinline__ void mx_iteration(f32x16_t (&acc)[MT], const Codes4& cur, uint2 sc,
+                                             const unsigned char* arows, size_t plane, int nrt, int hh,
+                                             int& blk_split) {
+  if constexpr (MXM == kSortMxFold) {
+    bool ok = true;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ok = ok && mx_fold_exact(mx_scale_byte(sc, q, hh));
+    if (!ok) blk_split = 1;  // the exact pass recomputes this block
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float fs = __uint_as_float(mx_scale_byte(sc, q, hh) << 23);  // 2^(e - 127) for 1 <= e <= 254
+      uint4 bq[4];
+      bq[0] = mx_word_bf16(cur.q[q].x, fs);
+      bq[1] = mx_word_bf16(cur.q[q].y, fs);
+      bq[2] = mx_word_bf16(cur.q[q].z, fs);
+      bq[3] = mx_word_bf16(cur.q[q].w, fs);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m < nrt) {
+          const unsigned char* const r = arows + (size_t)m * kRowTile * kV2Row + 128 * q;
+          const unsigned char* ap[NPL];
+#pragma unroll
+          for (int pl = 0; pl < NPL; ++pl) ap[pl] = r + pl * plane;
+          mx_mfma_folded<NPL>(acc[m], bq, ap);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float s0, s1;
+      mx_group_scales(mx_scale_byte(sc, q, hh), hh, s0, s1);
+      uint4 bq[4];
+      bq[0] = mx_word_bf16(cur.q[q].x, 1.0f);
+      bq[1] = mx_word_bf16(cur.q[q].y, 1.0f);
+      bq[2] = mx_word_bf16(cur.q[q].z, 1.0f);
+      bq[3] = mx_word_bf16(cur.q[q].w, 1.0f);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m < nrt) {
+          const unsigned char* const r = arows + (size_t)m * kRowTile * kV2Row + 128 * q;
+          const unsigned char* ap[NPL];
+#pragma unroll
+          for (int pl = 0; pl < NPL; ++pl) ap[pl] = r + pl * plane;
+          mx_mfma_split<NPL>(acc[m], bq, ap, s0, s1, hh);
+        }
+      }
+    }
+  }
+}
+
+template <int MT, int MXM>
 __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) {
+  constexpr bool MX = MXM != kSortAffine;
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int blk_split;  // kSortMxFold: some group of this block needs the exact pass
   const int H = a.H, I = a.I, G = H / 64;
   const int nit = G / 4, nch = G / 16;
   const int ncb = (I + kV2GuCols - 1) / kV2GuCols;
   int tile, cb;
   tile_of_block(ncb, tile, cb);
   if (tile >= (int)a.hdr[3]) return;
+  if (MXM == kSortMxExact && a.mxflag_gu[blockIdx.x] == 0) return;
   const int4 td = a.tiles[tile];
   const int e = td.x, r0 = td.y, nrows = td.z;
   const int nrt = (nrows + kRowTile - 1) / kRowTile;
@@ -575,6 +712,7 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
   float* sbuf0 = reinterpret_cast<float*>(smem + 2 * kRows * kV2Row);      // [2][4][kRows]
   int32_t* tok = reinterpret_cast<int32_t*>(sbuf0 + 8 * kRows);            // [kRows]
   for (int r = tid; r < kRows; r += kV2Threads) tok[r] = a.perm[r0 + min(r, nrows - 1)] / a.k;
+  if (tid == 0) blk_split = 0;
   __syncthreads();
 
   constexpr int kPer = kRows * 32 / kV2Threads;  // uint4 of x per thread and iteration
@@ -586,17 +724,20 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
       const int idx = tid + kV2Threads * j, r = idx >> 5, w = idx & 31;
       st[j] = *reinterpret_cast<const uint4*>(a.x + (size_t)tok[r] * H + 256 * it + 8 * w);
     }
-    const int si = min(tid, 4 * kRows - 1), q = si / kRows, r = si % kRows;
-    sst = a.asum[(size_t)tok[r] * G + 4 * it + q];
+    if constexpr (!MX) {
+      const int si = min(tid, 4 * kRows - 1), q = si / kRows, r = si % kRows;
+      sst = a.asum[(size_t)tok[r] * G + 4 * it + q];
+    }
   };
   auto stage_store = [&](int buf) {
     unsigned char* abuf = abuf0 + (size_t)buf * kRows * kV2Row;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int idx = tid + kV2Threads * j, r = idx >> 5, w = idx & 31;
-      *reinterpret_cast<uint4*>(abuf + (size_t)r * kV2Row + 16 * w) = pair_activations(st[j]);
+      // affine codes unpack in nibble-pair order, E2M1 conversions in element order
+      *reinterpret_cast<uint4*>(abuf + (size_t)r * kV2Row + 16 * w) = MX ? st[j] : pair_activations(st[j]);
     }
-    if (tid < 4 * kRows) sbuf0[buf * 4 * kRows + tid] = sst;  // [q][r] with q = tid / kRows
+    if (!MX && tid < 4 * kRows) sbuf0[buf * 4 * kRows + tid] = sst;  // [q][r] with q = tid / kRows
   };
 
   const uint32_t* W = mat ? a.wu : a.wg;
@@ -604,6 +745,8 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
   const uint16_t* B = mat ? a.bu : a.bg;
   const size_t rowc = ((size_t)e * I + col) * (size_t)(H / 8);
   const size_t rows = ((size_t)e * I + col) * (size_t)G;
+  const unsigned char* MS = reinterpret_cast<const unsigned char*>(S);  // mxfp4: E8M0 bytes [E][I][H / 32]
+  const size_t rowb = ((size_t)e * I + col) * (size_t)(H / 32);
 
   f32x16_t acc[MT];
 #pragma unroll
@@ -613,7 +756,14 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
 
   Codes4 cur = load_codes4(W, rowc, 0, hh);
   Codes4 nx = load_codes4(W, rowc, 4 * min(1, nit - 1), hh);  // codes stay two iterations ahead
-  Chunk16 ch = load_chunk16(S, B, rows);
+  Chunk16 ch{};
+  uint2 mcur{}, mnx{};
+  if constexpr (MX) {
+    mcur = load_mx_scales(MS, rowb, 0);
+    mnx = load_mx_scales(MS, rowb, 4 * min(1, nit - 1));
+  } else {
+    ch = load_chunk16(S, B, rows);
+  }
   stage_load(0);
   stage_store(0);
   __syncthreads();
@@ -627,8 +777,13 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
       const float* sbuf = sbuf0 + (ii & 1) * 4 * kRows;
       stage_load(min(it + 1, nit - 1));
       const Codes4 nn = load_codes4(W, rowc, 4 * min(it + 2, nit - 1), hh);
-      if (ii == 0) chn = load_chunk16(S, B, rows + 16 * min(c + 1, nch - 1));
-      if (wave_on) {
+      uint2 mnn{};
+      if constexpr (MX) mnn = load_mx_scales(MS, rowb, 4 * min(it + 2, nit - 1));
+      else if (ii == 0) chn = load_chunk16(S, B, rows + 16 * min(c + 1, nch - 1));
+      if (MX && wave_on) {
+        const unsigned char* const arows = abuf + (size_t)lc * kV2Row + 64 * hh;
+        mx_iteration<MT, MXM, 1>(acc, cur, mcur, arows, 0, nrt, hh, blk_split);
+      } else if (!MX && wave_on) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t w4[4] = {cur.q[q].x, cur.q[q].y, cur.q[q].z, cur.q[q].w};
@@ -661,6 +816,8 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
       __syncthreads();
       cur = nx;
       nx = nn;
+      mcur = mnx;
+      mnx = mnn;
     }
     ch = chn;
   }
@@ -675,8 +832,10 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
         for (int i = 0; i < 16; ++i) xch[(m * kRowTile + c_row(i, hh)) * kV2GuCols + 32 * cw + lc] = acc[m][i];
   }
   __syncthreads();
+  if (MXM == kSortMxFold && tid == 0) a.mxflag_gu[blockIdx.x] = blk_split;
   if (mat == 1 || !wave_on) return;
-  const int scol = (col & ~7) | ((col & 7) >> 1) | ((col & 1) << 2);
+  // affine: h columns in the down codes' nibble-pair order; mxfp4: element order
+  const int scol = MX ? col : ((col & ~7) | ((col & 7) >> 1) | ((col & 1) << 2));
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     if (m < nrt) {
@@ -689,12 +848,12 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
         const uint32_t hi = f32_to_bf16_rne(hv);
         const float hif = __uint_as_float(hi << 16);
         const uint32_t lo = f32_to_bf16_rne(hv - hif);
-        const float v = group_sum<32>(hif + __uint_as_float(lo << 16));
+        const float v = MX ? 0.0f : group_sum<32>(hif + __uint_as_float(lo << 16));
         if (r < nrows) {
           const size_t o = (size_t)(r0 + r) * I;
           a.hhi[o + scol] = (uint16_t)hi;
           a.hlo[o + scol] = (uint16_t)lo;
-          if (lc == 0) a.hsum2[(size_t)(r0 + r) * (I / 32) + col0 / 32] = v;
+          if (!MX && lc == 0) a.hsum2[(size_t)(r0 + r) * (I / 32) + col0 / 32] = v;
         }
       }
     }
@@ -704,15 +863,19 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
 // staging buffers of the down streaming kernel: two while they fit the LDS
 constexpr int down2_buffers(int mt) { return (size_t)2 * 2 * mt * kRowTile * kV2Row + 8 * mt * kRowTile * 4 <= 160 * 1024 ? 2 : 1; }
 
-template <int MT>
+template <int MT, int MXM>
 __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
+  constexpr bool MX = MXM != kSortAffine;
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int blk_split;  // kSortMxFold: some group of this block needs the exact pass
   const int H = a.H, I = a.I, G = I / 64;
   const int nit = G / 4, nch = G / 16;
   const int ncb = (H + kV2DnCols - 1) / kV2DnCols;
   int tile, cb;
   tile_of_block(ncb, tile, cb);
   if (tile >= (int)a.hdr[3]) return;
+  if (MXM == kSortMxExact && a.mxflag_dn[blockIdx.x] == 0) return;
+  if (threadIdx.x == 0) blk_split = 0;  // published by the first barrier of the stream loop
   const int4 td = a.tiles[tile];
   const int e = td.x, r0 = td.y, nrows = td.z;
   const int nrt = (nrows + kRowTile - 1) / kRowTile;
@@ -739,9 +902,11 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
       sth[j] = *reinterpret_cast<const u32x4_t*>(a.hhi + o);
       stl[j] = *reinterpret_cast<const u32x4_t*>(a.hlo + o);
     }
-    const int si = min(tid, 4 * kRows - 1), q = si / kRows, r = min(si % kRows, nrows - 1);
-    const float* hs = a.hsum2 + (size_t)(r0 + r) * (I / 32) + 2 * (4 * it + q);
-    sst = hs[0] + hs[1];
+    if constexpr (!MX) {
+      const int si = min(tid, 4 * kRows - 1), q = si / kRows, r = min(si % kRows, nrows - 1);
+      const float* hs = a.hsum2 + (size_t)(r0 + r) * (I / 32) + 2 * (4 * it + q);
+      sst = hs[0] + hs[1];
+    }
   };
   auto stage_store = [&](int buf) {
     unsigned char* abuf = abuf0 + (size_t)buf * 2 * kRows * kV2Row;
@@ -751,11 +916,13 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
       *reinterpret_cast<u32x4_t*>(abuf + (size_t)r * kV2Row + 16 * w) = sth[j];
       *reinterpret_cast<u32x4_t*>(abuf + (size_t)(kRows + r) * kV2Row + 16 * w) = stl[j];
     }
-    if (tid < 4 * kRows) sbuf0[buf * 4 * kRows + tid] = sst;
+    if (!MX && tid < 4 * kRows) sbuf0[buf * 4 * kRows + tid] = sst;
   };
 
   const size_t rowc = ((size_t)e * H + col) * (size_t)(I / 8);
   const size_t rows = ((size_t)e * H + col) * (size_t)G;
+  const unsigned char* MS = reinterpret_cast<const unsigned char*>(a.sd);  // mxfp4: E8M0 bytes [E][H][I / 32]
+  const size_t rowb = ((size_t)e * H + col) * (size_t)(I / 32);
 
   f32x16_t acc[MT];
 #pragma unroll
@@ -765,7 +932,14 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
 
   Codes4 cur = load_codes4(a.wd, rowc, 0, hh);
   Codes4 nx = load_codes4(a.wd, rowc, 4 * min(1, nit - 1), hh);  // codes stay two iterations ahead
-  Chunk16 ch = load_chunk16(a.sd, a.bd, rows);
+  Chunk16 ch{};
+  uint2 mcur{}, mnx{};
+  if constexpr (MX) {
+    mcur = load_mx_scales(MS, rowb, 0);
+    mnx = load_mx_scales(MS, rowb, 4 * min(1, nit - 1));
+  } else {
+    ch = load_chunk16(a.sd, a.bd, rows);
+  }
   stage_load(0);
   stage_store(0);
   __syncthreads();
@@ -780,8 +954,13 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
       const float* sbuf = sbuf0 + cbuf * 4 * kRows;
       stage_load(min(it + 1, nit - 1));
       const Codes4 nn = load_codes4(a.wd, rowc, 4 * min(it + 2, nit - 1), hh);
-      if (ii == 0) chn = load_chunk16(a.sd, a.bd, rows + 16 * min(c + 1, nch - 1));
-      if (wave_on) {
+      uint2 mnn{};
+      if constexpr (MX) mnn = load_mx_scales(MS, rowb, 4 * min(it + 2, nit - 1));
+      else if (ii == 0) chn = load_chunk16(a.sd, a.bd, rows + 16 * min(c + 1, nch - 1));
+      if (MX && wave_on) {
+        const unsigned char* const arows = abuf + (size_t)lc * kV2Row + 64 * hh;
+        mx_iteration<MT, MXM, 2>(acc, cur, mcur, arows, (size_t)kRows * kV2Row, nrt, hh, blk_split);
+      } else if (!MX && wave_on) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t w4[4] = {cur.q[q].x, cur.q[q].y, cur.q[q].z, cur.q[q].w};
@@ -819,10 +998,13 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
       __syncthreads();
       cur = nx;
       nx = nn;
+      mcur = mnx;
+      mnx = mnn;
     }
     ch = chn;
   }
 
+  if (MXM == kSortMxFold && tid == 0) a.mxflag_dn[blockIdx.x] = blk_split;  // after the loop's last barrier
   if (!wave_on) return;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
@@ -890,6 +1072,15 @@ int sorted_tiles_max(int T, int k, int E, int bm) {
   return (int)(P / bm + (P < E ? P : E) + 1);
 }
 
+// Blocks of the larger of the two streaming grids (tiles rounded up to 8,
+// times column blocks), for any row-block count.
+size_t sorted_flag_count(int T, int k, int E, int H, int I) {
+  // tiles of 32 rows: at least as many as any row-block count gives
+  const size_t tiles8 = (size_t)(sorted_tiles_max(T, k, E, kRowTile) + 7) / 8 * 8;
+  const int ngu = (I + kV2GuCols - 1) / kV2GuCols, ndn = (H + kV2DnCols - 1) / kV2DnCols;
+  return tiles8 * (size_t)(ngu > ndn ? ngu : ndn);
+}
+
 SortedWorkspace sorted_workspace_layout(int T, int k, int E, int H, int I) {
   SortedWorkspace w{};
   const size_t P = (size_t)T * k;
@@ -905,8 +1096,14 @@ SortedWorkspace sorted_workspace_layout(int T, int k, int E, int H, int I) {
   w.hlo = off;      off = r256(off + P * I * 2);
   w.hsum2 = off;    off = r256(off + P * (I / 32) * 4);
   w.ys = off;       off = r256(off + P * H * 4);
+  // mxfp4: one flag per block of the streaming gate/up and down grids
+  w.mxflag = off;   off = r256(off + (size_t)2 * sorted_flag_count(T, k, E, H, I) * 4);
   w.total = off;
   return w;
+}
+
+bool sorted_mx_shape_supported(int T, int k, int E, int H, int I) {
+  return H % 1024 == 0 && I % 1024 == 0 && sorted_shape_supported(T, k, E, H, I);
 }
 
 bool sorted_shape_supported(int T, int k, int E, int H, int I) {
@@ -933,12 +1130,31 @@ size_t down2_lds(int mt) {
 template <int MT>
 int gemm_launch(const SortedArgs& a, bool down, hipStream_t stream) {
   const int tiles8 = (a.tiles_max + 7) / 8 * 8;
-  if (!down && a.H % 1024 == 0) {
+  if (a.fmt == kFmtMxfp4) {
+    // the streaming kernels only (H and I multiples of 1024, checked by the caller)
+    if (a.H % 1024 || a.I % 1024) return MOE_Q4_ERR_UNSUPPORTED;
+    // the folded pass, then the exact pass over the blocks it flagged
+    if (!down) {
+      const int ncb = (a.I + kV2GuCols - 1) / kV2GuCols;
+      hipLaunchKernelGGL((k_sorted_gateup2<MT, kSortMxFold>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT),
+                         stream, a);
+      if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;
+      hipLaunchKernelGGL((k_sorted_gateup2<MT, kSortMxExact>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT),
+                         stream, a);
+    } else {
+      const int ncb = (a.H + kV2DnCols - 1) / kV2DnCols;
+      hipLaunchKernelGGL((k_sorted_down2<MT, kSortMxFold>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT),
+                         stream, a);
+      if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;
+      hipLaunchKernelGGL((k_sorted_down2<MT, kSortMxExact>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT),
+                         stream, a);
+    }
+  } else if (!down && a.H % 1024 == 0) {
     const int ncb = (a.I + kV2GuCols - 1) / kV2GuCols;
-    hipLaunchKernelGGL(k_sorted_gateup2<MT>, dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT), stream, a);
+    hipLaunchKernelGGL((k_sorted_gateup2<MT, kSortAffine>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT), stream, a);
   } else if (down && a.I % 1024 == 0) {
     const int ncb = (a.H + kV2DnCols - 1) / kV2DnCols;
-    hipLaunchKernelGGL(k_sorted_down2<MT>, dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT), stream, a);
+    hipLaunchKernelGGL((k_sorted_down2<MT, kSortAffine>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT), stream, a);
   } else if (!down) {
     const int ncb = (a.I + kGuCols - 1) / kGuCols;
     hipLaunchKernelGGL(k_sorted_gateup<MT>, dim3(tiles8 * ncb), dim3(kMmThreads), gateup_lds(MT), stream, a);
@@ -963,8 +1179,10 @@ int sorted_forward_launch(const SortedArgs& a, unsigned stages, hipStream_t stre
   if (stages & MOE_Q4_STAGE_GATEUP) {
     int st = sort_launch(a, stream);
     if (st) return st;
-    hipLaunchKernelGGL(k_token_gsum, dim3(a.T), dim3(256), 0, stream, a);
-    if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;
+    if (a.fmt != kFmtMxfp4) {  // the activation group sums serve the affine correction only
+      hipLaunchKernelGGL(k_token_gsum, dim3(a.T), dim3(256), 0, stream, a);
+      if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;
+    }
     st = gemm_dispatch(a, false, stream);
     if (st) return st;
   }

@@ -222,6 +222,21 @@ def test_codec_long_inputs_run_as_token_chunks(codec):
     assert rel_err_rows(out2.cpu().numpy(), oracle.forward_pairs_q(codec, x, keep, tw0, bank)).max() <= ARITH
 
 
+@pytest.mark.parametrize("codec", CODECS)
+def test_codec_wide_hidden_runs_smaller_chunks(codec):
+    # H = 4096: 32 tokens' activations do not fit one workgroup's LDS, so the
+    # chunks hold fewer tokens (mxfp4 stays on the union path: I is not a
+    # multiple of 1024)
+    q = _q()
+    L, k, E, H, I = 40, 8, 16, 4096, 256
+    x, ids, tw, bank = synth.random_problem_q(codec, L, k, E, H, I, seed=23)
+    say(codec, "wide hidden L=40 H=4096")
+    ref = oracle.forward_pairs_q(codec, x, ids, tw, bank)
+    out, ws = run_layer(x, ids, tw, bank)
+    assert rel_err_rows(out.cpu().numpy(), ref).max() <= ARITH
+    assert q.moe_q4_read_device_status(ws) == (0, q.MOE_Q4_PATH_UNION)
+
+
 def test_codec_entry_for_affine_group64_is_the_q4_forward():
     q = _q()
     x, ids, tw, bank = synth.random_problem(4, 4, 9, 1024, 512, seed=14)
