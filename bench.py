@@ -78,29 +78,40 @@ def kernel_source_hash() -> str:
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
 
-def bench_sorted(args, Ts, q, synth, torch, np, dev, stream, sleep_cycles_for):
+def bench_sorted(args, Ts, q, synth, torch, np, dev, stream, sleep_cycles_for, codec="affine4_g64"):
     """Chains of distinct prefill layers (E=256 top-8 H=4096 I=2048, uniform routes)
-    through the sorted path: full forward, then gate+up and down stages alone."""
+    through the sorted path: full forward, then gate+up and down stages alone.
+    ``codec`` is affine4_g64 (the prefill configuration) or mxfp4."""
     w = synth.WORKLOADS["prefill"]
     H, I, E, k = w.H, w.I, w.E, w.k
-    eb = expert_bytes(H, I)
-    out = {"workload": f"{w.name}: uniform top-{k}, {args.sorted_layers} distinct layers per chain",
-           "per_T": {}}
+    mx = codec == "mxfp4"
+    eb = expert_bytes_codec(codec, H, I) if mx else expert_bytes(H, I)
+    gu_eb, dn_eb = (2 * eb // 3, eb // 3) if mx else (gateup_bytes(H, I), down_bytes(H, I))
+    out = {"workload": f"{w.name}{' in mxfp4' if mx else ''}: uniform top-{k}, "
+                       f"{args.sorted_layers} distinct layers per chain", "per_T": {}}
+    stage_codes = (("all", q.MOE_Q4_STAGE_ALL), ("gateup", q.MOE_Q4_STAGE_GATEUP), ("down", q.MOE_Q4_STAGE_DOWN))
     for T in Ts:
         layers = []
         for layer in range(args.sorted_layers):
-            lay = synth.make_layer(w, T, layer, seed=0, device=dev)
+            lay = (synth.make_layer_mx if mx else synth.make_layer)(w, T, layer, seed=0, device=dev)
             ids = torch.from_numpy(lay.ids).to(dev)
             tw = torch.from_numpy(lay.weights).to(dev)
             o = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-            ws = q.new_workspace(T, k, E, H, I, dev)
             bt = lay.bank.tensors()
-            layers.append({"u": int(lay.bank.E), "keep": (lay, ids, tw, o, ws),
-                           "calls": {st: q.PreparedForward(lay.x, ids, tw, bt, o, ws, code, stream)
-                                     for st, code in (("all", q.MOE_Q4_STAGE_ALL), ("gateup", q.MOE_Q4_STAGE_GATEUP),
-                                                      ("down", q.MOE_Q4_STAGE_DOWN))}})
-        assert q.moe_swiglu_q4_select_path(T, k, E, H, I) == q.MOE_Q4_PATH_SORTED
+            if mx:
+                ws = torch.empty(q.moe_swiglu_mxfp4_workspace_bytes(T, k, lay.bank.E, H, I), dtype=torch.uint8,
+                                 device=dev)
+                calls = {st: q.PreparedForwardMX(lay.x, ids, tw, bt, o, ws, code, stream) for st, code in stage_codes}
+            else:
+                ws = q.new_workspace(T, k, E, H, I, dev)
+                calls = {st: q.PreparedForward(lay.x, ids, tw, bt, o, ws, code, stream) for st, code in stage_codes}
+            layers.append({"u": int(lay.bank.E), "keep": (lay, ids, tw, o, ws), "calls": calls})
+        if not mx:
+            assert q.moe_swiglu_q4_select_path(T, k, E, H, I) == q.MOE_Q4_PATH_SORTED
         torch.cuda.synchronize()
+        if mx:
+            layers[0]["calls"]["all"]()
+            assert q.moe_q4_read_device_status(layers[0]["keep"][4], stream)[1] == q.MOE_Q4_PATH_SORTED
 
         def chain(which, delay):
             torch.cuda._sleep(delay)
@@ -124,8 +135,8 @@ def bench_sorted(args, Ts, q, synth, torch, np, dev, stream, sleep_cycles_for):
         u_sum = sum(l["u"] for l in layers)
         P = T * k
         flops = 6.0 * P * I * H                          # gate, up, down: 2 flops per weight per pair
-        gu_bytes = (u_sum / nl) * gateup_bytes(H, I) + 2 * T * H + 8 * T * k
-        dn_bytes = (u_sum / nl) * down_bytes(H, I)
+        gu_bytes = (u_sum / nl) * gu_eb + 2 * T * H + 8 * T * k
+        dn_bytes = (u_sum / nl) * dn_eb
         gb = (u_sum / nl) * eb / (med["all"] * 1e-3) / 1e9
         tf = flops / (med["all"] * 1e-3) / 1e12
         gu_ms, dn_ms = med["gateup"], med["down"]
@@ -264,6 +275,8 @@ def main():
                     help="token counts of the prefill (sorted-path) measurement (512 and 2048 are the "
                          "prefill configuration; 16384 is the long-prefill regime); empty to skip")
     ap.add_argument("--sorted-layers", type=int, default=4, help="distinct layers per prefill chain")
+    ap.add_argument("--sorted-mx-Ts", default="512,2048",
+                    help="token counts of the same prefill workload over mxfp4 banks (sorted path); empty to skip")
     ap.add_argument("--pair-layers", type=int, default=20,
                     help="layers of each chain timed again as a per-pair baseline (one call per token, so "
                          "an expert shared by tokens is streamed once per token); 0 to skip")
@@ -510,6 +523,10 @@ def main():
     if sorted_Ts:
         result["sorted_path"] = bench_sorted(args, sorted_Ts, q, synth, torch, np, dev, stream,
                                              lambda ms: sleep_cycles_for(ms))
+        mx_Ts = [int(v) for v in args.sorted_mx_Ts.split(",") if v.strip()]
+        if mx_Ts:
+            result["sorted_path_mxfp4"] = bench_sorted(args, mx_Ts, q, synth, torch, np, dev, stream,
+                                                       lambda ms: sleep_cycles_for(ms), codec="mxfp4")
 
     # ---- the same verify workload over banks in other codecs ----
     codecs = [c for c in args.codecs.split(",") if c.strip()]

@@ -38,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "moe_q4.h"
 #include "moe_q4_device.h"
 #include "moe_q4_internal.h"
@@ -584,15 +586,6 @@ __device__ __forceinline__ uint4 mx_word_bf16(uint32_t w, float sc) {
 //           scaled in fp32 afterwards by s0 (inputs 0..31) or s1 (32..63),
 //           which also carries NaN (e = 255) and subnormal scales.
 template <int NPL>
-__device__ __forceinline__ void mx_mfma_folded(f32x16_t& acc, const uint4 (&bq)[4],
-                                               const unsigned char* const (&ap)[NPL]) {
-#pragma unroll
-  for (int pl = 0; pl < NPL; ++pl)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mfma_bf16(*reinterpret_cast<const uint4*>(ap[pl] + 16 * s), bq[s], acc);
-}
-
-template <int NPL>
 __device__ __forceinline__ void mx_mfma_split(f32x16_t& acc, const uint4 (&bq)[4], const unsigned char* const (&ap)[NPL],
                                               float s0, float s1, int hh) {
   const uint4 z = make_uint4(0u, 0u, 0u, 0u);
@@ -621,6 +614,20 @@ __device__ __forceinline__ void mx_group_scales(uint32_t e, int hh, float& s0, f
   s1 = hh ? own : oth;
 }
 
+// Runs f(std::integral_constant<int, n>) with n = min(nrt, MT): the stream
+// loops get the tile's count of 32-row blocks as a constant, so the MFMAs of
+// all its blocks form one branch-free sequence whose LDS operand reads the
+// compiler can overlap with the matrix work of the other blocks.
+template <int MT, class F>
+__device__ __forceinline__ void with_row_blocks(int nrt, F&& f) {
+  if constexpr (MT == 1) {
+    f(std::integral_constant<int, 1>{});
+  } else {
+    if (nrt >= MT) f(std::integral_constant<int, MT>{});
+    else with_row_blocks<MT - 1>(nrt, f);
+  }
+}
+
 // Kernel modes of the streaming kernels.  mxfp4 runs in two passes:
 // kSortMxFold folds every block scale into the conversions (the fast form,
 // exact while every exponent byte of the block's groups passes
@@ -631,8 +638,9 @@ constexpr int kSortAffine = 0, kSortMxFold = 1, kSortMxExact = 2;
 
 // One iteration (4 groups of 64 inputs) of an mxfp4 column wave: acc[m] +=
 // rows of block m (NPL planes `plane` bytes apart, from `arows`) x this
-// lane's codes `cur` with exponent bytes `sc`.
-template <int MT, int MXM, int NPL>
+// lane's codes `cur` with exponent bytes `sc`, for the row blocks m < NRT
+// and m < nrt (NRT a compile-time count, or MT with the run-time nrt).
+template <int MT, int NRT, int MXM, int NPL>
 __device__ __forceinline__ void mx_iteration(f32x16_t (&acc)[MT], const Codes4& cur, uint2 sc,
                                              const unsigned char* arows, size_t plane, int nrt, int hh,
                                              int& blk_split) {
@@ -649,15 +657,38 @@ __device__ __forceinline__ void mx_iteration(f32x16_t (&acc)[MT], const Codes4& 
       bq[1] = mx_word_bf16(cur.q[q].y, fs);
       bq[2] = mx_word_bf16(cur.q[q].z, fs);
       bq[3] = mx_word_bf16(cur.q[q].w, fs);
+      if constexpr (NPL == 2) {
+        // two planes (h hi and lo): one row block at a time, so the operands
+        // of both planes stay few
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m < nrt) {
-          const unsigned char* const r = arows + (size_t)m * kRowTile * kV2Row + 128 * q;
-          const unsigned char* ap[NPL];
+        for (int m = 0; m < NRT; ++m) {
+          if (m < nrt) {
 #pragma unroll
-          for (int pl = 0; pl < NPL; ++pl) ap[pl] = r + pl * plane;
-          mx_mfma_folded<NPL>(acc[m], bq, ap);
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+              for (int pl = 0; pl < NPL; ++pl)
+                acc[m] = mfma_bf16(*reinterpret_cast<const uint4*>(arows + (size_t)m * kRowTile * kV2Row +
+                                                                   pl * plane + 128 * q + 16 * s),
+                                   bq[s], acc[m]);
+          }
         }
+        continue;
+      }
+#pragma unroll
+      for (int pl = 0; pl < NPL; ++pl) {
+        // the group's operand reads first, then the MFMAs with the row
+        // blocks interleaved (consecutive MFMAs write different accumulators)
+        uint4 av[NRT][4];
+#pragma unroll
+        for (int m = 0; m < NRT; ++m)
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            av[m][s] = *reinterpret_cast<const uint4*>(arows + (size_t)m * kRowTile * kV2Row + pl * plane + 128 * q +
+                                                       16 * s);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int m = 0; m < NRT; ++m) acc[m] = mfma_bf16(av[m][s], bq[s], acc[m]);
       }
     }
   } else {
@@ -672,7 +703,7 @@ __device__ __forceinline__ void mx_iteration(f32x16_t (&acc)[MT], const Codes4& 
       bq[3] = mx_word_bf16(cur.q[q].w, 1.0f);
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        if (m < nrt) {
+        if (m < NRT && m < nrt) {
           const unsigned char* const r = arows + (size_t)m * kRowTile * kV2Row + 128 * q;
           const unsigned char* ap[NPL];
 #pragma unroll
@@ -782,7 +813,10 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
       else if (ii == 0) chn = load_chunk16(S, B, rows + 16 * min(c + 1, nch - 1));
       if (MX && wave_on) {
         const unsigned char* const arows = abuf + (size_t)lc * kV2Row + 64 * hh;
-        mx_iteration<MT, MXM, 1>(acc, cur, mcur, arows, 0, nrt, hh, blk_split);
+        with_row_blocks<MT>(nrt, [&](auto nrt_c) {
+          constexpr int NRT = decltype(nrt_c)::value;
+          mx_iteration<MT, NRT, MXM, 1>(acc, cur, mcur, arows, 0, NRT, hh, blk_split);
+        });
       } else if (!MX && wave_on) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -959,7 +993,9 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
       else if (ii == 0) chn = load_chunk16(a.sd, a.bd, rows + 16 * min(c + 1, nch - 1));
       if (MX && wave_on) {
         const unsigned char* const arows = abuf + (size_t)lc * kV2Row + 64 * hh;
-        mx_iteration<MT, MXM, 2>(acc, cur, mcur, arows, (size_t)kRows * kV2Row, nrt, hh, blk_split);
+        // row blocks tested at run time: the two planes leave no registers
+        // for a copy of the loop per row-block count
+        mx_iteration<MT, MT, MXM, 2>(acc, cur, mcur, arows, (size_t)kRows * kV2Row, nrt, hh, blk_split);
       } else if (!MX && wave_on) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
