@@ -51,3 +51,38 @@ def test_forward_replays_under_graph_capture(shape):
         torch.cuda.synchronize()
         assert torch.equal(other, ref)
     assert np.isfinite(ref.cpu().numpy()).all()
+
+
+def test_mxfp4_sorted_forward_replays_under_graph_capture():
+    # the mxfp4 sorted path: folded pass, exact pass over the blocks it flags
+    # (one expert's gate scales are subnormal, so the flags are set on every
+    # replay), combine; replays checked against the eager result bit for bit
+    q = _q()
+    T, k, E, H, I = 48, 4, 6, 1024, 1024
+    x, ids, tw, bank = synth.random_problem_mx(T, k, E, H, I, seed=22)
+    bank.sg[2, :, ::3] = 0
+    print("[case] graph mxfp4 sorted", (T, k, E, H, I), flush=True)
+    dev = torch.device("cuda")
+    xd, idd, twd, bk = x.to(dev), torch.from_numpy(ids).to(dev), torch.from_numpy(tw).to(dev), bank.to(dev)
+    ws = torch.empty(q.moe_swiglu_mxfp4_workspace_bytes(T, k, E, H, I), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ref = q.forward_bank_mx(xd, idd, twd, bk, out_dtype=torch.float32, workspace=ws).clone()
+    torch.cuda.synchronize()
+    assert q.moe_q4_read_device_status(ws) == (0, q.MOE_Q4_PATH_SORTED)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            q.forward_bank_mx(xd, idd, twd, bk, out=out, out_dtype=torch.float32, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep}"
+        other = q.forward_bank_mx(xd, idd, twd, bk, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(other, ref)
+    assert np.isfinite(ref.cpu().numpy()).all()

@@ -227,10 +227,11 @@ def test_mx_sorted_nan_scale_reaches_exactly_its_outputs():
 
 # ---------------------------------------------------------------------------
 # the prefill workload (E = 256, top-8, H = 4096, I = 2048) in mxfp4 at full
-# size: sampled tokens against the oracle
+# size, and the long-prefill regime (T = 16384, 4 row blocks per tile):
+# sampled tokens against the oracle
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("T", [512, 2048])
+@pytest.mark.parametrize("T", [512, 2048, 16384])
 def test_mx_sorted_prefill_full_size_sampled(T):
     w = synth.WORKLOADS["prefill"]
     lay = synth.make_layer_mx(w, T, 0, seed=0, device="cuda")
