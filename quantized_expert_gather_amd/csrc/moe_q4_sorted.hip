@@ -541,6 +541,12 @@ __device__ __forceinline__ float chunk_elem(const uint4& lo, const uint4& hi, in
   return (j & 1) ? bf16_hi_to_f32(w) : bf16_lo_to_f32(w);
 }
 
+// bf16 element q (compile-time after unrolling) of 4 packed in two words
+__device__ __forceinline__ float sb4_elem(uint32_t w01, uint32_t w23, int q) {
+  const uint32_t w = q < 2 ? w01 : w23;
+  return (q & 1) ? bf16_hi_to_f32(w) : bf16_lo_to_f32(w);
+}
+
 struct Codes4 {
   uint4 q[4];  // this lane's half (4 words) of each of 4 consecutive groups
 };
@@ -635,6 +641,51 @@ __device__ __forceinline__ void with_row_blocks(int nrt, F&& f) {
 // recomputes only the flagged blocks with per-32-input chains and fp32
 // scaling, and returns at once elsewhere.
 constexpr int kSortAffine = 0, kSortMxFold = 1, kSortMxExact = 2;
+// kSortAffineSbl: affine, with the workgroup's scales and biases for the
+// whole reduction read once into LDS at its start (one coalesced read of
+// contiguous rows) instead of 16-group chunks along the stream, whose
+// 128-byte lines had left L2 between chunks and were fetched again (1.35 x
+// the algorithmic bytes).  Used for tiles of two or more row blocks where
+// the LDS holds them (down at T = 2048: 10 % faster); with one row block the
+// read ahead of the stream cost more than the refetches (T = 512: 6 %
+// slower).
+constexpr int kSortAffineSbl = 3;
+constexpr bool sort_mode_mx(int m) { return m == kSortMxFold || m == kSortMxExact; }
+
+// Copies rows [c0, c0 + ncols) of nar scale / bias arrays (bf16 [.., G] per
+// row, row c of expert e at (e * N + c) * G) into LDS rows of G + 4 elements
+// (the pad spreads a column group's reads over the banks); rows at or past N
+// are skipped.  The global reads are 16-byte pieces of contiguous rows.
+template <int NTHREADS, int NAR>
+__device__ __forceinline__ void stage_scale_rows(uint16_t* dst, const uint16_t* const (&src)[NAR], int e, int N,
+                                                 int c0, int ncols, int G, int tid) {
+  const int per_row = G / 8, GS = G + 4;
+  const int total = NAR * ncols * per_row;
+  for (int base = tid; base < total; base += 4 * NTHREADS) {
+    uint4 v[4];
+    int to[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = base + u * NTHREADS;
+      to[u] = -1;
+      if (idx < total) {
+        const int arr = idx / (ncols * per_row), rem = idx % (ncols * per_row);
+        const int cl = rem / per_row, j = rem % per_row;
+        if (c0 + cl < N) {
+          v[u] = *reinterpret_cast<const uint4*>(src[arr] + ((size_t)e * N + c0 + cl) * G + 8 * j);
+          to[u] = (arr * ncols + cl) * GS + 8 * j;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (to[u] >= 0) {  // rows of G + 4 elements are 8-byte aligned, not 16
+        *reinterpret_cast<uint2*>(dst + to[u]) = make_uint2(v[u].x, v[u].y);
+        *reinterpret_cast<uint2*>(dst + to[u] + 4) = make_uint2(v[u].z, v[u].w);
+      }
+    }
+  }
+}
 
 // One iteration (4 groups of 64 inputs) of an mxfp4 column wave: acc[m] +=
 // rows of block m (NPL planes `plane` bytes apart, from `arows`) x this
@@ -717,7 +768,7 @@ __device__ __forceinline__ void mx_iteration(f32x16_t (&acc)[MT], const Codes4& 
 
 template <int MT, int MXM>
 __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) {
-  constexpr bool MX = MXM != kSortAffine;
+  constexpr bool MX = sort_mode_mx(MXM), SBL = MXM == kSortAffineSbl;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int blk_split;  // kSortMxFold: some group of this block needs the exact pass
   const int H = a.H, I = a.I, G = H / 64;
@@ -742,6 +793,8 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
   unsigned char* abuf0 = smem;                                              // [2][kRows][kV2Row]
   float* sbuf0 = reinterpret_cast<float*>(smem + 2 * kRows * kV2Row);      // [2][4][kRows]
   int32_t* tok = reinterpret_cast<int32_t*>(sbuf0 + 8 * kRows);            // [kRows]
+  // kSortAffineSbl: [sg, bg, su, bu][128 columns][G + 4] bf16
+  uint16_t* sbl = reinterpret_cast<uint16_t*>(tok + kRows);
   for (int r = tid; r < kRows; r += kV2Threads) tok[r] = a.perm[r0 + min(r, nrows - 1)] / a.k;
   if (tid == 0) blk_split = 0;
   __syncthreads();
@@ -792,10 +845,14 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
   if constexpr (MX) {
     mcur = load_mx_scales(MS, rowb, 0);
     mnx = load_mx_scales(MS, rowb, 4 * min(1, nit - 1));
-  } else {
+  } else if constexpr (!SBL) {
     ch = load_chunk16(S, B, rows);
   }
   stage_load(0);
+  if constexpr (SBL) {  // after the first code and row requests, so its wait overlaps theirs
+    const uint16_t* const arrs[4] = {a.sg, a.bg, a.su, a.bu};
+    stage_scale_rows<kV2Threads, 4>(sbl, arrs, e, I, cb * kV2GuCols, kV2GuCols, G, tid);
+  }
   stage_store(0);
   __syncthreads();
 
@@ -810,7 +867,7 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
       const Codes4 nn = load_codes4(W, rowc, 4 * min(it + 2, nit - 1), hh);
       uint2 mnn{};
       if constexpr (MX) mnn = load_mx_scales(MS, rowb, 4 * min(it + 2, nit - 1));
-      else if (ii == 0) chn = load_chunk16(S, B, rows + 16 * min(c + 1, nch - 1));
+      else if (!SBL && ii == 0) chn = load_chunk16(S, B, rows + 16 * min(c + 1, nch - 1));
       if (MX && wave_on) {
         const unsigned char* const arows = abuf + (size_t)lc * kV2Row + 64 * hh;
         with_row_blocks<MT>(nrt, [&](auto nrt_c) {
@@ -818,14 +875,20 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
           mx_iteration<MT, NRT, MXM, 1>(acc, cur, mcur, arows, 0, NRT, hh, blk_split);
         });
       } else if (!MX && wave_on) {
+        uint2 sv{}, bv{};  // kSortAffineSbl: this column's 4 scales and 4 biases of the iteration
+        if constexpr (SBL) {
+          const uint16_t* sl = sbl + (size_t)(2 * mat * kV2GuCols + 32 * cw + lc) * (G + 4) + 4 * it;
+          sv = *reinterpret_cast<const uint2*>(sl);
+          bv = *reinterpret_cast<const uint2*>(sl + (size_t)kV2GuCols * (G + 4));
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t w4[4] = {cur.q[q].x, cur.q[q].y, cur.q[q].z, cur.q[q].w};
           uint4 bq[4];
 #pragma unroll
           for (int s = 0; s < 4; ++s) bq[s] = unpack_codes(w4[s]);
-          const float sc = chunk_elem(ch.s0, ch.s1, 4 * ii + q);
-          const float bc = chunk_elem(ch.b0, ch.b1, 4 * ii + q) - 128.0f * sc;
+          const float sc = SBL ? sb4_elem(sv.x, sv.y, q) : chunk_elem(ch.s0, ch.s1, 4 * ii + q);
+          const float bc = (SBL ? sb4_elem(bv.x, bv.y, q) : chunk_elem(ch.b0, ch.b1, 4 * ii + q)) - 128.0f * sc;
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
             if (m < nrt) {
@@ -899,7 +962,7 @@ constexpr int down2_buffers(int mt) { return (size_t)2 * 2 * mt * kRowTile * kV2
 
 template <int MT, int MXM>
 __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
-  constexpr bool MX = MXM != kSortAffine;
+  constexpr bool MX = sort_mode_mx(MXM), SBL = MXM == kSortAffineSbl;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int blk_split;  // kSortMxFold: some group of this block needs the exact pass
   const int H = a.H, I = a.I, G = I / 64;
@@ -924,6 +987,7 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
   constexpr int NB = down2_buffers(MT);
   unsigned char* abuf0 = smem;                                                     // [NB][2 planes][kRows][kV2Row]
   float* sbuf0 = reinterpret_cast<float*>(smem + (size_t)NB * 2 * kRows * kV2Row);  // [NB][4][kRows]
+  uint16_t* sbl = reinterpret_cast<uint16_t*>(sbuf0 + NB * 4 * kRows);  // kSortAffineSbl: [sd, bd][256][G + 4]
 
   constexpr int kPer = kRows * 32 / kV2Threads;  // 16-byte pieces per thread, iteration and plane
   u32x4_t sth[kPer], stl[kPer];
@@ -971,10 +1035,14 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
   if constexpr (MX) {
     mcur = load_mx_scales(MS, rowb, 0);
     mnx = load_mx_scales(MS, rowb, 4 * min(1, nit - 1));
-  } else {
+  } else if constexpr (!SBL) {
     ch = load_chunk16(a.sd, a.bd, rows);
   }
   stage_load(0);
+  if constexpr (SBL) {  // after the first code and row requests, so its wait overlaps theirs
+    const uint16_t* const arrs[2] = {a.sd, a.bd};
+    stage_scale_rows<kV2Threads, 2>(sbl, arrs, e, H, cb * kV2DnCols, kV2DnCols, G, tid);
+  }
   stage_store(0);
   __syncthreads();
 
@@ -990,21 +1058,27 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
       const Codes4 nn = load_codes4(a.wd, rowc, 4 * min(it + 2, nit - 1), hh);
       uint2 mnn{};
       if constexpr (MX) mnn = load_mx_scales(MS, rowb, 4 * min(it + 2, nit - 1));
-      else if (ii == 0) chn = load_chunk16(a.sd, a.bd, rows + 16 * min(c + 1, nch - 1));
+      else if (!SBL && ii == 0) chn = load_chunk16(a.sd, a.bd, rows + 16 * min(c + 1, nch - 1));
       if (MX && wave_on) {
         const unsigned char* const arows = abuf + (size_t)lc * kV2Row + 64 * hh;
         // row blocks tested at run time: the two planes leave no registers
         // for a copy of the loop per row-block count
         mx_iteration<MT, MT, MXM, 2>(acc, cur, mcur, arows, (size_t)kRows * kV2Row, nrt, hh, blk_split);
       } else if (!MX && wave_on) {
+        uint2 sv{}, bv{};  // kSortAffineSbl: this column's 4 scales and 4 biases of the iteration
+        if constexpr (SBL) {
+          const uint16_t* sl = sbl + (size_t)(32 * wid + lc) * (G + 4) + 4 * it;
+          sv = *reinterpret_cast<const uint2*>(sl);
+          bv = *reinterpret_cast<const uint2*>(sl + (size_t)kV2DnCols * (G + 4));
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t w4[4] = {cur.q[q].x, cur.q[q].y, cur.q[q].z, cur.q[q].w};
           uint4 bq[4];
 #pragma unroll
           for (int s = 0; s < 4; ++s) bq[s] = unpack_codes(w4[s]);
-          const float sc = chunk_elem(ch.s0, ch.s1, 4 * ii + q);
-          const float bc = chunk_elem(ch.b0, ch.b1, 4 * ii + q) - 128.0f * sc;
+          const float sc = SBL ? sb4_elem(sv.x, sv.y, q) : chunk_elem(ch.s0, ch.s1, 4 * ii + q);
+          const float bc = (SBL ? sb4_elem(bv.x, bv.y, q) : chunk_elem(ch.b0, ch.b1, 4 * ii + q)) - 128.0f * sc;
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
             if (m < nrt) {
@@ -1162,6 +1236,12 @@ size_t down2_lds(int mt) {
   const int nb = down2_buffers(mt);
   return (size_t)nb * 2 * mt * kRowTile * kV2Row + (size_t)nb * 4 * mt * kRowTile * 4;
 }
+// the same plus the workgroup's scale and bias rows (kSortAffineSbl)
+size_t gateup2_sbl_lds(int mt, int H) { return gateup2_lds(mt) + (size_t)4 * kV2GuCols * (H / 64 + 4) * 2; }
+size_t down2_sbl_lds(int mt, int I) { return down2_lds(mt) + (size_t)2 * kV2DnCols * (I / 64 + 4) * 2; }
+constexpr size_t kSortLdsMax = 160 * 1024 - 256;  // the static __shared__ word and slack
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 template <int MT>
 int gemm_launch(const SortedArgs& a, bool down, hipStream_t stream) {
@@ -1187,10 +1267,20 @@ int gemm_launch(const SortedArgs& a, bool down, hipStream_t stream) {
     }
   } else if (!down && a.H % 1024 == 0) {
     const int ncb = (a.I + kV2GuCols - 1) / kV2GuCols;
-    hipLaunchKernelGGL((k_sorted_gateup2<MT, kSortAffine>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT), stream, a);
+    const size_t sbl = gateup2_sbl_lds(MT, a.H);
+    if (MT >= 2 && sbl <= kSortLdsMax && aligned16(a.sg) && aligned16(a.bg) && aligned16(a.su) && aligned16(a.bu))
+      hipLaunchKernelGGL((k_sorted_gateup2<MT, kSortAffineSbl>), dim3(tiles8 * ncb), dim3(kV2Threads), sbl, stream, a);
+    else
+      hipLaunchKernelGGL((k_sorted_gateup2<MT, kSortAffine>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT),
+                         stream, a);
   } else if (down && a.I % 1024 == 0) {
     const int ncb = (a.H + kV2DnCols - 1) / kV2DnCols;
-    hipLaunchKernelGGL((k_sorted_down2<MT, kSortAffine>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT), stream, a);
+    const size_t sbl = down2_sbl_lds(MT, a.I);
+    if (MT >= 2 && sbl <= kSortLdsMax && aligned16(a.sd) && aligned16(a.bd))
+      hipLaunchKernelGGL((k_sorted_down2<MT, kSortAffineSbl>), dim3(tiles8 * ncb), dim3(kV2Threads), sbl, stream, a);
+    else
+      hipLaunchKernelGGL((k_sorted_down2<MT, kSortAffine>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT), stream,
+                         a);
   } else if (!down) {
     const int ncb = (a.I + kGuCols - 1) / kGuCols;
     hipLaunchKernelGGL(k_sorted_gateup<MT>, dim3(tiles8 * ncb), dim3(kMmThreads), gateup_lds(MT), stream, a);
