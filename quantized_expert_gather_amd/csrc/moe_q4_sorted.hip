@@ -838,8 +838,15 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[m][i] = 0.0f;
 
+  // codes stay two iterations ahead; with PAIR they are requested two
+  // iterations at a time (even iterations load it + 2 and it + 3 back to
+  // back), so the two 128-byte pieces of a weight row reach HBM together.
+  // Measured: faster for 2 and 3 row blocks (and mxfp4 gate/up with one),
+  // slower for the other single-block kernels and past the registers of 4.
+  constexpr bool PAIR = (MT == 2 || MT == 3) || (MXM == kSortMxFold && MT == 1);
   Codes4 cur = load_codes4(W, rowc, 0, hh);
-  Codes4 nx = load_codes4(W, rowc, 4 * min(1, nit - 1), hh);  // codes stay two iterations ahead
+  Codes4 nx = load_codes4(W, rowc, 4 * min(1, nit - 1), hh);
+  Codes4 pend;
   Chunk16 ch{};
   uint2 mcur{}, mnx{};
   if constexpr (MX) {
@@ -864,7 +871,13 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
       const unsigned char* abuf = abuf0 + (size_t)(ii & 1) * kRows * kV2Row;  // nit is a multiple of 4
       const float* sbuf = sbuf0 + (ii & 1) * 4 * kRows;
       stage_load(min(it + 1, nit - 1));
-      const Codes4 nn = load_codes4(W, rowc, 4 * min(it + 2, nit - 1), hh);
+      Codes4 nn;
+      if (!PAIR || (ii & 1) == 0) {  // ii is a compile-time value after unrolling
+        nn = load_codes4(W, rowc, 4 * min(it + 2, nit - 1), hh);
+        if (PAIR) pend = load_codes4(W, rowc, 4 * min(it + 3, nit - 1), hh);
+      } else {
+        nn = pend;
+      }
       uint2 mnn{};
       if constexpr (MX) mnn = load_mx_scales(MS, rowb, 4 * min(it + 2, nit - 1));
       else if (!SBL && ii == 0) chn = load_chunk16(S, B, rows + 16 * min(c + 1, nch - 1));
@@ -1028,8 +1041,15 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[m][i] = 0.0f;
 
+  // codes stay two iterations ahead; with PAIR they are requested two
+  // iterations at a time (even iterations load it + 2 and it + 3 back to
+  // back), so the two 128-byte pieces of a weight row reach HBM together.
+  // Measured: faster for 2 and 3 row blocks (and mxfp4 gate/up with one),
+  // slower for the other single-block kernels and past the registers of 4.
+  constexpr bool PAIR = MT == 2 || MT == 3;
   Codes4 cur = load_codes4(a.wd, rowc, 0, hh);
-  Codes4 nx = load_codes4(a.wd, rowc, 4 * min(1, nit - 1), hh);  // codes stay two iterations ahead
+  Codes4 nx = load_codes4(a.wd, rowc, 4 * min(1, nit - 1), hh);
+  Codes4 pend;
   Chunk16 ch{};
   uint2 mcur{}, mnx{};
   if constexpr (MX) {
@@ -1055,7 +1075,13 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
       const unsigned char* abuf = abuf0 + (size_t)cbuf * 2 * kRows * kV2Row;
       const float* sbuf = sbuf0 + cbuf * 4 * kRows;
       stage_load(min(it + 1, nit - 1));
-      const Codes4 nn = load_codes4(a.wd, rowc, 4 * min(it + 2, nit - 1), hh);
+      Codes4 nn;
+      if (!PAIR || (ii & 1) == 0) {  // ii is a compile-time value after unrolling
+        nn = load_codes4(a.wd, rowc, 4 * min(it + 2, nit - 1), hh);
+        if (PAIR) pend = load_codes4(a.wd, rowc, 4 * min(it + 3, nit - 1), hh);
+      } else {
+        nn = pend;
+      }
       uint2 mnn{};
       if constexpr (MX) mnn = load_mx_scales(MS, rowb, 4 * min(it + 2, nit - 1));
       else if (!SBL && ii == 0) chn = load_chunk16(a.sd, a.bd, rows + 16 * min(c + 1, nch - 1));
