@@ -265,6 +265,46 @@ def test_mx_host_checks():
     assert call_mx(out=fake(14) + 256) == q.MOE_Q4_ERR_ALIAS
 
 
+def test_mx_long_inputs_take_the_sorted_path_on_host():
+    # more tokens than one union launch, H and I multiples of 1024: the
+    # sorted path's workspace (the layout the q4 sorted path uses)
+    assert q.moe_swiglu_mxfp4_workspace_bytes(512, 8, 256, 4096, 2048) == \
+        q.moe_swiglu_q4_workspace_bytes(512, 8, 256, 4096, 2048) > 0
+    assert q.moe_swiglu_mxfp4_workspace_bytes(40, 8, 16, 4096, 1024) == \
+        q.moe_swiglu_q4_workspace_bytes(40, 8, 16, 4096, 1024)
+    # widths that are not multiples of 1024 stay on token chunks
+    assert q.moe_swiglu_mxfp4_workspace_bytes(512, 8, 256, 2048, 512) == \
+        q.moe_swiglu_mxfp4_workspace_bytes(32, 8, 256, 2048, 512)
+    # the sorted path takes stage-only calls (host checks pass; with no GPU
+    # the launch itself fails), token chunks do not
+    n = q.moe_swiglu_mxfp4_workspace_bytes(40, 8, 16, 4096, 1024)
+    assert call_mx(L=40, k=8, E=16, H=4096, I=1024, ws_bytes=n, stages=1) == q.MOE_Q4_ERR_LAUNCH
+    assert call_mx(L=40, k=8, E=16, H=4096, I=512, stages=1) == q.MOE_Q4_ERR_UNSUPPORTED
+    assert call_mx(L=40, k=8, E=16, H=4096, I=1024, ws_bytes=n - 1) == q.MOE_Q4_ERR_WORKSPACE
+    # scale arrays the sorted path cannot read 8 bytes at a time: token chunks
+    # where they fit, else an alignment error (H = 32768: not even one token
+    # of a union launch fits the LDS)
+    p = [fake(j) for j in range(9)]
+    p[4] += 4
+    assert call_mx(L=40, k=8, E=16, H=4096, I=1024, ws_bytes=n, ptrs=p, stages=1) == q.MOE_Q4_ERR_UNSUPPORTED
+    assert call_mx(L=40, k=8, E=16, H=4096, I=1024, ws_bytes=n, ptrs=p) == q.MOE_Q4_ERR_LAUNCH
+    assert q.moe_swiglu_codec_workspace_bytes(q.MOE_Q4_CODEC_NVFP4, 1, 8, 16, 32768, 1024) == 0
+    m = q.moe_swiglu_mxfp4_workspace_bytes(40, 8, 16, 32768, 1024)
+    assert m > 0
+    assert call_mx(L=40, k=8, E=16, H=32768, I=1024, ws_bytes=m, ptrs=p) == q.MOE_Q4_ERR_ALIGN
+    assert call_mx(L=40, k=8, E=16, H=32768, I=1024, ws_bytes=m) == q.MOE_Q4_ERR_LAUNCH
+
+
+def test_codec_chunks_shrink_to_fit_the_lds():
+    # H = 4096: 32 tokens' activations do not fit one workgroup's LDS, fewer do
+    nv = q.MOE_Q4_CODEC_NVFP4
+    assert q.moe_swiglu_codec_workspace_bytes(nv, 40, 8, 16, 4096, 256) > 0
+    assert q.moe_swiglu_codec_workspace_bytes(nv, 40, 8, 16, 4096, 256) == \
+        q.moe_swiglu_codec_workspace_bytes(nv, 5000, 8, 16, 4096, 256)
+    assert q.moe_swiglu_codec_workspace_bytes(nv, 40, 8, 16, 4096, 256) < \
+        q.moe_swiglu_codec_workspace_bytes(nv, 40, 8, 16, 2048, 256) * 2
+
+
 def call_codec(codec, L=2, k=2, E=8, H=256, I=128, out_dtype=0, ws_bytes=1 << 30, stages=3, ptrs=None, ws=None,
                out=None):
     p = [fake(i) for i in range(12)] if ptrs is None else ptrs
