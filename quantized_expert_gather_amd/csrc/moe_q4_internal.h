@@ -118,7 +118,7 @@ int sorted_tiles_max(int T, int k, int E, int bm);
 size_t sorted_flag_count(int T, int k, int E, int H, int I);
 SortedWorkspace sorted_workspace_layout(int T, int k, int E, int H, int I);
 bool sorted_shape_supported(int T, int k, int E, int H, int I);
-// mxfp4 banks on the sorted path: the streaming kernels, H and I multiples of 1024
+// mxfp4 banks on the sorted path: the streaming kernels, H and I multiples of 256
 bool sorted_mx_shape_supported(int T, int k, int E, int H, int I);
 int sort_launch(const SortedArgs& a, hipStream_t stream);
 int sorted_forward_launch(const SortedArgs& a, unsigned stages, hipStream_t stream);

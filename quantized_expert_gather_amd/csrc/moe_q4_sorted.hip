@@ -772,7 +772,10 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int blk_split;  // kSortMxFold: some group of this block needs the exact pass
   const int H = a.H, I = a.I, G = H / 64;
-  const int nit = G / 4, nch = G / 16;
+  // iterations of 4 groups (the width is a multiple of 256), in chunks of
+  // 4; the chunked scale loads run only when the chunks are whole (width a
+  // multiple of 1024)
+  const int nit = G / 4, nch = (nit + 3) / 4;
   const int ncb = (I + kV2GuCols - 1) / kV2GuCols;
   int tile, cb;
   tile_of_block(ncb, tile, cb);
@@ -868,7 +871,8 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int it = 4 * c + ii;
-      const unsigned char* abuf = abuf0 + (size_t)(ii & 1) * kRows * kV2Row;  // nit is a multiple of 4
+      if (it >= nit) break;  // uniform over the workgroup
+      const unsigned char* abuf = abuf0 + (size_t)(ii & 1) * kRows * kV2Row;  // it & 1
       const float* sbuf = sbuf0 + (ii & 1) * 4 * kRows;
       stage_load(min(it + 1, nit - 1));
       Codes4 nn;
@@ -979,7 +983,10 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int blk_split;  // kSortMxFold: some group of this block needs the exact pass
   const int H = a.H, I = a.I, G = I / 64;
-  const int nit = G / 4, nch = G / 16;
+  // iterations of 4 groups (the width is a multiple of 256), in chunks of
+  // 4; the chunked scale loads run only when the chunks are whole (width a
+  // multiple of 1024)
+  const int nit = G / 4, nch = (nit + 3) / 4;
   const int ncb = (H + kV2DnCols - 1) / kV2DnCols;
   int tile, cb;
   tile_of_block(ncb, tile, cb);
@@ -1071,7 +1078,8 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int it = 4 * c + ii;
-      const int cbuf = NB == 2 ? (ii & 1) : 0;  // nit is a multiple of 4
+      if (it >= nit) break;  // uniform over the workgroup
+      const int cbuf = NB == 2 ? (ii & 1) : 0;  // it & 1
       const unsigned char* abuf = abuf0 + (size_t)cbuf * 2 * kRows * kV2Row;
       const float* sbuf = sbuf0 + cbuf * 4 * kRows;
       stage_load(min(it + 1, nit - 1));
@@ -1239,7 +1247,7 @@ SortedWorkspace sorted_workspace_layout(int T, int k, int E, int H, int I) {
 }
 
 bool sorted_mx_shape_supported(int T, int k, int E, int H, int I) {
-  return H % 1024 == 0 && I % 1024 == 0 && sorted_shape_supported(T, k, E, H, I);
+  return H % 256 == 0 && I % 256 == 0 && sorted_shape_supported(T, k, E, H, I);
 }
 
 bool sorted_shape_supported(int T, int k, int E, int H, int I) {
@@ -1269,12 +1277,26 @@ constexpr size_t kSortLdsMax = 160 * 1024 - 256;  // the static __shared__ word 
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// The LDS-staged scales: widths that are multiples of 512 (a scale row is
+// copied in 16-byte pieces of 8 groups), where the LDS holds them and the
+// arrays allow 16-byte reads; used for 2 or more row blocks (with one, the
+// read ahead of the stream cost more than the refetches it saves) and for
+// widths that are not multiples of 1024.
+bool gateup2_sbl_fits(const SortedArgs& a, int mt) {
+  return a.H % 512 == 0 && (mt >= 2 || a.H % 1024 != 0) && gateup2_sbl_lds(mt, a.H) <= kSortLdsMax &&
+         aligned16(a.sg) && aligned16(a.bg) && aligned16(a.su) && aligned16(a.bu);
+}
+bool down2_sbl_fits(const SortedArgs& a, int mt) {
+  return a.I % 512 == 0 && (mt >= 2 || a.I % 1024 != 0) && down2_sbl_lds(mt, a.I) <= kSortLdsMax &&
+         aligned16(a.sd) && aligned16(a.bd);
+}
+
 template <int MT>
 int gemm_launch(const SortedArgs& a, bool down, hipStream_t stream) {
   const int tiles8 = (a.tiles_max + 7) / 8 * 8;
   if (a.fmt == kFmtMxfp4) {
-    // the streaming kernels only (H and I multiples of 1024, checked by the caller)
-    if (a.H % 1024 || a.I % 1024) return MOE_Q4_ERR_UNSUPPORTED;
+    // the streaming kernels only (H and I multiples of 256, checked by the caller)
+    if (a.H % 256 || a.I % 256) return MOE_Q4_ERR_UNSUPPORTED;
     // the folded pass, then the exact pass over the blocks it flagged
     if (!down) {
       const int ncb = (a.I + kV2GuCols - 1) / kV2GuCols;
@@ -1291,22 +1313,24 @@ int gemm_launch(const SortedArgs& a, bool down, hipStream_t stream) {
       hipLaunchKernelGGL((k_sorted_down2<MT, kSortMxExact>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT),
                          stream, a);
     }
+  } else if (!down && gateup2_sbl_fits(a, MT)) {
+    // scales in LDS: tiles of 2 or more row blocks, and any width that is not
+    // a multiple of 1024 (the chunked scale loads need whole chunks)
+    const int ncb = (a.I + kV2GuCols - 1) / kV2GuCols;
+    hipLaunchKernelGGL((k_sorted_gateup2<MT, kSortAffineSbl>), dim3(tiles8 * ncb), dim3(kV2Threads),
+                       gateup2_sbl_lds(MT, a.H), stream, a);
   } else if (!down && a.H % 1024 == 0) {
     const int ncb = (a.I + kV2GuCols - 1) / kV2GuCols;
-    const size_t sbl = gateup2_sbl_lds(MT, a.H);
-    if (MT >= 2 && sbl <= kSortLdsMax && aligned16(a.sg) && aligned16(a.bg) && aligned16(a.su) && aligned16(a.bu))
-      hipLaunchKernelGGL((k_sorted_gateup2<MT, kSortAffineSbl>), dim3(tiles8 * ncb), dim3(kV2Threads), sbl, stream, a);
-    else
-      hipLaunchKernelGGL((k_sorted_gateup2<MT, kSortAffine>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT),
-                         stream, a);
+    hipLaunchKernelGGL((k_sorted_gateup2<MT, kSortAffine>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT),
+                       stream, a);
+  } else if (down && down2_sbl_fits(a, MT)) {
+    const int ncb = (a.H + kV2DnCols - 1) / kV2DnCols;
+    hipLaunchKernelGGL((k_sorted_down2<MT, kSortAffineSbl>), dim3(tiles8 * ncb), dim3(kV2Threads),
+                       down2_sbl_lds(MT, a.I), stream, a);
   } else if (down && a.I % 1024 == 0) {
     const int ncb = (a.H + kV2DnCols - 1) / kV2DnCols;
-    const size_t sbl = down2_sbl_lds(MT, a.I);
-    if (MT >= 2 && sbl <= kSortLdsMax && aligned16(a.sd) && aligned16(a.bd))
-      hipLaunchKernelGGL((k_sorted_down2<MT, kSortAffineSbl>), dim3(tiles8 * ncb), dim3(kV2Threads), sbl, stream, a);
-    else
-      hipLaunchKernelGGL((k_sorted_down2<MT, kSortAffine>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT), stream,
-                         a);
+    hipLaunchKernelGGL((k_sorted_down2<MT, kSortAffine>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT), stream,
+                       a);
   } else if (!down) {
     const int ncb = (a.I + kGuCols - 1) / kGuCols;
     hipLaunchKernelGGL(k_sorted_gateup<MT>, dim3(tiles8 * ncb), dim3(kMmThreads), gateup_lds(MT), stream, a);

@@ -231,13 +231,14 @@ def test_mx_invalid_arguments_rejected_on_host(kw, status):
 def test_mx_host_checks():
     assert call_mx(L=0) == q.MOE_Q4_OK
     assert q.moe_swiglu_mxfp4_workspace_bytes(0, 2, 8, 256, 128) == 0
-    # more tokens than one union launch: the workspace of one 32-token chunk
-    assert q.moe_swiglu_mxfp4_workspace_bytes(33, 8, 256, 2048, 512) == \
-        q.moe_swiglu_mxfp4_workspace_bytes(32, 8, 256, 2048, 512) > 0
-    assert q.moe_swiglu_mxfp4_workspace_bytes(5000, 8, 256, 2048, 512) == \
-        q.moe_swiglu_mxfp4_workspace_bytes(32, 8, 256, 2048, 512)
-    assert q.moe_swiglu_mxfp4_workspace_bytes(100, 32, 256, 2048, 512) == \
-        q.moe_swiglu_mxfp4_workspace_bytes(32, 32, 256, 2048, 512)
+    # more tokens than one union launch, I not a multiple of 256 (so no sorted
+    # path): the workspace of one 32-token chunk
+    assert q.moe_swiglu_mxfp4_workspace_bytes(33, 8, 256, 2048, 480) == \
+        q.moe_swiglu_mxfp4_workspace_bytes(32, 8, 256, 2048, 480) > 0
+    assert q.moe_swiglu_mxfp4_workspace_bytes(5000, 8, 256, 2048, 480) == \
+        q.moe_swiglu_mxfp4_workspace_bytes(32, 8, 256, 2048, 480)
+    assert q.moe_swiglu_mxfp4_workspace_bytes(100, 32, 256, 2048, 480) == \
+        q.moe_swiglu_mxfp4_workspace_bytes(32, 32, 256, 2048, 480)
     # H and I multiples of 32 suffice; the layout is the union path's
     assert q.moe_swiglu_mxfp4_workspace_bytes(2, 2, 4, 96, 256) > 0
     assert q.moe_swiglu_mxfp4_workspace_bytes(2, 2, 4, 352, 224) > 0
@@ -266,20 +267,22 @@ def test_mx_host_checks():
 
 
 def test_mx_long_inputs_take_the_sorted_path_on_host():
-    # more tokens than one union launch, H and I multiples of 1024: the
+    # more tokens than one union launch, H and I multiples of 256: the
     # sorted path's workspace (the layout the q4 sorted path uses)
     assert q.moe_swiglu_mxfp4_workspace_bytes(512, 8, 256, 4096, 2048) == \
         q.moe_swiglu_q4_workspace_bytes(512, 8, 256, 4096, 2048) > 0
     assert q.moe_swiglu_mxfp4_workspace_bytes(40, 8, 16, 4096, 1024) == \
         q.moe_swiglu_q4_workspace_bytes(40, 8, 16, 4096, 1024)
-    # widths that are not multiples of 1024 stay on token chunks
-    assert q.moe_swiglu_mxfp4_workspace_bytes(512, 8, 256, 2048, 512) == \
-        q.moe_swiglu_mxfp4_workspace_bytes(32, 8, 256, 2048, 512)
+    assert q.moe_swiglu_mxfp4_workspace_bytes(512, 8, 256, 2048, 768) == \
+        q.moe_swiglu_q4_workspace_bytes(512, 8, 256, 2048, 768)
+    # widths that are not multiples of 256 stay on token chunks
+    assert q.moe_swiglu_mxfp4_workspace_bytes(512, 8, 256, 2048, 480) == \
+        q.moe_swiglu_mxfp4_workspace_bytes(32, 8, 256, 2048, 480)
     # the sorted path takes stage-only calls (host checks pass; with no GPU
     # the launch itself fails), token chunks do not
     n = q.moe_swiglu_mxfp4_workspace_bytes(40, 8, 16, 4096, 1024)
     assert call_mx(L=40, k=8, E=16, H=4096, I=1024, ws_bytes=n, stages=1) == q.MOE_Q4_ERR_LAUNCH
-    assert call_mx(L=40, k=8, E=16, H=4096, I=512, stages=1) == q.MOE_Q4_ERR_UNSUPPORTED
+    assert call_mx(L=40, k=8, E=16, H=4096, I=480, stages=1) == q.MOE_Q4_ERR_UNSUPPORTED
     assert call_mx(L=40, k=8, E=16, H=4096, I=1024, ws_bytes=n - 1) == q.MOE_Q4_ERR_WORKSPACE
     # scale arrays the sorted path cannot read 8 bytes at a time: token chunks
     # where they fit, else an alignment error (H = 32768: not even one token

@@ -1,7 +1,7 @@
 """GPU parity of the sorted (MFMA) path over mxfp4 banks (needs an MI355X).
 
 Inputs longer than one union launch (more than 32 tokens) with H and I
-multiples of 1024 take the sorted path: pairs sorted by expert, gate/up and
+multiples of 256 take the sorted path: pairs sorted by expert, gate/up and
 down as grouped bf16 MFMA GEMMs.  The E8M0 block scale 2^(e - 127) is folded
 into gfx950's scaled E2M1 -> bf16 conversion, which is exact while every
 E2M1 magnitude times the scale is a normal bf16 (2 <= e <= 252), so the
@@ -100,6 +100,10 @@ SMALL = [
     (203, 4, 8, 1024, 1024, False),   # ~100 -> 4 blocks, experts over several tiles
     (64, 8, 16, 1024, 1024, True),    # duplicate ids
     (300, 2, 4, 1024, 1024, False),   # 150 per expert
+    # widths that are multiples of 256, not of 1024 (one iteration at 256)
+    (40, 4, 8, 1280, 768, False),
+    (121, 4, 8, 768, 256, False),
+    (203, 4, 8, 256, 1280, False),
 ]
 
 

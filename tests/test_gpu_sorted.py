@@ -157,6 +157,12 @@ SMALL = [
     (121, 4, 8, 2048, 1024, False),  # 3 blocks
     (203, 4, 8, 1024, 2048, False),  # 4 blocks
     (150, 4, 6, 1088, 1024, True),   # gate/up on the general kernel, down on the streaming one
+    # multiples of 512 that are not multiples of 1024: the streaming kernels
+    # with the scales staged in LDS; 256 and 1280 stay on the general kernels
+    (40, 4, 8, 1536, 512, False),    # 1 block
+    (80, 4, 8, 512, 1536, False),    # 2 blocks
+    (121, 4, 8, 2560, 256, False),   # 3 blocks; down on the general kernel
+    (203, 4, 8, 1280, 2560, False),  # 4 blocks; gate/up on the general kernel
 ]
 
 
@@ -261,3 +267,13 @@ def test_sorted_long_prefill_ragged_widths():
     rng = np.random.default_rng(37)
     sample = sorted({0, T - 1, *rng.choice(T, size=6, replace=False).tolist()})
     _sampled_check(x, ids, tw, bank, sample, "ragged widths")
+
+
+def test_sorted_widths_multiple_of_256_full_size():
+    # H = 5120, I = 1536 (GLM-4.5-sized widths; I is not a multiple of 1024):
+    # T = 512 over 64 experts, 64 rows per expert, sampled rows
+    T, k, E, H, I = 512, 8, 64, 5120, 1536
+    x, ids, tw, bank = synth.random_problem(T, k, E, H, I, seed=41, device="cuda")
+    rng = np.random.default_rng(41)
+    sample = sorted({0, T - 1, *rng.choice(T, size=6, replace=False).tolist()})
+    _sampled_check(x, ids, tw, bank, sample, "widths multiple of 256")
