@@ -652,17 +652,20 @@ constexpr int kSortAffine = 0, kSortMxFold = 1, kSortMxExact = 2;
 constexpr int kSortAffineSbl = 3;
 constexpr bool sort_mode_mx(int m) { return m == kSortMxFold || m == kSortMxExact; }
 
-// Copies rows [c0, c0 + ncols) of nar scale / bias arrays (bf16 [.., G] per
-// row, row c of expert e at (e * N + c) * G) into LDS rows of G + 4 elements
-// (the pad spreads a column group's reads over the banks); rows at or past N
-// are skipped.  The global reads are 16-byte pieces of contiguous rows.
-template <int NTHREADS, int NAR>
-__device__ __forceinline__ void stage_scale_rows(uint16_t* dst, const uint16_t* const (&src)[NAR], int e, int N,
-                                                 int c0, int ncols, int G, int tid) {
-  const int per_row = G / 8, GS = G + 4;
+// Copies rows [c0, c0 + ncols) of NAR scale / bias arrays (bf16 [.., G] per
+// row, row c of expert e at (e * N + c) * G; G a multiple of 4) into LDS rows
+// of G + 4 elements (the pad spreads a column group's reads over the banks);
+// rows at or past N are skipped.  The global reads are PIECE-group pieces of
+// contiguous rows (8 groups, 16 bytes, when G allows it, else 4), four per
+// thread in flight at a time.
+template <int NTHREADS, int NAR, int PIECE>
+__device__ __forceinline__ void stage_scale_rows_p(uint16_t* dst, const uint16_t* const (&src)[NAR], int e, int N,
+                                                   int c0, int ncols, int G, int tid) {
+  typedef typename std::conditional<PIECE == 8, uint4, uint2>::type V;
+  const int per_row = G / PIECE, GS = G + 4;
   const int total = NAR * ncols * per_row;
   for (int base = tid; base < total; base += 4 * NTHREADS) {
-    uint4 v[4];
+    V v[4];
     int to[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -672,19 +675,31 @@ __device__ __forceinline__ void stage_scale_rows(uint16_t* dst, const uint16_t* 
         const int arr = idx / (ncols * per_row), rem = idx % (ncols * per_row);
         const int cl = rem / per_row, j = rem % per_row;
         if (c0 + cl < N) {
-          v[u] = *reinterpret_cast<const uint4*>(src[arr] + ((size_t)e * N + c0 + cl) * G + 8 * j);
-          to[u] = (arr * ncols + cl) * GS + 8 * j;
+          v[u] = *reinterpret_cast<const V*>(src[arr] + ((size_t)e * N + c0 + cl) * G + PIECE * j);
+          to[u] = (arr * ncols + cl) * GS + PIECE * j;
         }
       }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      if (to[u] >= 0) {  // rows of G + 4 elements are 8-byte aligned, not 16
+      if (to[u] < 0) continue;
+      if constexpr (PIECE == 8) {  // rows of G + 4 elements are 8-byte aligned, not 16
         *reinterpret_cast<uint2*>(dst + to[u]) = make_uint2(v[u].x, v[u].y);
         *reinterpret_cast<uint2*>(dst + to[u] + 4) = make_uint2(v[u].z, v[u].w);
+      } else {
+        *reinterpret_cast<uint2*>(dst + to[u]) = v[u];
       }
     }
   }
+}
+
+template <int NTHREADS, int NAR>
+__device__ __forceinline__ void stage_scale_rows(uint16_t* dst, const uint16_t* const (&src)[NAR], int e, int N,
+                                                 int c0, int ncols, int G, int tid) {
+  if (G % 8 == 0)
+    stage_scale_rows_p<NTHREADS, NAR, 8>(dst, src, e, N, c0, ncols, G, tid);
+  else
+    stage_scale_rows_p<NTHREADS, NAR, 4>(dst, src, e, N, c0, ncols, G, tid);
 }
 
 // One iteration (4 groups of 64 inputs) of an mxfp4 column wave: acc[m] +=
@@ -766,7 +781,10 @@ __device__ __forceinline__ void mx_iteration(f32x16_t (&acc)[MT], const Codes4& 
   }
 }
 
-template <int MT, int MXM>
+// TAIL: the width is not a multiple of 1024, so the last chunk of 4
+// iterations is partial (a compile-time switch: the check in the unrolled
+// loop slowed the whole-chunk kernels by 5-8 %).
+template <int MT, int MXM, bool TAIL>
 __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) {
   constexpr bool MX = sort_mode_mx(MXM), SBL = MXM == kSortAffineSbl;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -871,7 +889,7 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int it = 4 * c + ii;
-      if (it >= nit) break;  // uniform over the workgroup
+      if (TAIL && it >= nit) break;  // uniform over the workgroup
       const unsigned char* abuf = abuf0 + (size_t)(ii & 1) * kRows * kV2Row;  // it & 1
       const float* sbuf = sbuf0 + (ii & 1) * 4 * kRows;
       stage_load(min(it + 1, nit - 1));
@@ -977,7 +995,7 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
 // staging buffers of the down streaming kernel: two while they fit the LDS
 constexpr int down2_buffers(int mt) { return (size_t)2 * 2 * mt * kRowTile * kV2Row + 8 * mt * kRowTile * 4 <= 160 * 1024 ? 2 : 1; }
 
-template <int MT, int MXM>
+template <int MT, int MXM, bool TAIL>
 __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
   constexpr bool MX = sort_mode_mx(MXM), SBL = MXM == kSortAffineSbl;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1078,7 +1096,7 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int it = 4 * c + ii;
-      if (it >= nit) break;  // uniform over the workgroup
+      if (TAIL && it >= nit) break;  // uniform over the workgroup
       const int cbuf = NB == 2 ? (ii & 1) : 0;  // it & 1
       const unsigned char* abuf = abuf0 + (size_t)cbuf * 2 * kRows * kV2Row;
       const float* sbuf = sbuf0 + cbuf * 4 * kRows;
@@ -1275,23 +1293,24 @@ size_t gateup2_sbl_lds(int mt, int H) { return gateup2_lds(mt) + (size_t)4 * kV2
 size_t down2_sbl_lds(int mt, int I) { return down2_lds(mt) + (size_t)2 * kV2DnCols * (I / 64 + 4) * 2; }
 constexpr size_t kSortLdsMax = 160 * 1024 - 256;  // the static __shared__ word and slack
 
-bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+// alignment the scale-row pieces of a width need: 16 bytes for 8-group pieces, else 8
+bool aligned_for(int width, const void* p) { return ((uintptr_t)p & (width % 512 == 0 ? 15 : 7)) == 0; }
 
-// The LDS-staged scales: widths that are multiples of 512 (a scale row is
-// copied in 16-byte pieces of 8 groups), where the LDS holds them and the
-// arrays allow 16-byte reads; used for 2 or more row blocks (with one, the
+// The LDS-staged scales: widths that are multiples of 256 (a scale row is
+// copied in pieces of 8 or 4 groups), where the LDS holds them and the
+// arrays allow 16-byte (8 groups) or 8-byte reads; used for 2 or more row blocks (with one, the
 // read ahead of the stream cost more than the refetches it saves) and for
 // widths that are not multiples of 1024.
 bool gateup2_sbl_fits(const SortedArgs& a, int mt) {
-  return a.H % 512 == 0 && (mt >= 2 || a.H % 1024 != 0) && gateup2_sbl_lds(mt, a.H) <= kSortLdsMax &&
-         aligned16(a.sg) && aligned16(a.bg) && aligned16(a.su) && aligned16(a.bu);
+  return a.H % 256 == 0 && (mt >= 2 || a.H % 1024 != 0) && gateup2_sbl_lds(mt, a.H) <= kSortLdsMax &&
+         aligned_for(a.H, a.sg) && aligned_for(a.H, a.bg) && aligned_for(a.H, a.su) && aligned_for(a.H, a.bu);
 }
 bool down2_sbl_fits(const SortedArgs& a, int mt) {
-  return a.I % 512 == 0 && (mt >= 2 || a.I % 1024 != 0) && down2_sbl_lds(mt, a.I) <= kSortLdsMax &&
-         aligned16(a.sd) && aligned16(a.bd);
+  return a.I % 256 == 0 && (mt >= 2 || a.I % 1024 != 0) && down2_sbl_lds(mt, a.I) <= kSortLdsMax &&
+         aligned_for(a.I, a.sd) && aligned_for(a.I, a.bd);
 }
 
-template <int MT>
+template <int MT, bool TAIL>
 int gemm_launch(const SortedArgs& a, bool down, hipStream_t stream) {
   const int tiles8 = (a.tiles_max + 7) / 8 * 8;
   if (a.fmt == kFmtMxfp4) {
@@ -1300,36 +1319,36 @@ int gemm_launch(const SortedArgs& a, bool down, hipStream_t stream) {
     // the folded pass, then the exact pass over the blocks it flagged
     if (!down) {
       const int ncb = (a.I + kV2GuCols - 1) / kV2GuCols;
-      hipLaunchKernelGGL((k_sorted_gateup2<MT, kSortMxFold>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT),
+      hipLaunchKernelGGL((k_sorted_gateup2<MT, kSortMxFold, TAIL>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT),
                          stream, a);
       if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;
-      hipLaunchKernelGGL((k_sorted_gateup2<MT, kSortMxExact>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT),
+      hipLaunchKernelGGL((k_sorted_gateup2<MT, kSortMxExact, TAIL>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT),
                          stream, a);
     } else {
       const int ncb = (a.H + kV2DnCols - 1) / kV2DnCols;
-      hipLaunchKernelGGL((k_sorted_down2<MT, kSortMxFold>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT),
+      hipLaunchKernelGGL((k_sorted_down2<MT, kSortMxFold, TAIL>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT),
                          stream, a);
       if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;
-      hipLaunchKernelGGL((k_sorted_down2<MT, kSortMxExact>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT),
+      hipLaunchKernelGGL((k_sorted_down2<MT, kSortMxExact, TAIL>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT),
                          stream, a);
     }
   } else if (!down && gateup2_sbl_fits(a, MT)) {
     // scales in LDS: tiles of 2 or more row blocks, and any width that is not
     // a multiple of 1024 (the chunked scale loads need whole chunks)
     const int ncb = (a.I + kV2GuCols - 1) / kV2GuCols;
-    hipLaunchKernelGGL((k_sorted_gateup2<MT, kSortAffineSbl>), dim3(tiles8 * ncb), dim3(kV2Threads),
+    hipLaunchKernelGGL((k_sorted_gateup2<MT, kSortAffineSbl, TAIL>), dim3(tiles8 * ncb), dim3(kV2Threads),
                        gateup2_sbl_lds(MT, a.H), stream, a);
   } else if (!down && a.H % 1024 == 0) {
     const int ncb = (a.I + kV2GuCols - 1) / kV2GuCols;
-    hipLaunchKernelGGL((k_sorted_gateup2<MT, kSortAffine>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT),
+    hipLaunchKernelGGL((k_sorted_gateup2<MT, kSortAffine, false>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT),
                        stream, a);
   } else if (down && down2_sbl_fits(a, MT)) {
     const int ncb = (a.H + kV2DnCols - 1) / kV2DnCols;
-    hipLaunchKernelGGL((k_sorted_down2<MT, kSortAffineSbl>), dim3(tiles8 * ncb), dim3(kV2Threads),
+    hipLaunchKernelGGL((k_sorted_down2<MT, kSortAffineSbl, TAIL>), dim3(tiles8 * ncb), dim3(kV2Threads),
                        down2_sbl_lds(MT, a.I), stream, a);
   } else if (down && a.I % 1024 == 0) {
     const int ncb = (a.H + kV2DnCols - 1) / kV2DnCols;
-    hipLaunchKernelGGL((k_sorted_down2<MT, kSortAffine>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT), stream,
+    hipLaunchKernelGGL((k_sorted_down2<MT, kSortAffine, false>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT), stream,
                        a);
   } else if (!down) {
     const int ncb = (a.I + kGuCols - 1) / kGuCols;
@@ -1341,14 +1360,21 @@ int gemm_launch(const SortedArgs& a, bool down, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? MOE_Q4_OK : MOE_Q4_ERR_LAUNCH;
 }
 
-int gemm_dispatch(const SortedArgs& a, bool down, hipStream_t stream) {
+template <bool TAIL>
+int gemm_dispatch_tail(const SortedArgs& a, bool down, hipStream_t stream) {
   switch (a.bm / kRowTile) {
-    case 1: return gemm_launch<1>(a, down, stream);
-    case 2: return gemm_launch<2>(a, down, stream);
-    case 3: return gemm_launch<3>(a, down, stream);
-    case 4: return gemm_launch<4>(a, down, stream);
+    case 1: return gemm_launch<1, TAIL>(a, down, stream);
+    case 2: return gemm_launch<2, TAIL>(a, down, stream);
+    case 3: return gemm_launch<3, TAIL>(a, down, stream);
+    case 4: return gemm_launch<4, TAIL>(a, down, stream);
     default: return MOE_Q4_ERR_UNSUPPORTED;
   }
+}
+
+int gemm_dispatch(const SortedArgs& a, bool down, hipStream_t stream) {
+  // the streaming kernels' width: H for gate/up, I for down
+  return ((down ? a.I : a.H) % 1024) ? gemm_dispatch_tail<true>(a, down, stream)
+                                     : gemm_dispatch_tail<false>(a, down, stream);
 }
 
 int sorted_forward_launch(const SortedArgs& a, unsigned stages, hipStream_t stream) {

@@ -157,12 +157,14 @@ SMALL = [
     (121, 4, 8, 2048, 1024, False),  # 3 blocks
     (203, 4, 8, 1024, 2048, False),  # 4 blocks
     (150, 4, 6, 1088, 1024, True),   # gate/up on the general kernel, down on the streaming one
-    # multiples of 512 that are not multiples of 1024: the streaming kernels
-    # with the scales staged in LDS; 256 and 1280 stay on the general kernels
+    # multiples of 256 that are not multiples of 1024: the streaming kernels
+    # with the scales staged in LDS where it holds them, else the general ones
     (40, 4, 8, 1536, 512, False),    # 1 block
     (80, 4, 8, 512, 1536, False),    # 2 blocks
-    (121, 4, 8, 2560, 256, False),   # 3 blocks; down on the general kernel
-    (203, 4, 8, 1280, 2560, False),  # 4 blocks; gate/up on the general kernel
+    (121, 4, 8, 2560, 256, False),   # 3 blocks; down: a single iteration
+    (203, 4, 8, 1280, 2560, False),  # 4 blocks; both on the general kernels (LDS)
+    (40, 4, 8, 2048, 768, False),    # 1 block; down streamed with I = 768
+    (80, 4, 8, 768, 256, False),     # 2 blocks; gate/up streamed with H = 768
 ]
 
 
