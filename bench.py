@@ -35,6 +35,7 @@ Prints one JSON line.  Progress goes to stderr.
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -66,12 +67,17 @@ def down_bytes(H: int, I: int) -> int:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code: comments and whitespace do not count,
+    so the stored traffic figures stay valid across comment edits."""
     d = os.path.join(ROOT, "quantized_expert_gather_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(d)):
         if name.endswith((".hip", ".h", ".cpp")):
+            text = open(os.path.join(d, name), encoding="utf-8").read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+            text = re.sub(r"//[^\n]*", " ", text)                  # line comments
             h.update(name.encode())
-            h.update(open(os.path.join(d, name), "rb").read())
+            h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -571,7 +571,8 @@ __device__ __forceinline__ uint32_t mx_scale_byte(uint2 s, int q, int hh) {
 
 // Exponent bytes for which every E2M1 magnitude (0.5 to 6) times 2^(e - 127)
 // is a normal, finite bf16: there the scaled conversion is exact and the
-// scale can be folded into the MFMA operand.
+// scale can be folded into the MFMA operand.  (The conversion takes only the
+// exponent field of its f32 scale operand, which is all an E8M0 scale has.)
 __device__ __forceinline__ bool mx_fold_exact(uint32_t e) { return e >= 2u && e <= 252u; }
 
 // One code word (8 E2M1 codes, low nibble first) as 8 bf16 in element order,
@@ -583,14 +584,12 @@ __device__ __forceinline__ uint4 mx_word_bf16(uint32_t w, float sc) {
                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3)));
 }
 
-// acc += A x B for one 64-input mxfp4 group: A = NPL staged planes of the
-// rows (natural element order), B = the lane's 4 code words of its column.
-//   folded: the block scale went into the conversion of bq (exact, see
-//           mx_fold_exact), so the MFMAs accumulate straight into acc.
-//   split:  bq was converted with unit scale; each 32-input block gets its
-//           own MFMA chain (the A operand of the other lane half zeroed) and is
-//           scaled in fp32 afterwards by s0 (inputs 0..31) or s1 (32..63),
-//           which also carries NaN (e = 255) and subnormal scales.
+// The exact form of one 64-input mxfp4 group for one row block: acc += A x B
+// with A = NPL staged planes of the rows (element order) and B = bq, the
+// lane's 4 code words converted with unit scale.  Each 32-input block gets
+// its own MFMA chain (the A operand of the other lane half zeroed) and is
+// scaled in fp32 afterwards by s0 (inputs 0..31) or s1 (32..63), which also
+// carries NaN (e = 255), subnormal and overflowing scales.
 template <int NPL>
 __device__ __forceinline__ void mx_mfma_split(f32x16_t& acc, const uint4 (&bq)[4], const unsigned char* const (&ap)[NPL],
                                               float s0, float s1, int hh) {
@@ -610,9 +609,9 @@ __device__ __forceinline__ void mx_mfma_split(f32x16_t& acc, const uint4 (&bq)[4
   __builtin_amdgcn_sched_barrier(0);  // one row block at a time: no operand reads hoisted across blocks
 }
 
-// The scales of one group for the lane's column: s0 for inputs 0..31, s1 for
-// 32..63 (2^(e - 127), NaN for e = 255), and whether both halves of every
-// column of the wave can be folded.
+// The block scales of one group for the lane's column from the lane's own
+// exponent byte e and its partner half's: s0 for inputs 0..31, s1 for 32..63
+// (2^(e - 127), NaN for e = 255).
 __device__ __forceinline__ void mx_group_scales(uint32_t e, int hh, float& s0, float& s1) {
   const float own = mx_scaled(1.0f, e);
   const float oth = __shfl_xor(own, 32);
@@ -645,10 +644,11 @@ constexpr int kSortAffine = 0, kSortMxFold = 1, kSortMxExact = 2;
 // whole reduction read once into LDS at its start (one coalesced read of
 // contiguous rows) instead of 16-group chunks along the stream, whose
 // 128-byte lines had left L2 between chunks and were fetched again (1.35 x
-// the algorithmic bytes).  Used for tiles of two or more row blocks where
-// the LDS holds them (down at T = 2048: 10 % faster); with one row block the
-// read ahead of the stream cost more than the refetches (T = 512: 6 %
-// slower).
+// the algorithmic bytes).  Used where the LDS holds them, for tiles of two or
+// more row blocks (down at T = 2048: 7-10 % faster; with one row block the
+// read ahead of the stream cost more than the refetches, T = 512: 6 %
+// slower) and for every width that is not a multiple of 1024 (the chunk
+// loads need whole chunks).
 constexpr int kSortAffineSbl = 3;
 constexpr bool sort_mode_mx(int m) { return m == kSortMxFold || m == kSortMxExact; }
 
