@@ -203,8 +203,9 @@ def test_codec_full_size_verify_layers(codec, L, layer):
 def test_codec_long_inputs_run_as_token_chunks(codec):
     # 70 tokens at top-8: chunks of 32, 32 and 6 tokens on one workspace;
     # an invalid id in the last chunk must reach the call's status word
+    # (I = 320 is not a multiple of 256, so mxfp4 stays on token chunks too)
     q = _q()
-    L, k, E, H, I = 70, 8, 64, 512, 256
+    L, k, E, H, I = 70, 8, 64, 512, 320
     x, ids, tw, bank = synth.random_problem_q(codec, L, k, E, H, I, seed=21)
     say(codec, "token chunks L=70")
     ref = oracle.forward_pairs_q(codec, x, ids, tw, bank)
@@ -225,10 +226,10 @@ def test_codec_long_inputs_run_as_token_chunks(codec):
 @pytest.mark.parametrize("codec", CODECS)
 def test_codec_wide_hidden_runs_smaller_chunks(codec):
     # H = 4096: 32 tokens' activations do not fit one workgroup's LDS, so the
-    # chunks hold fewer tokens (mxfp4 stays on the union path: I is not a
-    # multiple of 1024)
+    # chunks hold fewer tokens (mxfp4 stays on the union path: I = 320 is not
+    # a multiple of 256)
     q = _q()
-    L, k, E, H, I = 40, 8, 16, 4096, 256
+    L, k, E, H, I = 40, 8, 16, 4096, 320
     x, ids, tw, bank = synth.random_problem_q(codec, L, k, E, H, I, seed=23)
     say(codec, "wide hidden L=40 H=4096")
     ref = oracle.forward_pairs_q(codec, x, ids, tw, bank)
