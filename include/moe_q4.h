@@ -204,8 +204,8 @@ size_t moe_swiglu_codec_workspace_bytes(int codec, int L, int k, int E, int H, i
  * calls need stages == MOE_Q4_STAGE_ALL.  The device status word is the OR
  * over the chunks.
  *
- * MXFP4 with L > min(MOE_Q4_UNION_MAX_L, MOE_Q4_MAX_PAIRS / k) and H and I
- * multiples of 256 takes the sorted path instead (expert-sorted pairs,
+ * MXFP4 and MXFP8 with L > min(MOE_Q4_UNION_MAX_L, MOE_Q4_MAX_PAIRS / k) and
+ * H and I multiples of 256 take the sorted path instead (expert-sorted pairs,
  * grouped bf16 MFMA GEMMs, every bank byte read once per tile row block; the
  * device path word reads MOE_Q4_PATH_SORTED; stage-split calls allowed).
  * There the scale arrays sg, su and sd must be 8-byte aligned: unaligned

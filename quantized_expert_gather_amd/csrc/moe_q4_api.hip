@@ -62,9 +62,9 @@ static int select_path(int L, int k, int E, int H, int I) {
 // and I multiples of 32 (one scale per 32 inputs at least; 64 for the
 // group-64 8-bit affine codes).  More tokens than one union launch serves
 // run as consecutive token chunks: at most 32 tokens and 256 pairs, fewer
-// where the chunk's activations would not fit the LDS.  mxfp4 inputs longer
-// than that take the sorted (MFMA) path where its streaming kernels cover
-// the shape.
+// where the chunk's activations would not fit the LDS.  mxfp4 and mxfp8
+// inputs longer than that take the sorted (MFMA) path where its streaming
+// kernels cover the shape.
 static int union_token_cap(int k) { return std::min(MOE_Q4_UNION_MAX_L, MOE_Q4_MAX_PAIRS / k); }
 
 // Tokens per union launch; 0 if not even one token fits.
@@ -75,7 +75,7 @@ static int codec_chunk_tokens(int L, int k, int E, int H, int I, int fmt) {
 }
 
 static bool codec_sorted(int fmt, int L, int k, int E, int H, int I) {
-  return fmt == kFmtMxfp4 && L > union_token_cap(k) && sorted_mx_shape_supported(L, k, E, H, I);
+  return (fmt == kFmtMxfp4 || fmt == kFmtMxfp8) && L > union_token_cap(k) && sorted_mx_shape_supported(L, k, E, H, I);
 }
 
 static int codec_shape_status(int L, int k, int E, int H, int I, int fmt) {

@@ -91,7 +91,7 @@ struct SortedArgs {
   void* out;
   int out_f32;
   int T, k, E, H, I;
-  int fmt;            // kFmtAffine, or kFmtMxfp4 (scale slots hold E8M0 bytes, no biases)
+  int fmt;            // kFmtAffine, or kFmtMxfp4 / kFmtMxfp8 (scale slots hold E8M0 bytes, no biases)
   int bm;             // rows per tile (32, 64 or 128)
   int tiles_max;      // capacity of `tiles`
   uint32_t* hdr;      // [0] status, [1] path, [2] valid pairs, [3] tiles
@@ -118,7 +118,7 @@ int sorted_tiles_max(int T, int k, int E, int bm);
 size_t sorted_flag_count(int T, int k, int E, int H, int I);
 SortedWorkspace sorted_workspace_layout(int T, int k, int E, int H, int I);
 bool sorted_shape_supported(int T, int k, int E, int H, int I);
-// mxfp4 banks on the sorted path: the streaming kernels, H and I multiples of 256
+// mxfp4 and mxfp8 banks on the sorted path: the streaming kernels, H and I multiples of 256
 bool sorted_mx_shape_supported(int T, int k, int E, int H, int I);
 int sort_launch(const SortedArgs& a, hipStream_t stream);
 int sorted_forward_launch(const SortedArgs& a, unsigned stages, hipStream_t stream);

@@ -584,6 +584,47 @@ __device__ __forceinline__ uint4 mx_word_bf16(uint32_t w, float sc) {
                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3)));
 }
 
+// mxfp8: exponent bytes for which every nonzero E4M3 magnitude (2^-9 to 448)
+// times 2^(e - 127) is a normal, finite bf16.
+__device__ __forceinline__ bool mx8_fold_exact(uint32_t e) { return e >= 10u && e <= 246u; }
+
+// Two code words of 8-bit E4M3 codes (lowest byte first) as 8 bf16 in element
+// order, each multiplied by `sc` in the conversion.
+__device__ __forceinline__ uint4 mx8_words_bf16(uint32_t w0, uint32_t w1, float sc) {
+  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, true)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, true)));
+}
+
+// The 4 MFMA B operands of group q: fp4, one code word each (Codes4 c holds
+// the lane's 4 words of each group); fp8, two words each (c the first 4
+// words of each group, c2 the last 4).
+template <bool F8>
+__device__ __forceinline__ void mx_group_operands(const Codes4& c, const Codes4& c2, int q, float sc, uint4 (&bq)[4]) {
+  if constexpr (F8) {
+    bq[0] = mx8_words_bf16(c.q[q].x, c.q[q].y, sc);
+    bq[1] = mx8_words_bf16(c.q[q].z, c.q[q].w, sc);
+    bq[2] = mx8_words_bf16(c2.q[q].x, c2.q[q].y, sc);
+    bq[3] = mx8_words_bf16(c2.q[q].z, c2.q[q].w, sc);
+  } else {
+    bq[0] = mx_word_bf16(c.q[q].x, sc);
+    bq[1] = mx_word_bf16(c.q[q].y, sc);
+    bq[2] = mx_word_bf16(c.q[q].z, sc);
+    bq[3] = mx_word_bf16(c.q[q].w, sc);
+  }
+}
+
+// 8-bit codes: words 4 * part .. 4 * part + 3 of the lane half's 8 words in
+// each of 4 consecutive groups (a group of one row is 16 words).
+__device__ __forceinline__ Codes4 load_codes8(const uint32_t* W, size_t rowc, int g0, int hh, int part) {
+  Codes4 c;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    c.q[q] = *reinterpret_cast<const uint4*>(W + rowc + 16 * (g0 + q) + 8 * hh + 4 * part);
+  return c;
+}
+
 // The exact form of one 64-input mxfp4 group for one row block: acc += A x B
 // with A = NPL staged planes of the rows (element order) and B = bq, the
 // lane's 4 code words converted with unit scale.  Each 32-input block gets
@@ -650,7 +691,13 @@ constexpr int kSortAffine = 0, kSortMxFold = 1, kSortMxExact = 2;
 // slower) and for every width that is not a multiple of 1024 (the chunk
 // loads need whole chunks).
 constexpr int kSortAffineSbl = 3;
-constexpr bool sort_mode_mx(int m) { return m == kSortMxFold || m == kSortMxExact; }
+// mxfp8 (E4M3 codes, one byte per input; E8M0 scale per 32 inputs): the same
+// two passes.
+constexpr int kSortMx8Fold = 5, kSortMx8Exact = 6;
+constexpr bool sort_mode_fold(int m) { return m == kSortMxFold || m == kSortMx8Fold; }
+constexpr bool sort_mode_exact(int m) { return m == kSortMxExact || m == kSortMx8Exact; }
+constexpr bool sort_mode_mx(int m) { return sort_mode_fold(m) || sort_mode_exact(m); }
+constexpr bool sort_mode_f8(int m) { return m == kSortMx8Fold || m == kSortMx8Exact; }
 
 // Copies rows [c0, c0 + ncols) of NAR scale / bias arrays (bf16 [.., G] per
 // row, row c of expert e at (e * N + c) * G; G a multiple of 4) into LDS rows
@@ -707,22 +754,23 @@ __device__ __forceinline__ void stage_scale_rows(uint16_t* dst, const uint16_t* 
 // lane's codes `cur` with exponent bytes `sc`, for the row blocks m < NRT
 // and m < nrt (NRT a compile-time count, or MT with the run-time nrt).
 template <int MT, int NRT, int MXM, int NPL>
-__device__ __forceinline__ void mx_iteration(f32x16_t (&acc)[MT], const Codes4& cur, uint2 sc,
+__device__ __forceinline__ void mx_iteration(f32x16_t (&acc)[MT], const Codes4& cur, const Codes4& cur2, uint2 sc,
                                              const unsigned char* arows, size_t plane, int nrt, int hh,
                                              int& blk_split) {
-  if constexpr (MXM == kSortMxFold) {
+  constexpr bool F8 = sort_mode_f8(MXM);
+  if constexpr (sort_mode_fold(MXM)) {
     bool ok = true;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ok = ok && mx_fold_exact(mx_scale_byte(sc, q, hh));
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t e = mx_scale_byte(sc, q, hh);
+      ok = ok && (F8 ? mx8_fold_exact(e) : mx_fold_exact(e));
+    }
     if (!ok) blk_split = 1;  // the exact pass recomputes this block
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float fs = __uint_as_float(mx_scale_byte(sc, q, hh) << 23);  // 2^(e - 127) for 1 <= e <= 254
       uint4 bq[4];
-      bq[0] = mx_word_bf16(cur.q[q].x, fs);
-      bq[1] = mx_word_bf16(cur.q[q].y, fs);
-      bq[2] = mx_word_bf16(cur.q[q].z, fs);
-      bq[3] = mx_word_bf16(cur.q[q].w, fs);
+      mx_group_operands<F8>(cur, cur2, q, fs, bq);
       if constexpr (NPL == 2) {
         // two planes (h hi and lo): one row block at a time, so the operands
         // of both planes stay few
@@ -763,10 +811,7 @@ __device__ __forceinline__ void mx_iteration(f32x16_t (&acc)[MT], const Codes4& 
       float s0, s1;
       mx_group_scales(mx_scale_byte(sc, q, hh), hh, s0, s1);
       uint4 bq[4];
-      bq[0] = mx_word_bf16(cur.q[q].x, 1.0f);
-      bq[1] = mx_word_bf16(cur.q[q].y, 1.0f);
-      bq[2] = mx_word_bf16(cur.q[q].z, 1.0f);
-      bq[3] = mx_word_bf16(cur.q[q].w, 1.0f);
+      mx_group_operands<F8>(cur, cur2, q, 1.0f, bq);
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         if (m < NRT && m < nrt) {
@@ -786,7 +831,7 @@ __device__ __forceinline__ void mx_iteration(f32x16_t (&acc)[MT], const Codes4& 
 // loop slowed the whole-chunk kernels by 5-8 %).
 template <int MT, int MXM, bool TAIL>
 __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) {
-  constexpr bool MX = sort_mode_mx(MXM), SBL = MXM == kSortAffineSbl;
+  constexpr bool MX = sort_mode_mx(MXM), SBL = MXM == kSortAffineSbl, F8 = sort_mode_f8(MXM);
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int blk_split;  // kSortMxFold: some group of this block needs the exact pass
   const int H = a.H, I = a.I, G = H / 64;
@@ -798,7 +843,7 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
   int tile, cb;
   tile_of_block(ncb, tile, cb);
   if (tile >= (int)a.hdr[3]) return;
-  if (MXM == kSortMxExact && a.mxflag_gu[blockIdx.x] == 0) return;
+  if (sort_mode_exact(MXM) && a.mxflag_gu[blockIdx.x] == 0) return;
   const int4 td = a.tiles[tile];
   const int e = td.x, r0 = td.y, nrows = td.z;
   const int nrt = (nrows + kRowTile - 1) / kRowTile;
@@ -848,7 +893,7 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
   const uint32_t* W = mat ? a.wu : a.wg;
   const uint16_t* S = mat ? a.su : a.sg;
   const uint16_t* B = mat ? a.bu : a.bg;
-  const size_t rowc = ((size_t)e * I + col) * (size_t)(H / 8);
+  const size_t rowc = ((size_t)e * I + col) * (size_t)(H / (F8 ? 4 : 8));
   const size_t rows = ((size_t)e * I + col) * (size_t)G;
   const unsigned char* MS = reinterpret_cast<const unsigned char*>(S);  // mxfp4: E8M0 bytes [E][I][H / 32]
   const size_t rowb = ((size_t)e * I + col) * (size_t)(H / 32);
@@ -864,9 +909,11 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
   // back), so the two 128-byte pieces of a weight row reach HBM together.
   // Measured: faster for 2 and 3 row blocks (and mxfp4 gate/up with one),
   // slower for the other single-block kernels and past the registers of 4.
-  constexpr bool PAIR = (MT == 2 || MT == 3) || (MXM == kSortMxFold && MT == 1);
-  Codes4 cur = load_codes4(W, rowc, 0, hh);
-  Codes4 nx = load_codes4(W, rowc, 4 * min(1, nit - 1), hh);
+  constexpr bool PAIR = !F8 && ((MT == 2 || MT == 3) || (MXM == kSortMxFold && MT == 1));
+  // mxfp8: cur and nx hold the two halves of one iteration's 8-bit codes,
+  // loaded one iteration ahead (the same registers as two 4-bit iterations)
+  Codes4 cur = F8 ? load_codes8(W, rowc, 0, hh, 0) : load_codes4(W, rowc, 0, hh);
+  Codes4 nx = F8 ? load_codes8(W, rowc, 0, hh, 1) : load_codes4(W, rowc, 4 * min(1, nit - 1), hh);
   Codes4 pend;
   Chunk16 ch{};
   uint2 mcur{}, mnx{};
@@ -894,7 +941,10 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
       const float* sbuf = sbuf0 + (ii & 1) * 4 * kRows;
       stage_load(min(it + 1, nit - 1));
       Codes4 nn;
-      if (!PAIR || (ii & 1) == 0) {  // ii is a compile-time value after unrolling
+      if (F8) {
+        nn = load_codes8(W, rowc, 4 * min(it + 1, nit - 1), hh, 0);
+        pend = load_codes8(W, rowc, 4 * min(it + 1, nit - 1), hh, 1);
+      } else if (!PAIR || (ii & 1) == 0) {  // ii is a compile-time value after unrolling
         nn = load_codes4(W, rowc, 4 * min(it + 2, nit - 1), hh);
         if (PAIR) pend = load_codes4(W, rowc, 4 * min(it + 3, nit - 1), hh);
       } else {
@@ -907,7 +957,7 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
         const unsigned char* const arows = abuf + (size_t)lc * kV2Row + 64 * hh;
         with_row_blocks<MT>(nrt, [&](auto nrt_c) {
           constexpr int NRT = decltype(nrt_c)::value;
-          mx_iteration<MT, NRT, MXM, 1>(acc, cur, mcur, arows, 0, NRT, hh, blk_split);
+          mx_iteration<MT, NRT, MXM, 1>(acc, cur, nx, mcur, arows, 0, NRT, hh, blk_split);
         });
       } else if (!MX && wave_on) {
         uint2 sv{}, bv{};  // kSortAffineSbl: this column's 4 scales and 4 biases of the iteration
@@ -946,8 +996,13 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
       }
       stage_store((ii + 1) & 1);
       __syncthreads();
-      cur = nx;
-      nx = nn;
+      if (F8) {
+        cur = nn;
+        nx = pend;
+      } else {
+        cur = nx;
+        nx = nn;
+      }
       mcur = mnx;
       mnx = mnn;
     }
@@ -964,7 +1019,7 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
         for (int i = 0; i < 16; ++i) xch[(m * kRowTile + c_row(i, hh)) * kV2GuCols + 32 * cw + lc] = acc[m][i];
   }
   __syncthreads();
-  if (MXM == kSortMxFold && tid == 0) a.mxflag_gu[blockIdx.x] = blk_split;
+  if (sort_mode_fold(MXM) && tid == 0) a.mxflag_gu[blockIdx.x] = blk_split;
   if (mat == 1 || !wave_on) return;
   // affine: h columns in the down codes' nibble-pair order; mxfp4: element order
   const int scol = MX ? col : ((col & ~7) | ((col & 7) >> 1) | ((col & 1) << 2));
@@ -997,7 +1052,7 @@ constexpr int down2_buffers(int mt) { return (size_t)2 * 2 * mt * kRowTile * kV2
 
 template <int MT, int MXM, bool TAIL>
 __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
-  constexpr bool MX = sort_mode_mx(MXM), SBL = MXM == kSortAffineSbl;
+  constexpr bool MX = sort_mode_mx(MXM), SBL = MXM == kSortAffineSbl, F8 = sort_mode_f8(MXM);
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int blk_split;  // kSortMxFold: some group of this block needs the exact pass
   const int H = a.H, I = a.I, G = I / 64;
@@ -1009,7 +1064,7 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
   int tile, cb;
   tile_of_block(ncb, tile, cb);
   if (tile >= (int)a.hdr[3]) return;
-  if (MXM == kSortMxExact && a.mxflag_dn[blockIdx.x] == 0) return;
+  if (sort_mode_exact(MXM) && a.mxflag_dn[blockIdx.x] == 0) return;
   if (threadIdx.x == 0) blk_split = 0;  // published by the first barrier of the stream loop
   const int4 td = a.tiles[tile];
   const int e = td.x, r0 = td.y, nrows = td.z;
@@ -1055,7 +1110,7 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
     if (!MX && tid < 4 * kRows) sbuf0[buf * 4 * kRows + tid] = sst;
   };
 
-  const size_t rowc = ((size_t)e * H + col) * (size_t)(I / 8);
+  const size_t rowc = ((size_t)e * H + col) * (size_t)(I / (F8 ? 4 : 8));
   const size_t rows = ((size_t)e * H + col) * (size_t)G;
   const unsigned char* MS = reinterpret_cast<const unsigned char*>(a.sd);  // mxfp4: E8M0 bytes [E][H][I / 32]
   const size_t rowb = ((size_t)e * H + col) * (size_t)(I / 32);
@@ -1072,8 +1127,10 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
   // Measured: faster for 2 and 3 row blocks (and mxfp4 gate/up with one),
   // slower for the other single-block kernels and past the registers of 4.
   constexpr bool PAIR = MT == 2 || MT == 3;
-  Codes4 cur = load_codes4(a.wd, rowc, 0, hh);
-  Codes4 nx = load_codes4(a.wd, rowc, 4 * min(1, nit - 1), hh);
+  // mxfp8: cur and nx hold the two halves of one iteration's 8-bit codes,
+  // loaded one iteration ahead (the same registers as two 4-bit iterations)
+  Codes4 cur = F8 ? load_codes8(a.wd, rowc, 0, hh, 0) : load_codes4(a.wd, rowc, 0, hh);
+  Codes4 nx = F8 ? load_codes8(a.wd, rowc, 0, hh, 1) : load_codes4(a.wd, rowc, 4 * min(1, nit - 1), hh);
   Codes4 pend;
   Chunk16 ch{};
   uint2 mcur{}, mnx{};
@@ -1102,7 +1159,10 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
       const float* sbuf = sbuf0 + cbuf * 4 * kRows;
       stage_load(min(it + 1, nit - 1));
       Codes4 nn;
-      if (!PAIR || (ii & 1) == 0) {  // ii is a compile-time value after unrolling
+      if (F8) {
+        nn = load_codes8(a.wd, rowc, 4 * min(it + 1, nit - 1), hh, 0);
+        pend = load_codes8(a.wd, rowc, 4 * min(it + 1, nit - 1), hh, 1);
+      } else if (!PAIR || (ii & 1) == 0) {  // ii is a compile-time value after unrolling
         nn = load_codes4(a.wd, rowc, 4 * min(it + 2, nit - 1), hh);
         if (PAIR) pend = load_codes4(a.wd, rowc, 4 * min(it + 3, nit - 1), hh);
       } else {
@@ -1115,7 +1175,7 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
         const unsigned char* const arows = abuf + (size_t)lc * kV2Row + 64 * hh;
         // row blocks tested at run time: the two planes leave no registers
         // for a copy of the loop per row-block count
-        mx_iteration<MT, MT, MXM, 2>(acc, cur, mcur, arows, (size_t)kRows * kV2Row, nrt, hh, blk_split);
+        mx_iteration<MT, MT, MXM, 2>(acc, cur, nx, mcur, arows, (size_t)kRows * kV2Row, nrt, hh, blk_split);
       } else if (!MX && wave_on) {
         uint2 sv{}, bv{};  // kSortAffineSbl: this column's 4 scales and 4 biases of the iteration
         if constexpr (SBL) {
@@ -1158,15 +1218,20 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
       if (NB == 1) __syncthreads();
       stage_store(NB == 2 ? ((ii + 1) & 1) : 0);
       __syncthreads();
-      cur = nx;
-      nx = nn;
+      if (F8) {
+        cur = nn;
+        nx = pend;
+      } else {
+        cur = nx;
+        nx = nn;
+      }
       mcur = mnx;
       mnx = mnn;
     }
     ch = chn;
   }
 
-  if (MXM == kSortMxFold && tid == 0) a.mxflag_dn[blockIdx.x] = blk_split;  // after the loop's last barrier
+  if (sort_mode_fold(MXM) && tid == 0) a.mxflag_dn[blockIdx.x] = blk_split;  // after the loop's last barrier
   if (!wave_on) return;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
@@ -1310,28 +1375,33 @@ bool down2_sbl_fits(const SortedArgs& a, int mt) {
          aligned_for(a.I, a.sd) && aligned_for(a.I, a.bd);
 }
 
+// mxfp4 / mxfp8: the folded pass, then the exact pass over the blocks it flagged
+template <int MT, bool TAIL, int FOLD, int EXACT>
+int mx_launch(const SortedArgs& a, bool down, int tiles8, hipStream_t stream) {
+  if (!down) {
+    const int ncb = (a.I + kV2GuCols - 1) / kV2GuCols;
+    hipLaunchKernelGGL((k_sorted_gateup2<MT, FOLD, TAIL>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT), stream,
+                       a);
+    if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;
+    hipLaunchKernelGGL((k_sorted_gateup2<MT, EXACT, TAIL>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT), stream,
+                       a);
+  } else {
+    const int ncb = (a.H + kV2DnCols - 1) / kV2DnCols;
+    hipLaunchKernelGGL((k_sorted_down2<MT, FOLD, TAIL>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT), stream, a);
+    if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;
+    hipLaunchKernelGGL((k_sorted_down2<MT, EXACT, TAIL>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT), stream, a);
+  }
+  return hipGetLastError() == hipSuccess ? MOE_Q4_OK : MOE_Q4_ERR_LAUNCH;
+}
+
 template <int MT, bool TAIL>
 int gemm_launch(const SortedArgs& a, bool down, hipStream_t stream) {
   const int tiles8 = (a.tiles_max + 7) / 8 * 8;
-  if (a.fmt == kFmtMxfp4) {
+  if (a.fmt == kFmtMxfp4 || a.fmt == kFmtMxfp8) {
     // the streaming kernels only (H and I multiples of 256, checked by the caller)
     if (a.H % 256 || a.I % 256) return MOE_Q4_ERR_UNSUPPORTED;
-    // the folded pass, then the exact pass over the blocks it flagged
-    if (!down) {
-      const int ncb = (a.I + kV2GuCols - 1) / kV2GuCols;
-      hipLaunchKernelGGL((k_sorted_gateup2<MT, kSortMxFold, TAIL>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT),
-                         stream, a);
-      if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;
-      hipLaunchKernelGGL((k_sorted_gateup2<MT, kSortMxExact, TAIL>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT),
-                         stream, a);
-    } else {
-      const int ncb = (a.H + kV2DnCols - 1) / kV2DnCols;
-      hipLaunchKernelGGL((k_sorted_down2<MT, kSortMxFold, TAIL>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT),
-                         stream, a);
-      if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;
-      hipLaunchKernelGGL((k_sorted_down2<MT, kSortMxExact, TAIL>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT),
-                         stream, a);
-    }
+    return a.fmt == kFmtMxfp8 ? mx_launch<MT, TAIL, kSortMx8Fold, kSortMx8Exact>(a, down, tiles8, stream)
+                              : mx_launch<MT, TAIL, kSortMxFold, kSortMxExact>(a, down, tiles8, stream);
   } else if (!down && gateup2_sbl_fits(a, MT)) {
     // scales in LDS: tiles of 2 or more row blocks, and any width that is not
     // a multiple of 1024 (the chunked scale loads need whole chunks)
@@ -1381,7 +1451,7 @@ int sorted_forward_launch(const SortedArgs& a, unsigned stages, hipStream_t stre
   if (stages & MOE_Q4_STAGE_GATEUP) {
     int st = sort_launch(a, stream);
     if (st) return st;
-    if (a.fmt != kFmtMxfp4) {  // the activation group sums serve the affine correction only
+    if (a.fmt == kFmtAffine) {  // the activation group sums serve the affine correction only
       hipLaunchKernelGGL(k_token_gsum, dim3(a.T), dim3(256), 0, stream, a);
       if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;
     }
