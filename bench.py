@@ -87,27 +87,34 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 def bench_sorted(args, Ts, q, synth, torch, np, dev, stream, sleep_cycles_for, codec="affine4_g64"):
     """Chains of distinct prefill layers (E=256 top-8 H=4096 I=2048, uniform routes)
     through the sorted path: full forward, then gate+up and down stages alone.
-    ``codec`` is affine4_g64 (the prefill configuration) or mxfp4."""
+    ``codec`` is affine4_g64 (the prefill configuration), mxfp4 or mxfp8."""
     w = synth.WORKLOADS["prefill"]
     H, I, E, k = w.H, w.I, w.E, w.k
-    mx = codec == "mxfp4"
+    mx = codec in ("mxfp4", "mxfp8")
     eb = expert_bytes_codec(codec, H, I) if mx else expert_bytes(H, I)
     gu_eb, dn_eb = (2 * eb // 3, eb // 3) if mx else (gateup_bytes(H, I), down_bytes(H, I))
-    out = {"workload": f"{w.name}{' in mxfp4' if mx else ''}: uniform top-{k}, "
+    out = {"workload": f"{w.name}{' in ' + codec if mx else ''}: uniform top-{k}, "
                        f"{args.sorted_layers} distinct layers per chain", "per_T": {}}
     stage_codes = (("all", q.MOE_Q4_STAGE_ALL), ("gateup", q.MOE_Q4_STAGE_GATEUP), ("down", q.MOE_Q4_STAGE_DOWN))
     for T in Ts:
         layers = []
         for layer in range(args.sorted_layers):
-            lay = (synth.make_layer_mx if mx else synth.make_layer)(w, T, layer, seed=0, device=dev)
+            if codec == "mxfp8":
+                lay = synth.make_layer_q(codec, w, T, layer, seed=0, device=dev)
+            else:
+                lay = (synth.make_layer_mx if mx else synth.make_layer)(w, T, layer, seed=0, device=dev)
             ids = torch.from_numpy(lay.ids).to(dev)
             tw = torch.from_numpy(lay.weights).to(dev)
             o = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
             bt = lay.bank.tensors()
             if mx:
-                ws = torch.empty(q.moe_swiglu_mxfp4_workspace_bytes(T, k, lay.bank.E, H, I), dtype=torch.uint8,
-                                 device=dev)
-                calls = {st: q.PreparedForwardMX(lay.x, ids, tw, bt, o, ws, code, stream) for st, code in stage_codes}
+                ws = torch.empty(q.moe_swiglu_codec_workspace_bytes(q.CODECS[codec][0], T, k, lay.bank.E, H, I),
+                                 dtype=torch.uint8, device=dev)
+                if codec == "mxfp4":  # the six-tensor mxfp4 bank
+                    calls = {st: q.PreparedForwardMX(lay.x, ids, tw, bt, o, ws, code, stream) for st, code in stage_codes}
+                else:
+                    calls = {st: q.PreparedForwardCodec(codec, lay.x, ids, tw, bt, o, ws, code, stream)
+                             for st, code in stage_codes}
             else:
                 ws = q.new_workspace(T, k, E, H, I, dev)
                 calls = {st: q.PreparedForward(lay.x, ids, tw, bt, o, ws, code, stream) for st, code in stage_codes}
@@ -283,6 +290,8 @@ def main():
     ap.add_argument("--sorted-layers", type=int, default=4, help="distinct layers per prefill chain")
     ap.add_argument("--sorted-mx-Ts", default="512,2048",
                     help="token counts of the same prefill workload over mxfp4 banks (sorted path); empty to skip")
+    ap.add_argument("--sorted-mx8-Ts", default="512,2048",
+                    help="token counts of the same prefill workload over mxfp8 banks (sorted path); empty to skip")
     ap.add_argument("--pair-layers", type=int, default=20,
                     help="layers of each chain timed again as a per-pair baseline (one call per token, so "
                          "an expert shared by tokens is streamed once per token); 0 to skip")
@@ -529,10 +538,13 @@ def main():
     if sorted_Ts:
         result["sorted_path"] = bench_sorted(args, sorted_Ts, q, synth, torch, np, dev, stream,
                                              lambda ms: sleep_cycles_for(ms))
-        mx_Ts = [int(v) for v in args.sorted_mx_Ts.split(",") if v.strip()]
-        if mx_Ts:
-            result["sorted_path_mxfp4"] = bench_sorted(args, mx_Ts, q, synth, torch, np, dev, stream,
-                                                       lambda ms: sleep_cycles_for(ms), codec="mxfp4")
+    # the same prefill workload over the block-scaled banks
+    for key, opt, codec in (("sorted_path_mxfp4", args.sorted_mx_Ts, "mxfp4"),
+                            ("sorted_path_mxfp8", args.sorted_mx8_Ts, "mxfp8")):
+        cTs = [int(v) for v in opt.split(",") if v.strip()]
+        if cTs:
+            result[key] = bench_sorted(args, cTs, q, synth, torch, np, dev, stream, lambda ms: sleep_cycles_for(ms),
+                                       codec=codec)
 
     # ---- the same verify workload over banks in other codecs ----
     codecs = [c for c in args.codecs.split(",") if c.strip()]
