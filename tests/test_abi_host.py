@@ -298,6 +298,19 @@ def test_mx_long_inputs_take_the_sorted_path_on_host():
     assert call_mx(L=40, k=8, E=16, H=32768, I=1024, ws_bytes=m) == q.MOE_Q4_ERR_LAUNCH
 
 
+def test_mxfp8_long_inputs_take_the_sorted_path_on_host():
+    m8 = q.MOE_Q4_CODEC_MXFP8
+    assert q.moe_swiglu_codec_workspace_bytes(m8, 512, 8, 256, 4096, 2048) == \
+        q.moe_swiglu_q4_workspace_bytes(512, 8, 256, 4096, 2048) > 0
+    # not a multiple of 256: token chunks
+    assert q.moe_swiglu_codec_workspace_bytes(m8, 512, 8, 256, 2048, 320) == \
+        q.moe_swiglu_codec_workspace_bytes(m8, 32, 8, 256, 2048, 320)
+    # the other codecs keep token chunks at multiples of 256 too
+    for c in (q.MOE_Q4_CODEC_NVFP4, q.MOE_Q4_CODEC_AFFINE4_G32, q.MOE_Q4_CODEC_AFFINE8_G64):
+        assert q.moe_swiglu_codec_workspace_bytes(c, 512, 8, 256, 2048, 1024) == \
+            q.moe_swiglu_codec_workspace_bytes(c, 32, 8, 256, 2048, 1024), c
+
+
 def test_codec_chunks_shrink_to_fit_the_lds():
     # H = 4096: 32 tokens' activations do not fit one workgroup's LDS, fewer do
     nv = q.MOE_Q4_CODEC_NVFP4
