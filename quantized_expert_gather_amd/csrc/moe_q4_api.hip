@@ -61,7 +61,7 @@ static int select_path(int L, int k, int E, int H, int I) {
 // Codecs other than 4-bit affine group 64 run on the union kernels, with H
 // and I multiples of 32 (one scale per 32 inputs at least; 64 for the
 // group-64 8-bit affine codes).  More tokens than one union launch serves
-// run as consecutive token chunks: at most 32 tokens and 256 pairs, fewer
+// run as consecutive token chunks: at most 32 tokens and 1024 pairs, fewer
 // where the chunk's activations would not fit the LDS.  mxfp4 and mxfp8
 // inputs longer than that take the sorted (MFMA) path where its streaming
 // kernels cover the shape.
