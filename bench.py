@@ -183,6 +183,52 @@ def expert_bytes_codec(codec: str, H: int, I: int) -> int:
     return 3 * (H * I * bits // 8 + round(H * I * per))
 
 
+def bench_workload(wname, q, synth, torch, np, dev, stream, sleep_cycles_for, steps):
+    """Another q4 g64 decode / verify configuration, for context: a chain of
+    all its layers (distinct weights and routes) per L of the workload, full
+    forward; µs per layer and effective expert-weight GB/s."""
+    w = synth.WORKLOADS[wname]
+    H, I, k = w.H, w.I, w.k
+    eb = expert_bytes(H, I)
+    out = {"workload": f"{w.name}: {w.routing} routes, chain of {w.n_layers} layers", "per_L": {}}
+    for L in w.Ls:
+        layers = []
+        for layer in range(w.n_layers):
+            lay = synth.make_chain_layer(w, L, layer, seed=0, device=dev)
+            ids = torch.from_numpy(lay.ids).to(dev)
+            tw = torch.from_numpy(lay.weights).to(dev)
+            o = torch.empty((L, H), dtype=torch.bfloat16, device=dev)
+            ws = q.new_workspace(L, k, lay.bank.E, H, I, dev)
+            call = q.PreparedForward(lay.x, ids, tw, lay.bank.tensors(), o, ws, q.MOE_Q4_STAGE_ALL, stream)
+            layers.append({"u": int(lay.bank.E), "keep": (lay, ids, tw, o, ws), "call": call})
+        torch.cuda.synchronize()
+
+        def chain(delay):
+            torch.cuda._sleep(delay)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            th = time.perf_counter()
+            for lay in layers:
+                lay["call"]()
+            e1.record()
+            return e0, e1, (time.perf_counter() - th) * 1e3
+
+        warm = chain(0)
+        torch.cuda.synchronize()
+        delay = sleep_cycles_for(1.5 * warm[2] + 1.0)
+        recs = [chain(delay) for _ in range(max(3, steps))]
+        torch.cuda.synchronize()
+        nl = len(layers)
+        ms = float(np.median([a.elapsed_time(b) for a, b, _ in recs])) / nl
+        u_mean = sum(l["u"] for l in layers) / nl
+        gb = u_mean * eb / (ms * 1e-3) / 1e9
+        out["per_L"][str(L)] = {"us_per_layer": round(ms * 1e3, 2), "u_mean": round(u_mean, 2),
+                                "eff_GBps": round(gb, 1), "frac_peak": round(gb / PEAK_HBM_GBPS, 4)}
+        log(f"{w.name} L={L}: {ms * 1e3:.2f} us/layer, {gb:.0f} GB/s effective")
+        del layers
+    return out
+
+
 def bench_codec(codec, args, Ls, q, synth, torch, np, dev, stream, sleep_cycles_for):
     """The verify workload over banks in another codec: chains of layers
     spread over the depth profile (so over the overlap range), full forward
@@ -290,6 +336,10 @@ def main():
     ap.add_argument("--sorted-layers", type=int, default=4, help="distinct layers per prefill chain")
     ap.add_argument("--sorted-mx-Ts", default="512,2048",
                     help="token counts of the same prefill workload over mxfp4 banks (sorted path); empty to skip")
+    ap.add_argument("--workloads", default="flash,small,small_pooled",
+                    help="other q4 decode / verify configurations timed for context (flash: E=288 top-8 H=4096 "
+                         "I=2048 at L=1, 4; small / small_pooled: E=256 top-8 H=2048 I=512 at L=8, 16, 32); "
+                         "empty to skip")
     ap.add_argument("--sorted-mx8-Ts", default="512,2048",
                     help="token counts of the same prefill workload over mxfp8 banks (sorted path); empty to skip")
     ap.add_argument("--pair-layers", type=int, default=20,
@@ -545,6 +595,12 @@ def main():
         if cTs:
             result[key] = bench_sorted(args, cTs, q, synth, torch, np, dev, stream, lambda ms: sleep_cycles_for(ms),
                                        codec=codec)
+
+    # ---- the other decode / verify configurations (context, not the metric) ----
+    wnames = [v for v in args.workloads.split(",") if v.strip()]
+    if wnames:
+        result["other_workloads"] = {n: bench_workload(n, q, synth, torch, np, dev, stream,
+                                                        lambda ms: sleep_cycles_for(ms), args.steps) for n in wnames}
 
     # ---- the same verify workload over banks in other codecs ----
     codecs = [c for c in args.codecs.split(",") if c.strip()]
