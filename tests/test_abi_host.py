@@ -384,3 +384,18 @@ def test_codec_8bit_host_checks():
     assert call_codec(MX8, ptrs=p, ws=0) == q.MOE_Q4_ERR_WORKSPACE
     # 8-bit codes are twice the bytes: out just past the 4-bit size of wg still aliases
     assert call_codec(A8, out=fake(3) + 8 * 128 * 256 // 2 + 64) == q.MOE_Q4_ERR_ALIAS
+
+
+def test_kernel_source_hash_ignores_comments_and_whitespace(tmp_path, monkeypatch):
+    # the stored traffic figures stay valid across comment edits, not code edits
+    import bench
+    d = tmp_path / "quantized_expert_gather_amd" / "csrc"
+    d.mkdir(parents=True)
+    src = d / "k.hip"
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    src.write_text("int f(int a) { return a + 1; }  // one\n")
+    h0 = bench.kernel_source_hash()
+    src.write_text("/* block\\n comment */\nint f(int a) {\n  return a + 1;  // changed comment\n}\n")
+    assert bench.kernel_source_hash() == h0
+    src.write_text("int f(int a) { return a + 2; }\n")
+    assert bench.kernel_source_hash() != h0
