@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <stdint.h>
 #include <string.h>
 
@@ -99,6 +100,7 @@ static void sorted_workspace_args(SortedArgs& a, unsigned char* ws, const Sorted
   a.rank_tmp = reinterpret_cast<int32_t*>(ws + sw.rank_tmp);
   a.tiles = reinterpret_cast<int4*>(ws + sw.tiles);
   a.asum = reinterpret_cast<float*>(ws + sw.asum);
+  a.texp = reinterpret_cast<int32_t*>(ws + sw.texp);
   a.hhi = reinterpret_cast<uint16_t*>(ws + sw.hhi);
   a.hlo = reinterpret_cast<uint16_t*>(ws + sw.hlo);
   a.hsum2 = reinterpret_cast<float*>(ws + sw.hsum2);
@@ -127,14 +129,19 @@ static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return na && nb && x < y + nb && y < x + na;
 }
 
+// Compute units of the current device, cached per device (host threads may
+// call concurrently: each entry is one atomic int, written once).
 static int num_cus() {
-  static int cache[64];
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
-  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return -1;
-  if (dev < 64) cache[dev] = n;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 

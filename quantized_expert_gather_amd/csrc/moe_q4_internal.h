@@ -101,6 +101,7 @@ struct SortedArgs {
   int32_t* rank_tmp;  // [P] pairs scattered into their expert's segment, unordered
   int4* tiles;        // [tiles_max] (expert, first sorted row, rows, 0)
   float* asum;        // [T][H/64] per-token sums of x over each 64-input group
+  int32_t* texp;      // [T] exponent of each token's largest |x| (frexp; 0 for x = 0)
   uint16_t* hhi;      // [P][I] bf16 hi of h, columns in code order inside each 8
   uint16_t* hlo;      // [P][I] bf16 lo of h (h - hi, rounded)
   float* hsum2;       // [P][I/32] sum of hi + lo over each 32 columns
@@ -110,7 +111,7 @@ struct SortedArgs {
 };
 
 struct SortedWorkspace {
-  size_t hdr, offsets, perm, inv, rank_tmp, tiles, asum, hhi, hlo, hsum2, ys, mxflag, total;
+  size_t hdr, offsets, perm, inv, rank_tmp, tiles, asum, texp, hhi, hlo, hsum2, ys, mxflag, total;
 };
 
 int sorted_row_blocks(int T, int k, int E);

@@ -18,7 +18,9 @@
 //   k_sort_rank      one thread per pair: its rank by pair index inside its
 //                    expert's segment, which makes the order stable (sorted by
 //                    (expert, pair)) -> perm and inv.
-//   k_token_gsum     per token and 64-input group, the fp32 sum of x.
+//   k_token_gsum     per token and 64-input group, the fp32 sum of x; per
+//                    token the exponent e_t of its largest |x| (h is stored
+//                    times 2^-e_t and the combine undoes it exactly).
 //   k_sorted_gateup  per (tile, 128 hidden columns): the tile's gathered x rows
 //                    staged in LDS per 64-input group; gate and up codes go
 //                    straight from HBM into registers and become exact bf16
@@ -155,15 +157,38 @@ __global__ __launch_bounds__(256) void k_sort_rank(SortedArgs a) {
   a.inv[p] = lo + r;
 }
 
+// Per token: the fp32 sum of x over each 64-input group (affine banks only),
+// and the exponent e_t of the token's largest |x|.  The gate/up kernels
+// store h * 2^-e_t and the combine multiplies the token's output by 2^e_t
+// (both exact), so the bf16 hi + lo planes of h stay in the normal range for
+// tokens with tiny activations: h scales like x^2, and below about 2^-117
+// the lo plane would be subnormal, which the MFMAs flush to zero.
 __global__ __launch_bounds__(256) void k_token_gsum(SortedArgs a) {
   const int t = blockIdx.x;
   const int G = a.H / 64;
+  uint32_t mb = 0;  // largest |x| as bf16 magnitude bits (they order like the values)
   for (int g = threadIdx.x; g < G; g += 256) {
     const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)t * a.H + 64 * g);
     float acc = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc = sum8_bf16(src[c], acc);
-    a.asum[(size_t)t * G + g] = acc;
+    for (int c = 0; c < 8; ++c) {
+      const uint4 v = src[c];
+      acc = sum8_bf16(v, acc);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) mb = max(mb, max(w4[q] & 0x7FFFu, (w4[q] >> 16) & 0x7FFFu));
+    }
+    if (a.fmt == kFmtAffine) a.asum[(size_t)t * G + g] = acc;
+  }
+  __shared__ uint32_t wmax[4];
+  float m = __uint_as_float(mb << 16);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = __float_as_uint(m);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float mx = fmaxf(fmaxf(__uint_as_float(wmax[0]), __uint_as_float(wmax[1])),
+                           fmaxf(__uint_as_float(wmax[2]), __uint_as_float(wmax[3])));
+    a.texp[t] = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) : 0;
   }
 }
 
@@ -321,7 +346,7 @@ __global__ __launch_bounds__(kMmThreads, 2) void k_sorted_gateup(SortedArgs a) {
       for (int i = 0; i < 16; ++i) {
         const int r = m * kRowTile + c_row(i, hh);
         const float gv = og[m][i];
-        const float hv = gv / (1.0f + __expf(-gv)) * ou[m][i];
+        const float hv = __builtin_amdgcn_ldexpf(gv / (1.0f + __expf(-gv)) * ou[m][i], -a.texp[tok[r]]);
         const uint32_t hi = f32_to_bf16_rne(hv);
         const float hif = __uint_as_float(hi << 16);
         const uint32_t lo = f32_to_bf16_rne(hv - hif);
@@ -1031,7 +1056,7 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
         const int r = m * kRowTile + c_row(i, hh);
         const float gv = acc[m][i];
         const float uv = xch[r * kV2GuCols + 32 * cw + lc];
-        const float hv = gv / (1.0f + __expf(-gv)) * uv;
+        const float hv = __builtin_amdgcn_ldexpf(gv / (1.0f + __expf(-gv)) * uv, -a.texp[tok[r]]);
         const uint32_t hi = f32_to_bf16_rne(hv);
         const float hif = __uint_as_float(hi << 16);
         const uint32_t lo = f32_to_bf16_rne(hv - hif);
@@ -1266,6 +1291,12 @@ __global__ __launch_bounds__(256) void k_sorted_combine(SortedArgs a) {
     acc.z = fmaf(w, v.z, acc.z);
     acc.w = fmaf(w, v.w, acc.w);
   }
+  // the pairs' outputs carry the token's 2^-e_t (see k_token_gsum)
+  const int te = a.texp[t];
+  acc.x = __builtin_amdgcn_ldexpf(acc.x, te);
+  acc.y = __builtin_amdgcn_ldexpf(acc.y, te);
+  acc.z = __builtin_amdgcn_ldexpf(acc.z, te);
+  acc.w = __builtin_amdgcn_ldexpf(acc.w, te);
   if (a.out_f32) {
     reinterpret_cast<float4*>(a.out)[(size_t)t * n4 + it] = acc;
   } else {
@@ -1319,6 +1350,7 @@ SortedWorkspace sorted_workspace_layout(int T, int k, int E, int H, int I) {
   w.rank_tmp = off; off = r256(off + P * 4);
   w.tiles = off;    off = r256(off + (size_t)sorted_tiles_max(T, k, E, kRowTile) * 16);
   w.asum = off;     off = r256(off + (size_t)T * (H / 64) * 4);
+  w.texp = off;     off = r256(off + (size_t)T * 4);
   w.hhi = off;      off = r256(off + P * I * 2);
   w.hlo = off;      off = r256(off + P * I * 2);
   w.hsum2 = off;    off = r256(off + P * (I / 32) * 4);
@@ -1451,10 +1483,9 @@ int sorted_forward_launch(const SortedArgs& a, unsigned stages, hipStream_t stre
   if (stages & MOE_Q4_STAGE_GATEUP) {
     int st = sort_launch(a, stream);
     if (st) return st;
-    if (a.fmt == kFmtAffine) {  // the activation group sums serve the affine correction only
-      hipLaunchKernelGGL(k_token_gsum, dim3(a.T), dim3(256), 0, stream, a);
-      if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;
-    }
+    // per-token exponents (every format) and activation group sums (affine)
+    hipLaunchKernelGGL(k_token_gsum, dim3(a.T), dim3(256), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;
     st = gemm_dispatch(a, false, stream);
     if (st) return st;
   }

@@ -3,6 +3,7 @@
 // down kernel templates live in moe_q4_union_kernels.h and are instantiated
 // in the moe_q4_inst_*.hip units (compiled in parallel).
 #include <algorithm>
+#include <mutex>
 
 #include "moe_q4_union_kernels.h"
 #include "moe_q4_inst.h"
@@ -134,13 +135,20 @@ struct OccCache {
   int blocks;
 };
 
+// Resident blocks per CU of a kernel at an LDS size, cached (host threads may
+// call concurrently, so the cache is guarded).
 int blocks_per_cu(const void* fn, int threads, size_t lds) {
+  static std::mutex mu;
   static OccCache cache[64];
   static int n = 0;
-  for (int c = 0; c < n; ++c)
-    if (cache[c].fn == fn && cache[c].lds == lds) return cache[c].blocks;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int c = 0; c < n; ++c)
+      if (cache[c].fn == fn && cache[c].lds == lds) return cache[c].blocks;
+  }
   int b = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, fn, threads, lds) != hipSuccess || b < 1) b = 1;
+  std::lock_guard<std::mutex> lock(mu);
   if (n < 64) cache[n++] = OccCache{fn, lds, b};
   return b;
 }

@@ -625,8 +625,9 @@ __device__ __forceinline__ void dn_load(const UnionArgs& a, size_t row0, bool va
 // LDS of a down block: the union table, the work prefix per expert, then
 // per staged pair slot its hidden vector as fp16 pairs [NA][KU] (uint4; KU
 // positions of 8 NA inputs), the sums of each position's fp16 values [KU],
-// the router weight times the slot's 2^-k and the slot's ys row.
-__host__ __device__ constexpr size_t down_slot_bytes(int KU, int na = 4) { return (size_t)KU * (16 * na + 4) + 8; }
+// the router weight, the slot's ys row and the exponent that undoes the
+// slot's power-of-two scaling.
+__host__ __device__ constexpr size_t down_slot_bytes(int KU, int na = 4) { return (size_t)KU * (16 * na + 4) + 12; }
 __host__ __device__ constexpr size_t down_lds_base(int P) { return ((size_t)16 * P + 15) & ~size_t(15); }
 // bytes before the staged slots: the union table and the work prefix
 __host__ __device__ constexpr size_t down_lds_head(int P) {
@@ -635,12 +636,15 @@ __host__ __device__ constexpr size_t down_lds_head(int P) {
 
 // Converts pair slot `slot` (h of one (expert, token) pair, fp32) into staged
 // slot `ls`: scaled by the power of two that puts its largest magnitude in
-// [2^13, 2^14), rounded to fp16.  One wave per slot; a lane converts 32
-// inputs at a time (one position of 4-bit codes, two of 8-bit codes).  KU
-// counts 32-input blocks.
+// [2^13, 2^14), rounded to fp16.  The scaling is applied per element as an
+// exponent shift (v_ldexp), never as a multiplier 2^n, which would overflow
+// for vectors whose entries all lie below 2^-114; sexp gets the inverse
+// shift, applied to the slot's outputs.  One wave per slot; a lane converts
+// 32 inputs at a time (one position of 4-bit codes, two of 8-bit codes).
+// KU counts 32-input blocks.
 template <int NA>
 __device__ __forceinline__ void down_stage_slot(const UnionArgs& a, int ls, int slot, int KU, uint4* hvs, float* hss,
-                                                float* stw, int* sdst, bool natural) {
+                                                float* stw, int* sdst, int* sexp, bool natural) {
   const int lane = threadIdx.x & 63;
   const float* hrow = a.hbuf + (size_t)slot * a.I;
   auto load32 = [&](int j, float (&v)[32]) {
@@ -651,14 +655,14 @@ __device__ __forceinline__ void down_stage_slot(const UnionArgs& a, int ls, int 
       v[4 * q4 + 0] = f4.x; v[4 * q4 + 1] = f4.y; v[4 * q4 + 2] = f4.z; v[4 * q4 + 3] = f4.w;
     }
   };
-  auto convert = [&](int j, const float (&v)[32], float up) {
+  auto convert = [&](int j, const float (&v)[32], int up) {
     float sum = 0.0f;
 #pragma unroll
     for (int wi = 0; wi < 4; ++wi) {
       _Float16 hb[8];
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
-        hb[n] = (_Float16)(v[8 * wi + n] * up);
+        hb[n] = (_Float16)__builtin_amdgcn_ldexpf(v[8 * wi + n], up);
         sum += (float)hb[n];
       }
       uint4 pk;
@@ -691,7 +695,7 @@ __device__ __forceinline__ void down_stage_slot(const UnionArgs& a, int ls, int 
     for (int n = 0; n < 32; ++n) mx = fmaxf(mx, on ? fabsf(v[n]) : 0.0f);
     mx = wave_max(mx);
     ex = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) : 0;
-    if (on) convert(lane, v, __builtin_ldexpf(1.0f, 14 - ex));
+    if (on) convert(lane, v, 14 - ex);
   } else {  // several positions per lane: the maximum first, then a second read
     for (int j = lane; j < KU; j += 64) {
       float v[32];
@@ -701,7 +705,7 @@ __device__ __forceinline__ void down_stage_slot(const UnionArgs& a, int ls, int 
     }
     mx = wave_max(mx);
     ex = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) : 0;
-    const float up = __builtin_ldexpf(1.0f, 14 - ex);
+    const int up = 14 - ex;
     for (int j = lane; j < KU; j += 64) {
       float v[32];
       load32(j, v);
@@ -709,19 +713,21 @@ __device__ __forceinline__ void down_stage_slot(const UnionArgs& a, int ls, int 
     }
   }
   if (lane == 0) {
-    stw[ls] = a.slot_w[slot] * __builtin_ldexpf(1.0f, ex - 14);
+    stw[ls] = a.slot_w[slot];
     sdst[ls] = a.slot_dst[slot];
+    sexp[ls] = ex - 14;
   }
 }
 
 // One step: RS rows of this lane group against NT converted hidden vectors;
-// each token's RS row totals, times its router weight (and 2^-k), go to its
-// ys row in one store (every lane stores its residue's row; token slots past
-// the expert's count write to the sink).
+// each token's RS row totals, times its router weight and shifted back by
+// the exponent of its hidden vector's scaling, go to its ys row in one store
+// (every lane stores its residue's row; token slots past the expert's count
+// write to the sink).
 template <int LPR, int PPL, int RS, int NT, bool FULL, bool QS, int FMT = kFmtAffine>
 __device__ __forceinline__ void dn_step(const UnionArgs& a, const DnFrag<PPL, RS>& f, const uint32_t (&hv)[NT][PPL][16],
-                                       const float (&hs)[NT][PPL], const float (&tw)[NT], float* const (&dst)[NT],
-                                       int row0, int li, int KU, uint32_t sel) {
+                                       const float (&hs)[NT][PPL], const float (&tw)[NT], const int (&te)[NT],
+                                       float* const (&dst)[NT], int row0, int li, int KU, uint32_t sel) {
 #pragma unroll
   for (int r = 0; r < RS; ++r)
 #pragma unroll
@@ -773,7 +779,7 @@ __device__ __forceinline__ void dn_step(const UnionArgs& a, const DnFrag<PPL, RS
   }
   const int rr = li & (RS - 1);
 #pragma unroll
-  for (int c = 0; c < NT; ++c) dst[c][row0 + rr] = tw[c] * reduce_rows<LPR, RS>(acc[c]);
+  for (int c = 0; c < NT; ++c) dst[c][row0 + rr] = __builtin_amdgcn_ldexpf(tw[c] * reduce_rows<LPR, RS>(acc[c]), te[c]);
 }
 
 // One (expert, token chunk) segment of a down wave: read the chunk's
@@ -783,7 +789,7 @@ template <int LPR, int PPL, bool FULL, bool QS, int NT, int RS, int WSTEP, int F
 __device__ __forceinline__ void dn_segment(const UnionArgs& a, size_t ebase, int ls0, int nt, int gj, int klast,
                                            int li, int g, int KU, int KG, int H, const unsigned char* lane_sbase,
                                            const DnOffsets<PPL, RS>& o, uint32_t sel, const uint4* hvs,
-                                           const float* hss, const float* stw, const int* sdst,
+                                           const float* hss, const float* stw, const int* sdst, const int* sexp,
                                            float* rows_dst = nullptr) {
   // prefetches past the last step are zero-range no-ops
   auto load = [&](int kk, DnFrag<PPL, RS>& fr) {
@@ -797,6 +803,7 @@ __device__ __forceinline__ void dn_segment(const UnionArgs& a, size_t ebase, int
 
   uint32_t hv[NT][PPL][16];
   float hs[NT][PPL], tw[NT];
+  int te[NT];
   float* dst[NT];
 #pragma unroll
   for (int c = 0; c < NT; ++c) {
@@ -822,12 +829,13 @@ __device__ __forceinline__ void dn_segment(const UnionArgs& a, size_t ebase, int
       }
     }
     tw[c] = live ? stw[ls] : 0.0f;
+    te[c] = live ? sexp[ls] : 0;
     dst[c] = live ? a.ys + (size_t)wave_uniform(sdst[ls]) * H : a.ys_dummy;
     if (rows_dst) dst[c] = rows_dst;  // one token: the block's row slice in LDS
   }
 
   auto step = [&](int kk, const DnFrag<PPL, RS>& fr) {
-    dn_step<LPR, PPL, RS, NT, FULL, QS, FMT>(a, fr, hv, hs, tw, dst, (gj + kk) * WSTEP + g * RS, li, KU, sel);
+    dn_step<LPR, PPL, RS, NT, FULL, QS, FMT>(a, fr, hv, hs, tw, te, dst, (gj + kk) * WSTEP + g * RS, li, KU, sel);
   };
 #pragma unroll 1
   for (int kk = 0;; kk += 3) {
@@ -875,6 +883,7 @@ __global__ __launch_bounds__(down_threads(NT, PPL)) void k_down(UnionArgs a) {
   float* hss = reinterpret_cast<float*>(hvs + (size_t)SM * NA * KU);  // [SM][KU]
   float* stw = hss + (size_t)SM * KU;                                 // [SM]
   int* sdst = reinterpret_cast<int*>(stw + SM);                       // [SM]
+  int* sexp = sdst + SM;                                              // [SM]
   __shared__ int unit_q;  // next dynamically assigned unit (block-relative)
   const int tid = threadIdx.x;
   const int umax = min(P, a.E);
@@ -939,9 +948,9 @@ __global__ __launch_bounds__(down_threads(NT, PPL)) void k_down(UnionArgs a) {
     const int s0 = (int)((long long)spe * b / nblk), s1 = (int)((long long)spe * (b + 1) / nblk);
     const int ns = s1 - s0, nrows = ns * WSTEP;
     if (ns <= 0) return;  // uniform over the block
-    float* part = reinterpret_cast<float*>(sdst + SM);  // [u][nrows]
+    float* part = reinterpret_cast<float*>(sexp + SM);  // [u][nrows]
     for (int sl = wave; sl < u; sl += NW)
-      down_stage_slot<NA>(a, sl, sl, I >> 5, hvs, hss, stw, sdst, fmt_natural(FMT));
+      down_stage_slot<NA>(a, sl, sl, I >> 5, hvs, hss, stw, sdst, sexp, fmt_natural(FMT));
     __syncthreads();
     const int nch = max(1, min(ns, NW / max(u, 1)));  // step chunks per expert
     const int cs = (ns + nch - 1) / nch;
@@ -950,7 +959,7 @@ __global__ __launch_bounds__(down_threads(NT, PPL)) void k_down(UnionArgs a) {
       if (g0 >= g1) continue;
       const size_t ebase = (size_t)wave_uniform(utab[i].x) * H + (size_t)s0 * WSTEP;
       dn_segment<LPR, PPL, FULL, QS, 1, RS, WSTEP, FMT>(a, ebase, i, 1, g0, g1 - g0 - 1, li, g, KU, KG, H, lane_sbase,
-                                                       o, sel, hvs, hss, stw, sdst, part + (size_t)i * nrows);
+                                                       o, sel, hvs, hss, stw, sdst, sexp, part + (size_t)i * nrows);
     }
     __syncthreads();
     for (int r = tid; r < nrows; r += blockDim.x) {
@@ -991,7 +1000,7 @@ __global__ __launch_bounds__(down_threads(NT, PPL)) void k_down(UnionArgs a) {
     const int c1 = min(s_hi, c0 + SM);
     if (tid == 0) unit_q = NW;
     for (int sl = c0 + wave; sl < c1; sl += NW)
-      down_stage_slot<NA>(a, sl - c0, sl, I >> 5, hvs, hss, stw, sdst, fmt_natural(FMT));
+      down_stage_slot<NA>(a, sl - c0, sl, I >> 5, hvs, hss, stw, sdst, sexp, fmt_natural(FMT));
     __syncthreads();
     for (int j = wave; j < nub; j = grab()) {
       const int un = ub + j;
@@ -1006,10 +1015,10 @@ __global__ __launch_bounds__(down_threads(NT, PPL)) void k_down(UnionArgs a) {
         const int nt = min(NT, t_hi - t0);
         if (NT > 1 && nt == 1)
           dn_segment<LPR, PPL, FULL, QS, 1, RS, WSTEP, FMT>(a, ebase, t0 - c0, 1, gj, klast, li, g, KU, KG, H,
-                                                           lane_sbase, o, sel, hvs, hss, stw, sdst);
+                                                           lane_sbase, o, sel, hvs, hss, stw, sdst, sexp);
         else
           dn_segment<LPR, PPL, FULL, QS, NT, RS, WSTEP, FMT>(a, ebase, t0 - c0, nt, gj, klast, li, g, KU, KG, H,
-                                                            lane_sbase, o, sel, hvs, hss, stw, sdst);
+                                                            lane_sbase, o, sel, hvs, hss, stw, sdst, sexp);
       }
     }
     __syncthreads();  // the converted slots and the counter are reused

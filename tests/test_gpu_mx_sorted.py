@@ -25,6 +25,7 @@ import torch
 
 import oracle
 import synth
+from tile_sampling import coverage_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -244,8 +245,7 @@ def test_mx_sorted_prefill_full_size_sampled(T):
     got = out.cpu().numpy()
     assert np.isfinite(got).all()
     check_path(ws)
-    rng = np.random.default_rng(T)
-    sample = sorted({0, T - 1, *rng.choice(T, size=6, replace=False).tolist()})
+    sample = coverage_tokens(lay.ids, lay.bank.E, n=64, seed=T)
     used = np.unique(lay.ids[sample])
     sub = lay.bank.select(used).to("cpu")
     ref = oracle.forward_pairs_mx(lay.x[sample].cpu(), np.searchsorted(used, lay.ids[sample]).astype(np.int32),

@@ -17,6 +17,8 @@ import torch
 
 import oracle
 import synth
+from tile_sampling import coverage_tokens
+from tiny_cases import tiny_zero_saturated
 
 pytestmark = pytest.mark.gpu
 
@@ -218,8 +220,9 @@ def test_sorted_prefill_full_size_sampled(T):
     out, ws = run_layer(lay.x, lay.ids, lay.weights, lay.bank)
     got = out.cpu().numpy()
     assert np.isfinite(got).all()
-    rng = np.random.default_rng(T)
-    sample = sorted({0, T - 1, *rng.choice(T, size=6, replace=False).tolist()})
+    # 64+ tokens covering the first and last tiles of the largest and smallest
+    # experts and every partial-tile height
+    sample = coverage_tokens(lay.ids, lay.bank.E, n=64, seed=T)
     used = np.unique(lay.ids[sample])
     sub = lay.bank.select(used).to("cpu")
     ref = oracle.forward_pairs(lay.x[sample].cpu(), np.searchsorted(used, lay.ids[sample]).astype(np.int32),
@@ -257,8 +260,7 @@ def test_sorted_one_expert_over_32k_rows():
     T, k, E, H, I = 5000, 8, 8, 1024, 1024
     x, _, tw, bank = synth.random_problem(T, k, E, H, I, seed=31)
     ids = np.full((T, k), 5, np.int32)
-    rng = np.random.default_rng(31)
-    sample = sorted({0, T - 1, *rng.choice(T, size=6, replace=False).tolist()})
+    sample = coverage_tokens(ids, E, n=64, seed=31)
     _sampled_check(x, ids, tw, bank, sample, "one expert, 40000 rows")
 
 
@@ -266,8 +268,7 @@ def test_sorted_long_prefill_ragged_widths():
     # H and I not multiples of the streaming kernels' 1024: the general kernels at T = 4096
     T, k, E, H, I = 4096, 4, 16, 1088, 576
     x, ids, tw, bank = synth.random_problem(T, k, E, H, I, seed=37)
-    rng = np.random.default_rng(37)
-    sample = sorted({0, T - 1, *rng.choice(T, size=6, replace=False).tolist()})
+    sample = coverage_tokens(ids, E, n=64, seed=37)
     _sampled_check(x, ids, tw, bank, sample, "ragged widths")
 
 
@@ -276,6 +277,35 @@ def test_sorted_widths_multiple_of_256_full_size():
     # T = 512 over 64 experts, 64 rows per expert, sampled rows
     T, k, E, H, I = 512, 8, 64, 5120, 1536
     x, ids, tw, bank = synth.random_problem(T, k, E, H, I, seed=41, device="cuda")
-    rng = np.random.default_rng(41)
-    sample = sorted({0, T - 1, *rng.choice(T, size=6, replace=False).tolist()})
+    sample = coverage_tokens(ids, E, n=64, seed=41)
     _sampled_check(x, ids, tw, bank, sample, "widths multiple of 256")
+
+
+# ---------------------------------------------------------------------------
+# tiny, zero and saturated activations on the sorted path
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("codec", ["affine4_g64", "mxfp4", "mxfp8"])
+def test_sorted_tiny_and_zero_activations(codec):
+    # 40 tokens (sorted path; H and I multiples of 256 keep mxfp4 and mxfp8 on
+    # it too): token 0's activations scaled by 2^-66, token 1 zero, tokens 2
+    # and 3 with gates of about -95 and -86 on one expert
+    q = _q()
+    L, k, E, H, I = 40, 4, 8, 512, 256
+    x, ids, tw, bank = synth.random_problem_q(codec, L, k, E, H, I, seed=33)
+    x, ids, tw = tiny_zero_saturated(x, ids, tw, bank, e_star=5)
+    say("sorted tiny/zero/saturated", codec)
+    ref = oracle.forward_pairs_q(codec, x, ids, tw, bank)
+    dev = torch.device("cuda")
+    n = q.moe_swiglu_codec_workspace_bytes(q.CODECS[codec][0], L, k, E, H, I)
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    out = q.forward_bank_codec(x.to(dev), torch.from_numpy(ids).to(dev), torch.from_numpy(tw).to(dev),
+                               bank.to(dev), out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    assert q.moe_q4_read_device_status(ws) == (0, q.MOE_Q4_PATH_SORTED)
+    got = out.cpu().numpy()
+    err = rel_err_rows(got, ref)
+    print(f"  row rel errs (first 5) {err[:5]}; max {err.max():.3e}", flush=True)
+    assert np.isfinite(got).all()
+    assert (got[1] == 0).all()
+    assert err.max() <= ARITH

@@ -16,6 +16,7 @@ import torch
 
 import oracle
 import synth
+from tiny_cases import ALL_CODECS, tiny_zero_saturated
 
 pytestmark = pytest.mark.gpu
 
@@ -294,3 +295,43 @@ def test_deepseek_shaped_layer_full_size(L):
     say("full", w.name, "L", L)
     lay = synth.make_layer(w, L, 1, seed=0, device="cuda")
     check_layer(lay.x, lay.ids, lay.weights, lay.bank, w.name)
+
+
+# ---------------------------------------------------------------------------
+# tiny, zero and saturated activations (every codec)
+# ---------------------------------------------------------------------------
+
+def _check_tiny(x, ids, tw, bank, label):
+    q = _q()
+    say(label, bank.codec, "L=%d k=%d E=%d H=%d I=%d" % (ids.shape[0], ids.shape[1], bank.E, x.shape[1],
+                                                         bank.wg.shape[1]))
+    ref = oracle.forward_pairs_q(bank.codec, x.cpu(), ids, tw, bank.to("cpu"))
+    dev = torch.device("cuda")
+    bk = bank.to(dev)
+    out = q.forward_bank_codec(x.to(dev), torch.from_numpy(ids).to(dev), torch.from_numpy(tw).to(dev), bk,
+                               out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    err = rel_err_rows(got, ref)
+    print(f"  row rel errs {err}; |ref| row maxima {np.abs(ref).max(axis=1)}", flush=True)
+    assert np.isfinite(got).all()
+    assert np.abs(ref[0]).max() < 1e-30 and np.abs(ref[3]).max() < 1e-30  # the regime the case is about
+    assert (got[1] == 0).all() and (ref[1] == 0).all()
+    assert err.max() <= ARITH
+
+
+@pytest.mark.parametrize("codec", ALL_CODECS)
+def test_tiny_and_zero_activations(codec):
+    H, I = (512, 256)
+    x, ids, tw, bank = synth.random_problem_q(codec, 5, 4, 8, H, I, seed=31)
+    x, ids, tw = tiny_zero_saturated(x, ids, tw, bank, e_star=5)
+    _check_tiny(x, ids, tw, bank, "tiny/zero/saturated small")
+
+
+@pytest.mark.parametrize("codec", ALL_CODECS)
+def test_tiny_and_zero_activations_full_size(codec):
+    # one GLM-5.2-style verify layer (E=256 top-8, H=6144, I=2048) at L=4
+    w = synth.WORKLOADS["verify"]
+    lay = synth.make_layer_q(codec, w, 4, 30, seed=0, device="cuda")
+    x, ids, tw = tiny_zero_saturated(lay.x, lay.ids, lay.weights, lay.bank, e_star=int(lay.ids[2, 1]))
+    _check_tiny(x, ids, tw, lay.bank, "tiny/zero/saturated full-size verify")
