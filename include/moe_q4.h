@@ -53,6 +53,8 @@ extern "C" {
 #define MOE_Q4_ERR_WORKSPACE 5   /* workspace NULL or smaller than moe_swiglu_q4_workspace_bytes */
 #define MOE_Q4_ERR_LAUNCH 6      /* a HIP launch or runtime call failed                       */
 #define MOE_Q4_ERR_ALIAS 7       /* `out` overlaps an input or the workspace                  */
+#define MOE_Q4_ERR_SCRATCH 8     /* the shape needs more workspace than the allocation-free   */
+                                 /* entry point's scratch holds (MOE_Q4_NOALLOC_SCRATCH_BYTES) */
 
 /* ---- device status bits (status word in the workspace header) ---- */
 #define MOE_Q4_DEV_BAD_ID 1u     /* an expert id outside [0, E) was seen; its routes were dropped */
@@ -71,6 +73,7 @@ extern "C" {
 #define MOE_Q4_MAX_PAIRS 1024    /* L * k on the union path                                    */
 #define MOE_Q4_MAX_E 16384
 #define MOE_Q4_CODEC_MAX_L 65535 /* tokens of one moe_swiglu_codec_forward call          */
+#define MOE_Q4_NOALLOC_SCRATCH_BYTES (16u << 20) /* scratch of moe_swiglu_q4_forward_noalloc, per GPU */
 
 /* ---- weight codecs (moe_swiglu_codec_forward) ---- */
 #define MOE_Q4_CODEC_AFFINE4_G64 0 /* 4-bit affine, bf16 scale + bias per 64 inputs (= moe_swiglu_q4_forward) */
@@ -137,6 +140,34 @@ int moe_swiglu_q4_forward(const void *x, const int32_t *topk_ids, const float *t
                           int L, int k, int E, int H, int I, int group_size, int bits,
                           void *out, int out_dtype, void *workspace, size_t workspace_bytes,
                           hipStream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (work recorded under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * moe_swiglu_q4_forward without the workspace arguments.  The workspace is a
+ * static device array of the library, MOE_Q4_NOALLOC_SCRATCH_BYTES (16 MiB)
+ * per GPU, held from the library's load until the process ends; the call
+ * allocates and frees nothing.  The first call on a device looks that
+ * device's copy up (hipGetSymbolAddress, with the device current).
+ *
+ * Arguments, results and status codes are those of moe_swiglu_q4_forward,
+ * plus MOE_Q4_ERR_SCRATCH (host check, nothing enqueued) when the shape's
+ * moe_swiglu_q4_workspace_bytes exceeds the scratch: every union-path shape
+ * with L * k * (H + I) * 4 bytes of hidden and per-route output rows under
+ * about 16 MiB fits (e.g. L = 32, k = 8, H = 6144, I = 2048), long sorted-path
+ * inputs do not.
+ *
+ * Every call on one GPU shares that GPU's scratch, and the scratch keeps the
+ * last call's contents: two calls that may run at the same time on one GPU
+ * (different streams, or host threads) race and give undefined results.
+ * Calls in one stream order are safe.
+ */
+int moe_swiglu_q4_forward_noalloc(const void *x, const int32_t *topk_ids, const float *topk_weights,
+                                  const uint32_t *wg, const void *sg, const void *bg,
+                                  const uint32_t *wu, const void *su, const void *bu,
+                                  const uint32_t *wd, const void *sd, const void *bd,
+                                  int L, int k, int E, int H, int I, int group_size, int bits,
+                                  void *out, int out_dtype, hipStream_t stream);
 
 /*
  * Same as moe_swiglu_q4_forward, restricted to the stages in `stages`

@@ -25,6 +25,7 @@ MOE_Q4_ERR_ALIGN = 4
 MOE_Q4_ERR_WORKSPACE = 5
 MOE_Q4_ERR_LAUNCH = 6
 MOE_Q4_ERR_ALIAS = 7
+MOE_Q4_ERR_SCRATCH = 8
 MOE_Q4_DEV_BAD_ID = 1
 MOE_Q4_OUT_BF16 = 0
 MOE_Q4_OUT_F32 = 1
@@ -47,12 +48,14 @@ CODECS = {"affine4_g64": (MOE_Q4_CODEC_AFFINE4_G64, 64, 4), "affine4_g32": (MOE_
 MOE_Q4_UNION_MAX_L = 32
 MOE_Q4_MAX_PAIRS = 1024
 MOE_Q4_CODEC_MAX_L = 65535
+MOE_Q4_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTS = (
     "moe_swiglu_q4_workspace_bytes",
     "moe_swiglu_q4_select_path",
     "moe_swiglu_q4_forward",
     "moe_swiglu_q4_forward_stages",
+    "moe_swiglu_q4_forward_noalloc",
     "moe_swiglu_codec_workspace_bytes",
     "moe_swiglu_codec_forward",
     "moe_swiglu_codec_forward_stages",
@@ -95,6 +98,8 @@ def lib() -> ctypes.CDLL:
     L.moe_swiglu_q4_forward.restype = I32
     L.moe_swiglu_q4_forward_stages.argtypes = fwd + [U, P]
     L.moe_swiglu_q4_forward_stages.restype = I32
+    L.moe_swiglu_q4_forward_noalloc.argtypes = [P] * 12 + [I32] * 7 + [P, I32, P]
+    L.moe_swiglu_q4_forward_noalloc.restype = I32
     L.moe_swiglu_codec_workspace_bytes.argtypes = [I32] * 6
     L.moe_swiglu_codec_workspace_bytes.restype = SZ
     fwd_c = [I32] + [P] * 12 + [I32] * 5 + [P, I32, P, SZ]
@@ -219,6 +224,28 @@ def moe_swiglu_q4_forward(x, topk_ids, topk_weights, wg, sg, bg, wu, su, bu, wd,
         _dev_ptr(workspace, (torch.uint8,), "workspace"), workspace.numel(),
         int(stages), _stream_ptr(stream))
     _check(st, "moe_swiglu_q4_forward")
+    return out
+
+
+def moe_swiglu_q4_forward_noalloc(x, topk_ids, topk_weights, wg, sg, bg, wu, su, bu, wd, sd, bd, out,
+                                  stream=None) -> torch.Tensor:
+    """The layer through the allocation-free entry point: no workspace
+    argument (the library's static scratch serves as one) and a caller-owned
+    ``out`` (bf16 or fp32 [L, H]); shapes as for :func:`moe_swiglu_q4_forward`."""
+    L, H = x.shape
+    k = topk_ids.shape[1]
+    E, I = wg.shape[0], wg.shape[1]
+    od = MOE_Q4_OUT_F32 if out.dtype == torch.float32 else MOE_Q4_OUT_BF16
+    if tuple(out.shape) != (L, H):
+        raise ValueError("out must be [L, H]")
+    st = lib().moe_swiglu_q4_forward_noalloc(
+        _dev_ptr(x, _BF16, "x"), _dev_ptr(topk_ids, _I32, "topk_ids"), _dev_ptr(topk_weights, _F32, "topk_weights"),
+        _dev_ptr(wg, _U32, "wg"), _dev_ptr(sg, _BF16, "sg"), _dev_ptr(bg, _BF16, "bg"),
+        _dev_ptr(wu, _U32, "wu"), _dev_ptr(su, _BF16, "su"), _dev_ptr(bu, _BF16, "bu"),
+        _dev_ptr(wd, _U32, "wd"), _dev_ptr(sd, _BF16, "sd"), _dev_ptr(bd, _BF16, "bd"),
+        L, k, E, H, I, 64, 4,
+        _dev_ptr(out, (torch.float32,) if od == MOE_Q4_OUT_F32 else _BF16, "out"), od, _stream_ptr(stream))
+    _check(st, "moe_swiglu_q4_forward_noalloc")
     return out
 
 

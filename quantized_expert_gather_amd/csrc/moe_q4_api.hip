@@ -470,6 +470,9 @@ const char* moe_q4_status_string(int status) {
     case MOE_Q4_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_Q4_ERR_LAUNCH: return "HIP launch or runtime call failed";
     case MOE_Q4_ERR_ALIAS: return "output overlaps an input or the workspace";
+    case MOE_Q4_ERR_SCRATCH:
+      return "the shape needs more workspace than the allocation-free entry point's scratch "
+             "(MOE_Q4_NOALLOC_SCRATCH_BYTES) holds";
   }
   return "unknown status";
 }

@@ -162,6 +162,20 @@ int main() {
         CHECK(path != MOE_Q4_PATH_UNION || L <= MOE_Q4_UNION_MAX_L, "union past 32 tokens");
       }
   CHECK(moe_swiglu_q4_select_path(64, 8, 16385, 256, 128) == -MOE_Q4_ERR_UNSUPPORTED, "E limit");
+  // the allocation-free entry point refuses shapes beyond its scratch on the host
+  {
+    Call c;
+    c.L = 512; c.k = 8; c.E = 16; c.H = 1024; c.I = 256;
+    CHECK(moe_swiglu_q4_workspace_bytes(512, 8, 16, 1024, 256) > MOE_Q4_NOALLOC_SCRATCH_BYTES, "scratch case");
+    const int st = moe_swiglu_q4_forward_noalloc(c.p[0], (const int32_t*)c.p[1], (const float*)c.p[2],
+                                                 (const uint32_t*)c.p[3], c.p[4], c.p[5], (const uint32_t*)c.p[6],
+                                                 c.p[7], c.p[8], (const uint32_t*)c.p[9], c.p[10], c.p[11], 512, 8, 16,
+                                                 1024, 256, 64, 4, c.out, 0, nullptr);
+    CHECK(st == MOE_Q4_ERR_SCRATCH, "noalloc scratch: %d", st);
+    CHECK(moe_swiglu_q4_forward_noalloc(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                        nullptr, nullptr, nullptr, nullptr, 2, 9, 8, 256, 128, 64, 4, nullptr, 0,
+                                        nullptr) == MOE_Q4_ERR_SHAPE, "noalloc shape");
+  }
   // route union / sort argument checks
   CHECK(moe_route_union(nullptr, nullptr, 0, 8, 256, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr) ==
             MOE_Q4_ERR_SHAPE, "route union L=0");
