@@ -332,6 +332,18 @@ int moe_q4_read_device_status(const void *workspace, uint32_t *status, uint32_t 
 /* Clears the device status word (enqueued on `stream`, no sync). */
 int moe_q4_clear_device_status(void *workspace, hipStream_t stream);
 
+/*
+ * Measurement reference, not part of the layer: reads `bytes` bytes of the
+ * device buffer `buf` (16-byte aligned) once with 16-byte nontemporal loads,
+ * the analogue of the plain streaming sum() that the mlx issue "gather_qmm at
+ * M=1 streams 4-bit expert weights at ~half the bandwidth of M=4" (section
+ * "Numbers") times beside its layers.  `sink` (device, 4-byte aligned) receives
+ * one XOR word per workgroup and must hold at least twice the device's compute
+ * unit count (sink_words); MOE_Q4_ERR_WORKSPACE otherwise.  Enqueued on
+ * `stream`, no synchronisation.
+ */
+int moe_q4_stream_read(const void *buf, size_t bytes, uint32_t *sink, size_t sink_words, hipStream_t stream);
+
 /* Static description of a status code; never NULL. */
 const char *moe_q4_status_string(int status);
 

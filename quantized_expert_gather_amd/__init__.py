@@ -68,6 +68,7 @@ EXPORTS = (
     "moe_q4_read_device_status",
     "moe_q4_clear_device_status",
     "moe_q4_status_string",
+    "moe_q4_stream_read",
 )
 
 _lib = None
@@ -126,6 +127,8 @@ def lib() -> ctypes.CDLL:
     L.moe_q4_clear_device_status.restype = I32
     L.moe_q4_status_string.argtypes = [I32]
     L.moe_q4_status_string.restype = ctypes.c_char_p
+    L.moe_q4_stream_read.argtypes = [P, SZ, P, SZ, P]
+    L.moe_q4_stream_read.restype = I32
     _lib = L
     return L
 
@@ -518,3 +521,11 @@ class PreparedForwardCodec:
         st = self._fn(*self._args)
         if st:
             raise MoeQ4Error(st, "moe_swiglu_codec_forward_stages")
+
+
+def moe_q4_stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Measurement reference: one streaming read of ``buf`` (device tensor);
+    ``sink`` is an int32 device tensor of at least 2 x CU-count words."""
+    st = lib().moe_q4_stream_read(_dev_ptr(buf, (buf.dtype,), "buf"), buf.numel() * buf.element_size(),
+                                  _dev_ptr(sink, _I32, "sink"), sink.numel(), _stream_ptr(stream))
+    _check(st, "moe_q4_stream_read")

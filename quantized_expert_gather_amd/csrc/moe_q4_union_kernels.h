@@ -894,14 +894,19 @@ __global__ __launch_bounds__(down_threads(NT, PPL)) void k_down(UnionArgs a) {
   // wpre[i] = work of the units of experts before i (wave 0, straight from
   // the table in memory); blocks take equal shares of the total, each share
   // a contiguous range of units.
-  // (with at most NT tokens per token row set, every unit is one chunk and
-  // the shares are plain unit counts)
-  const bool uniform = a.L <= NT;
+  // A unit's work counts its token chunks (weight 4 each: each streams the
+  // unit's rows) plus its tokens (weight 1 each: the products per token),
+  // so a chunk of NT tokens weighs more than a chunk of one (measured: the
+  // blocks holding two-token experts had set the kernel's tail at L = 8).
+  // With one token every unit is one single-token chunk and the shares are
+  // plain unit counts.
+  const bool uniform = a.L == 1;
   if (tid < 64 && !uniform) {
     int carry = 0;
     for (int base = 0; base < u; base += 64) {
       const int i = base + tid;
-      const int w = i < u ? nrb * ((__popc((uint32_t)a.utab[i].y) + NT - 1) / NT) : 0;
+      const int n = i < u ? __popc((uint32_t)a.utab[i].y) : 0;
+      const int w = i < u ? nrb * (4 * ((n + NT - 1) / NT) + n) : 0;
       const int incl = wave_incl_scan(w);
       if (i < u) wpre[i] = carry + incl - w;
       carry += __shfl(incl, 63, 64);
