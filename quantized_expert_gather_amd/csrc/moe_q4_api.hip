@@ -227,6 +227,10 @@ int moe_swiglu_q4_forward_stages(const void* x, const int32_t* topk_ids, const f
   a.out = out;
   a.out_f32 = out_dtype == MOE_Q4_OUT_F32;
   a.L = L; a.k = k; a.E = E; a.H = H; a.I = I;
+  // matrix-core tiles for experts with many tokens: whole 4-group iterations
+  // over both widths and 8-byte scale pieces
+  a.mfma = H % 256 == 0 && I % 256 == 0 && aligned(sg, 8) && aligned(bg, 8) && aligned(su, 8) && aligned(bu, 8) &&
+           aligned(sd, 8) && aligned(bd, 8);
   a.hdr = reinterpret_cast<uint32_t*>(ws + lay.hdr);
   a.utab = reinterpret_cast<int4*>(ws + lay.utab);
   a.slot_w = reinterpret_cast<float*>(ws + lay.slot_w);

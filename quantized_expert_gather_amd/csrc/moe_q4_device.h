@@ -334,10 +334,21 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Index of the n-th set bit (n counted from 0) of m; m has more than n bits set.
+// Index of the n-th set bit (n counted from 0) of m; m has more than n bits
+// set.  Binary search by population counts of the low halves (five steps,
+// no loop over the bits).
 __device__ __forceinline__ int nth_set_bit(uint32_t m, int n) {
-  for (int c = 0; c < n; ++c) m &= m - 1u;
-  return __builtin_ctz(m);
+  int base = 0;
+#pragma unroll
+  for (int w = 16; w >= 1; w >>= 1) {
+    const uint32_t lo = m & ((1u << w) - 1u);
+    const int c = __popc(lo);
+    const bool up = n >= c;
+    n = up ? n - c : n;
+    m = up ? m >> w : lo;
+    base += up ? w : 0;
+  }
+  return base;
 }
 
 // Union of the routes, built in LDS by one workgroup.

@@ -8,6 +8,14 @@ namespace moeq4 {
 // loads `qs` (and tokens per register pass `nt`); nullptr if not built.
 const void* gateup_kernel(int lpr, int ppl, bool full, bool qs);
 const void* down_kernel(int lpr, int ppl, bool full, bool qs, int nt);
+// matrix-core instances (4-bit affine group 64, quad-shared scale loads;
+// at most 6 positions per lane for gate/up, 2 for down; nullptr past what is
+// built, and the launch takes the plain instance)
+const void* gateup_kernel_mf(int lpr, int ppl, bool full);
+const void* down_kernel_mf(int lpr, int ppl, bool full, int nt);
+const void* gateup_kernel_mf_0(int lpr, int ppl, bool full);
+const void* gateup_kernel_mf_1(int lpr, int ppl, bool full);
+const void* down_kernel_mf_0(int lpr, int ppl, bool full, int nt);
 // the same for the other weight formats (kFmt*; no quad-shared scale loads)
 const void* gateup_kernel_fmt(int fmt, int lpr, int ppl, bool full);
 const void* down_kernel_fmt(int fmt, int lpr, int ppl, bool full, int nt);

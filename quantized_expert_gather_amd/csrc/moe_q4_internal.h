@@ -26,6 +26,11 @@ __host__ __device__ constexpr bool fmt_biased(int f) { return !fmt_fp4(f) && f !
 // one 16-byte weight load: 32 for 4-bit codes, 16 for 8-bit codes
 __host__ __device__ constexpr int fmt_na(int f) { return fmt_8bit(f) ? 2 : 4; }
 __host__ __device__ constexpr int fmt_pos_inputs(int f) { return 8 * fmt_na(f); }
+// LDS stride of one token's staged activations (one pair slot's hidden
+// vector) in 16-byte units, for a width of `inputs`: 2 bytes an input plus
+// one pad unit, so the rows of a matrix-core operand (one token each) fall
+// in different LDS banks
+__host__ __device__ constexpr int lds_row_units(int inputs) { return inputs / 8 + 1; }
 
 // Arguments of one union-path forward (device pointers; LDS offsets in bytes).
 struct UnionArgs {
@@ -59,6 +64,10 @@ struct UnionArgs {
   int dn_rows;   // one token: down blocks own output rows of all experts and write out (no combine kernel)
   int status_or; // later token chunk of one call: OR this chunk's status into the call's status word
   int fmt;       // weight format (kFmt*): for the FP4 formats sg/su/sd hold scale bytes, bg/bu/bd unused
+  int mfma;      // 4-bit affine banks that the matrix-core tiles can read (widths multiples of 256, scale
+                 // arrays 8-byte aligned): experts with many tokens take them
+  size_t lds_mlist;  // gate/up LDS: the distinct experts on the matrix cores, then the others ([2][pairs])
+  size_t lds_red;    // gate/up LDS: the waves' partial tile sums ([kWaves][8][64] fp32)
 };
 
 // Workspace layout (byte offsets from the workspace base, 256-aligned regions).

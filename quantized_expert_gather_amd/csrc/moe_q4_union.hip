@@ -117,15 +117,26 @@ size_t align16(size_t v) { return (v + 15) & ~size_t(15); }
 
 size_t union_lds(int E, int P) { return (size_t)4 * (2 * ((E + 31) >> 5) + 5 * P + 1 + 2); }
 
-// gate/up LDS: activations of all L tokens | their 32-input sums | route union
-size_t gateup_lds_layout(UnionArgs& a) {
+// gate/up LDS: activations of all L tokens | their 32-input sums | route
+// union | the matrix-core expert list | (matrix-core instances) the waves'
+// partial tile sums
+size_t gateup_lds_layout(UnionArgs& a, bool mf = false) {
   const int KU = a.H / fmt_pos_inputs(a.fmt);  // positions; the activations take 2 H bytes per token
   size_t off = 0;
-  a.lds_act = off;   off = align16(off + (size_t)a.L * fmt_na(a.fmt) * KU * 16);
+  a.lds_act = off;   off = align16(off + (size_t)a.L * lds_row_units(a.H) * 16);
   a.lds_asum = off;  off = align16(off + (size_t)a.L * KU * 4);
   a.lds_union = off; off = align16(off + union_lds(a.E, a.L * a.k));
+  a.lds_mlist = off; off = align16(off + (size_t)8 * a.L * a.k);
+  a.lds_red = off;
+  if (mf) off = align16(off + (size_t)kWaves * 8 * 64 * 4);
   return off;
 }
+
+// Matrix-core instances run only above this many tokens: at or below it an
+// expert rarely gathers enough tokens to pay for the tiles, and the GEMV
+// instances keep their own register budget.
+constexpr int kMfmaMinL = 8;
+bool use_mfma(const UnionArgs& a) { return a.fmt == kFmtAffine && a.mfma && a.L > kMfmaMinL; }
 
 constexpr size_t kMaxLds = 160 * 1024;
 
@@ -188,9 +199,12 @@ int union_forward_launch(const UnionArgs& base, unsigned stages, int num_cu, hip
     UnionArgs a = base;
     const int KU = a.H / fmt_pos_inputs(a.fmt);
     const int lpr = lanes_per_row(KU), ppl = positions_per_lane(KU, lpr, false);
-    const size_t lds = gateup_lds_layout(a);
-    const void* fn = a.fmt != kFmtAffine ? gateup_kernel_fmt(a.fmt, lpr, ppl, lpr * ppl == KU)
-                                         : gateup_kernel(lpr, ppl, lpr * ppl == KU, (a.H / 64) % 2 == 0);
+    const void* fn = use_mfma(a) && gateup_lds_layout(a, true) <= kMaxLds ? gateup_kernel_mf(lpr, ppl, lpr * ppl == KU)
+                                                                           : nullptr;
+    const size_t lds = gateup_lds_layout(a, fn != nullptr);
+    if (!fn)
+      fn = a.fmt != kFmtAffine ? gateup_kernel_fmt(a.fmt, lpr, ppl, lpr * ppl == KU)
+                               : gateup_kernel(lpr, ppl, lpr * ppl == KU, (a.H / 64) % 2 == 0);
     if (!fn || lds > kMaxLds) return MOE_Q4_ERR_UNSUPPORTED;
     const int wunits = u_max * (a.I / (gateup_rows(ppl) * (64 / lpr)));
     int grid = num_cu * blocks_per_cu(fn, kThreads, lds);
@@ -227,8 +241,12 @@ int union_forward_launch(const UnionArgs& base, unsigned stages, int num_cu, hip
       a.dn_slots = P;
       lds = rows_lds;
     }
-    const void* fn = a.fmt != kFmtAffine ? down_kernel_fmt(a.fmt, lpr, ppl, lpr * ppl == KU, nt)
-                                         : down_kernel(lpr, ppl, lpr * ppl == KU, qs, nt);
+    const void* fn = use_mfma(a) && !a.dn_rows && down_threads(nt, ppl) == 512
+                         ? down_kernel_mf(lpr, ppl, lpr * ppl == KU, nt)
+                         : nullptr;
+    if (!fn)
+      fn = a.fmt != kFmtAffine ? down_kernel_fmt(a.fmt, lpr, ppl, lpr * ppl == KU, nt)
+                               : down_kernel(lpr, ppl, lpr * ppl == KU, qs, nt);
     if (!fn || lds > kMaxLds) return MOE_Q4_ERR_UNSUPPORTED;
     // one block per CU: the CU's waves share the block's converted hidden
     // vectors and its work counter
@@ -262,6 +280,13 @@ const void* down_kernel(int lpr, int ppl, bool full, bool qs, int nt) {
   if (!f) f = down_kernel_3(lpr, ppl, full, qs, nt);
   return f;
 }
+
+const void* gateup_kernel_mf(int lpr, int ppl, bool full) {
+  const void* f = gateup_kernel_mf_0(lpr, ppl, full);
+  return f ? f : gateup_kernel_mf_1(lpr, ppl, full);
+}
+
+const void* down_kernel_mf(int lpr, int ppl, bool full, int nt) { return down_kernel_mf_0(lpr, ppl, full, nt); }
 
 const void* gateup_kernel_fmt(int fmt, int lpr, int ppl, bool full) {
   const void* f = nullptr;

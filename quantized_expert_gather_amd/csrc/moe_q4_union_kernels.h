@@ -45,6 +45,7 @@
 #include "moe_q4.h"
 #include "moe_q4_device.h"
 #include "moe_q4_internal.h"
+#include "moe_q4_union_mfma.h"
 
 namespace moeq4 {
 
@@ -289,7 +290,7 @@ __device__ __forceinline__ void gu_compute(const UnionArgs& a, const GuFrag<PPL,
       const int j = li + LPR * p;
       if (FULL || j < KU) {
         constexpr int NA = fmt_na(FMT);
-        const uint4* xa = act + (size_t)t * NA * KU + j;
+        const uint4* xa = act + (size_t)t * lds_row_units(8 * NA * KU) + j;
         uint32_t xv[16];
 #pragma unroll
         for (int c = 0; c < NA; ++c) {
@@ -428,7 +429,7 @@ __device__ inline void write_union_tables(const UnionArgs& a, const UnionLds& s,
   }
 }
 
-template <int LPR, int PPL, bool FULL, bool QS, int FMT = kFmtAffine>
+template <int LPR, int PPL, bool FULL, bool QS, int FMT = kFmtAffine, bool MF = false>
 __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
   constexpr int G = 64 / LPR;           // lane groups per wave
   constexpr int RG = gateup_rows(PPL);
@@ -438,12 +439,13 @@ __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
   const int P = L * k;
   constexpr int NA = fmt_na(FMT);
   const int KU = H / fmt_pos_inputs(FMT), KG = FMT == kFmtAffine32 ? KU : H >> 6;  // positions, affine groups
-  uint4* act = reinterpret_cast<uint4*>(smem + a.lds_act);      // [L][NA][KU] bf16 pairs
+  uint4* act = reinterpret_cast<uint4*>(smem + a.lds_act);      // [L][NA][KU] bf16 pairs, rows padded
   float* asum = reinterpret_cast<float*>(smem + a.lds_asum);     // [L][KU] sums of each position's inputs
   UnionLds s;
   carve_union(smem + a.lds_union, E, P, s);
   const int tid = threadIdx.x;
   __shared__ int unit_q;  // next dynamically assigned unit of this block
+  __shared__ int n_mfma;  // distinct experts on the matrix cores
   if (tid == 0) unit_q = 2 * kWaves;
   stage_routes(a.ids, a.tw, P, s);  // first loads of the kernel
   // stage all tokens' activations (independent of the union; overlaps it):
@@ -471,7 +473,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
           for (int c = 0; c < NA; ++c) {
             if (fmt_biased(FMT)) sum = sum8_bf16(v[b][c], sum);
             // FP4 and 8-bit codes convert to pairs in natural element order
-            act[((size_t)t * NA + c) * KU + j] = fmt_natural(FMT) ? v[b][c] : pair_activations(v[b][c]);
+            act[(size_t)t * lds_row_units(H) + c * KU + j] = fmt_natural(FMT) ? v[b][c] : pair_activations(v[b][c]);
           }
           if (fmt_biased(FMT)) asum[(size_t)t * KU + j] = sum;
         }
@@ -480,6 +482,41 @@ __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
   }
   build_union(P, k, E, s);  // ends with a barrier
   const int u = s.scal[0];
+  // Matrix-core instances: distinct experts with at least kMfmaMinTokens
+  // tokens take the matrix cores (16-row tiles, every token at once) when
+  // mfma_engaged, the others the GEMV units.  mlist: their indices in
+  // ascending order, then the others' at + P.
+  int* mlist = reinterpret_cast<int*>(smem + a.lds_mlist);
+  int nm = 0;
+  if constexpr (MF) {
+    static_assert(FMT == kFmtAffine, "matrix-core tiles read 4-bit affine group-64 banks");
+    // every wave counts (the same answer), so a call without tiles skips
+    // the list and its barrier
+    int nmany = 0;
+    for (int base = 0; base < u; base += 64) {
+      const int i = base + (tid & 63);
+      nmany += __popcll(__ballot(i < u && __popc(s.mask[i]) >= kMfmaMinTokens));
+    }
+    if (mfma_engaged(nmany, u)) {
+      if (tid < 64) {
+        int cm = 0, cv = 0;
+        for (int base = 0; base < u; base += 64) {
+          const int i = base + tid;
+          const bool many = i < u && __popc(s.mask[i]) >= kMfmaMinTokens;
+          const bool few = i < u && !many;
+          const unsigned long long bm = __ballot(many), bf = __ballot(few);
+          const unsigned long long below = (1ull << tid) - 1ull;
+          if (many) mlist[cm + __popcll(bm & below)] = i;
+          if (few) mlist[P + cv + __popcll(bf & below)] = i;
+          cm += __popcll(bm);
+          cv += __popcll(bf);
+        }
+        if (tid == 0) n_mfma = cm;
+      }
+      __syncthreads();
+      nm = n_mfma;
+    }
+  }
 
   const int lane = tid & 63;
   const int wave = wave_uniform(tid >> 6);
@@ -511,22 +548,35 @@ __global__ __launch_bounds__(kThreads) void k_gateup(UnionArgs a) {
   // fragments, two in flight while the third is computed; a unit index past
   // the block's share loads the share's last unit again (cache-resident), so
   // every load is unconditional.
+  const int nblk = gridDim.x;
+  int b = blockIdx.x;
+  if constexpr (MF) {
+    if (nm > 0) {
+      // the matrix-core tiles first (tile t in block t % nblk); the GEMV
+      // units then start at the first block after the tiles, so the blocks
+      // that ran a tile take one unit fewer where the units do not divide
+      gu_mfma_phase<kWaves>(a, s, mlist, nm, act, asum, reinterpret_cast<float*>(smem + a.lds_red), b, nblk);
+      const int ntm = nm * (I / kMfmaRows);
+      b = (b + nblk - ntm % nblk) % nblk;
+    }
+  }
+  // GEMV units over the other distinct experts
+  auto vexp = [&](int x) { return MF && nm ? mlist[P + x] : x; };
   const int upe = I / WROWS;                // wave units per expert
-  const int nunits = u * upe;
-  const int nblk = gridDim.x, b = blockIdx.x;
+  const int nunits = (u - nm) * upe;
   const int nub = nunits > b ? (nunits - 1 - b) / nblk + 1 : 0;  // units of this block
   if (wave < nub) {
     auto load = [&](int j, GuFrag<PPL, RG>& f) {
       const int un = b + min(j, nub - 1) * nblk;
-      const int i = un / upe;
-      gu_load<PPL, RG, FULL, QS, FMT>(a, (size_t)wave_uniform(s.uniq[i]) * I + (un - i * upe) * WROWS, WROWS, KU, KG,
+      const int x = un / upe, i = vexp(x);
+      gu_load<PPL, RG, FULL, QS, FMT>(a, (size_t)wave_uniform(s.uniq[i]) * I + (un - x * upe) * WROWS, WROWS, KU, KG,
                                      li, LPR, lane_sbase, o, f);
     };
     auto compute = [&](int j, const GuFrag<PPL, RG>& f) {
       const int un = b + j * nblk;
-      const int i = un / upe;
+      const int x = un / upe, i = vexp(x);
       gu_compute<LPR, PPL, RG, FULL, QS, FMT>(a, f, wave_uniform((int)s.mask[i]), wave_uniform(s.off[i]),
-                                         (un - i * upe) * WROWS + g * RG, li, KU, act, asum, sel);
+                                         (un - x * upe) * WROWS + g * RG, li, KU, act, asum, sel);
     };
     auto grab = [&]() {
       int v = 0;
@@ -624,10 +674,10 @@ __device__ __forceinline__ void dn_load(const UnionArgs& a, size_t row0, bool va
 
 // LDS of a down block: the union table, the work prefix per expert, then
 // per staged pair slot its hidden vector as fp16 pairs [NA][KU] (uint4; KU
-// positions of 8 NA inputs), the sums of each position's fp16 values [KU],
+// positions of 8 NA inputs; plus one pad unit, lds_row_units), the sums of each position's fp16 values [KU],
 // the router weight, the slot's ys row and the exponent that undoes the
 // slot's power-of-two scaling.
-__host__ __device__ constexpr size_t down_slot_bytes(int KU, int na = 4) { return (size_t)KU * (16 * na + 4) + 12; }
+__host__ __device__ constexpr size_t down_slot_bytes(int KU, int na = 4) { return (size_t)KU * (16 * na + 4) + 16 + 12; }
 __host__ __device__ constexpr size_t down_lds_base(int P) { return ((size_t)16 * P + 15) & ~size_t(15); }
 // bytes before the staged slots: the union table and the work prefix
 __host__ __device__ constexpr size_t down_lds_head(int P) {
@@ -674,9 +724,9 @@ __device__ __forceinline__ void down_stage_slot(const UnionArgs& a, int ls, int 
         pw[kk] = (uint32_t)__builtin_bit_cast(uint16_t, hb[lo]) | ((uint32_t)__builtin_bit_cast(uint16_t, hb[hi]) << 16);
       }
       if constexpr (NA == 4) {
-        hvs[((size_t)ls * 4 + wi) * KU + j] = pk;
+        hvs[(size_t)ls * lds_row_units(32 * KU) + wi * KU + j] = pk;
       } else {  // positions 2j and 2j + 1 of 16 inputs, two uint4 each
-        hvs[((size_t)ls * 2 + (wi & 1)) * (2 * KU) + 2 * j + (wi >> 1)] = pk;
+        hvs[(size_t)ls * lds_row_units(32 * KU) + (wi & 1) * (2 * KU) + 2 * j + (wi >> 1)] = pk;
         if (wi & 1) {
           hss[(size_t)ls * 2 * KU + 2 * j + (wi >> 1)] = sum;
           sum = 0.0f;
@@ -814,7 +864,7 @@ __device__ __forceinline__ void dn_segment(const UnionArgs& a, size_t ebase, int
       const int j = li + LPR * p;
       if (FULL || j < KU) {
         constexpr int NA = fmt_na(FMT);
-        const uint4* hp = hvs + (size_t)ls * NA * KU + j;
+        const uint4* hp = hvs + (size_t)ls * lds_row_units(8 * NA * KU) + j;
 #pragma unroll
         for (int wi = 0; wi < NA; ++wi) {
           const uint4 h4 = hp[wi * KU];
@@ -865,7 +915,7 @@ constexpr int kDownUnitSteps = 4;  // row steps per down work unit
 // once).  Its waves take the units from an LDS counter (the first unit of
 // each wave fixed), so waves that get fewer issue slots do less of the
 // block's share.  A unit runs every token of its expert, NT at a time.
-template <int LPR, int PPL, bool FULL, bool QS, int NT, int FMT = kFmtAffine>
+template <int LPR, int PPL, bool FULL, bool QS, int NT, int FMT = kFmtAffine, bool MF = false>
 __global__ __launch_bounds__(down_threads(NT, PPL)) void k_down(UnionArgs a) {
   constexpr int G = 64 / LPR;
   constexpr int RS = down_rows(G);  // a wave step covers G * RS rows
@@ -879,8 +929,8 @@ __global__ __launch_bounds__(down_threads(NT, PPL)) void k_down(UnionArgs a) {
   const int SM = a.dn_slots;  // pair slots converted at a time
   int4* utab = reinterpret_cast<int4*>(smem);
   int* wpre = reinterpret_cast<int*>(smem + down_lds_base(P));     // [P + 1] work prefix per expert
-  uint4* hvs = reinterpret_cast<uint4*>(smem + down_lds_head(P));  // [SM][NA][KU]
-  float* hss = reinterpret_cast<float*>(hvs + (size_t)SM * NA * KU);  // [SM][KU]
+  uint4* hvs = reinterpret_cast<uint4*>(smem + down_lds_head(P));  // [SM][NA][KU], rows padded
+  float* hss = reinterpret_cast<float*>(hvs + (size_t)SM * lds_row_units(I));  // [SM][KU]
   float* stw = hss + (size_t)SM * KU;                                 // [SM]
   int* sdst = reinterpret_cast<int*>(stw + SM);                       // [SM]
   int* sexp = sdst + SM;                                              // [SM]
@@ -901,12 +951,29 @@ __global__ __launch_bounds__(down_threads(NT, PPL)) void k_down(UnionArgs a) {
   // With one token every unit is one single-token chunk and the shares are
   // plain unit counts.
   const bool uniform = a.L == 1;
+  // Matrix-core instances: experts with at least kMfmaMinTokens tokens run
+  // 16-row tiles, every token of the pass at once, when mfma_engaged (the
+  // same rule as the gate/up kernel's); a unit of theirs streams its rows
+  // once, so it weighs one chunk plus an eighth per token.
+  static_assert(!MF || (FMT == kFmtAffine && down_threads(NT, PPL) == 512),
+                "matrix-core tiles: 4-bit affine banks, 512-thread blocks");
+  __shared__ int mf_min;  // tokens from which an expert runs as tiles
   if (tid < 64 && !uniform) {
+    int nmany = 0;
+    if (MF)
+      for (int base = 0; base < u; base += 64) {
+        const int i = base + tid;
+        nmany += __popcll(__ballot(i < u && __popc((uint32_t)a.utab[i].y) >= kMfmaMinTokens));
+      }
+    const int mmin = MF && mfma_engaged(nmany, u) ? kMfmaMinTokens : 33;
+    if (tid == 0) mf_min = mmin;
     int carry = 0;
     for (int base = 0; base < u; base += 64) {
       const int i = base + tid;
       const int n = i < u ? __popc((uint32_t)a.utab[i].y) : 0;
-      const int w = i < u ? nrb * (4 * ((n + NT - 1) / NT) + n) : 0;
+      const int w = i >= u        ? 0
+                    : n >= mmin ? nrb * (4 + (n + 7) / 8)
+                                : nrb * (4 * ((n + NT - 1) / NT) + n);
       const int incl = wave_incl_scan(w);
       if (i < u) wpre[i] = carry + incl - w;
       carry += __shfl(incl, 63, 64);
@@ -914,8 +981,12 @@ __global__ __launch_bounds__(down_threads(NT, PPL)) void k_down(UnionArgs a) {
     if (tid == 0) wpre[u] = carry;
   }
   for (int i = tid; i < umax; i += blockDim.x) utab[i] = a.utab[i];
-  if (tid == 0) unit_q = NW;
+  if (tid == 0) {
+    unit_q = NW;
+    if (uniform) mf_min = 33;
+  }
   __syncthreads();
+  const int tile_min = mf_min;
   const int nblk = gridDim.x, b = blockIdx.x;
   const int lane = tid & 63;
   const int wave = wave_uniform(tid >> 6);
@@ -1007,12 +1078,36 @@ __global__ __launch_bounds__(down_threads(NT, PPL)) void k_down(UnionArgs a) {
     for (int sl = c0 + wave; sl < c1; sl += NW)
       down_stage_slot<NA>(a, sl - c0, sl, I >> 5, hvs, hss, stw, sdst, sexp, fmt_natural(FMT));
     __syncthreads();
+    if constexpr (MF) {
+      // Matrix-core instances: the tiles of the block's matrix-core units
+      // first (task j: 16-row tile j % TPU of unit ub + j / TPU; wave w
+      // takes tasks w, w + NW, ..., all through one ring), then the GEMV
+      // units from the counter.
+      constexpr int TPU = kDownUnitSteps * WSTEP / kMfmaRows;
+      static_assert((kDownUnitSteps * WSTEP) % kMfmaRows == 0, "whole tiles per unit");
+      auto mtile = [&](int j, DnTile& t) {
+        const int un = ub + j / TPU, sub = j % TPU;
+        const int i = un / nrb, rb = un - i * nrb;
+        const int4 ent = utab[i];
+        const int n = __popc((uint32_t)wave_uniform(ent.y)), off = wave_uniform(ent.z);
+        const int gj = rb * kDownUnitSteps, rows = min(kDownUnitSteps, spe - gj) * WSTEP;
+        const int t_lo = max(off, c0), t_hi = min(off + n, c1);
+        if (n < tile_min || sub * kMfmaRows >= rows || t_hi <= t_lo) return false;
+        t.e = wave_uniform(ent.x);
+        t.r0 = gj * WSTEP + sub * kMfmaRows;
+        t.ls0 = t_lo - c0;
+        t.n = t_hi - t_lo;
+        return true;
+      };
+      if (tile_min <= 32) dn_mfma_run(a, mtile, wave, NW, nub * TPU, hvs, hss, stw, sdst, sexp);
+    }
     for (int j = wave; j < nub; j = grab()) {
       const int un = ub + j;
       const int i = un / nrb, rb = un - i * nrb;
       const int4 ent = utab[i];
-      const int e = wave_uniform(ent.x), off = wave_uniform(ent.z);
-      const int t_lo = max(off, c0), t_hi = min(off + __popc((uint32_t)wave_uniform(ent.y)), c1);
+      const int e = wave_uniform(ent.x), off = wave_uniform(ent.z), n = __popc((uint32_t)wave_uniform(ent.y));
+      if (MF && n >= tile_min) continue;  // ran as tiles
+      const int t_lo = max(off, c0), t_hi = min(off + n, c1);
       const size_t ebase = (size_t)e * H;
       const int gj = rb * kDownUnitSteps;
       const int klast = min(kDownUnitSteps, spe - gj) - 1;

@@ -10,6 +10,8 @@ power-of-two scaling -- unit roundoff 2^-11 = 4.9e-4 per element, about
 outputs equal the round-to-nearest-even of the fp32 outputs bit for bit.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -335,3 +337,70 @@ def test_tiny_and_zero_activations_full_size(codec):
     lay = synth.make_layer_q(codec, w, 4, 30, seed=0, device="cuda")
     x, ids, tw = tiny_zero_saturated(lay.x, lay.ids, lay.weights, lay.bank, e_star=int(lay.ids[2, 1]))
     _check_tiny(x, ids, tw, lay.bank, "tiny/zero/saturated full-size verify")
+
+
+# ---------------------------------------------------------------------------
+# matrix-core tiles (more than 8 tokens; experts with at least 4 tokens when
+# such experts are at least half of the distinct ones)
+# ---------------------------------------------------------------------------
+
+def _pooled_ids(rng, L, k, pool, E):
+    """Each token takes its k experts from a shared pool of `pool` ids."""
+    members = rng.permutation(E)[:pool]
+    return np.stack([rng.permutation(members)[:k] for _ in range(L)]).astype(np.int32)
+
+
+def test_matrix_core_tile_token_counts():
+    # one expert per token count around the 16-token blocks of a tile:
+    # 32, 17, 16 and 15 tokens (every expert has at least 4)
+    E, H, I, L = 8, 512, 256, 32
+    x, _, tw, bank = synth.random_problem(L, 3, E, H, I, seed=91)
+    t = np.arange(L)
+    ids = np.stack([np.full(L, 2), np.where(t < 17, 0, 5), np.where(t >= 16, 1, 6)], axis=1).astype(np.int32)
+    check_layer(x, ids, tw, bank, "tile token counts 32/17/16/15")
+
+
+@pytest.mark.parametrize("L,k,pool,E,H,I", [(16, 4, 8, 32, 512, 256), (32, 8, 12, 64, 256, 512),
+                                            (12, 2, 4, 16, 768, 768), (24, 6, 16, 64, 2048, 512)])
+def test_matrix_core_pooled_routes(L, k, pool, E, H, I):
+    rng = np.random.default_rng(1000 + L + pool)
+    x, _, tw, bank = synth.random_problem(L, k, E, H, I, seed=L * pool)
+    ids = _pooled_ids(rng, L, k, pool, E)
+    check_layer(x, ids, tw, bank, "pooled pool=%d" % pool)
+
+
+def test_matrix_core_tiles_beside_gemv_experts():
+    # 8 hot experts with 9 tokens each run as tiles; the cold experts (1 to
+    # 5 tokens) of the same call run on the GEMV units
+    rng = np.random.default_rng(77)
+    E, H, I, L = 32, 1024, 512, 24
+    x, _, tw, bank = synth.random_problem(L, 4, E, H, I, seed=77)
+    hot = np.arange(8)
+    ids = np.stack([np.concatenate([rng.permutation(hot)[:3], rng.integers(8, 16, size=1)]) for _ in range(L)])
+    ids = ids.astype(np.int32)
+    n = np.bincount(ids.ravel(), minlength=E)
+    assert (n[:8] >= 4).all() and (n[8:16] < 4).any()
+    check_layer(x, ids, tw, bank, "tiles beside GEMV experts")
+
+
+def test_matrix_core_unaligned_scales_take_gemv_units():
+    # scale arrays 4 but not 8 bytes aligned: the launch keeps the GEMV
+    # kernels (the tiles read 8-byte scale pieces)
+    rng = np.random.default_rng(5)
+    E, H, I, L = 16, 512, 256, 16
+    x, _, tw, bank = synth.random_problem(L, 4, E, H, I, seed=5)
+    ids = _pooled_ids(rng, L, 4, 8, E)
+
+    def shifted(t):  # a device view 4 bytes past an 8-byte boundary (the binding keeps device tensors as they are)
+        flat = torch.empty(t.numel() + 2, dtype=t.dtype, device="cuda")
+        view = flat[2:].view(t.shape)
+        view.copy_(t.to("cuda"))
+        assert view.data_ptr() % 8 == 4
+        return view
+
+    gpu = bank.to("cuda")
+    unaligned = dataclasses.replace(gpu, sg=shifted(bank.sg), bg=shifted(bank.bg), su=shifted(bank.su),
+                                    bu=shifted(bank.bu), sd=shifted(bank.sd), bd=shifted(bank.bd))
+    got, ref = check_layer(x, ids, tw, unaligned, "unaligned scales")
+    aligned, _ = check_layer(x, ids, tw, bank, "aligned scales")
+    assert np.abs(got - aligned).max() <= 1e-3 * np.abs(ref).max()
