@@ -691,21 +691,25 @@ __host__ __device__ constexpr size_t down_lds_head(int P) {
 // for vectors whose entries all lie below 2^-114; sexp gets the inverse
 // shift, applied to the slot's outputs.  One wave per slot; a lane converts
 // 32 inputs at a time (one position of 4-bit codes, two of 8-bit codes).
-// KU counts 32-input blocks.
-template <int NA>
+// With TWO and `two`, the wave converts slot2 into ls2 as well, both slots'
+// loads in flight together (at one position per lane; the 1024-thread
+// kernels, at 128 registers a lane, leave TWO off).  KU counts 32-input
+// blocks.
+template <int NA, bool TWO = false>
 __device__ __forceinline__ void down_stage_slot(const UnionArgs& a, int ls, int slot, int KU, uint4* hvs, float* hss,
-                                                float* stw, int* sdst, int* sexp, bool natural) {
+                                                float* stw, int* sdst, int* sexp, bool natural, bool two = false,
+                                                int ls2 = 0, int slot2 = 0) {
+  two = TWO && two;
   const int lane = threadIdx.x & 63;
-  const float* hrow = a.hbuf + (size_t)slot * a.I;
-  auto load32 = [&](int j, float (&v)[32]) {
-    const float4* src = reinterpret_cast<const float4*>(hrow + 32 * j);
+  auto load32 = [&](int sl, int j, float (&v)[32]) {
+    const float4* src = reinterpret_cast<const float4*>(a.hbuf + (size_t)sl * a.I + 32 * j);
 #pragma unroll
     for (int q4 = 0; q4 < 8; ++q4) {
       const float4 f4 = src[q4];
       v[4 * q4 + 0] = f4.x; v[4 * q4 + 1] = f4.y; v[4 * q4 + 2] = f4.z; v[4 * q4 + 3] = f4.w;
     }
   };
-  auto convert = [&](int j, const float (&v)[32], int up) {
+  auto convert = [&](int ls_, int j, const float (&v)[32], int up) {
     float sum = 0.0f;
 #pragma unroll
     for (int wi = 0; wi < 4; ++wi) {
@@ -724,48 +728,67 @@ __device__ __forceinline__ void down_stage_slot(const UnionArgs& a, int ls, int 
         pw[kk] = (uint32_t)__builtin_bit_cast(uint16_t, hb[lo]) | ((uint32_t)__builtin_bit_cast(uint16_t, hb[hi]) << 16);
       }
       if constexpr (NA == 4) {
-        hvs[(size_t)ls * lds_row_units(32 * KU) + wi * KU + j] = pk;
+        hvs[(size_t)ls_ * lds_row_units(32 * KU) + wi * KU + j] = pk;
       } else {  // positions 2j and 2j + 1 of 16 inputs, two uint4 each
-        hvs[(size_t)ls * lds_row_units(32 * KU) + (wi & 1) * (2 * KU) + 2 * j + (wi >> 1)] = pk;
+        hvs[(size_t)ls_ * lds_row_units(32 * KU) + (wi & 1) * (2 * KU) + 2 * j + (wi >> 1)] = pk;
         if (wi & 1) {
-          hss[(size_t)ls * 2 * KU + 2 * j + (wi >> 1)] = sum;
+          hss[(size_t)ls_ * 2 * KU + 2 * j + (wi >> 1)] = sum;
           sum = 0.0f;
         }
       }
     }
-    if constexpr (NA == 4) hss[(size_t)ls * KU + j] = sum;
+    if constexpr (NA == 4) hss[(size_t)ls_ * KU + j] = sum;
   };
-  float mx = 0.0f;
-  int ex;
+  auto finish = [&](int ls_, int slot_, int ex) {
+    if (lane == 0) {
+      stw[ls_] = a.slot_w[slot_];
+      sdst[ls_] = a.slot_dst[slot_];
+      sexp[ls_] = ex - 14;
+    }
+  };
+  // frexp exponent of a wave-wide maximum magnitude (0 for an all-zero vector)
+  auto exp_of = [&](float mx) {
+    mx = wave_max(mx);
+    return mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) : 0;
+  };
   if (KU <= 64) {  // one position per lane: a single pass over registers
-    float v[32];
     const bool on = lane < KU;
-    load32(on ? lane : 0, v);
+    float v[32], v2[32];
+    load32(slot, on ? lane : 0, v);
+    if (two) load32(slot2, on ? lane : 0, v2);
+    float mx = 0.0f;
 #pragma unroll
     for (int n = 0; n < 32; ++n) mx = fmaxf(mx, on ? fabsf(v[n]) : 0.0f);
-    mx = wave_max(mx);
-    ex = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) : 0;
-    if (on) convert(lane, v, 14 - ex);
-  } else {  // several positions per lane: the maximum first, then a second read
+    const int ex = exp_of(mx);
+    if (on) convert(ls, lane, v, 14 - ex);
+    finish(ls, slot, ex);
+    if (two) {
+      float mx2 = 0.0f;
+#pragma unroll
+      for (int n = 0; n < 32; ++n) mx2 = fmaxf(mx2, on ? fabsf(v2[n]) : 0.0f);
+      const int ex2 = exp_of(mx2);
+      if (on) convert(ls2, lane, v2, 14 - ex2);
+      finish(ls2, slot2, ex2);
+    }
+    return;
+  }
+  // several positions per lane: the maximum first, then a second read
+  for (int q = 0; q < (two ? 2 : 1); ++q) {
+    const int sl = q ? slot2 : slot, ls_ = q ? ls2 : ls;
+    float mx = 0.0f;
     for (int j = lane; j < KU; j += 64) {
       float v[32];
-      load32(j, v);
+      load32(sl, j, v);
 #pragma unroll
       for (int n = 0; n < 32; ++n) mx = fmaxf(mx, fabsf(v[n]));
     }
-    mx = wave_max(mx);
-    ex = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) : 0;
-    const int up = 14 - ex;
+    const int ex = exp_of(mx);
     for (int j = lane; j < KU; j += 64) {
       float v[32];
-      load32(j, v);
-      convert(j, v, up);
+      load32(sl, j, v);
+      convert(ls_, j, v, 14 - ex);
     }
-  }
-  if (lane == 0) {
-    stw[ls] = a.slot_w[slot];
-    sdst[ls] = a.slot_dst[slot];
-    sexp[ls] = ex - 14;
+    finish(ls_, sl, ex);
   }
 }
 
@@ -1025,8 +1048,9 @@ __global__ __launch_bounds__(down_threads(NT, PPL)) void k_down(UnionArgs a) {
     const int ns = s1 - s0, nrows = ns * WSTEP;
     if (ns <= 0) return;  // uniform over the block
     float* part = reinterpret_cast<float*>(sexp + SM);  // [u][nrows]
-    for (int sl = wave; sl < u; sl += NW)
-      down_stage_slot<NA>(a, sl, sl, I >> 5, hvs, hss, stw, sdst, sexp, fmt_natural(FMT));
+    for (int sl = wave; sl < u; sl += 2 * NW)  // this wave's slots two at a time
+      down_stage_slot<NA, (NW < 16)>(a, sl, sl, I >> 5, hvs, hss, stw, sdst, sexp, fmt_natural(FMT), sl + NW < u,
+                                     sl + NW, sl + NW);
     __syncthreads();
     const int nch = max(1, min(ns, NW / max(u, 1)));  // step chunks per expert
     const int cs = (ns + nch - 1) / nch;
@@ -1075,8 +1099,9 @@ __global__ __launch_bounds__(down_threads(NT, PPL)) void k_down(UnionArgs a) {
   for (int c0 = s_lo; c0 < s_hi; c0 += SM) {
     const int c1 = min(s_hi, c0 + SM);
     if (tid == 0) unit_q = NW;
-    for (int sl = c0 + wave; sl < c1; sl += NW)
-      down_stage_slot<NA>(a, sl - c0, sl, I >> 5, hvs, hss, stw, sdst, sexp, fmt_natural(FMT));
+    for (int sl = c0 + wave; sl < c1; sl += 2 * NW)  // this wave's slots two at a time
+      down_stage_slot<NA, (NW < 16)>(a, sl - c0, sl, I >> 5, hvs, hss, stw, sdst, sexp, fmt_natural(FMT),
+                                     sl + NW < c1, sl + NW - c0, sl + NW);
     __syncthreads();
     if constexpr (MF) {
       // Matrix-core instances: the tiles of the block's matrix-core units
@@ -1101,25 +1126,37 @@ __global__ __launch_bounds__(down_threads(NT, PPL)) void k_down(UnionArgs a) {
       };
       if (tile_min <= 32) dn_mfma_run(a, mtile, wave, NW, nub * TPU, hvs, hss, stw, sdst, sexp);
     }
-    for (int j = wave; j < nub; j = grab()) {
-      const int un = ub + j;
+    // GEMV tasks: (unit, chunk of NT tokens), cpu chunks a unit -- the most
+    // any of the block's experts has in this pass (units with fewer skip the
+    // rest).  The chunks of one unit are consecutive tasks, so the waves run
+    // them side by side (the re-read rows hit the caches) instead of one
+    // wave running them in turn, which had left the waves holding experts
+    // with many tokens as the block's tail.
+    int cpu = 1;
+    for (int i = ub / nrb; i <= (ub + nub - 1) / nrb; ++i) {
+      const int4 ent = utab[i];
+      const int n = __popc((uint32_t)ent.y);
+      if (!(MF && n >= tile_min)) cpu = max(cpu, (min(ent.z + n, c1) - max(ent.z, c0) + NT - 1) / NT);
+    }
+    for (int j = wave; j < nub * cpu; j = grab()) {
+      const int jd = j / cpu;
+      const int un = ub + jd, ch = j - jd * cpu;
       const int i = un / nrb, rb = un - i * nrb;
       const int4 ent = utab[i];
       const int e = wave_uniform(ent.x), off = wave_uniform(ent.z), n = __popc((uint32_t)wave_uniform(ent.y));
       if (MF && n >= tile_min) continue;  // ran as tiles
-      const int t_lo = max(off, c0), t_hi = min(off + n, c1);
+      const int t0 = max(off, c0) + ch * NT, t_hi = min(off + n, c1);
+      if (t0 >= t_hi) continue;
+      const int nt = min(NT, t_hi - t0);
       const size_t ebase = (size_t)e * H;
       const int gj = rb * kDownUnitSteps;
       const int klast = min(kDownUnitSteps, spe - gj) - 1;
-      for (int t0 = t_lo; t0 < t_hi; t0 += NT) {
-        const int nt = min(NT, t_hi - t0);
-        if (NT > 1 && nt == 1)
-          dn_segment<LPR, PPL, FULL, QS, 1, RS, WSTEP, FMT>(a, ebase, t0 - c0, 1, gj, klast, li, g, KU, KG, H,
-                                                           lane_sbase, o, sel, hvs, hss, stw, sdst, sexp);
-        else
-          dn_segment<LPR, PPL, FULL, QS, NT, RS, WSTEP, FMT>(a, ebase, t0 - c0, nt, gj, klast, li, g, KU, KG, H,
-                                                            lane_sbase, o, sel, hvs, hss, stw, sdst, sexp);
-      }
+      if (NT > 1 && nt == 1)
+        dn_segment<LPR, PPL, FULL, QS, 1, RS, WSTEP, FMT>(a, ebase, t0 - c0, 1, gj, klast, li, g, KU, KG, H,
+                                                         lane_sbase, o, sel, hvs, hss, stw, sdst, sexp);
+      else
+        dn_segment<LPR, PPL, FULL, QS, NT, RS, WSTEP, FMT>(a, ebase, t0 - c0, nt, gj, klast, li, g, KU, KG, H,
+                                                          lane_sbase, o, sel, hvs, hss, stw, sdst, sexp);
     }
     __syncthreads();  // the converted slots and the counter are reused
   }
