@@ -553,6 +553,41 @@ def stream_references(q, torch, dev, stream, timer):
     return res
 
 
+def profile_pass(args):
+    """One forward call per layer, synchronised, in a fixed order: the first
+    args.profile_pass layers of each verify chain (args.Ls), then of the
+    pooled small-expert chains at L = 8, 16, 32.  Each call launches k_gateup
+    then k_down (then k_combine when L > 1), so a counter trace lines up with
+    the manifest printed here: per call the workload, L, layer, distinct
+    experts and the algorithmic bytes of the gate+up and down kernels."""
+    import numpy as np
+    import torch
+
+    import quantized_expert_gather_amd as q
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    calls = []
+    plan = [("verify", int(v)) for v in args.Ls.split(",")] + [("small_pooled", L) for L in (8, 16, 32)]
+    for wname, L in plan:
+        w = synth.WORKLOADS[wname]
+        for layer in range(args.profile_pass):
+            lay = synth.make_chain_layer(w, L, layer, seed=0, device=dev)
+            ids = torch.from_numpy(lay.ids).to(dev)
+            tw = torch.from_numpy(lay.weights).to(dev)
+            ws = q.new_workspace(L, w.k, lay.bank.E, w.H, w.I, dev)
+            torch.cuda.synchronize()
+            q.forward_bank(lay.x, ids, tw, lay.bank, workspace=ws)
+            torch.cuda.synchronize()
+            u = int(lay.bank.E)
+            calls.append({"workload": wname, "L": L, "layer": layer, "u": u, "H": w.H, "I": w.I, "k": w.k,
+                          "gateup_alg_bytes": u * gateup_bytes(w.H, w.I) + 2 * L * w.H + 8 * L * w.k,
+                          "down_alg_bytes": u * down_bytes(w.H, w.I) + 2 * L * w.H + 8 * L * w.k})
+        log(f"profile pass: {wname} L={L}, {args.profile_pass} layers")
+    print(json.dumps({"profile_pass": calls}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -589,6 +624,10 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (reference for hardware "
                          "byte counters) and exit")
+    ap.add_argument("--profile-pass", type=int, default=0, metavar="N",
+                    help="only run N layers of each verify chain (--Ls) and of the pooled small-expert chains "
+                         "(L = 8, 16, 32) once each, in a fixed order, for hardware-counter passes; prints a "
+                         "JSON manifest of the calls (algorithmic bytes per kernel) and exits")
     args = ap.parse_args()
     args.k_scaling = [int(v) for v in args.k_scaling.split(",") if v.strip()]
 
@@ -601,6 +640,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
+        return
+
+    if args.profile_pass:
+        profile_pass(args)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
