@@ -549,6 +549,86 @@ struct Chunk16 {
   uint4 s0, s1, b0, b1;  // 16 consecutive bf16 scales and biases of one row
 };
 
+// The affine correction's second half on the matrix cores.  Per 64-input
+// group g the layer needs out += s_g * P_g + (b_g - 128 s_g) * A_g (P_g the
+// group's MFMA chain over the 128 + q operands, A_g the rows' input sums).
+// The s_g * P_g half stays a per-group fp32 FMA; the other half is, over
+// the 16 groups of a chunk, a product with K = 16 groups: A (rows x groups)
+// times b and times -128 s (groups x columns).  b and -128 s are exact bf16
+// operands; A is fp32, so it enters as three bf16 planes whose sum is A to
+// within 2^-27 of it.  This takes the per-group row-sum reads (as many LDS
+// bytes as the activation operands) and half the per-group FMAs off the
+// stream loop.
+constexpr int kSumRow = 20;  // LDS floats per tile row of a chunk's group sums: 16 groups + pad
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));  // RNE
+}
+
+// Three bf16 planes of eight fp32 values: plane p is the remainder left by
+// planes 0..p-1 rounded to bf16 (each remainder is exact in fp32).
+__device__ __forceinline__ void split3_bf16(const float (&v)[8], uint4 (&pl)[3]) {
+  float r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = v[i];
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[j] = bf16_pair(r[2 * j], r[2 * j + 1]);
+      r[2 * j] -= __uint_as_float(w[j] << 16);
+      r[2 * j + 1] -= __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+    pl[p] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// Eight bf16 scales times -128: exact (a power-of-two multiple of a bf16
+// value is one), except past the bf16 range, where fp32 b - 128 s overflows too.
+__device__ __forceinline__ uint4 times_m128(uint4 s) {
+  const uint32_t w[4] = {s.x, s.y, s.z, s.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = bf16_pair(-128.0f * __uint_as_float(w[j] << 16), -128.0f * __uint_as_float(w[j] & 0xFFFF0000u));
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// The chunk correction for one row block: acc += A x b + A x (-128 s) over the
+// 16 groups of the chunk.  sums: this lane's row of the chunk's group sums
+// (groups 8 hh .. 8 hh + 7 at sums[0..7]); nvalid: how many of those 8 groups
+// exist (a partial last chunk; a multiple of 4), the rest count as zero.
+__device__ __forceinline__ void chunk_bias_mfma(f32x16_t& acc, const float* sums, uint4 bb, uint4 bs, int nvalid) {
+  const float4 v0 = *reinterpret_cast<const float4*>(sums);
+  const float4 v1 = *reinterpret_cast<const float4*>(sums + 4);
+  float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  if (nvalid < 8) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = j < nvalid ? v[j] : 0.0f;
+  }
+  uint4 pl[3];
+  split3_bf16(v, pl);
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    acc = mfma_bf16(pl[p], bb, acc);
+    acc = mfma_bf16(pl[p], bs, acc);
+  }
+}
+
+// The chunk's B operands from LDS-staged scale rows (row: this column's
+// bf16 scales or biases, G + 4 per row; groups g0 .. g0 + 7): 4-group pieces
+// at or past G read as zero and are not read.
+__device__ __forceinline__ uint4 sbl_groups8(const uint16_t* row, int g0, int G) {
+  const uint2 z = make_uint2(0u, 0u);
+  const uint2 p0 = g0 < G ? *reinterpret_cast<const uint2*>(row + g0) : z;
+  const uint2 p1 = g0 + 4 < G ? *reinterpret_cast<const uint2*>(row + g0 + 4) : z;
+  return make_uint4(p0.x, p0.y, p1.x, p1.y);
+}
+
 __device__ __forceinline__ Chunk16 load_chunk16(const uint16_t* S, const uint16_t* B, size_t off) {
   Chunk16 c;
   c.s0 = *reinterpret_cast<const uint4*>(S + off);
@@ -882,8 +962,10 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
   // two staging buffers: iteration it reads buffer it & 1 while the rows of
   // it + 1 are written to the other, so one barrier per iteration suffices
   unsigned char* abuf0 = smem;                                              // [2][kRows][kV2Row]
-  float* sbuf0 = reinterpret_cast<float*>(smem + 2 * kRows * kV2Row);      // [2][4][kRows]
-  int32_t* tok = reinterpret_cast<int32_t*>(sbuf0 + 8 * kRows);            // [kRows]
+  // affine: the group sums of the tile's rows for the 16 groups of a chunk,
+  // [2 chunks][kRows][kSumRow] (chunk c in buffer c & 1)
+  float* sums0 = reinterpret_cast<float*>(smem + 2 * kRows * kV2Row);
+  int32_t* tok = reinterpret_cast<int32_t*>(sums0 + (MX ? 0 : 2 * kRows * kSumRow));  // [kRows]
   // kSortAffineSbl: [sg, bg, su, bu][128 columns][G + 4] bf16
   uint16_t* sbl = reinterpret_cast<uint16_t*>(tok + kRows);
   for (int r = tid; r < kRows; r += kV2Threads) tok[r] = a.perm[r0 + min(r, nrows - 1)] / a.k;
@@ -904,7 +986,7 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
       sst = a.asum[(size_t)tok[r] * G + 4 * it + q];
     }
   };
-  auto stage_store = [&](int buf) {
+  auto stage_store = [&](int buf, int itn) {
     unsigned char* abuf = abuf0 + (size_t)buf * kRows * kV2Row;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
@@ -912,7 +994,8 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
       // affine codes unpack in nibble-pair order, E2M1 conversions in element order
       *reinterpret_cast<uint4*>(abuf + (size_t)r * kV2Row + 16 * w) = MX ? st[j] : pair_activations(st[j]);
     }
-    if (!MX && tid < 4 * kRows) sbuf0[buf * 4 * kRows + tid] = sst;  // [q][r] with q = tid / kRows
+    if (!MX && tid < 4 * kRows)  // group 4 itn + q of row r, q = tid / kRows, r = tid % kRows
+      sums0[((itn >> 2) & 1) * kRows * kSumRow + (tid % kRows) * kSumRow + 4 * (itn & 3) + tid / kRows] = sst;
   };
 
   const uint32_t* W = mat ? a.wu : a.wg;
@@ -953,7 +1036,7 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
     const uint16_t* const arrs[4] = {a.sg, a.bg, a.su, a.bu};
     stage_scale_rows<kV2Threads, 4>(sbl, arrs, e, I, cb * kV2GuCols, kV2GuCols, G, tid);
   }
-  stage_store(0);
+  stage_store(0, 0);
   __syncthreads();
 
   for (int c = 0; c < nch; ++c) {
@@ -963,7 +1046,6 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
       const int it = 4 * c + ii;
       if (TAIL && it >= nit) break;  // uniform over the workgroup
       const unsigned char* abuf = abuf0 + (size_t)(ii & 1) * kRows * kV2Row;  // it & 1
-      const float* sbuf = sbuf0 + (ii & 1) * 4 * kRows;
       stage_load(min(it + 1, nit - 1));
       Codes4 nn;
       if (F8) {
@@ -985,12 +1067,8 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
           mx_iteration<MT, NRT, MXM, 1>(acc, cur, nx, mcur, arows, 0, NRT, hh, blk_split);
         });
       } else if (!MX && wave_on) {
-        uint2 sv{}, bv{};  // kSortAffineSbl: this column's 4 scales and 4 biases of the iteration
-        if constexpr (SBL) {
-          const uint16_t* sl = sbl + (size_t)(2 * mat * kV2GuCols + 32 * cw + lc) * (G + 4) + 4 * it;
-          sv = *reinterpret_cast<const uint2*>(sl);
-          bv = *reinterpret_cast<const uint2*>(sl + (size_t)kV2GuCols * (G + 4));
-        }
+        uint2 sv{};  // kSortAffineSbl: this column's 4 scales of the iteration
+        if constexpr (SBL) sv = *reinterpret_cast<const uint2*>(sbl + (size_t)(2 * mat * kV2GuCols + 32 * cw + lc) * (G + 4) + 4 * it);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t w4[4] = {cur.q[q].x, cur.q[q].y, cur.q[q].z, cur.q[q].w};
@@ -998,7 +1076,6 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
 #pragma unroll
           for (int s = 0; s < 4; ++s) bq[s] = unpack_codes(w4[s]);
           const float sc = SBL ? sb4_elem(sv.x, sv.y, q) : chunk_elem(ch.s0, ch.s1, 4 * ii + q);
-          const float bc = (SBL ? sb4_elem(bv.x, bv.y, q) : chunk_elem(ch.b0, ch.b1, 4 * ii + q)) - 128.0f * sc;
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
             if (m < nrt) {
@@ -1006,20 +1083,13 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
               f32x16_t p = {};
 #pragma unroll
               for (int s = 0; s < 4; ++s) p = mfma_bf16(*reinterpret_cast<const uint4*>(arow + 16 * s), bq[s], p);
-              const float* srow = sbuf + q * kRows + m * kRowTile + 4 * hh;
 #pragma unroll
-              for (int qq = 0; qq < 4; ++qq) {
-                const float4 sa = *reinterpret_cast<const float4*>(srow + 8 * qq);
-                acc[m][4 * qq + 0] = fmaf(bc, sa.x, fmaf(sc, p[4 * qq + 0], acc[m][4 * qq + 0]));
-                acc[m][4 * qq + 1] = fmaf(bc, sa.y, fmaf(sc, p[4 * qq + 1], acc[m][4 * qq + 1]));
-                acc[m][4 * qq + 2] = fmaf(bc, sa.z, fmaf(sc, p[4 * qq + 2], acc[m][4 * qq + 2]));
-                acc[m][4 * qq + 3] = fmaf(bc, sa.w, fmaf(sc, p[4 * qq + 3], acc[m][4 * qq + 3]));
-              }
+              for (int i = 0; i < 16; ++i) acc[m][i] = fmaf(sc, p[i], acc[m][i]);  // (b - 128 s) A: per chunk
             }
           }
         }
       }
-      stage_store((ii + 1) & 1);
+      stage_store((ii + 1) & 1, min(it + 1, nit - 1));
       __syncthreads();
       if (F8) {
         cur = nn;
@@ -1030,6 +1100,26 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
       }
       mcur = mnx;
       mnx = mnn;
+    }
+    // the chunk's (b - 128 s) A half of the correction (its group sums are
+    // all staged: the last one landed before the barrier above)
+    if (!MX && wave_on) {
+      const int g0 = 16 * c + 8 * hh;
+      uint4 bs, bb;
+      if constexpr (SBL) {
+        const uint16_t* srow_s = sbl + (size_t)(2 * mat * kV2GuCols + 32 * cw + lc) * (G + 4);
+        bs = sbl_groups8(srow_s, g0, G);
+        bb = sbl_groups8(srow_s + (size_t)kV2GuCols * (G + 4), g0, G);
+      } else {
+        bs = hh ? ch.s1 : ch.s0;
+        bb = hh ? ch.b1 : ch.b0;
+      }
+      bs = times_m128(bs);
+      const int nvalid = min(8, max(0, G - g0));
+      const float* srow = sums0 + (c & 1) * kRows * kSumRow + 8 * hh;
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        if (m < nrt) chunk_bias_mfma(acc[m], srow + (m * kRowTile + lc) * kSumRow, bb, bs, nvalid);
     }
     ch = chn;
   }
@@ -1073,7 +1163,9 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
 }
 
 // staging buffers of the down streaming kernel: two while they fit the LDS
-constexpr int down2_buffers(int mt) { return (size_t)2 * 2 * mt * kRowTile * kV2Row + 8 * mt * kRowTile * 4 <= 160 * 1024 ? 2 : 1; }
+constexpr int down2_buffers(int mt) {
+  return (size_t)2 * 2 * mt * kRowTile * kV2Row + (size_t)2 * mt * kRowTile * kSumRow * 4 <= 160 * 1024 ? 2 : 1;
+}
 
 template <int MT, int MXM, bool TAIL>
 __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
@@ -1104,8 +1196,11 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
   // else one (a second barrier before the rows of the next iteration land)
   constexpr int NB = down2_buffers(MT);
   unsigned char* abuf0 = smem;                                                     // [NB][2 planes][kRows][kV2Row]
-  float* sbuf0 = reinterpret_cast<float*>(smem + (size_t)NB * 2 * kRows * kV2Row);  // [NB][4][kRows]
-  uint16_t* sbl = reinterpret_cast<uint16_t*>(sbuf0 + NB * 4 * kRows);  // kSortAffineSbl: [sd, bd][256][G + 4]
+  // affine: the group sums of the tile's rows for the 16 groups of a chunk,
+  // [2 chunks][kRows][kSumRow] (chunk c in buffer c & 1)
+  float* sums0 = reinterpret_cast<float*>(smem + (size_t)NB * 2 * kRows * kV2Row);
+  // kSortAffineSbl: [sd, bd][256][G + 4]
+  uint16_t* sbl = reinterpret_cast<uint16_t*>(sums0 + (MX ? 0 : 2 * kRows * kSumRow));
 
   constexpr int kPer = kRows * 32 / kV2Threads;  // 16-byte pieces per thread, iteration and plane
   u32x4_t sth[kPer], stl[kPer];
@@ -1124,7 +1219,7 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
       sst = hs[0] + hs[1];
     }
   };
-  auto stage_store = [&](int buf) {
+  auto stage_store = [&](int buf, int itn) {
     unsigned char* abuf = abuf0 + (size_t)buf * 2 * kRows * kV2Row;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
@@ -1132,7 +1227,8 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
       *reinterpret_cast<u32x4_t*>(abuf + (size_t)r * kV2Row + 16 * w) = sth[j];
       *reinterpret_cast<u32x4_t*>(abuf + (size_t)(kRows + r) * kV2Row + 16 * w) = stl[j];
     }
-    if (!MX && tid < 4 * kRows) sbuf0[buf * 4 * kRows + tid] = sst;
+    if (!MX && tid < 4 * kRows)  // group 4 itn + q of row r, q = tid / kRows, r = tid % kRows
+      sums0[((itn >> 2) & 1) * kRows * kSumRow + (tid % kRows) * kSumRow + 4 * (itn & 3) + tid / kRows] = sst;
   };
 
   const size_t rowc = ((size_t)e * H + col) * (size_t)(I / (F8 ? 4 : 8));
@@ -1170,7 +1266,7 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
     const uint16_t* const arrs[2] = {a.sd, a.bd};
     stage_scale_rows<kV2Threads, 2>(sbl, arrs, e, H, cb * kV2DnCols, kV2DnCols, G, tid);
   }
-  stage_store(0);
+  stage_store(0, 0);
   __syncthreads();
 
   for (int c = 0; c < nch; ++c) {
@@ -1181,7 +1277,6 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
       if (TAIL && it >= nit) break;  // uniform over the workgroup
       const int cbuf = NB == 2 ? (ii & 1) : 0;  // it & 1
       const unsigned char* abuf = abuf0 + (size_t)cbuf * 2 * kRows * kV2Row;
-      const float* sbuf = sbuf0 + cbuf * 4 * kRows;
       stage_load(min(it + 1, nit - 1));
       Codes4 nn;
       if (F8) {
@@ -1202,12 +1297,8 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
         // for a copy of the loop per row-block count
         mx_iteration<MT, MT, MXM, 2>(acc, cur, nx, mcur, arows, (size_t)kRows * kV2Row, nrt, hh, blk_split);
       } else if (!MX && wave_on) {
-        uint2 sv{}, bv{};  // kSortAffineSbl: this column's 4 scales and 4 biases of the iteration
-        if constexpr (SBL) {
-          const uint16_t* sl = sbl + (size_t)(32 * wid + lc) * (G + 4) + 4 * it;
-          sv = *reinterpret_cast<const uint2*>(sl);
-          bv = *reinterpret_cast<const uint2*>(sl + (size_t)kV2DnCols * (G + 4));
-        }
+        uint2 sv{};  // kSortAffineSbl: this column's 4 scales of the iteration
+        if constexpr (SBL) sv = *reinterpret_cast<const uint2*>(sbl + (size_t)(32 * wid + lc) * (G + 4) + 4 * it);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t w4[4] = {cur.q[q].x, cur.q[q].y, cur.q[q].z, cur.q[q].w};
@@ -1215,7 +1306,6 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
 #pragma unroll
           for (int s = 0; s < 4; ++s) bq[s] = unpack_codes(w4[s]);
           const float sc = SBL ? sb4_elem(sv.x, sv.y, q) : chunk_elem(ch.s0, ch.s1, 4 * ii + q);
-          const float bc = (SBL ? sb4_elem(bv.x, bv.y, q) : chunk_elem(ch.b0, ch.b1, 4 * ii + q)) - 128.0f * sc;
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
             if (m < nrt) {
@@ -1227,21 +1317,14 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
                 p = mfma_bf16(*reinterpret_cast<const uint4*>(ph + 16 * s), bq[s], p);
                 p = mfma_bf16(*reinterpret_cast<const uint4*>(pl + 16 * s), bq[s], p);
               }
-              const float* srow = sbuf + q * kRows + m * kRowTile + 4 * hh;
 #pragma unroll
-              for (int qq = 0; qq < 4; ++qq) {
-                const float4 sa = *reinterpret_cast<const float4*>(srow + 8 * qq);
-                acc[m][4 * qq + 0] = fmaf(bc, sa.x, fmaf(sc, p[4 * qq + 0], acc[m][4 * qq + 0]));
-                acc[m][4 * qq + 1] = fmaf(bc, sa.y, fmaf(sc, p[4 * qq + 1], acc[m][4 * qq + 1]));
-                acc[m][4 * qq + 2] = fmaf(bc, sa.z, fmaf(sc, p[4 * qq + 2], acc[m][4 * qq + 2]));
-                acc[m][4 * qq + 3] = fmaf(bc, sa.w, fmaf(sc, p[4 * qq + 3], acc[m][4 * qq + 3]));
-              }
+              for (int i = 0; i < 16; ++i) acc[m][i] = fmaf(sc, p[i], acc[m][i]);  // (b - 128 s) A: per chunk
             }
           }
         }
       }
       if (NB == 1) __syncthreads();
-      stage_store(NB == 2 ? ((ii + 1) & 1) : 0);
+      stage_store(NB == 2 ? ((ii + 1) & 1) : 0, min(it + 1, nit - 1));
       __syncthreads();
       if (F8) {
         cur = nn;
@@ -1252,6 +1335,26 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
       }
       mcur = mnx;
       mnx = mnn;
+    }
+    // the chunk's (b - 128 s) A half of the correction, A = sum of h hi + lo
+    // over each group (all staged: the last one landed before the barrier above)
+    if (!MX && wave_on) {
+      const int g0 = 16 * c + 8 * hh;
+      uint4 bs, bb;
+      if constexpr (SBL) {
+        const uint16_t* srow_s = sbl + (size_t)(32 * wid + lc) * (G + 4);
+        bs = sbl_groups8(srow_s, g0, G);
+        bb = sbl_groups8(srow_s + (size_t)kV2DnCols * (G + 4), g0, G);
+      } else {
+        bs = hh ? ch.s1 : ch.s0;
+        bb = hh ? ch.b1 : ch.b0;
+      }
+      bs = times_m128(bs);
+      const int nvalid = min(8, max(0, G - g0));
+      const float* srow = sums0 + (c & 1) * kRows * kSumRow + 8 * hh;
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        if (m < nrt) chunk_bias_mfma(acc[m], srow + (m * kRowTile + lc) * kSumRow, bb, bs, nvalid);
     }
     ch = chn;
   }
@@ -1380,14 +1483,16 @@ int sort_launch(const SortedArgs& a, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? MOE_Q4_OK : MOE_Q4_ERR_LAUNCH;
 }
 
-size_t gateup2_lds(int mt) { return (size_t)2 * mt * kRowTile * kV2Row + 9 * mt * kRowTile * 4; }
-size_t down2_lds(int mt) {
-  const int nb = down2_buffers(mt);
-  return (size_t)nb * 2 * mt * kRowTile * kV2Row + (size_t)nb * 4 * mt * kRowTile * 4;
+// staged rows, the affine chunk sums (mx: none) and the row tokens (gate/up)
+size_t gateup2_lds(int mt, bool mx) {
+  return (size_t)2 * mt * kRowTile * kV2Row + (mx ? 0 : (size_t)2 * mt * kRowTile * kSumRow * 4) + mt * kRowTile * 4;
+}
+size_t down2_lds(int mt, bool mx) {
+  return (size_t)down2_buffers(mt) * 2 * mt * kRowTile * kV2Row + (mx ? 0 : (size_t)2 * mt * kRowTile * kSumRow * 4);
 }
 // the same plus the workgroup's scale and bias rows (kSortAffineSbl)
-size_t gateup2_sbl_lds(int mt, int H) { return gateup2_lds(mt) + (size_t)4 * kV2GuCols * (H / 64 + 4) * 2; }
-size_t down2_sbl_lds(int mt, int I) { return down2_lds(mt) + (size_t)2 * kV2DnCols * (I / 64 + 4) * 2; }
+size_t gateup2_sbl_lds(int mt, int H) { return gateup2_lds(mt, false) + (size_t)4 * kV2GuCols * (H / 64 + 4) * 2; }
+size_t down2_sbl_lds(int mt, int I) { return down2_lds(mt, false) + (size_t)2 * kV2DnCols * (I / 64 + 4) * 2; }
 constexpr size_t kSortLdsMax = 160 * 1024 - 256;  // the static __shared__ word and slack
 
 // alignment the scale-row pieces of a width need: 16 bytes for 8-group pieces, else 8
@@ -1412,16 +1517,16 @@ template <int MT, bool TAIL, int FOLD, int EXACT>
 int mx_launch(const SortedArgs& a, bool down, int tiles8, hipStream_t stream) {
   if (!down) {
     const int ncb = (a.I + kV2GuCols - 1) / kV2GuCols;
-    hipLaunchKernelGGL((k_sorted_gateup2<MT, FOLD, TAIL>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT), stream,
+    hipLaunchKernelGGL((k_sorted_gateup2<MT, FOLD, TAIL>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT, true), stream,
                        a);
     if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;
-    hipLaunchKernelGGL((k_sorted_gateup2<MT, EXACT, TAIL>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT), stream,
+    hipLaunchKernelGGL((k_sorted_gateup2<MT, EXACT, TAIL>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT, true), stream,
                        a);
   } else {
     const int ncb = (a.H + kV2DnCols - 1) / kV2DnCols;
-    hipLaunchKernelGGL((k_sorted_down2<MT, FOLD, TAIL>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT), stream, a);
+    hipLaunchKernelGGL((k_sorted_down2<MT, FOLD, TAIL>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT, true), stream, a);
     if (hipGetLastError() != hipSuccess) return MOE_Q4_ERR_LAUNCH;
-    hipLaunchKernelGGL((k_sorted_down2<MT, EXACT, TAIL>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT), stream, a);
+    hipLaunchKernelGGL((k_sorted_down2<MT, EXACT, TAIL>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT, true), stream, a);
   }
   return hipGetLastError() == hipSuccess ? MOE_Q4_OK : MOE_Q4_ERR_LAUNCH;
 }
@@ -1442,7 +1547,7 @@ int gemm_launch(const SortedArgs& a, bool down, hipStream_t stream) {
                        gateup2_sbl_lds(MT, a.H), stream, a);
   } else if (!down && a.H % 1024 == 0) {
     const int ncb = (a.I + kV2GuCols - 1) / kV2GuCols;
-    hipLaunchKernelGGL((k_sorted_gateup2<MT, kSortAffine, false>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT),
+    hipLaunchKernelGGL((k_sorted_gateup2<MT, kSortAffine, false>), dim3(tiles8 * ncb), dim3(kV2Threads), gateup2_lds(MT, false),
                        stream, a);
   } else if (down && down2_sbl_fits(a, MT)) {
     const int ncb = (a.H + kV2DnCols - 1) / kV2DnCols;
@@ -1450,7 +1555,7 @@ int gemm_launch(const SortedArgs& a, bool down, hipStream_t stream) {
                        down2_sbl_lds(MT, a.I), stream, a);
   } else if (down && a.I % 1024 == 0) {
     const int ncb = (a.H + kV2DnCols - 1) / kV2DnCols;
-    hipLaunchKernelGGL((k_sorted_down2<MT, kSortAffine, false>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT), stream,
+    hipLaunchKernelGGL((k_sorted_down2<MT, kSortAffine, false>), dim3(tiles8 * ncb), dim3(kV2Threads), down2_lds(MT, false), stream,
                        a);
   } else if (!down) {
     const int ncb = (a.I + kGuCols - 1) / kGuCols;
