@@ -61,22 +61,6 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.c_void_p
     Lg = ctypes.c_long
-    lib.oracle_forward_pairs.argtypes = [P, P, P, Lg, Lg, Lg, Lg, Lg] + [P] * 9 + [P, P, P]
-    lib.oracle_forward_pairs.restype = ctypes.c_int
-    lib.oracle_forward_union.argtypes = [P, P, P, Lg, Lg, Lg, Lg, Lg] + [P] * 9 + [P]
-    lib.oracle_forward_union.restype = ctypes.c_int
-    lib.oracle_output_element.argtypes = [P, P, P, Lg, Lg, Lg, Lg, Lg] + [P] * 9 + [Lg, Lg]
-    lib.oracle_output_element.restype = ctypes.c_double
-    lib.oracle_dequant.argtypes = [P, P, P, Lg, Lg, P]
-    lib.oracle_dequant.restype = ctypes.c_int
-    lib.oracle_forward_pairs_mx.argtypes = [P, P, P, Lg, Lg, Lg, Lg, Lg] + [P] * 6 + [P, P, P]
-    lib.oracle_forward_pairs_mx.restype = ctypes.c_int
-    lib.oracle_forward_union_mx.argtypes = [P, P, P, Lg, Lg, Lg, Lg, Lg] + [P] * 6 + [P]
-    lib.oracle_forward_union_mx.restype = ctypes.c_int
-    lib.oracle_output_element_mx.argtypes = [P, P, P, Lg, Lg, Lg, Lg, Lg] + [P] * 6 + [Lg, Lg]
-    lib.oracle_output_element_mx.restype = ctypes.c_double
-    lib.oracle_dequant_mx.argtypes = [P, P, Lg, Lg, P]
-    lib.oracle_dequant_mx.restype = ctypes.c_int
     I32 = ctypes.c_int
     lib.oracle_forward_pairs_q.argtypes = [P, P, P, Lg, Lg, Lg, Lg, Lg, I32, I32, I32] + [P] * 9 + [P, P, P]
     lib.oracle_forward_pairs_q.restype = ctypes.c_int
@@ -150,21 +134,6 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
-def _bank_arrays(bank) -> List[np.ndarray]:
-    ts = bank.tensors() if hasattr(bank, "tensors") else bank
-    out = []
-    for i, t in enumerate(ts):
-        out.append(_u32(t) if i % 3 == 0 else _u16(t))
-    return out
-
-
-def _shapes(x, ids, bank_arrays) -> Tuple[int, int, int, int, int]:
-    ids = np.asarray(ids)
-    L, k = ids.shape
-    E, I, h8 = bank_arrays[0].shape
-    return L, k, E, h8 * 8, I
-
-
 def set_threads(n: int) -> None:
     _load().oracle_set_threads(int(n))
 
@@ -172,79 +141,6 @@ def set_threads(n: int) -> None:
 def threads() -> int:
     return int(_load().oracle_threads())
 
-
-def dequant(W, S, B) -> np.ndarray:
-    """Dense double copy of packed rows: W [..., N, K/8], S/B [..., N, K/64] -> [..., N, K]."""
-    w = _u32(W)
-    s = _u16(S)
-    b = _u16(B)
-    *lead, n, k8 = w.shape
-    K = k8 * 8
-    rows = int(np.prod(lead, dtype=np.int64)) * n if lead else n
-    out = np.empty((rows, K), np.float64)
-    st = _load().oracle_dequant(_ptr(w), _ptr(s), _ptr(b), rows, K, _ptr(out))
-    if st:
-        raise OracleError(f"oracle_dequant status {st}")
-    return out.reshape(*lead, n, K)
-
-
-def forward_pairs(x, ids, tw, bank, want_hidden: bool = False, want_pair_out: bool = False):
-    """Per-pair SwitchGLU + router-weighted combine.  Returns out [L, H] float64
-    (and, on request, the pair hidden vectors [L*k, I] and pair outputs [L*k, H])."""
-    xa = _u16(x)
-    ia = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
-    wa = np.ascontiguousarray(np.asarray(tw, dtype=np.float32))
-    ba = _bank_arrays(bank)
-    L, k, E, H, I = _shapes(xa, ia, ba)
-    out = np.empty((L, H), np.float64)
-    hb = np.empty((L * k, I), np.float64) if want_hidden else None
-    yb = np.empty((L * k, H), np.float64) if want_pair_out else None
-    st = _load().oracle_forward_pairs(_ptr(xa), _ptr(ia), _ptr(wa), L, k, E, H, I,
-                                      *[_ptr(a) for a in ba], _ptr(out),
-                                      _ptr(hb) if hb is not None else None,
-                                      _ptr(yb) if yb is not None else None)
-    if st:
-        raise OracleError(f"oracle_forward_pairs status {st}")
-    res = [out]
-    if want_hidden:
-        res.append(hb)
-    if want_pair_out:
-        res.append(yb)
-    return res[0] if len(res) == 1 else tuple(res)
-
-
-def forward_union(x, ids, tw, bank) -> np.ndarray:
-    """Union (deduplicated) evaluation; must agree with :func:`forward_pairs`."""
-    xa = _u16(x)
-    ia = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
-    wa = np.ascontiguousarray(np.asarray(tw, dtype=np.float32))
-    ba = _bank_arrays(bank)
-    L, k, E, H, I = _shapes(xa, ia, ba)
-    out = np.empty((L, H), np.float64)
-    st = _load().oracle_forward_union(_ptr(xa), _ptr(ia), _ptr(wa), L, k, E, H, I,
-                                      *[_ptr(a) for a in ba], _ptr(out))
-    if st:
-        raise OracleError(f"oracle_forward_union status {st}")
-    return out
-
-
-def output_element(x, ids, tw, bank, t: int, m: int) -> float:
-    """out[t, m] alone (per-pair evaluation of token t's k experts)."""
-    xa = _u16(x)
-    ia = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
-    wa = np.ascontiguousarray(np.asarray(tw, dtype=np.float32))
-    ba = _bank_arrays(bank)
-    L, k, E, H, I = _shapes(xa, ia, ba)
-    v = _load().oracle_output_element(_ptr(xa), _ptr(ia), _ptr(wa), L, k, E, H, I,
-                                      *[_ptr(a) for a in ba], int(t), int(m))
-    if np.isnan(v):
-        raise OracleError("oracle_output_element: invalid arguments")
-    return float(v)
-
-
-# --------------------------------------------------------------------------
-# mxfp4 gs32 banks (FP4 E2M1 elements, one E8M0 scale byte per 32 inputs)
-# --------------------------------------------------------------------------
 
 def _u8(a) -> np.ndarray:
     try:
@@ -257,78 +153,6 @@ def _u8(a) -> np.ndarray:
     a = np.asarray(a)
     assert a.dtype == np.uint8
     return np.ascontiguousarray(a)
-
-
-def _bank_arrays_mx(bank) -> List[np.ndarray]:
-    """(wg, eg, wu, eu, wd, ed): packed uint32 codes and uint8 scale bytes."""
-    ts = bank.tensors() if hasattr(bank, "tensors") else bank
-    return [_u32(t) if i % 2 == 0 else _u8(t) for i, t in enumerate(ts)]
-
-
-def dequant_mx(W, S) -> np.ndarray:
-    """Dense double copy of mxfp4 rows: W [..., N, K/8], S [..., N, K/32] -> [..., N, K]."""
-    w = _u32(W)
-    s = _u8(S)
-    *lead, n, k8 = w.shape
-    K = k8 * 8
-    rows = int(np.prod(lead, dtype=np.int64)) * n if lead else n
-    out = np.empty((rows, K), np.float64)
-    st = _load().oracle_dequant_mx(_ptr(w), _ptr(s), rows, K, _ptr(out))
-    if st:
-        raise OracleError(f"oracle_dequant_mx status {st}")
-    return out.reshape(*lead, n, K)
-
-
-def forward_pairs_mx(x, ids, tw, bank, want_hidden: bool = False) -> np.ndarray:
-    """Per-pair SwitchGLU + combine over an mxfp4 bank; out [L, H] float64."""
-    xa = _u16(x)
-    ia = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
-    wa = np.ascontiguousarray(np.asarray(tw, dtype=np.float32))
-    ba = _bank_arrays_mx(bank)
-    L, k = ia.shape
-    E, I, h8 = ba[0].shape
-    H = h8 * 8
-    out = np.empty((L, H), np.float64)
-    hb = np.empty((L * k, I), np.float64) if want_hidden else None
-    st = _load().oracle_forward_pairs_mx(_ptr(xa), _ptr(ia), _ptr(wa), L, k, E, H, I,
-                                         *[_ptr(a) for a in ba], _ptr(out),
-                                         _ptr(hb) if hb is not None else None, None)
-    if st:
-        raise OracleError(f"oracle_forward_pairs_mx status {st}")
-    return (out, hb) if want_hidden else out
-
-
-def forward_union_mx(x, ids, tw, bank) -> np.ndarray:
-    """Union evaluation over an mxfp4 bank; must agree with :func:`forward_pairs_mx`."""
-    xa = _u16(x)
-    ia = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
-    wa = np.ascontiguousarray(np.asarray(tw, dtype=np.float32))
-    ba = _bank_arrays_mx(bank)
-    L, k = ia.shape
-    E, I, h8 = ba[0].shape
-    H = h8 * 8
-    out = np.empty((L, H), np.float64)
-    st = _load().oracle_forward_union_mx(_ptr(xa), _ptr(ia), _ptr(wa), L, k, E, H, I,
-                                         *[_ptr(a) for a in ba], _ptr(out))
-    if st:
-        raise OracleError(f"oracle_forward_union_mx status {st}")
-    return out
-
-
-def output_element_mx(x, ids, tw, bank, t: int, m: int) -> float:
-    """out[t, m] alone over an mxfp4 bank."""
-    xa = _u16(x)
-    ia = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
-    wa = np.ascontiguousarray(np.asarray(tw, dtype=np.float32))
-    ba = _bank_arrays_mx(bank)
-    L, k = ia.shape
-    E, I, h8 = ba[0].shape
-    H = h8 * 8
-    v = _load().oracle_output_element_mx(_ptr(xa), _ptr(ia), _ptr(wa), L, k, E, H, I,
-                                         *[_ptr(a) for a in ba], int(t), int(m))
-    if np.isnan(v):
-        raise OracleError("oracle_output_element_mx: invalid arguments")
-    return float(v)
 
 
 # --------------------------------------------------------------------------
@@ -375,8 +199,10 @@ def _p(a):
     return _ptr(a) if a is not None else None
 
 
-def forward_pairs_q(codec: str, x, ids, tw, bank, want_hidden: bool = False):
-    """Per-pair SwitchGLU + combine over a bank in ``codec``; out [L, H] float64."""
+def forward_pairs_q(codec: str, x, ids, tw, bank, want_hidden: bool = False, want_pair_out: bool = False):
+    """Per-pair SwitchGLU + router-weighted combine over a bank in ``codec``.
+    Returns out [L, H] float64 (and, on request, the pair hidden vectors
+    [L*k, I] and pair outputs [L*k, H])."""
     fmt, bits, gs = CODECS[codec]
     xa = _u16(x)
     ia = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
@@ -385,11 +211,13 @@ def forward_pairs_q(codec: str, x, ids, tw, bank, want_hidden: bool = False):
     L, k, E, H, I = _codec_shapes(codec, ia, ba)
     out = np.empty((L, H), np.float64)
     hb = np.empty((L * k, I), np.float64) if want_hidden else None
+    yb = np.empty((L * k, H), np.float64) if want_pair_out else None
     st = _load().oracle_forward_pairs_q(_ptr(xa), _ptr(ia), _ptr(wa), L, k, E, H, I, fmt, bits, gs,
-                                        *[_p(a) for a in ba], _ptr(out), _p(hb), None)
+                                        *[_p(a) for a in ba], _ptr(out), _p(hb), _p(yb))
     if st:
         raise OracleError(f"oracle_forward_pairs_q({codec}) status {st}")
-    return (out, hb) if want_hidden else out
+    res = [out] + ([hb] if want_hidden else []) + ([yb] if want_pair_out else [])
+    return res[0] if len(res) == 1 else tuple(res)
 
 
 def forward_union_q(codec: str, x, ids, tw, bank) -> np.ndarray:
@@ -436,6 +264,63 @@ def dequant_q(codec: str, W, S, B=None) -> np.ndarray:
     if st:
         raise OracleError(f"oracle_dequant_q({codec}) status {st}")
     return out.reshape(*lead, n, K)
+
+
+# --------------------------------------------------------------------------
+# the 4-bit affine group-64 banks (nine arrays) and the six-array mxfp4 banks
+# (no bias arrays): the codec entry points above
+# --------------------------------------------------------------------------
+
+def _mx_bank9(bank) -> list:
+    """(wg, eg, wu, eu, wd, ed) -> the nine-array codec order with no biases."""
+    ts = list(bank.tensors() if hasattr(bank, "tensors") else bank)
+    return [ts[0], ts[1], None, ts[2], ts[3], None, ts[4], ts[5], None]
+
+
+def _element_or_raise(v: float, what: str) -> float:
+    if np.isnan(v):
+        raise OracleError(f"{what}: invalid arguments")
+    return v
+
+
+def dequant(W, S, B) -> np.ndarray:
+    """Dense double copy of packed rows: W [..., N, K/8], S/B [..., N, K/64] -> [..., N, K]."""
+    return dequant_q("affine4_g64", W, S, B)
+
+
+def forward_pairs(x, ids, tw, bank, want_hidden: bool = False, want_pair_out: bool = False):
+    """Per-pair SwitchGLU + router-weighted combine over a 4-bit affine group-64 bank."""
+    return forward_pairs_q("affine4_g64", x, ids, tw, bank, want_hidden, want_pair_out)
+
+
+def forward_union(x, ids, tw, bank) -> np.ndarray:
+    """Union (deduplicated) evaluation; must agree with :func:`forward_pairs`."""
+    return forward_union_q("affine4_g64", x, ids, tw, bank)
+
+
+def output_element(x, ids, tw, bank, t: int, m: int) -> float:
+    """out[t, m] alone (per-pair evaluation of token t's k experts)."""
+    return _element_or_raise(output_element_q("affine4_g64", x, ids, tw, bank, t, m), "output_element")
+
+
+def dequant_mx(W, S) -> np.ndarray:
+    """Dense double copy of mxfp4 rows: W [..., N, K/8], S [..., N, K/32] -> [..., N, K]."""
+    return dequant_q("mxfp4", W, S)
+
+
+def forward_pairs_mx(x, ids, tw, bank, want_hidden: bool = False):
+    """Per-pair SwitchGLU + combine over an mxfp4 bank (wg, eg, wu, eu, wd, ed)."""
+    return forward_pairs_q("mxfp4", x, ids, tw, _mx_bank9(bank), want_hidden)
+
+
+def forward_union_mx(x, ids, tw, bank) -> np.ndarray:
+    """Union evaluation over an mxfp4 bank; must agree with :func:`forward_pairs_mx`."""
+    return forward_union_q("mxfp4", x, ids, tw, _mx_bank9(bank))
+
+
+def output_element_mx(x, ids, tw, bank, t: int, m: int) -> float:
+    """out[t, m] alone over an mxfp4 bank."""
+    return _element_or_raise(output_element_q("mxfp4", x, ids, tw, _mx_bank9(bank), t, m), "output_element_mx")
 
 
 def e4m3_value(b: int) -> float:

@@ -82,12 +82,6 @@ static unsigned code_at(const uint32_t *row_words, long c) {
     return (row_words[c / 8] >> (4 * (c % 8))) & 0xFu;
 }
 
-/* Dequantized weight at (row, c) of a matrix with K inputs per row. */
-static double weight_at(const uint32_t *W, const uint16_t *S, const uint16_t *B, long row, long K, long c) {
-    long g = row * (K / 64) + c / 64;
-    return bf16_to_double(S[g]) * (double)code_at(W + row * (K / 8), c) + bf16_to_double(B[g]);
-}
-
 /* Value of a 4-bit FP4 E2M1 code (OCP MX v1.0 element encoding). */
 static double e2m1_value(unsigned code) {
     unsigned sign = (code >> 3) & 1u, expo = (code >> 1) & 3u, mant = code & 1u;
@@ -180,37 +174,14 @@ void oracle_set_threads(int n) {
 #endif
 }
 
-/* Dense dequantized copy of `rows` rows with K inputs each: out[r * K + c]. */
-int oracle_dequant(const uint32_t *W, const uint16_t *S, const uint16_t *B, long rows, long K, double *out) {
-    if (!W || !S || !B || !out || rows < 0 || K <= 0 || K % 64) return ORC_EINVAL;
-    for (long r = 0; r < rows; ++r)
-        for (long c = 0; c < K; ++c) out[r * K + c] = weight_at(W, S, B, r, K, c);
-    return ORC_OK;
-}
-
+/* The three quantized matrices of one layer's experts: gate, up, down (one codec). */
 typedef struct {
-    const uint32_t *wg; const uint16_t *sg; const uint16_t *bg;
-    const uint32_t *wu; const uint16_t *su; const uint16_t *bu;
-    const uint32_t *wd; const uint16_t *sd; const uint16_t *bd;
-    /* mxfp4 banks: the scale bytes of gate, up, down (then sg..bd are unused) */
-    const uint8_t *eg, *eu, *ed;
-    int mx;
-    /* any codec: gate, up, down (used when q is set) */
-    int q;
     qmat_t m[3];
 } bank_t;
 
 /* Weight of matrix mat (0 gate, 1 up, 2 down) at (row, c). */
 static double bank_weight(const bank_t *bk, int mat, long row, long K, long c) {
-    if (bk->q) return weight_at_q(&bk->m[mat], row, K, c);
-    if (bk->mx) {
-        const uint32_t *W = mat == 0 ? bk->wg : mat == 1 ? bk->wu : bk->wd;
-        const uint8_t *S = mat == 0 ? bk->eg : mat == 1 ? bk->eu : bk->ed;
-        return weight_at_mx(W, S, row, K, c);
-    }
-    if (mat == 0) return weight_at(bk->wg, bk->sg, bk->bg, row, K, c);
-    if (mat == 1) return weight_at(bk->wu, bk->su, bk->bu, row, K, c);
-    return weight_at(bk->wd, bk->sd, bk->bd, row, K, c);
+    return weight_at_q(&bk->m[mat], row, K, c);
 }
 
 /* Hidden activation of one (token, expert) pair: h[n] = silu(gate[n]) * up[n]. */
@@ -240,14 +211,10 @@ static int check_shapes_q(const int32_t *ids, long L, long k, long E, long H, lo
     return ORC_OK;
 }
 
-static int check_shapes(const int32_t *ids, long L, long k, long E, long H, long I) {
-    return check_shapes_q(ids, L, k, E, H, I, 64);
-}
-
 /*
  * Per-pair evaluation.  x bf16 [L, H]; ids int32 [L, k]; tw fp32 [L, k];
- * banks as packed uint32 codes plus bf16 scale/bias (gate/up [E, I, .], down
- * [E, H, .]).  Writes out[L, H] (double).  If h_out is not NULL it also gets
+ * the bank's matrices gate/up [E, I, .] and down [E, H, .].  Writes out[L, H]
+ * (double).  If h_out is not NULL it also gets
  * every pair's hidden vector, h_out[(t * k + j) * I + n]; if y_out is not NULL,
  * every pair's down output y_out[(t * k + j) * H + m].
  */
@@ -286,37 +253,11 @@ static int forward_pairs_bank(const uint16_t *x, const int32_t *ids, const float
     return ORC_OK;
 }
 
-int oracle_forward_pairs(const uint16_t *x, const int32_t *ids, const float *tw,
-                         long L, long k, long E, long H, long I,
-                         const uint32_t *wg, const uint16_t *sg, const uint16_t *bg,
-                         const uint32_t *wu, const uint16_t *su, const uint16_t *bu,
-                         const uint32_t *wd, const uint16_t *sd, const uint16_t *bd,
-                         double *out, double *h_out, double *y_out) {
-    if (!out || (L > 0 && (!x || !ids || !tw))) return ORC_EINVAL;
-    int st = check_shapes(ids, L, k, E, H, I);
-    if (st) return st;
-    bank_t bk = {wg, sg, bg, wu, su, bu, wd, sd, bd, NULL, NULL, NULL, 0, 0, {{0}}};
-    return forward_pairs_bank(x, ids, tw, L, k, H, I, &bk, out, h_out, y_out);
-}
-
-/* Per-pair evaluation over an mxfp4 bank: scales eg/eu/ed are uint8 [rows, K/32]. */
-int oracle_forward_pairs_mx(const uint16_t *x, const int32_t *ids, const float *tw,
-                            long L, long k, long E, long H, long I,
-                            const uint32_t *wg, const uint8_t *eg, const uint32_t *wu, const uint8_t *eu,
-                            const uint32_t *wd, const uint8_t *ed,
-                            double *out, double *h_out, double *y_out) {
-    if (!out || (L > 0 && (!x || !ids || !tw))) return ORC_EINVAL;
-    int st = check_shapes_q(ids, L, k, E, H, I, 32);
-    if (st) return st;
-    bank_t bk = {wg, NULL, NULL, wu, NULL, NULL, wd, NULL, NULL, eg, eu, ed, 1, 0, {{0}}};
-    return forward_pairs_bank(x, ids, tw, L, k, H, I, &bk, out, h_out, y_out);
-}
-
 /*
  * Union evaluation: the distinct experts of all L * k routes, ascending; each
  * one's hidden and down vectors computed once per token routed to it, then
  * added with that token's summed router weight for the expert.  Same
- * arguments and output as oracle_forward_pairs.
+ * arguments and output as forward_pairs_bank.
  */
 static int forward_union_bank(const uint16_t *x, const int32_t *ids, const float *tw,
                               long L, long k, long H, long I, const bank_t *bkp, double *out) {
@@ -370,43 +311,10 @@ static int forward_union_bank(const uint16_t *x, const int32_t *ids, const float
     return ORC_OK;
 }
 
-int oracle_forward_union(const uint16_t *x, const int32_t *ids, const float *tw,
-                         long L, long k, long E, long H, long I,
-                         const uint32_t *wg, const uint16_t *sg, const uint16_t *bg,
-                         const uint32_t *wu, const uint16_t *su, const uint16_t *bu,
-                         const uint32_t *wd, const uint16_t *sd, const uint16_t *bd,
-                         double *out) {
-    if (!out || (L > 0 && (!x || !ids || !tw))) return ORC_EINVAL;
-    int st = check_shapes(ids, L, k, E, H, I);
-    if (st) return st;
-    bank_t bk = {wg, sg, bg, wu, su, bu, wd, sd, bd, NULL, NULL, NULL, 0, 0, {{0}}};
-    return forward_union_bank(x, ids, tw, L, k, H, I, &bk, out);
-}
-
-/* Union evaluation over an mxfp4 bank (arguments as oracle_forward_pairs_mx). */
-int oracle_forward_union_mx(const uint16_t *x, const int32_t *ids, const float *tw,
-                            long L, long k, long E, long H, long I,
-                            const uint32_t *wg, const uint8_t *eg, const uint32_t *wu, const uint8_t *eu,
-                            const uint32_t *wd, const uint8_t *ed, double *out) {
-    if (!out || (L > 0 && (!x || !ids || !tw))) return ORC_EINVAL;
-    int st = check_shapes_q(ids, L, k, E, H, I, 32);
-    if (st) return st;
-    bank_t bk = {wg, NULL, NULL, wu, NULL, NULL, wd, NULL, NULL, eg, eu, ed, 1, 0, {{0}}};
-    return forward_union_bank(x, ids, tw, L, k, H, I, &bk, out);
-}
-
-/* Dense dequantized copy of mxfp4 rows: out[r * K + c] (K a multiple of 32). */
-int oracle_dequant_mx(const uint32_t *W, const uint8_t *S, long rows, long K, double *out) {
-    if (!W || !S || !out || rows < 0 || K <= 0 || K % 32) return ORC_EINVAL;
-    for (long r = 0; r < rows; ++r)
-        for (long c = 0; c < K; ++c) out[r * K + c] = weight_at_mx(W, S, r, K, c);
-    return ORC_OK;
-}
-
 /*
  * One output element computed on its own: out[t, m] for token t and output
  * row m, per-pair evaluation.  Lets tests sample single outputs of full-size
- * layers.  Returns NAN on invalid arguments.
+ * layers.
  */
 static double output_element_bank(const uint16_t *x, const int32_t *ids, const float *tw, long k, long H, long I,
                                   const bank_t *bk, long t, long m) {
@@ -423,30 +331,11 @@ static double output_element_bank(const uint16_t *x, const int32_t *ids, const f
     return acc;
 }
 
-double oracle_output_element(const uint16_t *x, const int32_t *ids, const float *tw,
-                             long L, long k, long E, long H, long I,
-                             const uint32_t *wg, const uint16_t *sg, const uint16_t *bg,
-                             const uint32_t *wu, const uint16_t *su, const uint16_t *bu,
-                             const uint32_t *wd, const uint16_t *sd, const uint16_t *bd,
-                             long t, long m) {
-    if (t < 0 || t >= L || m < 0 || m >= H || check_shapes(ids, L, k, E, H, I)) return NAN;
-    bank_t bk = {wg, sg, bg, wu, su, bu, wd, sd, bd, NULL, NULL, NULL, 0, 0, {{0}}};
-    return output_element_bank(x, ids, tw, k, H, I, &bk, t, m);
-}
-
-/* One output element over an mxfp4 bank (arguments as oracle_forward_pairs_mx). */
-double oracle_output_element_mx(const uint16_t *x, const int32_t *ids, const float *tw,
-                                long L, long k, long E, long H, long I,
-                                const uint32_t *wg, const uint8_t *eg, const uint32_t *wu, const uint8_t *eu,
-                                const uint32_t *wd, const uint8_t *ed, long t, long m) {
-    if (t < 0 || t >= L || m < 0 || m >= H || check_shapes_q(ids, L, k, E, H, I, 32)) return NAN;
-    bank_t bk = {wg, NULL, NULL, wu, NULL, NULL, wd, NULL, NULL, eg, eu, ed, 1, 0, {{0}}};
-    return output_element_bank(x, ids, tw, k, H, I, &bk, t, m);
-}
-
 /*
- * Any codec (ORC_FMT_* with its bits and group size): the per-pair, union and
- * single-element evaluations and a dense dequantized copy.  Codes are packed
+ * The entry points, for any codec (ORC_FMT_* with its bits and group size; the
+ * 4-bit affine group-64 banks are ORC_FMT_AFFINE, 4, 64): the per-pair, union
+ * and single-element evaluations and a dense dequantized copy.  The
+ * single-element form returns NAN on invalid arguments.  Codes are packed
  * uint32 words [rows, K * bits / 32]; scales are bf16 (affine) or uint8 (the
  * others) [rows, K / gs]; biases bf16 [rows, K / gs] for affine, else unused.
  */
@@ -458,7 +347,6 @@ static int make_bank_q(bank_t *bk, int fmt, int bits, int gs,
     if (!wg || !sg || !wu || !su || !wd || !sd) return ORC_EINVAL;
     if (fmt == ORC_FMT_AFFINE && (!bg || !bu || !bd)) return ORC_EINVAL;
     memset(bk, 0, sizeof *bk);
-    bk->q = 1;
     const uint32_t *w[3] = {wg, wu, wd};
     const void *sc[3] = {sg, su, sd};
     const uint16_t *bi[3] = {bg, bu, bd};

@@ -12,18 +12,6 @@
 #include <stdlib.h>
 #include <string.h>
 
-int oracle_forward_pairs(const uint16_t *, const int32_t *, const float *, long, long, long, long, long,
-                         const uint32_t *, const uint16_t *, const uint16_t *, const uint32_t *, const uint16_t *,
-                         const uint16_t *, const uint32_t *, const uint16_t *, const uint16_t *, double *, double *,
-                         double *);
-int oracle_forward_union(const uint16_t *, const int32_t *, const float *, long, long, long, long, long,
-                         const uint32_t *, const uint16_t *, const uint16_t *, const uint32_t *, const uint16_t *,
-                         const uint16_t *, const uint32_t *, const uint16_t *, const uint16_t *, double *);
-double oracle_output_element(const uint16_t *, const int32_t *, const float *, long, long, long, long, long,
-                             const uint32_t *, const uint16_t *, const uint16_t *, const uint32_t *,
-                             const uint16_t *, const uint16_t *, const uint32_t *, const uint16_t *,
-                             const uint16_t *, long, long);
-int oracle_dequant(const uint32_t *, const uint16_t *, const uint16_t *, long, long, double *);
 int oracle_forward_pairs_q(const uint16_t *, const int32_t *, const float *, long, long, long, long, long, int, int,
                            int, const uint32_t *, const void *, const uint16_t *, const uint32_t *, const void *,
                            const uint16_t *, const uint32_t *, const void *, const uint16_t *, double *, double *,
@@ -126,22 +114,6 @@ static void codec_case(int fmt, int bits, int gs, long L, long k, long E, long H
   double *dq = malloc(sizeof(double) * E * I * H);
   st = oracle_dequant_q(fmt, bits, gs, wg, sg, b_g, E * I, H, dq);
   CHECK(st == 0, "dequant_q status %d", st);
-  if (fmt == 0 && bits == 4 && gs == 64) {
-    /* the legacy affine entry points agree with the codec ones */
-    double *o3 = calloc(L * H, 8), *o4 = calloc(L * H, 8), *dq2 = malloc(sizeof(double) * E * I * H);
-    const uint16_t *s_g = (const uint16_t *)sg, *s_u = (const uint16_t *)su, *s_d = (const uint16_t *)sd;
-    CHECK(oracle_forward_pairs(x, ids, tw, L, k, E, H, I, wg, s_g, bg, wu, s_u, bu, wd, s_d, bd, o3, NULL, NULL) == 0,
-          "forward_pairs");
-    CHECK(oracle_forward_union(x, ids, tw, L, k, E, H, I, wg, s_g, bg, wu, s_u, bu, wd, s_d, bd, o4) == 0,
-          "forward_union");
-    CHECK(rel(o3, o1, L * H) == 0.0 && rel(o4, o1, L * H) <= 1e-12, "legacy entry points differ");
-    CHECK(oracle_dequant(wg, s_g, bg, E * I, H, dq2) == 0, "dequant");
-    CHECK(memcmp(dq, dq2, sizeof(double) * E * I * H) == 0, "dequant differs");
-    const double v = oracle_output_element(x, ids, tw, L, k, E, H, I, wg, s_g, bg, wu, s_u, bu, wd, s_d, bd, L - 1,
-                                           H - 1);
-    CHECK(fabs(v - o1[L * H - 1]) <= 1e-12 * (1.0 + fabs(v)), "legacy element");
-    free(o3); free(o4); free(dq2);
-  }
   /* invalid arguments: every call returns an error without touching memory */
   int32_t bad_ids[2] = {0, (int32_t)E};
   CHECK(oracle_forward_pairs_q(x, bad_ids, tw, 1, 2, E, H, I, fmt, bits, gs, wg, sg, b_g, wu, su, b_u, wd, sd, b_d,

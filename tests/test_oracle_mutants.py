@@ -16,9 +16,9 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), 
 
 MUTANTS = {
     "high_nibble_first": ("(4 * (c % 8))", "(4 * (7 - c % 8))"),
-    "bias_dropped": ("* (double)code_at(W + row * (K / 8), c) + bf16_to_double(B[g])",
-                     "* (double)code_at(W + row * (K / 8), c)"),
-    "scale_group_shifted": ("long g = row * (K / 64) + c / 64;", "long g = row * (K / 64) + ((c / 64) + 1) % (K / 64);"),
+    "bias_dropped": ("* (double)q + bf16_to_double(m->B[g])", "* (double)q"),
+    "scale_group_shifted": ("long g = row * (K / m->gs) + c / m->gs;",
+                            "long g = row * (K / m->gs) + ((c / m->gs) + 1) % (K / m->gs);"),
     "gate_up_swapped": ("return silu(g) * u;", "return silu(u) * g;"),
     "router_weight_dropped": ("acc += (double)tw[t * k + j] * y[(t * k + j) * H + m];",
                               "acc += y[(t * k + j) * H + m];"),
