@@ -91,6 +91,10 @@ SORT_CASES = {
     "E1": (50, 1, 1, 32, lambda r, L, k, E: np.zeros((L, k))),
     "E16384": (64, 8, 16384, 32, lambda r, L, k, E: r.integers(0, E, size=(L, k))),
     "bm1": (40, 2, 7, 1, lambda r, L, k, E: r.integers(0, E, size=(L, k))),
+    # every token on the same 8 experts: eight segments of 8192 rows
+    "all_on_8_experts": (8192, 8, 256, 128, lambda r, L, k, E: np.stack([r.permutation(8) for _ in range(L)])),
+    # a large expert count with 40,000 pairs
+    "E9000": (5000, 8, 9000, 32, lambda r, L, k, E: np.stack([r.permutation(E)[:k] for _ in range(L)])),
 }
 
 
@@ -114,10 +118,11 @@ def test_sort_pairs_bit_exact(case):
     assert [tuple(t[:3]) for t in got_tiles.tolist()] == tiles
 
 
-def test_sort_pairs_invalid_ids_go_last():
+@pytest.mark.parametrize("L", [100, 2000])
+def test_sort_pairs_invalid_ids_go_last(L):
     q = _q()
     rng = np.random.default_rng(3)
-    L, k, E = 100, 4, 16
+    k, E = 4, 16
     ids = rng.integers(0, E, size=(L, k)).astype(np.int32)
     bad = rng.random((L, k)) < 0.1
     ids[bad] = rng.choice([-1, E, 1 << 20], size=int(bad.sum()))
