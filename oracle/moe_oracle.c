@@ -4,7 +4,7 @@
  * benchmark's CPU-baseline leg use it; the product path never does.  It shares
  * no code with the GPU library.
  *
- * What it computes (sources are the web pages this build follows):
+ * What it computes (sources are the web pages named below):
  *
  *  - SwitchGLU per (token, expert) pair, in the order up, gate,
  *    silu(gate) * up, down -- mlx issue "gather_qmm at M=1 streams 4-bit expert

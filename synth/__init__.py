@@ -18,7 +18,7 @@ splash PR "Apple7/8 MoE gate and up in one decode pass" (p4)):
 * pooled routes: 8-32 rows whose experts come from a shared pool (p4, results
   table of the expert-kernel benchmark).
 
-Storage format (the reading this build takes; the pages give shapes only):
+Storage format (the reading taken here; the pages give shapes only):
 element ``c`` of an output row sits in nibble ``c % 8`` of 32-bit word
 ``c // 8``, lowest nibble first; a (scale, bias) pair of bf16 values covers
 each run of 64 consecutive elements along the input dimension.
