@@ -399,3 +399,14 @@ def test_kernel_source_hash_ignores_comments_and_whitespace(tmp_path, monkeypatc
     assert bench.kernel_source_hash() == h0
     src.write_text("int f(int a) { return a + 2; }\n")
     assert bench.kernel_source_hash() != h0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the benchmark measures one GPU; asking for more exits at once with a message (no GPU touched)
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
