@@ -155,6 +155,10 @@ SMALL_SHAPES = [
     (5, 3, 3, 128, 8192, True),
     # gate/up with 4 positions per lane on a ragged row (H = 7168: 224 of 256)
     (4, 8, 16, 7168, 256, False),
+    # the most pairs the union path takes (L * k = 1024): 32 tokens x 32 experts each
+    # (matrix-core tiles: every expert serves about 16 tokens), and 16 x 64 on the GEMV units
+    (32, 32, 64, 512, 256, False),
+    (16, 64, 96, 256, 128, False),
 ]
 
 
