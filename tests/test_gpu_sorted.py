@@ -172,6 +172,7 @@ SMALL = [
     (203, 4, 8, 1280, 2560, False),  # 4 blocks; both on the general kernels (LDS)
     (40, 4, 8, 2048, 768, False),    # 1 block; down streamed with I = 768
     (80, 4, 8, 768, 256, False),     # 2 blocks; gate/up streamed with H = 768
+    (64, 8, 16384, 64, 64, False),   # the largest expert count: ~500 experts of 16384 used, one row each
 ]
 
 

@@ -159,6 +159,8 @@ SMALL_SHAPES = [
     # (matrix-core tiles: every expert serves about 16 tokens), and 16 x 64 on the GEMV units
     (32, 32, 64, 512, 256, False),
     (16, 64, 96, 256, 128, False),
+    # the largest expert count (E = 16384)
+    (8, 8, 16384, 64, 64, False),
 ]
 
 
