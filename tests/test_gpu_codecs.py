@@ -101,6 +101,7 @@ SMALL_SHAPES = [
     (4, 4, 4, 8192, 192, False),
     (3, 4, 4, 256, 4096, True),
     (4, 8, 16, 7168, 256, False),
+    (32, 32, 64, 512, 256, False),   # the union path's pair limit, L * k = 1024
 ]
 
 
@@ -119,6 +120,7 @@ SMALL_SHAPES_64 = [
     (4, 4, 4, 8192, 192, False),
     (3, 4, 4, 256, 4096, True),
     (4, 8, 16, 7168, 256, False),
+    (32, 32, 64, 512, 256, False),
 ]
 SHAPE_CASES = [(c, sh) for c in CODECS for sh in (SMALL_SHAPES_64 if c == "affine8_g64" else SMALL_SHAPES)]
 

@@ -173,6 +173,7 @@ SMALL = [
     (40, 4, 8, 2048, 768, False),    # 1 block; down streamed with I = 768
     (80, 4, 8, 768, 256, False),     # 2 blocks; gate/up streamed with H = 768
     (64, 8, 16384, 64, 64, False),   # the largest expert count: ~500 experts of 16384 used, one row each
+    (20, 64, 128, 256, 128, False),  # 20 tokens but 1280 pairs: past the union path's pair limit
 ]
 
 
