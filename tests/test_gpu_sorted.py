@@ -174,6 +174,8 @@ SMALL = [
     (80, 4, 8, 768, 256, False),     # 2 blocks; gate/up streamed with H = 768
     (64, 8, 16384, 64, 64, False),   # the largest expert count: ~500 experts of 16384 used, one row each
     (20, 64, 128, 256, 128, False),  # 20 tokens but 1280 pairs: past the union path's pair limit
+    (8, 4, 8, 16384, 128, False),    # 8 tokens whose activation rows outgrow the union kernels' LDS
+    (16, 8, 16, 8192, 256, False),   # the same at 16 tokens
 ]
 
 
