@@ -1076,13 +1076,23 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_gateup2(SortedArgs a) 
 #pragma unroll
           for (int s = 0; s < 4; ++s) bq[s] = unpack_codes(w4[s]);
           const float sc = SBL ? sb4_elem(sv.x, sv.y, q) : chunk_elem(ch.s0, ch.s1, 4 * ii + q);
+          // the first two operand pieces of each row block are read during the
+          // previous block's matrix chain (row blocks are tested at run time)
+          const unsigned char* arow0 = abuf + (size_t)lc * kV2Row + 128 * q + 64 * hh;
+          uint4 an0 = *reinterpret_cast<const uint4*>(arow0), an1 = *reinterpret_cast<const uint4*>(arow0 + 16);
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
             if (m < nrt) {
-              const unsigned char* arow = abuf + (size_t)(m * kRowTile + lc) * kV2Row + 128 * q + 64 * hh;
-              f32x16_t p = {};
-#pragma unroll
-              for (int s = 0; s < 4; ++s) p = mfma_bf16(*reinterpret_cast<const uint4*>(arow + 16 * s), bq[s], p);
+              const unsigned char* arow = arow0 + (size_t)m * kRowTile * kV2Row;
+              f32x16_t p = mfma_bf16(an0, bq[0], f32x16_t{});
+              p = mfma_bf16(an1, bq[1], p);
+              const uint4 a2 = *reinterpret_cast<const uint4*>(arow + 32), a3 = *reinterpret_cast<const uint4*>(arow + 48);
+              if (m + 1 < MT) {  // unconditional at run time: every row of the tile is staged
+                an0 = *reinterpret_cast<const uint4*>(arow + (size_t)kRowTile * kV2Row);
+                an1 = *reinterpret_cast<const uint4*>(arow + (size_t)kRowTile * kV2Row + 16);
+              }
+              p = mfma_bf16(a2, bq[2], p);
+              p = mfma_bf16(a3, bq[3], p);
 #pragma unroll
               for (int i = 0; i < 16; ++i) acc[m][i] = fmaf(sc, p[i], acc[m][i]);  // (b - 128 s) A: per chunk
             }
@@ -1306,14 +1316,24 @@ __global__ __launch_bounds__(kV2Threads, 1) void k_sorted_down2(SortedArgs a) {
 #pragma unroll
           for (int s = 0; s < 4; ++s) bq[s] = unpack_codes(w4[s]);
           const float sc = SBL ? sb4_elem(sv.x, sv.y, q) : chunk_elem(ch.s0, ch.s1, 4 * ii + q);
+          // the first hi and lo operand pieces of each row block are read during
+          // the previous block's matrix chain (row blocks are tested at run time)
+          const unsigned char* ph0 = abuf + (size_t)lc * kV2Row + 128 * q + 64 * hh;
+          uint4 anh = *reinterpret_cast<const uint4*>(ph0),
+                anl = *reinterpret_cast<const uint4*>(ph0 + (size_t)kRows * kV2Row);
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
             if (m < nrt) {
-              const unsigned char* ph = abuf + (size_t)(m * kRowTile + lc) * kV2Row + 128 * q + 64 * hh;
+              const unsigned char* ph = ph0 + (size_t)m * kRowTile * kV2Row;
               const unsigned char* pl = ph + (size_t)kRows * kV2Row;
-              f32x16_t p = {};
+              f32x16_t p = mfma_bf16(anh, bq[0], f32x16_t{});
+              p = mfma_bf16(anl, bq[0], p);
+              if (m + 1 < MT) {  // unconditional at run time: every row of the tile is staged
+                anh = *reinterpret_cast<const uint4*>(ph + (size_t)kRowTile * kV2Row);
+                anl = *reinterpret_cast<const uint4*>(pl + (size_t)kRowTile * kV2Row);
+              }
 #pragma unroll
-              for (int s = 0; s < 4; ++s) {
+              for (int s = 1; s < 4; ++s) {
                 p = mfma_bf16(*reinterpret_cast<const uint4*>(ph + 16 * s), bq[s], p);
                 p = mfma_bf16(*reinterpret_cast<const uint4*>(pl + 16 * s), bq[s], p);
               }
